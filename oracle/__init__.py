@@ -1,0 +1,235 @@
+"""SharQ CPU oracle (ctypes wrapper over ``sharq_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg use this package; the product path (the HIP
+library and its Python binding) never imports it, and this package imports
+nothing from the product.
+
+The C source states each step and the reading of the SharQ abstract
+(arXiv:2606.26587, sentences 3-5 and 7) it follows.  Arrays are numpy;
+bf16 values travel as their uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+MXFP4 = 0
+NVFP4 = 1
+BLOCK = {MXFP4: 32, NVFP4: 16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sharq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# IEEE binary32 semantics: no contraction into FMA, no fast-math, single thread.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+        L.oracle_e2m1_encode.restype = ctypes.c_int
+        L.oracle_e2m1_decode.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_decode.restype = ctypes.c_double
+        L.oracle_mx_scale_exp.argtypes = [ctypes.c_double]
+        L.oracle_mx_scale_exp.restype = ctypes.c_int
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_e4m3_encode.restype = ctypes.c_int
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_tree_sum.argtypes = [P, I64]
+        L.oracle_tree_sum.restype = ctypes.c_float
+        L.oracle_nv_tensor_scale.argtypes = [ctypes.c_float]
+        L.oracle_nv_tensor_scale.restype = ctypes.c_float
+        L.oracle_rmsnorm_row.argtypes = [P, P, I64, ctypes.c_float, P]
+        L.oracle_rmsnorm_row.restype = None
+        L.oracle_mask_group.argtypes = [P, P, P]
+        L.oracle_mask_group.restype = None
+        L.oracle_normalize.argtypes = [P, I64, I64, P, ctypes.c_float, P]
+        L.oracle_normalize.restype = ctypes.c_int
+        L.oracle_residual_f32.argtypes = [ctypes.c_int, P, I64, I64, ctypes.c_float, P]
+        L.oracle_residual_f32.restype = ctypes.c_int
+        L.oracle_prepare.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_float,
+                                     P, P, P, P, P, P, P]
+        L.oracle_prepare.restype = ctypes.c_int
+        L.oracle_quantize_weight.argtypes = [ctypes.c_int, P, I64, I64, P, P, P]
+        L.oracle_quantize_weight.restype = ctypes.c_int
+        L.oracle_dual_gemm_pairs.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, I64,
+                                             P, P, I64, P, P]
+        L.oracle_dual_gemm_pairs.restype = ctypes.c_int
+        L.oracle_dual_gemm.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, I64,
+                                       P, P]
+        L.oracle_dual_gemm.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+# ---------------------------------------------------------------- codecs
+def e2m1_encode(t: float) -> int:
+    return lib().oracle_e2m1_encode(float(t))
+
+
+def e2m1_decode(code: int) -> float:
+    return lib().oracle_e2m1_decode(int(code))
+
+
+def mx_scale_exp(amax: float) -> int:
+    return lib().oracle_mx_scale_exp(float(amax))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().oracle_e4m3_encode(float(v))
+
+
+def e4m3_decode(b: int) -> float:
+    return lib().oracle_e4m3_decode(int(b))
+
+
+def bf16_to_f32(h: int) -> float:
+    return lib().oracle_bf16_to_f32(int(h))
+
+
+def f32_to_bf16(f: float) -> int:
+    return lib().oracle_f32_to_bf16(float(f))
+
+
+def tree_sum(q: np.ndarray) -> np.float32:
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    return np.float32(lib().oracle_tree_sum(_p(q), q.size))
+
+
+def nv_tensor_scale(amax: float) -> np.float32:
+    return np.float32(lib().oracle_nv_tensor_scale(float(amax)))
+
+
+def mask_group(v) -> tuple:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    assert v.size == 4
+    i0 = ctypes.c_int()
+    i1 = ctypes.c_int()
+    lib().oracle_mask_group(_p(v), ctypes.byref(i0), ctypes.byref(i1))
+    return i0.value, i1.value
+
+
+# ---------------------------------------------------------------- steps
+def normalize(x: np.ndarray, gamma: Optional[np.ndarray], eps: float = 1e-5) -> np.ndarray:
+    x = _u16(x)
+    m, k = x.shape
+    out = np.empty_like(x)
+    g = None if gamma is None else _u16(gamma)
+    lib().oracle_normalize(_p(x), m, k, _p(g), eps, _p(out))
+    return out
+
+
+def residual_f32(fmt: int, xn: np.ndarray, s_t: float = 1.0) -> np.ndarray:
+    xn = _u16(xn)
+    m, k = xn.shape
+    r = np.empty((m, k), dtype=np.float32)
+    rc = lib().oracle_residual_f32(fmt, _p(xn), m, k, float(s_t), _p(r))
+    assert rc == 0
+    return r
+
+
+def prepare(fmt: int, x: np.ndarray, gamma: Optional[np.ndarray] = None, eps: float = 1e-5,
+            dense_backbone: bool = False) -> dict:
+    """Preparation operator on X [m, k]; returns the exported arrays."""
+    x = _u16(x)
+    m, k = x.shape
+    blk = BLOCK[fmt]
+    out = {
+        "meta": np.zeros((m, k // 8), np.uint8),
+        "s_codes": np.zeros((m, k // 4), np.uint8),
+        "s_scales": np.zeros((m, k // blk), np.uint8),
+        "r_codes": np.zeros((m, k // 2), np.uint8),
+        "r_scales": np.zeros((m, k // blk), np.uint8),
+        "tensor_scale": np.ones(1, np.float32),
+    }
+    if dense_backbone:
+        out["s_dense"] = np.zeros((m, k // 2), np.uint8)
+    g = None if gamma is None else _u16(gamma)
+    rc = lib().oracle_prepare(fmt, _p(x), m, k, _p(g), eps, _p(out["meta"]), _p(out["s_codes"]),
+                              _p(out["s_scales"]), _p(out["r_codes"]), _p(out["r_scales"]),
+                              _p(out.get("s_dense")), _p(out["tensor_scale"]))
+    if rc != 0:
+        raise ValueError("oracle_prepare: bad arguments")
+    return out
+
+
+def quantize_weight(fmt: int, w: np.ndarray) -> dict:
+    w = _u16(w)
+    n, k = w.shape
+    blk = BLOCK[fmt]
+    out = {
+        "codes": np.zeros((n, k // 2), np.uint8),
+        "scales": np.zeros((n, k // blk), np.uint8),
+        "tensor_scale": np.ones(1, np.float32),
+    }
+    rc = lib().oracle_quantize_weight(fmt, _p(w), n, k, _p(out["codes"]), _p(out["scales"]),
+                                      _p(out["tensor_scale"]))
+    if rc != 0:
+        raise ValueError("oracle_quantize_weight: bad arguments")
+    return out
+
+
+def dual_gemm(fmt: int, prep: dict, wq: dict, want_f64: bool = False):
+    m = prep["r_codes"].shape[0]
+    k = prep["r_codes"].shape[1] * 2
+    n = wq["codes"].shape[0]
+    y = np.zeros((m, n), np.float32)
+    y64 = np.zeros((m, n), np.float64) if want_f64 else None
+    lib().oracle_dual_gemm(fmt, _p(prep["s_codes"]), _p(prep["meta"]), _p(prep["s_scales"]),
+                           _p(prep["r_codes"]), _p(prep["r_scales"]), _p(prep["tensor_scale"]),
+                           _p(wq["codes"]), _p(wq["scales"]), _p(wq["tensor_scale"]),
+                           m, n, k, _p(y), _p(y64))
+    return (y, y64) if want_f64 else y
+
+
+def dual_gemm_pairs(fmt: int, prep: dict, wq: dict, rows, cols, want_f64: bool = False):
+    """Y at the listed (row, col) pairs only (sorted by row is fastest)."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    k = prep["r_codes"].shape[1] * 2
+    y = np.zeros(rows.size, np.float32)
+    y64 = np.zeros(rows.size, np.float64) if want_f64 else None
+    lib().oracle_dual_gemm_pairs(fmt, _p(prep["s_codes"]), _p(prep["meta"]), _p(prep["s_scales"]),
+                                 _p(prep["r_codes"]), _p(prep["r_scales"]),
+                                 _p(prep["tensor_scale"]), _p(wq["codes"]), _p(wq["scales"]),
+                                 _p(wq["tensor_scale"]), k, _p(rows), _p(cols), rows.size,
+                                 _p(y), _p(y64))
+    return (y, y64) if want_f64 else y

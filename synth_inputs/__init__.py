@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs for the SharQ linear-layer path.
+
+This module is shared by the CPU oracle's tests and by the HIP path's tests
+and benchmark.  It holds no step of the method itself: it only draws random
+activations, weights and norm gains, and rounds them to bfloat16 bit patterns.
+
+The workloads stand in for the activations of the models evaluated in
+"SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM Inference"
+(arXiv:2606.26587), abstract, sentence 7 (Llama-3.1-8B and others).  Neither
+the weights nor the evaluation data are available, so the shapes follow
+Llama-3.1-8B's linear layers (hidden 4096, QKV 6144, MLP 14336, gate+up 28672)
+and a few channels are scaled up to model the input-dependent outliers that
+the abstract (sentence 1) says dominate FP4 block scales.
+
+Recipe (every config):
+  * ``rng = numpy.random.default_rng(seed_x)``; draw the base values in
+    float64 (``rng.standard_normal``, ``rng.standard_t`` ...);
+  * ``rng.choice(K, n_out, replace=False)`` picks the outlier channels
+    (columns k, shared by all rows), whose float64 values are multiplied by
+    the outlier factor;
+  * the float64 array is cast to float32 (round to nearest even) and then to
+    bfloat16 by round-to-nearest-even on the float32 bits.
+  * W uses its own ``default_rng(seed_w)`` and ``normal(0, 0.02, (N, K))``.
+  * gamma (when asked for a non-unit one) is ``1 + 0.1 * N(0,1)`` from
+    ``default_rng(seed_x + 500)``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+MXFP4 = 0
+NVFP4 = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    m: int
+    k: int
+    n: int
+    dist: str            # "normal" | "student_t4" | "silu_like"
+    n_outlier: int
+    outlier_scale: float
+    norm: bool
+    fmt: int
+    seed_x: int
+    seed_w: int
+
+
+# The five Llama-3.1-8B-shaped workloads (tiny check, QKV prefill, MLP down
+# prefill, decode gate+up, large NVFP4-style prefill).
+WORKLOADS = {
+    "tiny": Workload("tiny", 16, 256, 256, "normal", 4, 40.0, True, MXFP4, 1, 1001),
+    "qkv_prefill": Workload("qkv_prefill", 2048, 4096, 6144, "student_t4", 41, 50.0, True, MXFP4, 2, 1002),
+    "down_prefill": Workload("down_prefill", 2048, 14336, 4096, "silu_like", 72, 30.0, False, MXFP4, 3, 1003),
+    "decode_gate_up": Workload("decode_gate_up", 16, 4096, 28672, "student_t4", 41, 50.0, True, MXFP4, 4, 1004),
+    "nvfp4_prefill": Workload("nvfp4_prefill", 8192, 4096, 14336, "student_t4", 41, 50.0, True, NVFP4, 5, 1005),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values (finite) to bfloat16, nearest-even, as uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _base(rng: np.random.Generator, dist: str, m: int, k: int) -> np.ndarray:
+    if dist == "normal":
+        return rng.standard_normal((m, k))
+    if dist == "student_t4":
+        return rng.standard_t(4.0, (m, k))
+    if dist == "silu_like":
+        # two independent draws a * sigmoid(b); a is drawn first
+        a = rng.standard_normal((m, k))
+        b = rng.standard_normal((m, k))
+        return a / (1.0 + np.exp(-b))
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def activations(dist: str, m: int, k: int, n_outlier: int, outlier_scale: float,
+                seed: int) -> np.ndarray:
+    """bf16 bits [m, k] of a seeded activation tensor with outlier channels."""
+    rng = np.random.default_rng(seed)
+    x = _base(rng, dist, m, k)
+    if n_outlier > 0:
+        cols = rng.choice(k, n_outlier, replace=False)
+        x[:, cols] *= outlier_scale
+    return f32_to_bf16_bits(x.astype(np.float32))
+
+
+def weights(n: int, k: int, seed: int, std: float = 0.02) -> np.ndarray:
+    """bf16 bits [n, k] of a seeded N(0, std) weight matrix."""
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.normal(0.0, std, (n, k)).astype(np.float32))
+
+
+def gamma(k: int, seed: Optional[int]) -> np.ndarray:
+    """bf16 bits [k] of an RMSNorm gain: all ones when seed is None."""
+    if seed is None:
+        return f32_to_bf16_bits(np.ones(k, dtype=np.float32))
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32))
+
+
+def workload_x(w: Workload, m: Optional[int] = None) -> np.ndarray:
+    return activations(w.dist, w.m if m is None else m, w.k, w.n_outlier, w.outlier_scale, w.seed_x)
+
+
+def workload_w(w: Workload, n: Optional[int] = None) -> np.ndarray:
+    return weights(w.n if n is None else n, w.k, w.seed_w)
+
+
+def workload_gamma(w: Workload) -> Optional[np.ndarray]:
+    return gamma(w.k, None) if w.norm else None
+
+
+def outlier_count(frac: float, k: int) -> int:
+    return int(round(frac * k))

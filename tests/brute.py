@@ -1,0 +1,96 @@
+"""Brute-force restatements used to pin the CPU oracle.
+
+Each rule is stated in its defining form rather than the oracle's:
+rounding is an argmin over every code (ties to the even code), the mask is
+the lexicographically smallest valid pair, sums are exact rationals.  Values
+are numpy float32/float64; no code is shared with ``oracle/``.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_argmin(t: np.ndarray) -> np.ndarray:
+    """E2M1 codes of exact values t (float64): nearest magnitude among the 8,
+    ties to the code with mantissa bit 0, sign bit = signbit(t)."""
+    t = np.asarray(t, dtype=np.float64)
+    # every magnitude above 6 is nearest to 6; clipping keeps float64
+    # distances meaningful for huge inputs
+    a = np.minimum(np.abs(t), 16.0)[..., None]
+    d = np.abs(a - E2M1_MAGS)                        # [..., 8]
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # among tied candidates prefer an even code (mantissa bit 0)
+    even = cand & (np.arange(8) % 2 == 0)
+    pick = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    return (pick | (np.signbit(t) * 8)).astype(np.uint8)
+
+
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    code = np.asarray(code).astype(np.int64)
+    return E2M1_MAGS[code & 7] * np.where(code & 8, -1.0, 1.0)
+
+
+def e4m3_table() -> np.ndarray:
+    """Values of the 127 non-negative finite E4M3 codes 0x00..0x7E."""
+    vals = []
+    for b in range(0x7F):
+        e, m = b >> 3, b & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+E4M3_VALUES = e4m3_table()
+
+
+def e4m3_argmin(v: np.ndarray) -> np.ndarray:
+    """Nearest non-negative finite E4M3 code, ties to even mantissa; values
+    beyond the largest finite magnitude saturate to 0x7E."""
+    # every value above 448 is nearest to 448; clip to keep distances exact
+    v = np.minimum(np.asarray(v, dtype=np.float64), 1024.0)[..., None]
+    d = np.abs(v - E4M3_VALUES)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    even = cand & (np.arange(0x7F) % 2 == 0)
+    pick = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    return pick.astype(np.uint8)
+
+
+def mask_pair_brute(v) -> tuple:
+    """Among the 6 index pairs whose kept magnitudes are all >= every dropped
+    magnitude, the lexicographically smallest (i0, i1)."""
+    a = [abs(float(x)) for x in v]
+    for i0 in range(4):
+        for i1 in range(i0 + 1, 4):
+            kept = [a[i0], a[i1]]
+            dropped = [a[j] for j in range(4) if j not in (i0, i1)]
+            if min(kept) >= max(dropped):
+                return i0, i1
+    raise AssertionError("no valid pair")
+
+
+def mx_quantize_brute(v: np.ndarray):
+    """MXFP4 block (exact float64 values): scale exponent e is the one that
+    puts the block maximum into the top E2M1 binade [4, 8) (OCP MX floor
+    rule), clamped to the E8M0 range; codes by argmin on v / 2^e."""
+    v = np.asarray(v, dtype=np.float64)
+    amax = float(np.abs(v).max())
+    if amax == 0.0:
+        e = -127
+    else:
+        e = -200
+        while amax / 2.0 ** e >= 8.0:      # first e with amax / 2^e < 8
+            e += 1
+        # amax / 2^(e-1) >= 8, so amax / 2^e lies in [4, 8)
+        assert 4.0 <= amax / 2.0 ** e < 8.0
+        e = max(-127, min(127, e))
+    codes = e2m1_argmin(v / 2.0 ** e)
+    return codes, e + 127, e2m1_value(codes) * 2.0 ** e
+
+
+def fraction_dot(a, b) -> Fraction:
+    return sum((Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a, b)), Fraction(0))
