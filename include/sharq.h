@@ -1,0 +1,196 @@
+/*
+ * sharq.h - C ABI of the SharQ linear-layer hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "SharQ: Bridging Activation Sparsity and FP4
+ * Quantization for LLM Inference" (arXiv:2606.26587), abstract:
+ *   - sentence 3: per activation tensor, an input-adaptive N:M mask extracts an
+ *     outlier-dominated sparse backbone that is quantized to FP4, and a dense
+ *     residual is formed against the QUANTIZED backbone;
+ *   - sentence 4: a sparse-path FP4 GEMM on the backbone plus a dense-path FP4
+ *     GEMM on the residual;
+ *   - sentence 5: both paths read one FP4 weight payload through path-specific
+ *     scale views; one fused preparation operator does the layer
+ *     normalization, mask generation and residual construction;
+ *   - sentence 7: MXFP4 and NVFP4 formats.
+ * Concrete readings (2:4 along K, RMSNorm, block sizes, rounding) are stated
+ * at each entry point.
+ *
+ * Conventions for every entry point:
+ *   - All matrices are row-major, K contiguous.  X is [m, k] bf16, W is
+ *     [n, k] bf16, Y = X * W^T is [m, n] fp32.  bf16 values are passed as
+ *     their uint16 bit patterns.
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     allocates nothing, keeps no state between calls and never synchronizes.
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and is complete when the stream is.
+ *   - Leading dimensions (`ld_*`) are in elements of the array they describe
+ *     (bytes for uint8 arrays).
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued.  A launch failure reported by the HIP runtime
+ *     returns SHARQ_ERR_DEVICE; faults inside kernels surface at the caller's
+ *     next synchronization.  No C++ exception crosses this interface.
+ *   - Inputs must be finite (no NaN or Inf).
+ *   - Calls on different streams that write the same buffers race.
+ */
+#ifndef SHARQ_H
+#define SHARQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SHARQ_OK = 0,
+    SHARQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    SHARQ_ERR_SHAPE = 2,       /* a size, leading dimension or view pairing is invalid */
+    SHARQ_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned */
+    SHARQ_ERR_UNSUPPORTED = 4, /* valid request this build or the ISA cannot serve */
+    SHARQ_ERR_DEVICE = 5       /* the HIP runtime reported an error at launch */
+} sharq_status;
+
+typedef enum {
+    /* E2M1 elements, one E8M0 scale (2^(byte-127)) per 32 consecutive k (OCP MX v1.0) */
+    SHARQ_MXFP4 = 0,
+    /* E2M1 elements, one E4M3 scale per 16 consecutive k, and one fp32 tensor scale */
+    SHARQ_NVFP4 = 1
+} sharq_format;
+
+typedef enum {
+    SHARQ_GEMM_AUTO = 0,           /* the default variant for the format */
+    SHARQ_GEMM_DECOMPRESS = 1,     /* backbone expanded from its 2:4 form to dense FP4 while staged in LDS */
+    SHARQ_GEMM_DENSE_EXPANDED = 2, /* backbone read from the dense view written by sharq_prepare */
+    SHARQ_GEMM_SPARSE_MFMA = 3     /* backbone on the structured-sparse MFMA (see sharq_dual_gemm) */
+} sharq_gemm_variant;
+
+/* Which array sharq_bytes sizes. */
+enum {
+    SHARQ_BYTES_DENSE_CODES = 0,   /* dense FP4 codes: rows x k/2 */
+    SHARQ_BYTES_SPARSE_CODES = 1,  /* 2:4-compressed backbone codes: rows x k/4 */
+    SHARQ_BYTES_META = 2,          /* 2:4 indices: rows x k/8 */
+    SHARQ_BYTES_SCALES = 3         /* block scales: rows x k/32 (MX) or k/16 (NV) */
+};
+
+/*
+ * One FP4 operand view.  Rows are K-contiguous; all pointers are device pointers.
+ *
+ *   codes        dense operand: [rows, k/2], two E2M1 codes per byte, the lower
+ *                k in the low nibble.  2:4 backbone: [rows, k/4], one byte per
+ *                group of four k: the code of the lower kept index in the low
+ *                nibble, the code of the higher kept index in the high nibble.
+ *   meta         backbone only (else NULL): [rows, k/8]; per group of four k the
+ *                nibble i0 | i1 << 2 (kept indices, i0 < i1); group 2j sits in
+ *                the low nibble of byte j.
+ *   scales       [rows, k/32] E8M0 bytes (MXFP4) or [rows, k/16] E4M3 bytes (NVFP4).
+ *   dense_codes  optional backbone in the dense layout of `codes` (zeros at the
+ *                dropped positions); written by sharq_prepare when non-NULL and
+ *                read by SHARQ_GEMM_DENSE_EXPANDED.  NULL otherwise.
+ *   tensor_scale NVFP4: device float[2]; [0] is the fp32 tensor scale, [1] is
+ *                the amax the library reduces into while computing it.  MXFP4: NULL.
+ */
+typedef struct sharq_fp4_view {
+    uint8_t *codes;
+    int64_t ld_codes;
+    uint8_t *meta;
+    int64_t ld_meta;
+    uint8_t *scales;
+    int64_t ld_scales;
+    uint8_t *dense_codes;
+    int64_t ld_dense;
+    float *tensor_scale;
+} sharq_fp4_view;
+
+/*
+ * Quantize a weight matrix W [n, k] (bf16, row stride ld_w) to one FP4
+ * payload (abstract, sentence 5: a single FP4 weight payload serves both
+ * GEMM paths).  Each row is split into blocks of 32 (MX) or 16 (NV) along k:
+ *   MXFP4: scale exponent e = floor(log2(amax)) - 2 clamped to [-127, 127]
+ *          (e = -127 when amax = 0), byte e + 127; codes are E2M1 of w * 2^-e,
+ *          round to nearest, ties to even, saturating at 6; the sign of zero
+ *          is kept.
+ *   NVFP4: tensor scale s_t = amax(W) / 2688 (1 when W is all zero), block
+ *          scale byte = E4M3(amax_block / (6 s_t)) (nearest even, saturating
+ *          at 448), S = e4m3(byte) * s_t, codes = E2M1(w / S); every step is
+ *          one fp32 operation.
+ * Writes w_out->codes [n, k/2], w_out->scales, and for NVFP4
+ * w_out->tensor_scale[0..1].  meta and dense_codes are ignored.
+ * Requirements: n >= 1, k >= 32, k % 32 == 0, ld_w >= k, ld_w % 8 == 0;
+ * w_bf16 and codes 16-byte aligned; ld_codes >= k/2 and % 16 == 0;
+ * ld_scales >= k/blk; NVFP4: scales 2-byte aligned and ld_scales even.
+ */
+sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int64_t n,
+                                   int64_t k, int64_t ld_w, const sharq_fp4_view *w_out,
+                                   void *stream);
+
+/*
+ * The fused preparation operator (abstract, sentences 3 and 5), one HBM pass
+ * over X [m, k] (bf16, row stride ld_x):
+ *   1. RMSNorm when gamma_bf16 != NULL: ss = sum of x^2 as a perfect binary
+ *      tree of fp32 additions over 2^ceil(log2 k) leaves (missing leaves 0,
+ *      adjacent pairs); r = 1 / sqrt(ss / k + eps) with IEEE division and
+ *      square root; x_n = bf16((x * r) * gamma).  gamma_bf16 == NULL: x_n = x.
+ *   2. 2:4 mask: in every aligned group of four k keep the two largest |x_n|,
+ *      the lower index first on ties.
+ *   3. Backbone = x_n at kept positions, +0 elsewhere, quantized per block
+ *      exactly as sharq_quantize_weight quantizes a weight row (NVFP4: with
+ *      the activation tensor scale s_t = amax(x_n) / 2688, computed on the
+ *      device by a reduction pass before the preparation pass).
+ *   4. Residual R = x_n - deq(backbone) in fp32 (exact), quantized the same way
+ *      (NVFP4: same s_t).
+ * Outputs: sparse_out->codes (2:4-compressed), ->meta, ->scales and, when
+ * non-NULL, ->dense_codes; resid_out->codes (dense) and ->scales; NVFP4:
+ * sparse_out->tensor_scale[0..1] (resid_out->tensor_scale must be NULL or the
+ * same pointer: one tensor scale serves both paths).
+ * Requirements: m >= 1; k >= 32, k % 32 == 0; k <= 16384 when gamma is given;
+ * ld_x >= k, ld_x % 8 == 0; x 16-byte aligned; sparse codes 8-byte aligned with
+ * ld % 8 == 0; meta 4-byte aligned with ld % 4 == 0; residual codes and
+ * dense_codes 16-byte aligned with ld % 16 == 0; NVFP4 scales 2-byte aligned
+ * with even ld; every ld at least the row length it describes.
+ */
+sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
+                           int64_t ld_x, const uint16_t *gamma_bf16, float eps,
+                           const sharq_fp4_view *sparse_out, const sharq_fp4_view *resid_out,
+                           void *stream);
+
+/*
+ * Dual-path GEMM (abstract, sentences 4 and 5):
+ *   Y = deq(backbone) * deq(W)^T + deq(residual) * deq(W)^T
+ * accumulated in fp32 and stored as fp32 [m, n] (row stride ld_y).  NVFP4:
+ * block values are exact (E2M1 x E4M3) and the two tensor scales are applied
+ * to the fp32 sum.
+ * The weight is passed as two views of ONE payload: w_sparse_view->codes must
+ * equal w_dense_view->codes (otherwise SHARQ_ERR_SHAPE); each view brings its
+ * own scales pointer (the path-specific scale view; for MXFP4 the values must
+ * be the weight's scales, and both usually alias one buffer).
+ * Variants: AUTO and DECOMPRESS read the 2:4 backbone (codes + meta);
+ * DENSE_EXPANDED reads sparse->dense_codes instead.  SPARSE_MFMA: gfx950 has
+ * no structured-sparse MFMA for FP4 operands, so it returns
+ * SHARQ_ERR_UNSUPPORTED for MXFP4.
+ * Requirements: m, n >= 1; k >= 128, k % 128 == 0; ld_y >= n; codes 16-byte
+ * aligned with ld % 16 == 0 (backbone codes too;
+ * meta ld % 8 == 0 and 8-byte aligned); scales 4-byte aligned with ld % 4 == 0;
+ * y 4-byte aligned.
+ */
+sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sparse,
+                             const sharq_fp4_view *resid, const sharq_fp4_view *w_sparse_view,
+                             const sharq_fp4_view *w_dense_view, int64_t m, int64_t n, int64_t k,
+                             float *y, int64_t ld_y, sharq_gemm_variant variant, void *stream);
+
+/* Bytes of one packed array (`which` = SHARQ_BYTES_*) for `rows` rows of length k; 0 if invalid. */
+size_t sharq_bytes(sharq_format fmt, int which, int64_t rows, int64_t k);
+
+/* Static, NUL-terminated description of a status code. */
+const char *sharq_status_str(sharq_status status);
+
+/* ABI version of this header (increments on any incompatible change). */
+int sharq_abi_version(void);
+
+#define SHARQ_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARQ_H */

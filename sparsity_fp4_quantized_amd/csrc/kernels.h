@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (sharq_abi.cpp) and the HIP
+// kernels.  Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sharq {
+
+struct PrepArgs {
+  const uint16_t *x;
+  int64_t ld_x, m, k;
+  const uint16_t *gamma;   // nullptr: no normalization
+  float eps;
+  uint8_t *s_codes;  int64_t ld_sc;
+  uint8_t *meta;     int64_t ld_meta;
+  uint8_t *s_scales; int64_t ld_ss;
+  uint8_t *r_codes;  int64_t ld_rc;
+  uint8_t *r_scales; int64_t ld_rs;
+  uint8_t *s_dense;  int64_t ld_sd;   // optional
+  float *tensor_scale;                // NVFP4: [0] scale, [1] amax
+};
+
+struct QuantArgs {
+  const uint16_t *w;
+  int64_t ld_w, n, k;
+  uint8_t *codes;  int64_t ld_c;
+  uint8_t *scales; int64_t ld_s;
+  float *tensor_scale;                // NVFP4
+};
+
+struct GemmArgs {
+  const uint8_t *s_codes;  int64_t ld_sc;   // 2:4 backbone [m, k/4]
+  const uint8_t *meta;     int64_t ld_meta; // [m, k/8]
+  const uint8_t *s_dense;  int64_t ld_sd;   // dense backbone [m, k/2] (DENSE_EXPANDED)
+  const uint8_t *s_scales; int64_t ld_ss;
+  const uint8_t *r_codes;  int64_t ld_rc;
+  const uint8_t *r_scales; int64_t ld_rs;
+  const uint8_t *w_codes;  int64_t ld_wc;
+  const uint8_t *ws_scales; int64_t ld_wss; // sparse-path scale view of W
+  const uint8_t *wd_scales; int64_t ld_wds; // dense-path scale view of W
+  const float *a_tensor_scale;              // NVFP4
+  const float *w_tensor_scale;              // NVFP4
+  float *y;                int64_t ld_y;
+  int64_t m, n, k;
+};
+
+hipError_t launch_prepare_mx(const PrepArgs &a, hipStream_t s);
+hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s);
+hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s);
+hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s);
+hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s);
+hipError_t launch_dual_gemm_nv(const GemmArgs &a, int variant, hipStream_t s);
+
+}  // namespace sharq

@@ -64,9 +64,12 @@ WORKLOADS = {
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values (finite) to bfloat16, nearest-even, as uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    u = a.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    lsb += np.uint32(0x7FFF)
+    lsb += u                      # no wrap-around for finite inputs
+    lsb >>= np.uint32(16)
+    return lsb.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

@@ -1,0 +1,127 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid requests before any HIP call (every
+request here fails validation, so nothing reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparsity_fp4_quantized_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "sharq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sharq_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    L = sq.lib()
+    names = header_functions()
+    assert set(names) == set(sq.EXPORTS), names
+    for name in names:
+        assert hasattr(L, name), name
+    assert L.sharq_abi_version() == sq.ABI_VERSION
+
+
+def test_status_strings_and_sizes():
+    for s in range(6):
+        assert sq.status_str(s)
+    assert sq.status_str(99) == "unknown status"
+    assert sq.nbytes(sq.MXFP4, sq.BYTES_DENSE_CODES, 16, 256) == 16 * 128
+    assert sq.nbytes(sq.MXFP4, sq.BYTES_SPARSE_CODES, 16, 256) == 16 * 64
+    assert sq.nbytes(sq.MXFP4, sq.BYTES_META, 16, 256) == 16 * 32
+    assert sq.nbytes(sq.MXFP4, sq.BYTES_SCALES, 16, 256) == 16 * 8
+    assert sq.nbytes(sq.NVFP4, sq.BYTES_SCALES, 16, 256) == 16 * 16
+    assert sq.nbytes(sq.MXFP4, 9, 16, 256) == 0
+    assert sq.nbytes(sq.MXFP4, 0, 16, 100) == 0
+
+
+FAKE = 1 << 20     # aligned, never dereferenced: validation fails first
+
+
+def view(codes=FAKE, ld_codes=128, meta=FAKE, ld_meta=32, scales=FAKE, ld_scales=8,
+         dense=None, ld_dense=0, ts=None):
+    v = sq.FP4ViewC()
+    v.codes, v.ld_codes, v.meta, v.ld_meta = codes, ld_codes, meta, ld_meta
+    v.scales, v.ld_scales, v.dense_codes, v.ld_dense, v.tensor_scale = scales, ld_scales, dense, ld_dense, ts
+    return v
+
+
+def prep(fmt=0, x=FAKE, m=16, k=256, ld_x=256, gamma=None, sp=None, rs=None):
+    sp = sp or view(ld_codes=64)
+    rs = rs or view(meta=None)
+    return sq.lib().sharq_prepare(fmt, x, m, k, ld_x, gamma, 1e-5, ctypes.byref(sp),
+                                  ctypes.byref(rs), None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=None), sq.ERR_NULL),
+    (dict(m=0), sq.ERR_SHAPE),
+    (dict(k=100, ld_x=100), sq.ERR_SHAPE),
+    (dict(k=0), sq.ERR_SHAPE),
+    (dict(ld_x=128), sq.ERR_SHAPE),
+    (dict(ld_x=260), sq.ERR_ALIGN),
+    (dict(x=FAKE + 2), sq.ERR_ALIGN),
+    (dict(k=32768, ld_x=32768, gamma=FAKE), sq.ERR_UNSUPPORTED),
+    (dict(fmt=7), sq.ERR_UNSUPPORTED),
+    (dict(sp=view(ld_codes=63)), sq.ERR_SHAPE),
+    (dict(sp=view(ld_codes=64, meta=None)), sq.ERR_NULL),
+    (dict(sp=view(ld_codes=64, meta=FAKE + 1)), sq.ERR_ALIGN),
+    (dict(rs=view(meta=None, codes=FAKE + 8)), sq.ERR_ALIGN),
+    (dict(rs=view(meta=None, scales=None)), sq.ERR_NULL),
+    (dict(fmt=1), sq.ERR_SHAPE),           # NVFP4 needs k/16 scales per row
+    (dict(fmt=1, sp=view(ld_codes=64, ld_scales=16), rs=view(meta=None, ld_scales=16)),
+     sq.ERR_NULL),                         # NVFP4 without a tensor-scale buffer
+])
+def test_prepare_validation(kwargs, status):
+    assert prep(**kwargs) == status
+
+
+def gemm(fmt=0, m=16, n=256, k=256, y=FAKE, ld_y=256, variant=0, sp=None, rs=None, ws=None,
+         wd=None):
+    sp = sp or view(ld_codes=64)
+    rs = rs or view(meta=None)
+    ws = ws or view(meta=None)
+    wd = wd or view(meta=None)
+    return sq.lib().sharq_dual_gemm(fmt, ctypes.byref(sp), ctypes.byref(rs), ctypes.byref(ws),
+                                    ctypes.byref(wd), m, n, k, y, ld_y, variant, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(y=None), sq.ERR_NULL),
+    (dict(k=192), sq.ERR_SHAPE),
+    (dict(n=0), sq.ERR_SHAPE),
+    (dict(ld_y=100), sq.ERR_SHAPE),
+    (dict(wd=view(meta=None, codes=FAKE + 4096)), sq.ERR_SHAPE),   # two payloads
+    (dict(variant=sq.GEMM_SPARSE_MFMA), sq.ERR_UNSUPPORTED),
+    (dict(variant=9), sq.ERR_UNSUPPORTED),
+    (dict(variant=sq.GEMM_DENSE_EXPANDED), sq.ERR_NULL),
+    (dict(rs=view(meta=None, scales=FAKE + 2)), sq.ERR_ALIGN),
+    (dict(sp=view(ld_codes=64, ld_scales=6)), sq.ERR_SHAPE),
+    (dict(sp=view(ld_codes=72)), sq.ERR_ALIGN),
+    (dict(y=FAKE + 1), sq.ERR_ALIGN),
+    (dict(fmt=1), sq.ERR_SHAPE),      # NVFP4 needs k/16 scales per row (ld 8 < 16)
+])
+def test_gemm_validation(kwargs, status):
+    assert gemm(**kwargs) == status
+
+
+def test_quantize_weight_validation():
+    L = sq.lib()
+    v = view(meta=None)
+    assert L.sharq_quantize_weight(0, None, 16, 256, 256, ctypes.byref(v), None) == sq.ERR_NULL
+    assert L.sharq_quantize_weight(0, FAKE, 16, 48, 48, ctypes.byref(v), None) == sq.ERR_SHAPE
+    assert L.sharq_quantize_weight(0, FAKE, 0, 256, 256, ctypes.byref(v), None) == sq.ERR_SHAPE
+    assert L.sharq_quantize_weight(0, FAKE + 4, 16, 256, 256, ctypes.byref(v), None) == sq.ERR_ALIGN
+    nv = view(meta=None, ld_scales=16)
+    assert L.sharq_quantize_weight(1, FAKE, 16, 256, 256, ctypes.byref(nv), None) == sq.ERR_NULL
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(sq, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(sq, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        sq.lib()

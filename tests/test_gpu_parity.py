@@ -1,0 +1,248 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
+
+Masks, FP4 codes and scales must be byte-identical; GEMM outputs must be
+within 1e-3 of the oracle's, normwise (max |dY| / max |Y|), the bound the
+SharQ path is built to; where the product is exact in fp32 the GEMM must match
+bit for bit.  Every call goes through the C ABI in include/sharq.h.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import sparsity_fp4_quantized_amd as sq  # noqa: E402
+
+DEV = "cuda:0"
+GEMM_TOL = 1e-3
+
+
+def dev16(bits: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV)
+
+
+def host(t) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_prep(fmt, x_bits, gamma_bits, eps=1e-5, dense=True, label=""):
+    ref = oracle.prepare(fmt, x_bits, gamma_bits, eps, dense_backbone=True)
+    sp, rs = sq.prepare(dev16(x_bits), None if gamma_bits is None else dev16(gamma_bits), eps,
+                        fmt=fmt, dense_backbone=dense)
+    got = {"meta": host(sp.meta), "s_codes": host(sp.codes), "s_scales": host(sp.scales),
+           "r_codes": host(rs.codes), "r_scales": host(rs.scales)}
+    if dense:
+        got["s_dense"] = host(sp.dense_codes)
+    for key, val in got.items():
+        want = ref[key]
+        if not np.array_equal(val, want):
+            bad = np.argwhere(val != want)
+            r, c = bad[0]
+            raise AssertionError(f"{label} {key}: {len(bad)} bytes differ; first at row {r} col {c}: "
+                                 f"gpu {val[r, c]:#04x} oracle {want[r, c]:#04x}")
+    if fmt == sq.NVFP4:
+        ts = host(sp.tensor_scale)
+        assert ts[0] == ref["tensor_scale"][0], (label, ts, ref["tensor_scale"])
+    return ref, sp, rs
+
+
+def to_dev_prep(fmt, p):
+    """Oracle preparation outputs as device FP4 tensors (GEMM-only tests)."""
+    m, kq = p["s_codes"].shape
+    k = kq * 4
+    sp = sq.FP4Tensor(fmt, m, k, torch.from_numpy(p["s_codes"]).to(DEV),
+                      torch.from_numpy(p["s_scales"]).to(DEV),
+                      meta=torch.from_numpy(p["meta"]).to(DEV))
+    if "s_dense" in p:
+        sp.dense_codes = torch.from_numpy(p["s_dense"]).to(DEV)
+    rs = sq.FP4Tensor(fmt, m, k, torch.from_numpy(p["r_codes"]).to(DEV),
+                      torch.from_numpy(p["r_scales"]).to(DEV))
+    if fmt == sq.NVFP4:
+        ts = torch.tensor([p["tensor_scale"][0], 0.0], dtype=torch.float32, device=DEV)
+        sp.tensor_scale = ts
+        rs.tensor_scale = ts
+    return sp, rs
+
+
+def normwise(y, ref):
+    den = np.abs(ref).max()
+    return float(np.abs(y - ref).max() / (den if den > 0 else 1.0))
+
+
+# ------------------------------------------------------------ preparation
+@pytest.mark.parametrize("m,k,norm", [
+    (1, 32, True), (5, 96, True), (7, 256, True), (37, 1024, True), (4, 4096, True),
+    (3, 14336, True), (9, 16384, True), (6, 32, False), (13, 14336, False), (2, 65536, False),
+])
+def test_prepare_mx_shapes(m, k, norm):
+    x = si.activations("student_t4", m, k, max(1, k // 100), 50.0, seed=m * 1000 + k)
+    g = si.gamma(k, seed=k) if norm else None
+    check_prep(sq.MXFP4, x, g, label=f"m{m} k{k} norm{norm}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "qkv_prefill", "down_prefill", "decode_gate_up"])
+def test_prepare_mx_workloads(name):
+    w = si.WORKLOADS[name]
+    check_prep(sq.MXFP4, si.workload_x(w), si.workload_gamma(w), label=name)
+
+
+def test_prepare_mx_degenerate_rows():
+    k = 256
+    x = np.zeros((6, k), np.float32)
+    x[1, 7] = -1000.0                 # a single outlier
+    x[2] = -0.0                       # signed zeros
+    x[3] = 1.0                        # all ties
+    x[4, ::3] = 3e-39                 # fp32-subnormal squares underflow
+    x[5] = np.tile([2.0, -2.0, 2.0, 1.0], k // 4)
+    xb = si.f32_to_bf16_bits(x)
+    check_prep(sq.MXFP4, xb, None, label="degenerate no-norm")
+    check_prep(sq.MXFP4, xb, si.gamma(k, None), label="degenerate norm")
+
+
+def test_prepare_padded_row_stride():
+    m, k, ld = 10, 512, 640
+    x = si.activations("normal", m, ld, 3, 40.0, seed=77)
+    g = si.gamma(k, seed=5)
+    xt = dev16(x)[:, :k]
+    assert xt.stride(0) == ld
+    sp, rs = sq.prepare(xt, dev16(g), 1e-5)
+    ref = oracle.prepare(sq.MXFP4, np.ascontiguousarray(x[:, :k]), g)
+    assert np.array_equal(host(sp.codes), ref["s_codes"])
+    assert np.array_equal(host(rs.codes), ref["r_codes"])
+    assert np.array_equal(host(sp.meta), ref["meta"])
+
+
+def test_prepare_nv_small():
+    for m, k, norm in [(3, 64, True), (17, 512, False), (8, 4096, True)]:
+        x = si.activations("student_t4", m, k, 2, 50.0, seed=31 + k)
+        check_prep(sq.NVFP4, x, si.gamma(k, 3) if norm else None, label=f"nv m{m} k{k}")
+
+
+def test_prepare_nv_workload():
+    w = si.WORKLOADS["nvfp4_prefill"]
+    check_prep(sq.NVFP4, si.workload_x(w), si.workload_gamma(w), label="nvfp4_prefill")
+
+
+def test_prepare_deterministic():
+    w = si.WORKLOADS["qkv_prefill"]
+    x = dev16(si.workload_x(w, m=512))
+    g = dev16(si.workload_gamma(w))
+    a = sq.prepare(x, g)
+    b = sq.prepare(x, g)
+    for t1, t2 in [(a[0].codes, b[0].codes), (a[0].meta, b[0].meta), (a[1].codes, b[1].codes)]:
+        assert torch.equal(t1, t2)
+
+
+# ------------------------------------------------------------ weights
+@pytest.mark.parametrize("fmt,n,k", [(0, 256, 256), (0, 6144, 4096), (0, 33, 96), (1, 256, 256),
+                                     (1, 1000, 4096)])
+def test_quantize_weight(fmt, n, k):
+    w = si.weights(n, k, seed=n + k)
+    ref = oracle.quantize_weight(fmt, w)
+    got = sq.quantize_weight(dev16(w), fmt)
+    assert np.array_equal(host(got.codes), ref["codes"])
+    assert np.array_equal(host(got.scales), ref["scales"])
+    if fmt == sq.NVFP4:
+        assert host(got.tensor_scale)[0] == ref["tensor_scale"][0]
+
+
+# ------------------------------------------------------------ GEMM
+def _gemm_case(m, n, k, seed, fmt=sq.MXFP4, norm=True):
+    x = si.activations("student_t4", m, k, max(1, k // 100), 50.0, seed=seed)
+    w = si.weights(n, k, seed=seed + 1)
+    g = si.gamma(k, seed + 2) if norm else None
+    p = oracle.prepare(fmt, x, g, dense_backbone=True)
+    q = oracle.quantize_weight(fmt, w)
+    return x, w, g, p, q
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 256, 256), (37, 75, 256), (130, 200, 384), (1, 1, 128),
+                                   (257, 129, 1024), (64, 512, 4096)])
+def test_dual_gemm_mx_vs_oracle(m, n, k):
+    x, w, g, p, q = _gemm_case(m, n, k, seed=m + 7 * n + k)
+    ref = oracle.dual_gemm(sq.MXFP4, p, q)
+    sp, rs = to_dev_prep(sq.MXFP4, p)
+    wq = sq.FP4Tensor(sq.MXFP4, n, k, torch.from_numpy(q["codes"]).to(DEV),
+                      torch.from_numpy(q["scales"]).to(DEV))
+    for variant in (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED):
+        y = host(sq.dual_gemm(sp, rs, wq, variant=variant))
+        err = normwise(y, ref)
+        assert err <= GEMM_TOL, (variant, err)
+
+
+def test_dual_gemm_variants_bitwise_equal():
+    x, w, g, p, q = _gemm_case(200, 300, 512, seed=3)
+    sp, rs = to_dev_prep(sq.MXFP4, p)
+    wq = sq.FP4Tensor(sq.MXFP4, 300, 512, torch.from_numpy(q["codes"]).to(DEV),
+                      torch.from_numpy(q["scales"]).to(DEV))
+    a = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS)
+    b = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DENSE_EXPANDED)
+    c = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS)
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_dual_gemm_exact_special_case():
+    """2:4-sparse FP4-representable X and FP4 W: the product is exact in fp32,
+    so the GPU must match the oracle bit for bit."""
+    rng = np.random.default_rng(5)
+    m, k, n = 64, 256, 96
+    from brute import e2m1_value
+    xv = e2m1_value(rng.integers(0, 16, (m, k)))
+    for i in range(m):
+        for gi in range(k // 4):
+            xv[i, 4 * gi + rng.choice(4, 2, replace=False)] = 0.0
+    xv = np.where(xv == 0, 0.0, xv) * 2.0 ** rng.integers(-3, 3, (m, 1))
+    wv = e2m1_value(rng.integers(0, 16, (n, k))) * 2.0 ** rng.integers(-8, -4, (n, 1))
+    xb = si.f32_to_bf16_bits(xv.astype(np.float32))
+    wb = si.f32_to_bf16_bits(wv.astype(np.float32))
+    p = oracle.prepare(sq.MXFP4, xb, None)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    ref = oracle.dual_gemm(sq.MXFP4, p, q)
+    assert (ref == (xv @ wv.T).astype(np.float32)).all()
+    sp, rs = sq.prepare(dev16(xb), None)
+    wq = sq.quantize_weight(dev16(wb))
+    y = host(sq.dual_gemm(sp, rs, wq))
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("name,samples", [("tiny", None), ("qkv_prefill", 4096),
+                                          ("down_prefill", 4096), ("decode_gate_up", 8192)])
+def test_end_to_end_workloads(name, samples):
+    """prepare + dual GEMM on the GPU vs the oracle's, at the full workload size
+    (sampled outputs for the large ones)."""
+    w = si.WORKLOADS[name]
+    x, W, g = si.workload_x(w), si.workload_w(w), si.workload_gamma(w)
+    p = oracle.prepare(sq.MXFP4, x, g)
+    q = oracle.quantize_weight(sq.MXFP4, W)
+    sp, rs = sq.prepare(dev16(x), None if g is None else dev16(g))
+    wq = sq.quantize_weight(dev16(W))
+    y = host(sq.dual_gemm(sp, rs, wq))
+    if samples is None:
+        ref = oracle.dual_gemm(sq.MXFP4, p, q)
+        assert normwise(y, ref) <= GEMM_TOL
+        return
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.integers(0, w.m, samples))
+    cols = rng.integers(0, w.n, samples)
+    rows[:4] = [0, 0, w.m - 1, w.m - 1]
+    cols[:4] = [0, w.n - 1, 0, w.n - 1]
+    order = np.argsort(rows, kind="stable")
+    rows, cols = rows[order], cols[order]
+    ref = oracle.dual_gemm_pairs(sq.MXFP4, p, q, rows, cols)
+    got = y[rows, cols]
+    # normalize by the largest |Y| over the sample (the full max is at least this)
+    assert normwise(got, ref) <= GEMM_TOL
+
+
+def test_sparse_mfma_unsupported_for_mxfp4():
+    x, w, g, p, q = _gemm_case(16, 128, 128, seed=9)
+    sp, rs = to_dev_prep(sq.MXFP4, p)
+    wq = sq.FP4Tensor(sq.MXFP4, 128, 128, torch.from_numpy(q["codes"]).to(DEV),
+                      torch.from_numpy(q["scales"]).to(DEV))
+    with pytest.raises(sq.SharqError) as e:
+        sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA)
+    assert e.value.status == sq.ERR_UNSUPPORTED
