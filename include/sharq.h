@@ -164,8 +164,9 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
  * equal w_dense_view->codes (otherwise SHARQ_ERR_SHAPE); each view brings its
  * own scales pointer (the path-specific scale view; for MXFP4 the values must
  * be the weight's scales, and both usually alias one buffer).
- * Variants: AUTO and DECOMPRESS read the 2:4 backbone (codes + meta);
- * DENSE_EXPANDED reads sparse->dense_codes instead.  SPARSE_MFMA: gfx950 has
+ * Variants: DECOMPRESS reads the 2:4 backbone (codes + meta) and expands it
+ * while staging; DENSE_EXPANDED reads sparse->dense_codes instead; AUTO is
+ * DENSE_EXPANDED when sparse->dense_codes is non-NULL, else DECOMPRESS.  SPARSE_MFMA: gfx950 has
  * no structured-sparse MFMA for FP4 operands, so it returns
  * SHARQ_ERR_UNSUPPORTED for MXFP4.
  * Requirements: m, n >= 1; k >= 128, k % 128 == 0; ld_y >= n; codes 16-byte

@@ -11,16 +11,28 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 (E2M1) A and B operands and one
 // E8M0 scale per 32 k per row and per column.  gfx950 has no structured-sparse
 // MFMA for FP4 operands, so the 2:4 backbone is expanded to dense FP4 (zeros
-// at the dropped positions) while it is staged into LDS.  Each K step stages
-// the W tile once and feeds it to the MFMAs of both paths, which accumulate
-// into the same registers.
+// at the dropped positions) while it is staged into LDS (or, in the
+// dense-expanded variant, read in the dense layout the preparation wrote).
+// Each K step stages the W tile once and feeds it to the MFMAs of both paths,
+// which accumulate into the same registers.
+//
+// Tiling: a workgroup of 8 wavefronts (2 per SIMD) owns a BM x BN tile of Y
+// (BM = 256); wavefront (wm, wn) of the 4 x 2 grid owns 64 rows x BN/2
+// columns, i.e. 2 x BN/64 MFMA tiles of 32 x 32.  K advances 128 per step
+// (one 32-bit word of four E8M0 scales per row).  The LDS holds two stages;
+// global loads of step k+1 are issued before the MFMAs of step k and written
+// to the other stage after them, with one barrier per step.  LDS rows are 64
+// bytes (four 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3),
+// so sixteen lanes reading one chunk of sixteen consecutive rows hit sixteen
+// different bank groups.
 //
 // Operand layout of the 32x32x64 FP4 MFMA (lane l, h = l / 32): A row l % 32
-// and B column l % 32, 32 consecutive k (16 bytes) per lane and MFMA; the E8M0
-// scale of that lane's 32 k comes from the lane's scale register.  Within a
-// 128-k step, lane half h takes the k blocks 2h (first MFMA) and 2h + 1
-// (second MFMA); A and B use the same assignment, so the dot products are
-// unchanged.
+// and B column l % 32, 32 consecutive k (16 bytes) per lane; the lane's scale
+// register holds the E8M0 byte of those k.  Within a 128-k step lane half h
+// takes the k blocks 2h (first MFMA) and 2h + 1 (second MFMA); A and B use the
+// same assignment, so the dot products are unchanged.  The row's scale word
+// is shifted right by 16h once and op_sel picks byte 0 or 1.
+// Accumulator: lane l holds column l % 32, rows 8 (r / 4) + 4 h + r % 4.
 #include "fp4_device.h"
 #include "kernels.h"
 
@@ -29,170 +41,491 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+// clang vector types (not HIP's uint4 struct) so that staged data stays in registers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kStride = 80;   // LDS bytes per tile row: 64 bytes of codes + 16 pad
+constexpr int BM = 256, BK = 128;
+constexpr int kThreads = 512;
 
-__device__ __forceinline__ v8i as_operand(uint4 v) {
+__device__ __forceinline__ v8i as_operand(u32x4 v) {
   v8i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   return r;
 }
 
+// 16-byte slot of logical chunk c of tile row r (tile rows are 64 bytes)
+__device__ __forceinline__ int lds_slot(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
 // Expand eight 2:4 groups (8 code bytes, 4 meta bytes) into 32 dense codes.
-__device__ __forceinline__ void expand8(uint2 codes, uint32_t meta, uint32_t out[4]) {
+__device__ __forceinline__ void expand8(uint32_t c_lo, uint32_t c_hi, uint32_t meta, uint32_t out[4]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t word = 0;
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
-      int g = 2 * q + gg;
-      uint32_t cb = ((g < 4 ? codes.x : codes.y) >> (8 * (g & 3))) & 0xFFu;
-      uint32_t nib = (meta >> (4 * g)) & 15u;
-      uint32_t i0 = nib & 3u, i1 = nib >> 2;
-      uint32_t d16 = ((cb & 15u) << (4u * i0)) | ((cb >> 4) << (4u * i1));
+      const int g = 2 * q + gg;
+      const uint32_t cb = ((g < 4 ? c_lo : c_hi) >> (8 * (g & 3))) & 0xFFu;
+      const uint32_t s0 = ((meta >> (4 * g)) & 3u) << 2;
+      const uint32_t s1 = ((meta >> (4 * g + 2)) & 3u) << 2;
+      const uint32_t d16 = ((cb & 15u) << s0) | ((cb >> 4) << s1);
       word |= d16 << (16 * gg);
     }
     out[q] = word;
   }
 }
 
-template <bool kDenseExpanded>
-__global__ __launch_bounds__(256) void dual_gemm_mx_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint8_t lds_as[BM * kStride];
-  __shared__ __align__(16) uint8_t lds_ar[BM * kStride];
-  __shared__ __align__(16) uint8_t lds_w[BN * kStride];
-  __shared__ uint32_t lds_sas[BM], lds_sar[BM], lds_sws[BN], lds_swd[BN];
+template <int BN, bool kDense>
+struct Stage {
+  static constexpr int kWChunks = BN * 4;                      // 16-byte chunks of the W tile
+  static constexpr int kWPer = (kWChunks + kThreads - 1) / kThreads;
+  u32x4 ar[2];        // residual tile: 256 rows x 4 chunks -> 2 per thread
+  u32x4 as[2];        // backbone: dense chunks, or [0] = 16 code bytes + [1].xy = 8 meta bytes
+  u32x4 w[kWPer];
+  uint32_t sc[2];     // scale words (see load)
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int BN>
+struct Smem {
+  u32x4 as[2][BM * 4];
+  u32x4 ar[2][BM * 4];
+  u32x4 w[2][BN * 4];
+  uint32_t sas[2][BM], sar[2][BM], sws[2][BN], swd[2][BN];
+};
+
+template <int BN, bool kDense>
+__device__ __forceinline__ void load_stage(const GemmArgs &a, int64_t m0, int64_t n0, int kt,
+                                           Stage<BN, kDense> &st) {
+  const int tid = threadIdx.x;
+  const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + kThreads * j, row = c >> 2, part = c & 3;
+    const int64_t gm = m0 + row;
+    st.ar[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.r_codes + gm * a.ld_rc + kt * 64 + part * 16) : z;
+    if (kDense)
+      st.as[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.s_dense + gm * a.ld_sd + kt * 64 + part * 16) : z;
+  }
+  if (!kDense) {
+    const int row = tid >> 1, half = tid & 1;
+    const int64_t gm = m0 + row;
+    if (gm < a.m) {
+      st.as[0] = *reinterpret_cast<const u32x4 *>(a.s_codes + gm * a.ld_sc + kt * 32 + half * 16);
+      u32x2 mv = *reinterpret_cast<const u32x2 *>(a.meta + gm * a.ld_meta + kt * 16 + half * 8);
+      st.as[1] = u32x4{mv.x, mv.y, 0u, 0u};
+    } else {
+      st.as[0] = z;
+      st.as[1] = u32x4{0x44444444u, 0x44444444u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<BN, kDense>::kWPer; ++j) {
+    const int c = tid + kThreads * j;
+    if (c < Stage<BN, kDense>::kWChunks) {
+      const int row = c >> 2, part = c & 3;
+      const int64_t gn = n0 + row;
+      st.w[j] = gn < a.n ? *reinterpret_cast<const u32x4 *>(a.w_codes + gn * a.ld_wc + kt * 64 + part * 16) : z;
+    }
+  }
+  // scale words: threads [0, 256) the two A paths of row tid; [256, 256 + BN) the two W views
+  if (tid < BM) {
+    const int64_t gm = m0 + tid;
+    st.sc[0] = gm < a.m ? *reinterpret_cast<const uint32_t *>(a.s_scales + gm * a.ld_ss + kt * 4) : 0u;
+    st.sc[1] = gm < a.m ? *reinterpret_cast<const uint32_t *>(a.r_scales + gm * a.ld_rs + kt * 4) : 0u;
+  } else if (tid < BM + BN) {
+    const int64_t gn = n0 + (tid - BM);
+    st.sc[0] = gn < a.n ? *reinterpret_cast<const uint32_t *>(a.ws_scales + gn * a.ld_wss + kt * 4) : 0u;
+    st.sc[1] = gn < a.n ? *reinterpret_cast<const uint32_t *>(a.wd_scales + gn * a.ld_wds + kt * 4) : 0u;
+  }
+}
+
+template <int BN, bool kDense>
+__device__ __forceinline__ void store_stage(Smem<BN> &sm, int buf, const Stage<BN, kDense> &st) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + kThreads * j, row = c >> 2, part = c & 3;
+    sm.ar[buf][lds_slot(row, part)] = st.ar[j];
+    if (kDense) sm.as[buf][lds_slot(row, part)] = st.as[j];
+  }
+  if (!kDense) {
+    const int row = tid >> 1, half = tid & 1;
+    uint32_t d0[4], d1[4];
+    expand8(st.as[0].x, st.as[0].y, st.as[1].x, d0);
+    expand8(st.as[0].z, st.as[0].w, st.as[1].y, d1);
+    sm.as[buf][lds_slot(row, 2 * half)] = u32x4{d0[0], d0[1], d0[2], d0[3]};
+    sm.as[buf][lds_slot(row, 2 * half + 1)] = u32x4{d1[0], d1[1], d1[2], d1[3]};
+  }
+#pragma unroll
+  for (int j = 0; j < Stage<BN, kDense>::kWPer; ++j) {
+    const int c = tid + kThreads * j;
+    if (c < Stage<BN, kDense>::kWChunks) {
+      const int row = c >> 2, part = c & 3;
+      sm.w[buf][lds_slot(row, part)] = st.w[j];
+    }
+  }
+  if (tid < BM) {
+    sm.sas[buf][tid] = st.sc[0];
+    sm.sar[buf][tid] = st.sc[1];
+  } else if (tid < BM + BN) {
+    sm.sws[buf][tid - BM] = st.sc[0];
+    sm.swd[buf][tid - BM] = st.sc[1];
+  }
+}
+
+template <int BN, bool kDense>
+__global__ __launch_bounds__(kThreads) void dual_gemm_mx_kernel(GemmArgs a) {
+  constexpr int TN = BN / 64;           // 32-column MFMA tiles per wavefront
+  __shared__ Smem<BN> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
   const int h = lane >> 5, li = lane & 31;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
 
-  v16f acc[2][2];
+  v16f acc[2][TN];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int ksteps = (int)(a.k / BK);
-  for (int kt = 0; kt < ksteps; ++kt) {
-    // ---- global -> LDS
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int c = tid + 256 * j, row = c >> 2, part = c & 3;
-      int64_t gm = m0 + row, gn = n0 + row;
-      uint4 vr = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-      if (gm < a.m)
-        vr = *reinterpret_cast<const uint4 *>(a.r_codes + gm * a.ld_rc + kt * 64 + part * 16);
-      if (gn < a.n)
-        vw = *reinterpret_cast<const uint4 *>(a.w_codes + gn * a.ld_wc + kt * 64 + part * 16);
-      *reinterpret_cast<uint4 *>(lds_ar + row * kStride + part * 16) = vr;
-      *reinterpret_cast<uint4 *>(lds_w + row * kStride + part * 16) = vw;
-      if (kDenseExpanded) {
-        uint4 vs = make_uint4(0, 0, 0, 0);
-        if (gm < a.m)
-          vs = *reinterpret_cast<const uint4 *>(a.s_dense + gm * a.ld_sd + kt * 64 + part * 16);
-        *reinterpret_cast<uint4 *>(lds_as + row * kStride + part * 16) = vs;
-      }
-    }
-    if (!kDenseExpanded) {
-      // two threads per row, 16 groups (16 code bytes, 8 meta bytes) each
-      int row = tid >> 1, half = tid & 1;
-      int64_t gm = m0 + row;
-      uint4 cv = make_uint4(0, 0, 0, 0);
-      uint2 mv = make_uint2(0x44444444u, 0x44444444u);
-      if (gm < a.m) {
-        cv = *reinterpret_cast<const uint4 *>(a.s_codes + gm * a.ld_sc + kt * 32 + half * 16);
-        mv = *reinterpret_cast<const uint2 *>(a.meta + gm * a.ld_meta + kt * 16 + half * 8);
-      }
-      uint32_t d0[4], d1[4];
-      expand8(make_uint2(cv.x, cv.y), mv.x, d0);
-      expand8(make_uint2(cv.z, cv.w), mv.y, d1);
-      uint8_t *dst = lds_as + row * kStride + half * 32;
-      *reinterpret_cast<uint4 *>(dst) = make_uint4(d0[0], d0[1], d0[2], d0[3]);
-      *reinterpret_cast<uint4 *>(dst + 16) = make_uint4(d1[0], d1[1], d1[2], d1[3]);
-    }
-    if (tid < BM) {
-      int64_t gm = m0 + tid;
-      uint32_t ss = 0, sr = 0;
-      if (gm < a.m) {
-        ss = *reinterpret_cast<const uint32_t *>(a.s_scales + gm * a.ld_ss + kt * 4);
-        sr = *reinterpret_cast<const uint32_t *>(a.r_scales + gm * a.ld_rs + kt * 4);
-      }
-      lds_sas[tid] = ss;
-      lds_sar[tid] = sr;
-    } else {
-      int row = tid - BM;
-      int64_t gn = n0 + row;
-      uint32_t s1 = 0, s2 = 0;
-      if (gn < a.n) {
-        s1 = *reinterpret_cast<const uint32_t *>(a.ws_scales + gn * a.ld_wss + kt * 4);
-        s2 = *reinterpret_cast<const uint32_t *>(a.wd_scales + gn * a.ld_wds + kt * 4);
-      }
-      lds_sws[row] = s1;
-      lds_swd[row] = s2;
-    }
-    __syncthreads();
+  Stage<BN, kDense> st;
+  load_stage<BN, kDense>(a, m0, n0, 0, st);
+  store_stage<BN, kDense>(sm, 0, st);
+  __syncthreads();
 
-    // ---- MFMA
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < ksteps;
+    if (more) load_stage<BN, kDense>(a, m0, n0, kt + 1, st);
+
+    // scale words of this lane's rows / columns, shifted to k blocks 2h, 2h + 1
+    int sas[2], sar[2], sws[TN], swd[TN];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int r = wm * 64 + it * 32 + li;
+      sas[it] = (int)(sm.sas[buf][r] >> (16 * h));
+      sar[it] = (int)(sm.sar[buf][r] >> (16 * h));
+    }
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) {
+      const int r = wn * (BN / 2) + jt * 32 + li;
+      sws[jt] = (int)(sm.sws[buf][r] >> (16 * h));
+      swd[jt] = (int)(sm.swd[buf][r] >> (16 * h));
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      v8i fas[2], far[2], fb[2];
-      int sas[2], sar[2], sws[2], swd[2];
-      const int off = h * 32 + s * 16, sh = 8 * (2 * h + s);
+      v8i fas[2], far[2], fb[TN];
+      const int c = 2 * h + s;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
-        int r = wm * 64 + it * 32 + li;
-        fas[it] = as_operand(*reinterpret_cast<const uint4 *>(lds_as + r * kStride + off));
-        far[it] = as_operand(*reinterpret_cast<const uint4 *>(lds_ar + r * kStride + off));
-        sas[it] = (int)((lds_sas[r] >> sh) & 0xFFu);
-        sar[it] = (int)((lds_sar[r] >> sh) & 0xFFu);
+        const int r = wm * 64 + it * 32 + li;
+        fas[it] = as_operand(sm.as[buf][lds_slot(r, c)]);
+        far[it] = as_operand(sm.ar[buf][lds_slot(r, c)]);
       }
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        int r = wn * 64 + jt * 32 + li;
-        fb[jt] = as_operand(*reinterpret_cast<const uint4 *>(lds_w + r * kStride + off));
-        sws[jt] = (int)((lds_sws[r] >> sh) & 0xFFu);
-        swd[jt] = (int)((lds_swd[r] >> sh) & 0xFFu);
+      for (int jt = 0; jt < TN; ++jt) {
+        const int r = wn * (BN / 2) + jt * 32 + li;
+        fb[jt] = as_operand(sm.w[buf][lds_slot(r, c)]);
       }
 #pragma unroll
       for (int it = 0; it < 2; ++it)
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fas[it], fb[jt], acc[it][jt], 4, 4, 0, sas[it], 0, sws[jt]);
-          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              far[it], fb[jt], acc[it][jt], 4, 4, 0, sar[it], 0, swd[jt]);
+        for (int jt = 0; jt < TN; ++jt) {
+          if (s == 0) {
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fas[it], fb[jt], acc[it][jt], 4, 4, 0, sas[it], 0, sws[jt]);
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                far[it], fb[jt], acc[it][jt], 4, 4, 0, sar[it], 0, swd[jt]);
+          } else {
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fas[it], fb[jt], acc[it][jt], 4, 4, 1, sas[it], 1, sws[jt]);
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                far[it], fb[jt], acc[it][jt], 4, 4, 1, sar[it], 1, swd[jt]);
+          }
         }
     }
+    if (more) store_stage<BN, kDense>(sm, buf ^ 1, st);
     __syncthreads();
   }
 
-  // ---- epilogue: lane l holds column l % 32, rows 8 (r / 4) + 4 h + r % 4
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      int64_t col = n0 + wn * 64 + jt * 32 + li;
+    for (int jt = 0; jt < TN; ++jt) {
+      const int64_t col = n0 + wn * (BN / 2) + jt * 32 + li;
       if (col >= a.n) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < a.m) a.y[row * a.ld_y + col] = acc[it][jt][r];
       }
     }
 }
 
+// ---------------------------------------------------------------------------
+// Dense-operand pipeline: the backbone is read in its dense layout, so all
+// three operand tiles and the four scale arrays go global -> LDS with
+// global_load_lds_dwordx{4,1} (lane l's bytes land at base + l * size), two K
+// steps ahead of the MFMAs, into a ring of three LDS stages.  Each wavefront
+// issues a fixed share of the load instructions of every stage; before a step
+// it waits until at most the next stage's share is still in flight, then a
+// barrier makes all wavefronts' loads visible and frees the stage read two
+// steps earlier.  Rows past M or N load the last valid row; their outputs are
+// never stored.
+
+template <int BN>
+struct DStage {
+  u32x4 as[BM * 4];
+  u32x4 ar[BM * 4];
+  u32x4 w[BN * 4];
+  uint32_t sas[BM], sar[BM], sws[BN], swd[BN];
+};
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xFFFF);
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// buffer_load ... lds: lane l's bytes land at M0 + l * size.  The asm has no
+// register result, and its completion is waited for explicitly (vmcnt).
+__device__ __forceinline__ void b2l16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void b2l4(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+// Load plan of one stage, per wavefront w: 16-byte chunk loads of 16 rows
+// each (A backbone, A residual: q = w, w + 8; W: q = w, w + 8 while
+// q < BN / 16) and 4-byte scale loads of 64 rows each (t = w, w + 8 while
+// t < kS, over the four scale arrays in turn).
+template <int BN>
+struct DPlan {
+  static constexpr int kW = BN / 16;
+  static constexpr int kS = 2 * (BM / 64) + 2 * (BN / 64);
+  static constexpr int kMinPerWave = 4 + kW / 8 + kS / 8;   // the waitcnt allowance
+};
+
+struct DRsrc {
+  i32x4 as, ar, w, sas, sar, sws, swd;
+};
+
+struct DOffs {
+  uint32_t as[2], ar[2], w[2], sc[2];
+};
+
+constexpr int kOffAr = BM * 64, kOffW = 2 * BM * 64;
+
+template <int BN>
+__device__ __forceinline__ void plan_loads(const GemmArgs &a, int64_t m0, int64_t n0, int wave,
+                                           int lane, DRsrc &R, DOffs &O) {
+  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  R.as = make_rsrc(a.s_dense + m0 * a.ld_sd, (uint32_t)((a.m - m0) * a.ld_sd));
+  R.ar = make_rsrc(a.r_codes + m0 * a.ld_rc, (uint32_t)((a.m - m0) * a.ld_rc));
+  R.w = make_rsrc(a.w_codes + n0 * a.ld_wc, (uint32_t)((a.n - n0) * a.ld_wc));
+  R.sas = make_rsrc(a.s_scales + m0 * a.ld_ss, (uint32_t)((a.m - m0) * a.ld_ss));
+  R.sar = make_rsrc(a.r_scales + m0 * a.ld_rs, (uint32_t)((a.m - m0) * a.ld_rs));
+  R.sws = make_rsrc(a.ws_scales + n0 * a.ld_wss, (uint32_t)((a.n - n0) * a.ld_wss));
+  R.swd = make_rsrc(a.wd_scales + n0 * a.ld_wds, (uint32_t)((a.n - n0) * a.ld_wds));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (wave + 8 * j) + lrow;
+    O.as[j] = (uint32_t)(row * a.ld_sd + lchunk * 16);
+    O.ar[j] = (uint32_t)(row * a.ld_rc + lchunk * 16);
+    O.w[j] = (uint32_t)(row * a.ld_wc + lchunk * 16);
+    // scale load t = wave + 8 j: array t / (rows / 64) in the order sas, sar, sws, swd
+    int t = wave + 8 * j;
+    int64_t ld;
+    if (t < BM / 64) ld = a.ld_ss;
+    else if ((t -= BM / 64) < BM / 64) ld = a.ld_rs;
+    else if ((t -= BM / 64) < BN / 64) ld = a.ld_wss;
+    else { t -= BN / 64; ld = a.ld_wds; }
+    O.sc[j] = (uint32_t)((64 * t + lane) * ld);
+  }
+}
+
+template <int BN>
+__device__ __forceinline__ void issue_stage(const DRsrc &R, const DOffs &O, int wave, int kt,
+                                            const DStage<BN> &S) {
+  using P = DPlan<BN>;
+  const uint32_t base = lds_addr(&S);
+  const uint32_t kc = (uint32_t)kt * 64u, ks = (uint32_t)kt * 4u;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = wave + 8 * j;
+    b2l16(R.as, O.as[j], kc, base + q * 1024);
+    b2l16(R.ar, O.ar[j], kc, base + kOffAr + q * 1024);
+    if (q < P::kW) b2l16(R.w, O.w[j], kc, base + kOffW + q * 1024);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int t = wave + 8 * j;
+    if (t >= P::kS) continue;
+    const uint32_t sbase = base + kOffW + BN * 64;
+    if (t < BM / 64) {
+      b2l4(R.sas, O.sc[j], ks, sbase + 256 * t);
+    } else if ((t -= BM / 64) < BM / 64) {
+      b2l4(R.sar, O.sc[j], ks, sbase + 4 * BM + 256 * t);
+    } else if ((t -= BM / 64) < BN / 64) {
+      b2l4(R.sws, O.sc[j], ks, sbase + 8 * BM + 256 * t);
+    } else {
+      t -= BN / 64;
+      b2l4(R.swd, O.sc[j], ks, sbase + 8 * BM + 4 * BN + 256 * t);
+    }
+  }
+}
+
+template <int BN>
+__device__ __forceinline__ void compute_stage(const DStage<BN> &S, v16f (&acc)[2][BN / 64], int wm,
+                                              int wn, int h, int li) {
+  constexpr int TN = BN / 64;
+  int sas[2], sar[2], sws[TN], swd[TN];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = wm * 64 + it * 32 + li;
+    sas[it] = (int)(S.sas[r] >> (16 * h));
+    sar[it] = (int)(S.sar[r] >> (16 * h));
+  }
+#pragma unroll
+  for (int jt = 0; jt < TN; ++jt) {
+    const int r = wn * (BN / 2) + jt * 32 + li;
+    sws[jt] = (int)(S.sws[r] >> (16 * h));
+    swd[jt] = (int)(S.swd[r] >> (16 * h));
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v8i fas[2], far[2], fb[TN];
+    const int c = 2 * h + s;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int r = wm * 64 + it * 32 + li;
+      fas[it] = as_operand(S.as[lds_slot(r, c)]);
+      far[it] = as_operand(S.ar[lds_slot(r, c)]);
+    }
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) {
+      const int r = wn * (BN / 2) + jt * 32 + li;
+      fb[jt] = as_operand(S.w[lds_slot(r, c)]);
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < TN; ++jt) {
+        if (s == 0) {
+          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fas[it], fb[jt], acc[it][jt], 4, 4, 0, sas[it], 0, sws[jt]);
+          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              far[it], fb[jt], acc[it][jt], 4, 4, 0, sar[it], 0, swd[jt]);
+        } else {
+          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fas[it], fb[jt], acc[it][jt], 4, 4, 1, sas[it], 1, sws[jt]);
+          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              far[it], fb[jt], acc[it][jt], 4, 4, 1, sar[it], 1, swd[jt]);
+        }
+      }
+  }
+}
+
+// Wait until this wave's loads of the current stage have landed (the next
+// stage's, if issued, may still be in flight), then make all waves' loads visible.
+template <int BN>
+__device__ __forceinline__ void stage_ready(bool next_in_flight) {
+  if (next_in_flight)
+    __builtin_amdgcn_s_waitcnt(0x3F70 | (DPlan<BN>::kMinPerWave & 0xF) |
+                               ((DPlan<BN>::kMinPerWave >> 4) << 14));
+  else
+    __builtin_amdgcn_s_waitcnt(0x3F70);   // vmcnt(0)
+  // a bare barrier: the loads above are the only memory traffic to order, and
+  // the memory clobber keeps the compiler from moving LDS reads across it
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int BN>
+__global__ __launch_bounds__(kThreads) void dual_gemm_dense_kernel(GemmArgs a) {
+  constexpr int TN = BN / 64;
+  __shared__ DStage<BN> st[3];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, li = lane & 31;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+
+  v16f acc[2][TN];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int ksteps = (int)(a.k / BK);
+  DRsrc R;
+  DOffs O;
+  plan_loads<BN>(a, m0, n0, wave, lane, R, O);
+  issue_stage<BN>(R, O, wave, 0, st[0]);
+  if (ksteps > 1) issue_stage<BN>(R, O, wave, 1, st[1]);
+
+  int cur = 0;                  // stage of step kt; (cur + 2) % 3 is free once all waves pass the barrier
+  for (int kt = 0; kt < ksteps; ++kt) {
+    stage_ready<BN>(kt + 1 < ksteps);
+    const int nxt = cur == 0 ? 2 : cur - 1;
+    if (kt + 2 < ksteps) issue_stage<BN>(R, O, wave, kt + 2, st[nxt]);
+    compute_stage<BN>(st[cur], acc, wm, wn, h, li);
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) {
+      const int64_t col = n0 + wn * (BN / 2) + jt * 32 + li;
+      if (col >= a.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < a.m) a.y[row * a.ld_y + col] = acc[it][jt][r];
+      }
+    }
+}
+
+template <int BN>
+void launch_bn(const GemmArgs &a, bool dense, hipStream_t s) {
+  dim3 grid((unsigned)((a.n + BN - 1) / BN), (unsigned)((a.m + BM - 1) / BM)), block(kThreads);
+  if (dense)
+    dual_gemm_dense_kernel<BN><<<grid, block, 0, s>>>(a);
+  else
+    dual_gemm_mx_kernel<BN, false><<<grid, block, 0, s>>>(a);
+}
+
 }  // namespace
 
+// Tile width: fill the 256 CUs with as few, as large tiles as possible.
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s) {
-  dim3 grid((unsigned)((a.n + BN - 1) / BN), (unsigned)((a.m + BM - 1) / BM)), block(256);
-  if (dense_expanded)
-    dual_gemm_mx_kernel<true><<<grid, block, 0, s>>>(a);
+  const int64_t mt = (a.m + BM - 1) / BM;
+  auto tiles = [&](int bn) { return mt * ((a.n + bn - 1) / bn); };
+  if (tiles(192) >= 256 || tiles(128) > 256)
+    launch_bn<192>(a, dense_expanded, s);
   else
-    dual_gemm_mx_kernel<false><<<grid, block, 0, s>>>(a);
+    launch_bn<128>(a, dense_expanded, s);
   return hipGetLastError();
 }
 

@@ -5,51 +5,82 @@
 // mask, FP4 backbone, residual against the quantized backbone) and sentence 5
 // (one fused operator that also absorbs the layer normalization).
 //
-// One wavefront owns one row of X.  Lane l owns the 32-element K blocks
-// b = c * 64 + l (c = 0, 1, ...), so each lane reads 64 contiguous bytes per
-// block and a block's MX scale, its eight 2:4 groups and all its output bytes
-// stay inside one lane.  The RMS reduction follows a fixed binary tree: a
-// tree over the 32 squares inside the lane, a xor butterfly across the 64
-// lanes (the 2048-element chunk sums) and a tree over the chunks, which is the
-// pairwise tree over 2^ceil(log2 K) leaves.  With normalization the row stays
-// in registers between the reduction and the quantization (one HBM pass).
+// Work split: one lane owns one 32-element block of a row (one MXFP4 scale
+// block, eight 2:4 groups, or two NVFP4 blocks), so each lane reads 64
+// contiguous bytes and writes whole words of every output.  With RMSNorm a
+// row is spread over ceil(K / 2048) wavefronts of one workgroup; the sum of
+// squares follows a fixed binary tree: a tree over the 32 squares inside the
+// lane, a xor butterfly across the 64 lanes (2048-element chunks), and an
+// 8-leaf tree over the chunk sums in LDS (missing chunks are +0).  That is
+// the pairwise tree over 2^ceil(log2 K) leaves, whatever the wave count.
+// Without normalization the blocks are independent and the grid is flat.
+//
+// MXFP4 element and scale conversions use the gfx950 instructions
+// v_cvt_scalef32_pk_fp4_{bf16,f32} (round to nearest even, saturating, sign
+// of zero kept; the scale operand acts as 2^(E8M0 byte - 127), also for byte 0)
+// and v_cvt_scalef32_pk_f32_fp4 (exact dequantization).  The NVFP4-style path
+// divides by its non-power-of-two scale in IEEE fp32 first and converts at
+// scale 1.
 #include "fp4_device.h"
 #include "kernels.h"
 
 namespace sharq {
 namespace {
 
-constexpr int kRowsPerBlock = 4;   // four wavefronts, one row each
-
-struct Block32 {
-  uint32_t v[16];   // 32 bf16, element 2i in the low half of v[i]
-};
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// X is read exactly once: non-temporal loads keep it from displacing the
-// outputs and the next kernel's operands in the caches.
-__device__ __forceinline__ void load_block(const uint16_t *p, Block32 &b) {
+constexpr int kMaxWavesPerRow = 8;     // K <= 16384 with normalization
+
+// ---------------------------------------------------------------- helpers
+
+// X is read exactly once: non-temporal loads keep it out of the way of the
+// outputs and of the next kernel's operands.
+__device__ __forceinline__ void load32(const uint16_t *p, uint32_t w[16]) {
   const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     u32x4 t = __builtin_nontemporal_load(q + i);
-    b.v[4 * i + 0] = t.x;
-    b.v[4 * i + 1] = t.y;
-    b.v[4 * i + 2] = t.z;
-    b.v[4 * i + 3] = t.w;
+    w[4 * i + 0] = t.x;
+    w[4 * i + 1] = t.y;
+    w[4 * i + 2] = t.z;
+    w[4 * i + 3] = t.w;
   }
 }
 
-// Tree sum of the 32 squares of a block (adjacent pairs at every level).
-__device__ __forceinline__ float block_sumsq(const Block32 &b) {
-  float q[32];
+__device__ __forceinline__ void load32_cached(const uint16_t *p, uint32_t w[16]) {
+  const uint4 *q = reinterpret_cast<const uint4 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 t = q[i];
+    w[4 * i + 0] = t.x;
+    w[4 * i + 1] = t.y;
+    w[4 * i + 2] = t.z;
+    w[4 * i + 3] = t.w;
+  }
+}
+
+__device__ __forceinline__ void unpack32(const uint32_t w[16], float f[32]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float lo = bf16_lo(b.v[i]), hi = bf16_hi(b.v[i]);
-    q[2 * i] = lo * lo;
-    q[2 * i + 1] = hi * hi;
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
   }
+}
+
+// two fp32 -> bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 v = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Tree sum of the 32 squares of a block (adjacent pairs at every level).
+__device__ __forceinline__ float block_sumsq(const float f[32]) {
+  float q[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) q[i] = f[i] * f[i];
 #pragma unroll
   for (int w = 16; w >= 1; w >>= 1) {
 #pragma unroll
@@ -58,192 +89,275 @@ __device__ __forceinline__ float block_sumsq(const Block32 &b) {
   return q[0];
 }
 
+// Butterfly over the 64 lanes: step j adds lane l ^ 2^j, so every lane ends
+// with the pairwise tree sum of the 64 values (fp32 addition commutes).
+template <int XOR>
+__device__ __forceinline__ float swz_xor(float v) {
+  // ds_swizzle bit-mask mode inside 32-lane halves: and 0x1F, or 0, xor XOR
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (XOR << 10)));
+}
+
 __device__ __forceinline__ float wave_tree_sum(float v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v = v + __shfl_xor(v, off, 64);
+  v = v + swz_xor<1>(v);
+  v = v + swz_xor<2>(v);
+  v = v + swz_xor<4>(v);
+  v = v + swz_xor<8>(v);
+  v = v + swz_xor<16>(v);
+  // lane l ^ 32: the other half of the wavefront
+  v = v + __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) & 63) << 2,
+                                                      __float_as_int(v)));
   return v;
 }
 
-// x_n = bf16((x * r) * gamma) for the 32 elements of a block.
-__device__ __forceinline__ void normalize_block(Block32 &b, const uint16_t *g, float r) {
-  Block32 gb;
-  const uint4 *q = reinterpret_cast<const uint4 *>(g);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 t = q[i];
-    gb.v[4 * i + 0] = t.x;
-    gb.v[4 * i + 1] = t.y;
-    gb.v[4 * i + 2] = t.z;
-    gb.v[4 * i + 3] = t.w;
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float lo = (bf16_lo(b.v[i]) * r) * bf16_lo(gb.v[i]);
-    float hi = (bf16_hi(b.v[i]) * r) * bf16_hi(gb.v[i]);
-    b.v[i] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
-  }
-}
+// E8M0 byte as the fp32 scale operand of the conversion instructions.
+__device__ __forceinline__ float e8m0_operand(uint32_t byte) { return __uint_as_float(byte << 23); }
 
-// 2:4 mask of one group from 15-bit magnitudes: keep the two largest, lower
-// index first on ties.  Returns the 4-bit keep mask and the meta nibble.
-__device__ __forceinline__ void mask_group(const uint32_t mag[4], uint32_t &keep,
-                                           uint32_t &nibble) {
-  // unique keys: magnitude, then lower index ranks higher
-  uint32_t k0 = (mag[0] << 2) | 3u, k1 = (mag[1] << 2) | 2u;
-  uint32_t k2 = (mag[2] << 2) | 1u, k3 = (mag[3] << 2) | 0u;
-  uint32_t a = max(k0, k1), b = min(k0, k1), c = max(k2, k3), d = min(k2, k3);
-  uint32_t top = max(a, c);
-  uint32_t second = max(min(a, c), max(b, d));
-  keep = (k0 >= second ? 1u : 0u) | (k1 >= second ? 2u : 0u) | (k2 >= second ? 4u : 0u) |
-         (k3 >= second ? 8u : 0u);
-  uint32_t it = 3u - (top & 3u), is = 3u - (second & 3u);
-  uint32_t i0 = min(it, is), i1 = max(it, is);
-  nibble = i0 | (i1 << 2);
-  (void)top;
-}
+// ---------------------------------------------------------------- 2:4 mask
 
-struct BlockOut {
-  uint32_t meta;        // 8 nibbles
-  uint32_t s_comp[2];   // 8 compressed bytes
-  uint32_t s_dense[4];  // 32 dense codes
-  uint32_t r_codes[4];  // 32 dense codes
-  uint32_t s_scale;     // MX: 1 byte; NV: 2 bytes
-  uint32_t r_scale;
+// Per group of four: keys order by magnitude, then by lower index.  u values
+// are 3 - index of the two kept entries (umax for the lower index).
+struct MaskOut {
+  uint32_t top[8];        // largest key per group (for the block amax)
+  uint32_t umax[8], umin[8];
+  uint32_t meta;          // 8 nibbles i0 | i1 << 2
 };
 
-// Compressed backbone byte of a group: code at i0 low, code at i1 high.
-__device__ __forceinline__ uint32_t compress_group(uint32_t dense16, uint32_t nibble) {
-  uint32_t i0 = nibble & 3u, i1 = nibble >> 2;
-  uint32_t c0 = (dense16 >> (4u * i0)) & 15u;
-  uint32_t c1 = (dense16 >> (4u * i1)) & 15u;
-  return c0 | (c1 << 4);
-}
-
-// FMT 0: MXFP4 (one 32-block); FMT 1: NVFP4 (two 16-blocks, tensor scale s_t).
-template <int FMT>
-__device__ __forceinline__ void quantize_block(const Block32 &xn, float s_t, BlockOut &o) {
-  uint32_t mag[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    mag[2 * i] = xn.v[i] & 0x7FFFu;
-    mag[2 * i + 1] = (xn.v[i] >> 16) & 0x7FFFu;
-  }
-  uint32_t keep = 0;
-  o.meta = 0;
+__device__ __forceinline__ void mask_block(const float xf[32], MaskOut &o) {
+  uint32_t acc = 0;
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
-    uint32_t kg, nib;
-    mask_group(&mag[4 * g], kg, nib);
-    keep |= kg << (4 * g);
-    o.meta |= nib << (4 * g);
+    uint32_t k0 = (__float_as_uint(xf[4 * g + 0]) & 0x7FFF0000u) | 3u;
+    uint32_t k1 = (__float_as_uint(xf[4 * g + 1]) & 0x7FFF0000u) | 2u;
+    uint32_t k2 = (__float_as_uint(xf[4 * g + 2]) & 0x7FFF0000u) | 1u;
+    uint32_t k3 = (__float_as_uint(xf[4 * g + 3]) & 0x7FFF0000u);
+    uint32_t a = max(k0, k1), b = min(k0, k1), c = max(k2, k3), d = min(k2, k3);
+    uint32_t top = max(a, c);
+    uint32_t second = max(max(min(a, c), b), d);
+    uint32_t ut = top & 3u, us = second & 3u;
+    uint32_t umax = max(ut, us), umin = min(ut, us);
+    o.top[g] = top;
+    o.umax[g] = umax;
+    o.umin[g] = umin;
+    // nibble = (3 - umax) | (3 - umin) << 2 = 15 - (umax + 4 umin)
+    acc |= (umax + (umin << 2)) << (4 * g);
   }
-
-  float xf[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    xf[2 * i] = bf16_lo(xn.v[i]);
-    xf[2 * i + 1] = bf16_hi(xn.v[i]);
-  }
-
-  uint32_t sc[32], rc[32];
-  float res[32];
-  constexpr int kBlk = FMT == 0 ? 32 : 16;
-  o.s_scale = 0;
-  o.r_scale = 0;
-#pragma unroll
-  for (int h = 0; h < 32 / kBlk; ++h) {
-    // backbone: block amax of x_n equals that of the kept values
-    uint32_t am = 0;
-#pragma unroll
-    for (int i = 0; i < kBlk; ++i) am = max(am, mag[h * kBlk + i]);
-    if (FMT == 0) {
-      uint32_t sb = e8m0_from_amax_bits(am << 16);
-      float inv = e8m0_inv(sb), val = e8m0_val(sb);
-      o.s_scale |= sb << (8 * h);
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        int j = h * kBlk + i;
-        bool kp = (keep >> j) & 1u;
-        uint32_t c = kp ? e2m1_encode(xf[j] * inv) : 0u;
-        float d = kp ? e2m1_value(c) * val : 0.0f;
-        sc[j] = c;
-        res[j] = xf[j] - d;
-      }
-    } else {
-      float d6 = 6.0f * s_t;
-      float ratio = __uint_as_float(am << 16) / d6;
-      uint32_t sb = e4m3_encode_pos(ratio);
-      float S = e4m3_value(sb) * s_t;
-      o.s_scale |= sb << (8 * h);
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        int j = h * kBlk + i;
-        bool kp = (keep >> j) & 1u;
-        uint32_t c;
-        float d;
-        if (S == 0.0f) {
-          c = (__float_as_uint(xf[j]) >> 28) & 8u;
-          d = __uint_as_float((c & 8u) << 28);
-        } else {
-          c = e2m1_encode(xf[j] / S);
-          d = e2m1_value(c) * S;
-        }
-        c = kp ? c : 0u;
-        d = kp ? d : 0.0f;
-        sc[j] = c;
-        res[j] = xf[j] - d;
-      }
-    }
-    // residual
-    uint32_t ar = 0;
-#pragma unroll
-    for (int i = 0; i < kBlk; ++i) ar = max(ar, __float_as_uint(res[h * kBlk + i]) & 0x7FFFFFFFu);
-    if (FMT == 0) {
-      uint32_t rb = e8m0_from_amax_bits(ar);
-      float inv = e8m0_inv(rb);
-      o.r_scale |= rb << (8 * h);
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) rc[h * kBlk + i] = e2m1_encode(res[h * kBlk + i] * inv);
-    } else {
-      float d6 = 6.0f * s_t;
-      float ratio = __uint_as_float(ar) / d6;
-      uint32_t rb = e4m3_encode_pos(ratio);
-      float S = e4m3_value(rb) * s_t;
-      o.r_scale |= rb << (8 * h);
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        float v = res[h * kBlk + i];
-        rc[h * kBlk + i] = (S == 0.0f) ? ((__float_as_uint(v) >> 28) & 8u) : e2m1_encode(v / S);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t s = 0, r = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s |= sc[8 * q + i] << (4 * i);
-      r |= rc[8 * q + i] << (4 * i);
-    }
-    o.s_dense[q] = s;
-    o.r_codes[q] = r;
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      int g = 4 * q + gg;
-      uint32_t dense16 = (o.s_dense[g >> 1] >> (16 * (g & 1))) & 0xFFFFu;
-      w |= compress_group(dense16, (o.meta >> (4 * g)) & 15u) << (8 * gg);
-    }
-    o.s_comp[q] = w;
-  }
+  o.meta = ~acc;
 }
 
+// ---------------------------------------------------------------- MXFP4 block
+
+struct BlockOut {
+  uint32_t meta;
+  uint32_t s_comp[2];     // 8 compressed backbone bytes
+  uint32_t s_dense[4];    // 32 backbone codes, dense layout
+  uint32_t r_codes[4];    // 32 residual codes
+  uint32_t s_scale, r_scale;
+};
+
+// xw: the 32 normalized values as bf16 pairs; xf: the same values as fp32.
+__device__ __forceinline__ void quantize_block_mx(const uint32_t xw[16], const float xf[32],
+                                                  BlockOut &o) {
+  MaskOut mk;
+  mask_block(xf, mk);
+  o.meta = mk.meta;
+
+  // backbone scale: each group keeps its largest entry, so the backbone's
+  // block amax is the block amax of x_n
+  uint32_t am = 0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) am = max(am, mk.top[g]);
+  int ex = (int)(am >> 23);
+  uint32_t sb = ex > 2 ? (uint32_t)(ex - 2) : 0u;
+  float ss = e8m0_operand(sb);
+  o.s_scale = sb;
+
+  // compressed backbone: v_perm gathers (x[i0], x[i1]) as a bf16 pair, one
+  // conversion gives the byte (code at i0 low, code at i1 high)
+  uint32_t comp[2] = {0u, 0u};
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    uint32_t z = mk.umax[g] | (mk.umin[g] << 16);
+    // selector bytes 2 i0, 2 i0 + 1, 2 i1, 2 i1 + 1 (z < 2^18: a 24-bit multiply)
+    uint32_t sel = 0x07060706u - __umul24(z, 0x0202u);
+    uint32_t pair = __builtin_amdgcn_perm(xw[2 * g + 1], xw[2 * g], sel);
+    bf16x2 pv = __builtin_bit_cast(bf16x2, pair);
+    uint32_t &w = comp[g >> 2];
+    switch (g & 3) {
+      case 0: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 0); break;
+      case 1: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 1); break;
+      case 2: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 2); break;
+      default: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 3); break;
+    }
+  }
+  o.s_comp[0] = comp[0];
+  o.s_comp[1] = comp[1];
+
+  // dense backbone codes: all codes, then the dropped nibbles cleared
+  uint32_t full[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    bf16x2 pv = __builtin_bit_cast(bf16x2, xw[i]);
+    uint32_t &w = full[i >> 2];
+    switch (i & 3) {
+      case 0: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 0); break;
+      case 1: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 1); break;
+      case 2: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 2); break;
+      default: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, pv, ss, 3); break;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int g = 2 * q + h;
+      uint32_t s0 = 12u - 4u * mk.umax[g], s1 = 12u - 4u * mk.umin[g];
+      m2[h] = (0xFu << s0) | (0xFu << s1);
+    }
+    o.s_dense[q] = full[q] & (m2[0] | (m2[1] << 16));
+  }
+
+  // residual against the quantized backbone (exact in fp32)
+  float res[32];
+  float ramax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    f32x2 d;
+    switch (i & 3) {
+      case 0: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], ss, 0); break;
+      case 1: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], ss, 1); break;
+      case 2: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], ss, 2); break;
+      default: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], ss, 3); break;
+    }
+    res[2 * i] = xf[2 * i] - d[0];
+    res[2 * i + 1] = xf[2 * i + 1] - d[1];
+    ramax = fmaxf(fmaxf(ramax, fabsf(res[2 * i])), fabsf(res[2 * i + 1]));
+  }
+  int rex = (int)(__float_as_uint(ramax) >> 23);
+  uint32_t rb = rex > 2 ? (uint32_t)(rex - 2) : 0u;
+  float rs = e8m0_operand(rb);
+  o.r_scale = rb;
+  uint32_t rc[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t &w = rc[i >> 2];
+    switch (i & 3) {
+      case 0: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, res[2 * i], res[2 * i + 1], rs, 0); break;
+      case 1: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, res[2 * i], res[2 * i + 1], rs, 1); break;
+      case 2: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, res[2 * i], res[2 * i + 1], rs, 2); break;
+      default: w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, res[2 * i], res[2 * i + 1], rs, 3); break;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o.r_codes[q] = rc[q];
+}
+
+// ---------------------------------------------------------------- NVFP4 block
+
+// E2M1 codes of fl32(v / S) for 32 values (two 16-blocks with scales S[0], S[1]),
+// signed zeros when S == 0; packed two per byte.
+__device__ __forceinline__ void nv_codes(const float v[32], const float S[2], uint32_t out[4]) {
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float s = S[i >> 3];
+    float t0 = v[2 * i], t1 = v[2 * i + 1];
+    // S == 0: keep only the sign (the conversion of +-0 keeps it)
+    t0 = s == 0.0f ? __uint_as_float(__float_as_uint(t0) & 0x80000000u) : t0 / s;
+    t1 = s == 0.0f ? __uint_as_float(__float_as_uint(t1) & 0x80000000u) : t1 / s;
+    uint32_t &x = w[i >> 2];
+    switch (i & 3) {
+      case 0: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, t0, t1, 1.0f, 0); break;
+      case 1: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, t0, t1, 1.0f, 1); break;
+      case 2: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, t0, t1, 1.0f, 2); break;
+      default: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, t0, t1, 1.0f, 3); break;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[q] = w[q];
+}
+
+// Block scale byte and effective scale S = fl32(e4m3(byte) * s_t).
+__device__ __forceinline__ uint32_t nv_scale(float amax, float s_t, float &S) {
+  float ratio = amax / (6.0f * s_t);
+  uint32_t sb = e4m3_encode_pos(ratio);
+  S = e4m3_value(sb) * s_t;
+  return sb;
+}
+
+__device__ __forceinline__ void quantize_block_nv(const float xf[32], float s_t, BlockOut &o) {
+  MaskOut mk;
+  mask_block(xf, mk);
+  o.meta = mk.meta;
+
+  float S[2];
+  uint32_t sb0, sb1;
+  {
+    uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) a0 = max(a0, mk.top[g]);
+#pragma unroll
+    for (int g = 4; g < 8; ++g) a1 = max(a1, mk.top[g]);
+    sb0 = nv_scale(__uint_as_float(a0 & 0x7FFF0000u), s_t, S[0]);
+    sb1 = nv_scale(__uint_as_float(a1 & 0x7FFF0000u), s_t, S[1]);
+  }
+  o.s_scale = sb0 | (sb1 << 8);
+
+  uint32_t full[4];
+  nv_codes(xf, S, full);
+  // keep mask per group from the two kept indices
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int g = 2 * q + h;
+      uint32_t s0 = 12u - 4u * mk.umax[g], s1 = 12u - 4u * mk.umin[g];
+      m2[h] = (0xFu << s0) | (0xFu << s1);
+    }
+    o.s_dense[q] = full[q] & (m2[0] | (m2[1] << 16));
+  }
+  // compressed bytes: nibbles at i0 and i1 of each group
+  uint32_t comp[2] = {0u, 0u};
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    uint32_t d16 = (o.s_dense[g >> 1] >> (16 * (g & 1))) & 0xFFFFu;
+    uint32_t s0 = 12u - 4u * mk.umax[g], s1 = 12u - 4u * mk.umin[g];
+    uint32_t byte = ((d16 >> s0) & 15u) | (((d16 >> s1) & 15u) << 4);
+    comp[g >> 2] |= byte << (8 * (g & 3));
+  }
+  o.s_comp[0] = comp[0];
+  o.s_comp[1] = comp[1];
+
+  // residual: R = x_n - fl32(value * S)
+  float res[32];
+  float ra0 = 0.0f, ra1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    f32x2 d;
+    switch (i & 3) {
+      case 0: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], 1.0f, 0); break;
+      case 1: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], 1.0f, 1); break;
+      case 2: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], 1.0f, 2); break;
+      default: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(o.s_dense[i >> 2], 1.0f, 3); break;
+    }
+    const float s = S[i >> 3];
+    res[2 * i] = xf[2 * i] - d[0] * s;
+    res[2 * i + 1] = xf[2 * i + 1] - d[1] * s;
+    float m = fmaxf(fabsf(res[2 * i]), fabsf(res[2 * i + 1]));
+    if (i < 8) ra0 = fmaxf(ra0, m); else ra1 = fmaxf(ra1, m);
+  }
+  float R[2];
+  uint32_t rb0 = nv_scale(ra0, s_t, R[0]);
+  uint32_t rb1 = nv_scale(ra1, s_t, R[1]);
+  o.r_scale = rb0 | (rb1 << 8);
+  nv_codes(res, R, o.r_codes);
+}
+
+// ---------------------------------------------------------------- stores
+
 template <int FMT>
-__device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int b,
+__device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int64_t b,
                                             const BlockOut &o) {
   *reinterpret_cast<uint2 *>(a.s_codes + row * a.ld_sc + 8 * b) = make_uint2(o.s_comp[0], o.s_comp[1]);
   *reinterpret_cast<uint32_t *>(a.meta + row * a.ld_meta + 4 * b) = o.meta;
@@ -266,237 +380,246 @@ __device__ __forceinline__ float nv_tensor_scale(const float *ts) {
   return amax == 0.0f ? 1.0f : amax / 2688.0f;
 }
 
-// Row RMS scale r = 1 / sqrt(ss / k + eps) from the row held in registers.
-template <int NB>
-__device__ __forceinline__ float row_rms_scale(const Block32 (&xb)[NB], int lane, int nblk,
-                                               int64_t k, float eps) {
-  float cs[NB];
+// ---------------------------------------------------------------- row RMS
+
+// Row reduction: `s` is the lane's block sum of squares (0 for lanes past the
+// row end); every thread of the workgroup calls this.  Returns
+// r = 1 / sqrt(ss / k + eps) of the lane's row.
+template <int WPR>
+__device__ __forceinline__ float row_rms(float s, int riw, int wir, int64_t k, float eps) {
+  __shared__ float part[4 * kMaxWavesPerRow];
+  s = wave_tree_sum(s);
+  if ((threadIdx.x & 63) == 0) part[riw * kMaxWavesPerRow + wir] = s;
+  __syncthreads();
+  float c[kMaxWavesPerRow];
 #pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    float s = (c * 64 + lane < nblk) ? block_sumsq(xb[c]) : 0.0f;
-    cs[c] = wave_tree_sum(s);
+  for (int i = 0; i < kMaxWavesPerRow; ++i) c[i] = i < WPR ? part[riw * kMaxWavesPerRow + i] : 0.0f;
+#pragma unroll
+  for (int w = kMaxWavesPerRow / 2; w >= 1; w >>= 1) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) c[i] = c[2 * i] + c[2 * i + 1];
   }
-#pragma unroll
-  for (int w = NB / 2; w >= 1; w >>= 1) {
-#pragma unroll
-    for (int i = 0; i < w; ++i) cs[i] = cs[2 * i] + cs[2 * i + 1];
-  }
-  float mean = cs[0] / (float)k;
+  float mean = c[0] / (float)k;
   float var = mean + eps;
-  float s = __builtin_sqrtf(var);
-  return 1.0f / s;
+  float sd = __builtin_sqrtf(var);
+  return 1.0f / sd;
 }
 
-template <int FMT, int NB>
-__global__ __launch_bounds__(256) void prep_norm_kernel(PrepArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= a.m) return;
-  const int nblk = (int)(a.k / 32);
-  const uint16_t *xr = a.x + row * a.ld_x;
-  Block32 xb[NB];
+// x_n = bf16((x * r) * gamma): returns the bf16 pairs and overwrites xf with x_n.
+__device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const uint16_t *g,
+                                            float r) {
+  uint32_t gw[16];
+  load32_cached(g, gw);
 #pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    int b = c * 64 + lane;
-    if (b < nblk) load_block(xr + 32 * b, xb[c]);
-  }
-  float r = row_rms_scale<NB>(xb, lane, nblk, a.k, a.eps);
-  float s_t = FMT == 1 ? nv_tensor_scale(a.tensor_scale) : 1.0f;
-  if (FMT == 1 && row == 0 && lane == 0) a.tensor_scale[0] = s_t;
-#pragma unroll
-  for (int c = 0; c < NB; ++c) {
-    int b = c * 64 + lane;
-    if (b < nblk) {
-      normalize_block(xb[c], a.gamma + 32 * b, r);
-      BlockOut o;
-      quantize_block<FMT>(xb[c], s_t, o);
-      store_block<FMT>(a, row, b, o);
-    }
+  for (int i = 0; i < 16; ++i) {
+    float lo = (xf[2 * i] * r) * bf16_lo(gw[i]);
+    float hi = (xf[2 * i + 1] * r) * bf16_hi(gw[i]);
+    xw[i] = pack_bf16x2(lo, hi);
+    xf[2 * i] = bf16_lo(xw[i]);
+    xf[2 * i + 1] = bf16_hi(xw[i]);
   }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256) void prep_plain_kernel(PrepArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= a.m) return;
-  const int nblk = (int)(a.k / 32);
-  const uint16_t *xr = a.x + row * a.ld_x;
-  float s_t = FMT == 1 ? nv_tensor_scale(a.tensor_scale) : 1.0f;
-  if (FMT == 1 && row == 0 && lane == 0) a.tensor_scale[0] = s_t;
-  for (int b = lane; b < nblk; b += 64) {
-    Block32 xb;
-    load_block(xr + 32 * b, xb);
-    BlockOut o;
-    quantize_block<FMT>(xb, s_t, o);
-    store_block<FMT>(a, row, b, o);
-  }
-}
+// ---------------------------------------------------------------- kernels
 
-// NVFP4 tensor amax of x_n: reduce |x_n| over the row, one atomic max per wave
-// (fp32 bit patterns of non-negative values order like unsigned integers).
-template <int NB, bool NORM>
-__global__ __launch_bounds__(256) void amax_rows_kernel(const uint16_t *x, int64_t ld_x,
-                                                        int64_t m, int64_t k,
-                                                        const uint16_t *gamma, float eps,
-                                                        float *ts) {
+// Workgroup = RPW rows x WPR waves; wave (riw, wir), lane -> block wir * 64 + lane.
+// Lanes past the row end (or past the last row) load a valid block of X and
+// contribute +0 to the sum of squares; they store nothing.
+template <int FMT, int WPR>
+__global__ __launch_bounds__(512) void prep_norm_kernel(PrepArgs a) {
+  constexpr int RPW = WPR <= 4 ? 4 / WPR : 1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= m) return;
-  const int nblk = (int)(k / 32);
-  const uint16_t *xr = x + row * ld_x;
-  uint32_t am = 0;
-  if (NORM) {
-    Block32 xb[NB];
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
-      int b = c * 64 + lane;
-      if (b < nblk) load_block(xr + 32 * b, xb[c]);
-    }
-    float r = row_rms_scale<NB>(xb, lane, nblk, k, eps);
-#pragma unroll
-    for (int c = 0; c < NB; ++c) {
-      int b = c * 64 + lane;
-      if (b < nblk) {
-        normalize_block(xb[c], gamma + 32 * b, r);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          am = max(am, max(xb[c].v[i] & 0x7FFFu, (xb[c].v[i] >> 16) & 0x7FFFu));
-      }
-    }
+  const int riw = wave / WPR, wir = wave - riw * WPR;
+  const int64_t row = (int64_t)blockIdx.x * RPW + riw;
+  const int64_t nblk = a.k / 32;
+  const int64_t b = (int64_t)wir * 64 + lane;
+  const bool has = row < a.m && b < nblk;
+  const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
+  uint32_t xw[16];
+  float xf[32];
+  load32(a.x + lrow * a.ld_x + 32 * lb, xw);
+  unpack32(xw, xf);
+  float s = block_sumsq(xf);
+  float r = row_rms<WPR>(has ? s : 0.0f, riw, wir, a.k, a.eps);
+  if (!has) return;
+  normalize32(xf, xw, a.gamma + 32 * b, r);
+  BlockOut o;
+  if (FMT == 0) {
+    quantize_block_mx(xw, xf, o);
   } else {
-    for (int b = lane; b < nblk; b += 64) {
-      Block32 xb;
-      load_block(xr + 32 * b, xb);
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        am = max(am, max(xb.v[i] & 0x7FFFu, (xb.v[i] >> 16) & 0x7FFFu));
-    }
+    float s_t = nv_tensor_scale(a.tensor_scale);
+    if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
+    quantize_block_nv(xf, s_t, o);
   }
+  store_block<FMT>(a, row, b, o);
+}
+
+// No normalization: blocks are independent.  Each wavefront takes 64
+// consecutive blocks of one row (chunk c of row r, wave-uniform).
+template <int FMT>
+__global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chunks) {
+  const uint32_t w = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t row32 = w / chunks;
+  const int64_t row = row32;
+  const int64_t b = (int64_t)(w - row32 * chunks) * 64 + (threadIdx.x & 63);
+  if (row >= a.m || b >= a.k / 32) return;
+  uint32_t xw[16];
+  float xf[32];
+  load32(a.x + row * a.ld_x + 32 * b, xw);
+  unpack32(xw, xf);
+  BlockOut o;
+  if (FMT == 0) {
+    quantize_block_mx(xw, xf, o);
+  } else {
+    float s_t = nv_tensor_scale(a.tensor_scale);
+    if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
+    quantize_block_nv(xf, s_t, o);
+  }
+  store_block<FMT>(a, row, b, o);
+}
+
+// NVFP4 tensor amax of x_n (one atomic max per wave; fp32 bit patterns of
+// non-negative values order like unsigned integers).
+__device__ __forceinline__ void wave_amax_atomic(uint32_t am, float *ts) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 64));
-  if (lane == 0) atomicMax(reinterpret_cast<unsigned int *>(ts + 1), am << 16);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int *>(ts + 1), am);
+}
+
+template <int WPR>
+__global__ __launch_bounds__(512) void amax_norm_kernel(PrepArgs a) {
+  constexpr int RPW = WPR <= 4 ? 4 / WPR : 1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int riw = wave / WPR, wir = wave - riw * WPR;
+  const int64_t row = (int64_t)blockIdx.x * RPW + riw;
+  const int64_t nblk = a.k / 32;
+  const int64_t b = (int64_t)wir * 64 + lane;
+  const bool has = row < a.m && b < nblk;
+  const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
+  uint32_t xw[16];
+  float xf[32];
+  load32_cached(a.x + lrow * a.ld_x + 32 * lb, xw);
+  unpack32(xw, xf);
+  float s = block_sumsq(xf);
+  float r = row_rms<WPR>(has ? s : 0.0f, riw, wir, a.k, a.eps);
+  uint32_t am = 0;
+  if (has) {
+    normalize32(xf, xw, a.gamma + 32 * b, r);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = max(am, __float_as_uint(xf[i]) & 0x7FFFFFFFu);
+  }
+  if (row < a.m) wave_amax_atomic(am, a.tensor_scale);
+}
+
+__global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *x, int64_t ld, int64_t m,
+                                                        int64_t k, float *ts) {
+  const int64_t nblk = k / 32;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t am = 0;
+  if (gid < m * nblk) {
+    const int64_t row = gid / nblk, b = gid - row * nblk;
+    uint32_t xw[16];
+    load32_cached(x + row * ld + 32 * b, xw);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = max(am, max(xw[i] & 0x7FFFu, (xw[i] >> 16) & 0x7FFFu));
+    am <<= 16;
+  }
+  wave_amax_atomic(am, ts);
 }
 
 __global__ void zero_amax_kernel(float *ts) { ts[1] = 0.0f; }
 
-int pick_nb(int64_t k) {
-  int64_t chunks = (k / 32 + 63) / 64;
-  int nb = 1;
-  while (nb < chunks) nb <<= 1;
-  return nb;
+template <int FMT, int WPR>
+void launch_norm(const PrepArgs &a, hipStream_t s) {
+  constexpr int RPW = WPR <= 4 ? 4 / WPR : 1;
+  const dim3 grid((unsigned)((a.m + RPW - 1) / RPW)), block(64 * WPR * RPW);
+  if (FMT == 1) amax_norm_kernel<WPR><<<grid, block, 0, s>>>(a);
+  prep_norm_kernel<FMT, WPR><<<grid, block, 0, s>>>(a);
 }
 
 template <int FMT>
 hipError_t launch_prepare(const PrepArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)((a.m + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
-  if (FMT == 1) {
-    zero_amax_kernel<<<1, 1, 0, s>>>(a.tensor_scale);
-    if (a.gamma) {
-      switch (pick_nb(a.k)) {
-        case 1: amax_rows_kernel<1, true><<<grid, block, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.gamma, a.eps, a.tensor_scale); break;
-        case 2: amax_rows_kernel<2, true><<<grid, block, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.gamma, a.eps, a.tensor_scale); break;
-        case 4: amax_rows_kernel<4, true><<<grid, block, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.gamma, a.eps, a.tensor_scale); break;
-        default: amax_rows_kernel<8, true><<<grid, block, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.gamma, a.eps, a.tensor_scale); break;
-      }
-    } else {
-      amax_rows_kernel<1, false><<<grid, block, 0, s>>>(a.x, a.ld_x, a.m, a.k, nullptr, a.eps, a.tensor_scale);
-    }
-  }
+  const int64_t total = a.m * (a.k / 32);
+  const dim3 flat_grid((unsigned)((total + 255) / 256));
+  if (FMT == 1) zero_amax_kernel<<<1, 1, 0, s>>>(a.tensor_scale);
   if (a.gamma) {
-    switch (pick_nb(a.k)) {
-      case 1: prep_norm_kernel<FMT, 1><<<grid, block, 0, s>>>(a); break;
-      case 2: prep_norm_kernel<FMT, 2><<<grid, block, 0, s>>>(a); break;
-      case 4: prep_norm_kernel<FMT, 4><<<grid, block, 0, s>>>(a); break;
-      default: prep_norm_kernel<FMT, 8><<<grid, block, 0, s>>>(a); break;
+    switch ((a.k / 32 + 63) / 64) {   // wavefronts per row
+      case 1: launch_norm<FMT, 1>(a, s); break;
+      case 2: launch_norm<FMT, 2>(a, s); break;
+      case 3: launch_norm<FMT, 3>(a, s); break;
+      case 4: launch_norm<FMT, 4>(a, s); break;
+      case 5: launch_norm<FMT, 5>(a, s); break;
+      case 6: launch_norm<FMT, 6>(a, s); break;
+      case 7: launch_norm<FMT, 7>(a, s); break;
+      default: launch_norm<FMT, 8>(a, s); break;
     }
   } else {
-    prep_plain_kernel<FMT><<<grid, block, 0, s>>>(a);
+    if (FMT == 1) amax_flat_kernel<<<flat_grid, 256, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.tensor_scale);
+    const uint32_t chunks = (uint32_t)((a.k / 32 + 63) / 64);
+    const uint64_t waves = (uint64_t)a.m * chunks;
+    prep_flat_kernel<FMT><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a, chunks);
   }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- weights
 
-// One lane per 32-element block of W (flat over rows); same block quantizer
-// as the residual of the preparation operator.
+// One lane per 32-element block of W: the same block quantizer as the
+// residual of the preparation operator (no mask, no normalization).
 template <int FMT>
 __global__ __launch_bounds__(256) void quant_weight_kernel(QuantArgs a) {
   const int64_t nblk = a.k / 32;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= a.n * nblk) return;
-  const int64_t row = gid / nblk;
-  const int b = (int)(gid - row * nblk);
-  Block32 wb;
-  load_block(a.w + row * a.ld_w + 32 * b, wb);
-  float s_t = 1.0f;
-  if (FMT == 1) {
-    s_t = nv_tensor_scale(a.tensor_scale);
-    if (gid == 0) a.tensor_scale[0] = s_t;
-  }
+  const int64_t row = gid / nblk, b = gid - row * nblk;
+  uint32_t ww[16];
   float v[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[2 * i] = bf16_lo(wb.v[i]);
-    v[2 * i + 1] = bf16_hi(wb.v[i]);
-  }
-  uint32_t c[32];
-  uint32_t scales = 0;
-  constexpr int kBlk = FMT == 0 ? 32 : 16;
-#pragma unroll
-  for (int h = 0; h < 32 / kBlk; ++h) {
+  load32(a.w + row * a.ld_w + 32 * b, ww);
+  unpack32(ww, v);
+  uint32_t q[4], scales;
+  if (FMT == 0) {
     uint32_t am = 0;
 #pragma unroll
-    for (int i = 0; i < kBlk; ++i) am = max(am, __float_as_uint(v[h * kBlk + i]) & 0x7FFFFFFFu);
-    if (FMT == 0) {
-      uint32_t sb = e8m0_from_amax_bits(am);
-      float inv = e8m0_inv(sb);
-      scales |= sb << (8 * h);
+    for (int i = 0; i < 16; ++i) am = max(am, max(ww[i] & 0x7FFFu, (ww[i] >> 16) & 0x7FFFu));
+    int ex = (int)(am >> 7);
+    uint32_t sb = ex > 2 ? (uint32_t)(ex - 2) : 0u;
+    float ss = e8m0_operand(sb);
+    scales = sb;
+    uint32_t w4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < kBlk; ++i) c[h * kBlk + i] = e2m1_encode(v[h * kBlk + i] * inv);
-    } else {
-      float ratio = __uint_as_float(am) / (6.0f * s_t);
-      uint32_t sb = e4m3_encode_pos(ratio);
-      float S = e4m3_value(sb) * s_t;
-      scales |= sb << (8 * h);
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        float t = v[h * kBlk + i];
-        c[h * kBlk + i] = (S == 0.0f) ? ((__float_as_uint(t) >> 28) & 8u) : e2m1_encode(t / S);
+    for (int i = 0; i < 16; ++i) {
+      bf16x2 pv = __builtin_bit_cast(bf16x2, ww[i]);
+      uint32_t &x = w4[i >> 2];
+      switch (i & 3) {
+        case 0: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(x, pv, ss, 0); break;
+        case 1: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(x, pv, ss, 1); break;
+        case 2: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(x, pv, ss, 2); break;
+        default: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(x, pv, ss, 3); break;
       }
     }
-  }
-  uint32_t q[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t w = 0;
+    for (int j = 0; j < 4; ++j) q[j] = w4[j];
+  } else {
+    float s_t = nv_tensor_scale(a.tensor_scale);
+    if (gid == 0) a.tensor_scale[0] = s_t;
+    uint32_t a0 = 0, a1 = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= c[8 * j + i] << (4 * i);
-    q[j] = w;
+    for (int i = 0; i < 8; ++i) a0 = max(a0, max(ww[i] & 0x7FFFu, (ww[i] >> 16) & 0x7FFFu));
+#pragma unroll
+    for (int i = 8; i < 16; ++i) a1 = max(a1, max(ww[i] & 0x7FFFu, (ww[i] >> 16) & 0x7FFFu));
+    float S[2];
+    uint32_t sb0 = nv_scale(__uint_as_float(a0 << 16), s_t, S[0]);
+    uint32_t sb1 = nv_scale(__uint_as_float(a1 << 16), s_t, S[1]);
+    scales = sb0 | (sb1 << 8);
+    nv_codes(v, S, q);
   }
   *reinterpret_cast<uint4 *>(a.codes + row * a.ld_c + 16 * b) = make_uint4(q[0], q[1], q[2], q[3]);
   if (FMT == 0)
     a.scales[row * a.ld_s + b] = (uint8_t)scales;
   else
     *reinterpret_cast<uint16_t *>(a.scales + row * a.ld_s + 2 * b) = (uint16_t)scales;
-}
-
-__global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *w, int64_t ld_w, int64_t n,
-                                                        int64_t k, float *ts) {
-  const int64_t nblk = k / 32;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  uint32_t am = 0;
-  if (gid < n * nblk) {
-    const int64_t row = gid / nblk;
-    const int b = (int)(gid - row * nblk);
-    Block32 wb;
-    load_block(w + row * ld_w + 32 * b, wb);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am = max(am, max(wb.v[i] & 0x7FFFu, (wb.v[i] >> 16) & 0x7FFFu));
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int *>(ts + 1), am << 16);
 }
 
 template <int FMT>

@@ -128,7 +128,10 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
   // one weight payload, two scale views
   if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes) return SHARQ_ERR_SHAPE;
   if (fmt == SHARQ_MXFP4 && variant == SHARQ_GEMM_SPARSE_MFMA) return SHARQ_ERR_UNSUPPORTED;
-  const bool dense_expanded = variant == SHARQ_GEMM_DENSE_EXPANDED;
+  // AUTO reads the dense backbone view when the caller has one (no expansion
+  // work in the GEMM), else the 2:4 form
+  const bool dense_expanded = variant == SHARQ_GEMM_DENSE_EXPANDED ||
+                              (variant == SHARQ_GEMM_AUTO && sp->dense_codes != nullptr);
   if (dense_expanded) {
     if (!sp->dense_codes) return SHARQ_ERR_NULL;
     if (sp->ld_dense < k / 2) return SHARQ_ERR_SHAPE;
