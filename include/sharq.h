@@ -65,6 +65,22 @@ typedef enum {
     SHARQ_GEMM_SPARSE_MFMA = 3     /* backbone on the structured-sparse MFMA (see sharq_dual_gemm) */
 } sharq_gemm_variant;
 
+/*
+ * Layout of a block-scale array (sharq_fp4_view.scale_layout).
+ *   ROW_MAJOR:   the scale byte of row r, k-block j sits at scales[r * ld_scales + j].
+ *   KSTEP_MAJOR: k is cut into steps of 128; the scale bytes of row r in step t
+ *                (4 for MXFP4, 8 for NVFP4, in k order) are contiguous, rows of a
+ *                step are contiguous: the bytes start at
+ *                scales + (t * ld_scales + r) * (128 / block); ld_scales >= rows
+ *                counts rows per step.  Needs k % 128 == 0.  This is the view the
+ *                GEMM reads fastest: 64 rows of one step are 256 (MX) or 512 (NV)
+ *                contiguous bytes.
+ */
+typedef enum {
+    SHARQ_SCALES_ROW_MAJOR = 0,
+    SHARQ_SCALES_KSTEP_MAJOR = 1
+} sharq_scale_layout;
+
 /* Which array sharq_bytes sizes. */
 enum {
     SHARQ_BYTES_DENSE_CODES = 0,   /* dense FP4 codes: rows x k/2 */
@@ -83,7 +99,8 @@ enum {
  *   meta         backbone only (else NULL): [rows, k/8]; per group of four k the
  *                nibble i0 | i1 << 2 (kept indices, i0 < i1); group 2j sits in
  *                the low nibble of byte j.
- *   scales       [rows, k/32] E8M0 bytes (MXFP4) or [rows, k/16] E4M3 bytes (NVFP4).
+ *   scales       E8M0 bytes (MXFP4, one per 32 k) or E4M3 bytes (NVFP4, one per
+ *                16 k) of every row, in the layout `scale_layout` names.
  *   dense_codes  optional backbone in the dense layout of `codes` (zeros at the
  *                dropped positions); written by sharq_prepare when non-NULL and
  *                read by SHARQ_GEMM_DENSE_EXPANDED.  NULL otherwise.
@@ -97,6 +114,8 @@ typedef struct sharq_fp4_view {
     int64_t ld_meta;
     uint8_t *scales;
     int64_t ld_scales;
+    int32_t scale_layout;   /* sharq_scale_layout */
+    int32_t reserved;       /* must be 0 */
     uint8_t *dense_codes;
     int64_t ld_dense;
     float *tensor_scale;
@@ -117,8 +136,9 @@ typedef struct sharq_fp4_view {
  * Writes w_out->codes [n, k/2], w_out->scales, and for NVFP4
  * w_out->tensor_scale[0..1].  meta and dense_codes are ignored.
  * Requirements: n >= 1, k >= 32, k % 32 == 0, ld_w >= k, ld_w % 8 == 0;
- * w_bf16 and codes 16-byte aligned; ld_codes >= k/2 and % 16 == 0;
- * ld_scales >= k/blk; NVFP4: scales 2-byte aligned and ld_scales even.
+ * w_bf16 and codes 16-byte aligned; ld_codes >= k/2 and % 16 == 0; scales:
+ * ROW_MAJOR ld_scales >= k/blk (NVFP4: 2-byte aligned, ld even); KSTEP_MAJOR
+ * k % 128 == 0, ld_scales >= n, 4-byte (MX) or 8-byte (NV) aligned.
  */
 sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int64_t n,
                                    int64_t k, int64_t ld_w, const sharq_fp4_view *w_out,
@@ -146,8 +166,9 @@ sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int
  * Requirements: m >= 1; k >= 32, k % 32 == 0; k <= 16384 when gamma is given;
  * ld_x >= k, ld_x % 8 == 0; x 16-byte aligned; sparse codes 8-byte aligned with
  * ld % 8 == 0; meta 4-byte aligned with ld % 4 == 0; residual codes and
- * dense_codes 16-byte aligned with ld % 16 == 0; NVFP4 scales 2-byte aligned
- * with even ld; every ld at least the row length it describes.
+ * dense_codes 16-byte aligned with ld % 16 == 0; scales as for
+ * sharq_quantize_weight (with m rows); every ld at least the row length it
+ * describes.
  */
 sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
                            int64_t ld_x, const uint16_t *gamma_bf16, float eps,
@@ -171,8 +192,9 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
  * SHARQ_ERR_UNSUPPORTED for MXFP4.
  * Requirements: m, n >= 1; k >= 128, k % 128 == 0; ld_y >= n; codes 16-byte
  * aligned with ld % 16 == 0 (backbone codes too;
- * meta ld % 8 == 0 and 8-byte aligned); scales 4-byte aligned with ld % 4 == 0;
- * y 4-byte aligned.
+ * meta ld % 8 == 0 and 8-byte aligned); scales ROW_MAJOR 4-byte aligned with
+ * ld % 4 == 0, or KSTEP_MAJOR with ld >= rows (the fast path: all four views
+ * KSTEP_MAJOR); y 4-byte aligned.
  */
 sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sparse,
                              const sharq_fp4_view *resid, const sharq_fp4_view *w_sparse_view,
@@ -188,7 +210,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 1
+#define SHARQ_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -29,13 +29,16 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_DEVICE = range(6)
 
 BYTES_DENSE_CODES, BYTES_SPARSE_CODES, BYTES_META, BYTES_SCALES = range(4)
 
+SCALES_ROW_MAJOR = 0
+SCALES_KSTEP_MAJOR = 1
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 # every symbol include/sharq.h declares
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_dual_gemm", "sharq_bytes",
            "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class SharqError(RuntimeError):
@@ -50,6 +53,7 @@ class FP4ViewC(ctypes.Structure):
         ("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
         ("meta", ctypes.c_void_p), ("ld_meta", ctypes.c_int64),
         ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64),
+        ("scale_layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("dense_codes", ctypes.c_void_p), ("ld_dense", ctypes.c_int64),
         ("tensor_scale", ctypes.c_void_p),
     ]
@@ -118,6 +122,12 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _ld(t) -> int:
+    """Row stride of a row-major 2-D tensor, in elements (the stride of a
+    single-row tensor is arbitrary; its row length is used instead)."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
 def _bits16(t):
     """bf16 (or int16/uint16 bit pattern) tensor -> its data, as stored."""
     torch = _torch()
@@ -130,28 +140,40 @@ def _bits16(t):
 
 @dataclasses.dataclass
 class FP4Tensor:
-    """Device buffers of one FP4 operand (see ``sharq_fp4_view``)."""
+    """Device buffers of one FP4 operand (see ``sharq_fp4_view``).
+
+    scales: uint8 [rows, k/blk] (row-major) or [k/128, rows, 128/blk]
+    (k-step-major, the layout the GEMM reads fastest)."""
     fmt: int
     rows: int
     k: int
     codes: object                   # uint8 [rows, k/2] or [rows, k/4] (backbone)
-    scales: object                  # uint8 [rows, k/blk]
+    scales: object
     meta: object = None             # uint8 [rows, k/8] (backbone)
     dense_codes: object = None      # uint8 [rows, k/2] (optional backbone view)
     tensor_scale: object = None     # float32 [2] (NVFP4)
+    scale_layout: int = SCALES_ROW_MAJOR
 
     def view(self) -> FP4ViewC:
         v = FP4ViewC()
         v.codes = _ptr(self.codes)
-        v.ld_codes = self.codes.stride(0)
+        v.ld_codes = _ld(self.codes)
         if self.meta is not None:
             v.meta = _ptr(self.meta)
-            v.ld_meta = self.meta.stride(0)
+            v.ld_meta = _ld(self.meta)
         v.scales = _ptr(self.scales)
-        v.ld_scales = self.scales.stride(0)
+        v.scale_layout = self.scale_layout
+        if self.scale_layout == SCALES_KSTEP_MAJOR:
+            sc = self.scales                     # [k/128, rows, 128/blk]
+            if sc.stride(2) != 1 or (sc.shape[1] > 1 and sc.stride(1) != sc.shape[2]):
+                raise ValueError("k-step-major scales must be contiguous within a step")
+            # rows per k step
+            v.ld_scales = sc.stride(0) // sc.shape[2] if sc.shape[0] > 1 else sc.shape[1]
+        else:
+            v.ld_scales = _ld(self.scales)
         if self.dense_codes is not None:
             v.dense_codes = _ptr(self.dense_codes)
-            v.ld_dense = self.dense_codes.stride(0)
+            v.ld_dense = _ld(self.dense_codes)
         if self.tensor_scale is not None:
             v.tensor_scale = _ptr(self.tensor_scale)
         return v
@@ -162,34 +184,57 @@ def _alloc(rows, cols, device, dtype=None):
     return torch.empty((rows, cols), dtype=dtype or torch.uint8, device=device)
 
 
-def quantize_weight(w, fmt: int = MXFP4, stream=None) -> FP4Tensor:
+def default_scale_layout(k: int) -> int:
+    return SCALES_KSTEP_MAJOR if k % 128 == 0 else SCALES_ROW_MAJOR
+
+
+def alloc_scales(fmt: int, rows: int, k: int, layout: int, device):
+    """Scale array of `rows` rows in the given layout."""
+    torch = _torch()
+    blk = BLOCK[fmt]
+    if layout == SCALES_KSTEP_MAJOR:
+        return torch.empty((k // 128, rows, 128 // blk), dtype=torch.uint8, device=device)
+    return torch.empty((rows, k // blk), dtype=torch.uint8, device=device)
+
+
+def scales_row_major(t: FP4Tensor):
+    """The operand's scales as a [rows, k/blk] tensor (a copy if k-step-major)."""
+    if t.scale_layout == SCALES_KSTEP_MAJOR:
+        return t.scales.permute(1, 0, 2).reshape(t.rows, -1)
+    return t.scales
+
+
+def quantize_weight(w, fmt: int = MXFP4, scale_layout: Optional[int] = None,
+                    stream=None) -> FP4Tensor:
     """One FP4 payload of W [n, k] (both GEMM paths read it)."""
     torch = _torch()
     w = _bits16(w)
     n, k = w.shape
-    blk = BLOCK[fmt]
-    out = FP4Tensor(fmt, n, k, _alloc(n, k // 2, w.device), _alloc(n, k // blk, w.device))
+    layout = default_scale_layout(k) if scale_layout is None else scale_layout
+    out = FP4Tensor(fmt, n, k, _alloc(n, k // 2, w.device),
+                    alloc_scales(fmt, n, k, layout, w.device), scale_layout=layout)
     if fmt == NVFP4:
         out.tensor_scale = torch.zeros(2, dtype=torch.float32, device=w.device)
     v = out.view()
-    _check(lib().sharq_quantize_weight(fmt, w.data_ptr(), n, k, w.stride(0), ctypes.byref(v),
+    _check(lib().sharq_quantize_weight(fmt, w.data_ptr(), n, k, _ld(w), ctypes.byref(v),
                                        _stream_ptr(stream)), "sharq_quantize_weight")
     return out
 
 
 def prepare(x, gamma=None, eps: float = 1e-5, fmt: int = MXFP4, dense_backbone: bool = False,
-            stream=None):
+            scale_layout: Optional[int] = None, stream=None):
     """Fused preparation of X [m, k]: returns (backbone, residual) FP4 operands."""
     torch = _torch()
     x = _bits16(x)
     m, k = x.shape
-    blk = BLOCK[fmt]
     dev = x.device
-    sp = FP4Tensor(fmt, m, k, _alloc(m, k // 4, dev), _alloc(m, k // blk, dev),
-                   meta=_alloc(m, k // 8, dev))
+    layout = default_scale_layout(k) if scale_layout is None else scale_layout
+    sp = FP4Tensor(fmt, m, k, _alloc(m, k // 4, dev), alloc_scales(fmt, m, k, layout, dev),
+                   meta=_alloc(m, k // 8, dev), scale_layout=layout)
     if dense_backbone:
         sp.dense_codes = _alloc(m, k // 2, dev)
-    rs = FP4Tensor(fmt, m, k, _alloc(m, k // 2, dev), _alloc(m, k // blk, dev))
+    rs = FP4Tensor(fmt, m, k, _alloc(m, k // 2, dev), alloc_scales(fmt, m, k, layout, dev),
+                   scale_layout=layout)
     if fmt == NVFP4:
         sp.tensor_scale = torch.zeros(2, dtype=torch.float32, device=dev)
         rs.tensor_scale = sp.tensor_scale
@@ -203,7 +248,7 @@ def prepare_into(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None):
     g = None if gamma is None else _bits16(gamma)
     m, k = x.shape
     vs, vr = sp.view(), rs.view()
-    _check(lib().sharq_prepare(sp.fmt, x.data_ptr(), m, k, x.stride(0), _ptr(g), float(eps),
+    _check(lib().sharq_prepare(sp.fmt, x.data_ptr(), m, k, _ld(x), _ptr(g), float(eps),
                                ctypes.byref(vs), ctypes.byref(vr), _stream_ptr(stream)),
            "sharq_prepare")
 
@@ -216,12 +261,12 @@ def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AU
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=w.codes.device)
     wv_s = w.view()
-    wv_d = w.view()
     if w_dense_scales is not None:
-        wv_d.scales = _ptr(w_dense_scales)
-        wv_d.ld_scales = w_dense_scales.stride(0)
+        wv_d = dataclasses.replace(w, scales=w_dense_scales).view()
+    else:
+        wv_d = w.view()
     vs, vr = sp.view(), rs.view()
     _check(lib().sharq_dual_gemm(sp.fmt, ctypes.byref(vs), ctypes.byref(vr), ctypes.byref(wv_s),
-                                 ctypes.byref(wv_d), m, n, k, out.data_ptr(), out.stride(0),
+                                 ctypes.byref(wv_d), m, n, k, out.data_ptr(), _ld(out),
                                  variant, _stream_ptr(stream)), "sharq_dual_gemm")
     return out

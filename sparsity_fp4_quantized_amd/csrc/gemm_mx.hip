@@ -33,6 +33,8 @@
 // same assignment, so the dot products are unchanged.  The row's scale word
 // is shifted right by 16h once and op_sel picks byte 0 or 1.
 // Accumulator: lane l holds column l % 32, rows 8 (r / 4) + 4 h + r % 4.
+#include <stddef.h>
+
 #include "fp4_device.h"
 #include "kernels.h"
 
@@ -92,6 +94,13 @@ struct Smem {
   uint32_t sas[2][BM], sar[2][BM], sws[2][BN], swd[2][BN];
 };
 
+// The 32-bit word of E8M0 scales of row r for 128-k step kt.
+__device__ __forceinline__ uint32_t scale_word(const uint8_t *p, int64_t ld, int kstep, int64_t r,
+                                               int kt) {
+  const int64_t off = kstep ? ((int64_t)kt * ld + r) * 4 : r * ld + (int64_t)kt * 4;
+  return *reinterpret_cast<const uint32_t *>(p + off);
+}
+
 template <int BN, bool kDense>
 __device__ __forceinline__ void load_stage(const GemmArgs &a, int64_t m0, int64_t n0, int kt,
                                            Stage<BN, kDense> &st) {
@@ -129,12 +138,12 @@ __device__ __forceinline__ void load_stage(const GemmArgs &a, int64_t m0, int64_
   // scale words: threads [0, 256) the two A paths of row tid; [256, 256 + BN) the two W views
   if (tid < BM) {
     const int64_t gm = m0 + tid;
-    st.sc[0] = gm < a.m ? *reinterpret_cast<const uint32_t *>(a.s_scales + gm * a.ld_ss + kt * 4) : 0u;
-    st.sc[1] = gm < a.m ? *reinterpret_cast<const uint32_t *>(a.r_scales + gm * a.ld_rs + kt * 4) : 0u;
+    st.sc[0] = gm < a.m ? scale_word(a.s_scales, a.ld_ss, a.ss_kstep, gm, kt) : 0u;
+    st.sc[1] = gm < a.m ? scale_word(a.r_scales, a.ld_rs, a.rs_kstep, gm, kt) : 0u;
   } else if (tid < BM + BN) {
     const int64_t gn = n0 + (tid - BM);
-    st.sc[0] = gn < a.n ? *reinterpret_cast<const uint32_t *>(a.ws_scales + gn * a.ld_wss + kt * 4) : 0u;
-    st.sc[1] = gn < a.n ? *reinterpret_cast<const uint32_t *>(a.wd_scales + gn * a.ld_wds + kt * 4) : 0u;
+    st.sc[0] = gn < a.n ? scale_word(a.ws_scales, a.ld_wss, a.wss_kstep, gn, kt) : 0u;
+    st.sc[1] = gn < a.n ? scale_word(a.wd_scales, a.ld_wds, a.wds_kstep, gn, kt) : 0u;
   }
 }
 
@@ -269,21 +278,14 @@ __global__ __launch_bounds__(kThreads) void dual_gemm_mx_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Dense-operand pipeline: the backbone is read in its dense layout, so all
 // three operand tiles and the four scale arrays go global -> LDS with
-// global_load_lds_dwordx{4,1} (lane l's bytes land at base + l * size), two K
-// steps ahead of the MFMAs, into a ring of three LDS stages.  Each wavefront
-// issues a fixed share of the load instructions of every stage; before a step
-// it waits until at most the next stage's share is still in flight, then a
-// barrier makes all wavefronts' loads visible and frees the stage read two
-// steps earlier.  Rows past M or N load the last valid row; their outputs are
-// never stored.
-
-template <int BN>
-struct DStage {
-  u32x4 as[BM * 4];
-  u32x4 ar[BM * 4];
-  u32x4 w[BN * 4];
-  uint32_t sas[BM], sar[BM], sws[BN], swd[BN];
-};
+// buffer_load ... lds (lane l's bytes land at M0 + l * size; loads past the
+// end of an operand read 0), STAGES - 1 K steps ahead of the MFMAs, into a
+// ring of STAGES LDS stages.  A workgroup of NW wavefronts owns a TBM x TBN
+// tile; small tiles let two workgroups share a CU, so that one workgroup's
+// MFMAs run while the other waits at its barrier.  Before a step each
+// wavefront waits until at most the later stages' loads are in flight, then
+// a barrier makes all wavefronts' loads visible and frees the stage read on
+// the previous step.
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -302,8 +304,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-// buffer_load ... lds: lane l's bytes land at M0 + l * size.  The asm has no
-// register result, and its completion is waited for explicitly (vmcnt).
+// buffer_load ... lds: the asm has no register result, and its completion is
+// waited for explicitly (vmcnt) before the barrier that publishes the stage.
 __device__ __forceinline__ void b2l16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
@@ -313,90 +315,106 @@ __device__ __forceinline__ void b2l4(i32x4 rsrc, uint32_t voff, uint32_t soff, u
                :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
-// Load plan of one stage, per wavefront w: 16-byte chunk loads of 16 rows
-// each (A backbone, A residual: q = w, w + 8; W: q = w, w + 8 while
-// q < BN / 16) and 4-byte scale loads of 64 rows each (t = w, w + 8 while
-// t < kS, over the four scale arrays in turn).
-template <int BN>
+template <int TBM, int TBN>
+struct DStage {
+  u32x4 as[TBM * 4];
+  u32x4 ar[TBM * 4];
+  u32x4 w[TBN * 4];
+  uint32_t sas[TBM], sar[TBM], sws[TBN], swd[TBN];
+};
+
+// Load plan of one stage: 16-byte chunk loads of 16 rows each (A backbone,
+// A residual, W), then 4-byte scale loads of 64 rows each (backbone, residual,
+// W sparse view, W dense view); wavefront w takes loads w, w + NW, ...
+template <int TBM, int TBN, int NW>
 struct DPlan {
-  static constexpr int kW = BN / 16;
-  static constexpr int kS = 2 * (BM / 64) + 2 * (BN / 64);
-  static constexpr int kMinPerWave = 4 + kW / 8 + kS / 8;   // the waitcnt allowance
+  static constexpr int kA = TBM / 16, kW = TBN / 16;
+  static constexpr int kS = 2 * (TBM / 64) + 2 * (TBN / 64);
+  static constexpr int kChunkPer = (2 * kA + kW + NW - 1) / NW;
+  static constexpr int kScalePer = (kS + NW - 1) / NW;
+  static constexpr int kMinPerWave = (2 * kA + kW) / NW + kS / NW;   // waitcnt allowance per stage
 };
 
 struct DRsrc {
   i32x4 as, ar, w, sas, sar, sws, swd;
 };
 
+template <int TBM, int TBN, int NW>
 struct DOffs {
-  uint32_t as[2], ar[2], w[2], sc[2];
+  uint32_t chunk[DPlan<TBM, TBN, NW>::kChunkPer];
+  uint32_t scale[DPlan<TBM, TBN, NW>::kScalePer];
+  uint32_t ld_ss, ld_rs, ld_wss, ld_wds;   // bytes per 128-k step of each scale view
 };
 
-constexpr int kOffAr = BM * 64, kOffW = 2 * BM * 64;
-
-template <int BN>
+template <int TBM, int TBN, int NW>
 __device__ __forceinline__ void plan_loads(const GemmArgs &a, int64_t m0, int64_t n0, int wave,
-                                           int lane, DRsrc &R, DOffs &O) {
+                                           int lane, DRsrc &R, DOffs<TBM, TBN, NW> &O) {
+  using P = DPlan<TBM, TBN, NW>;
   const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   R.as = make_rsrc(a.s_dense + m0 * a.ld_sd, (uint32_t)((a.m - m0) * a.ld_sd));
   R.ar = make_rsrc(a.r_codes + m0 * a.ld_rc, (uint32_t)((a.m - m0) * a.ld_rc));
   R.w = make_rsrc(a.w_codes + n0 * a.ld_wc, (uint32_t)((a.n - n0) * a.ld_wc));
-  R.sas = make_rsrc(a.s_scales + m0 * a.ld_ss, (uint32_t)((a.m - m0) * a.ld_ss));
-  R.sar = make_rsrc(a.r_scales + m0 * a.ld_rs, (uint32_t)((a.m - m0) * a.ld_rs));
-  R.sws = make_rsrc(a.ws_scales + n0 * a.ld_wss, (uint32_t)((a.n - n0) * a.ld_wss));
-  R.swd = make_rsrc(a.wd_scales + n0 * a.ld_wds, (uint32_t)((a.n - n0) * a.ld_wds));
+  // k-step-major scales: step t of row r at (t * ld + r) * 4; the resource
+  // starts at the tile's first row and ends at the array's last row of the
+  // last step, so rows past M (N) of the last step read 0
+  const int64_t steps = a.k / BK;
+  R.sas = make_rsrc(a.s_scales + m0 * 4, (uint32_t)(((steps - 1) * a.ld_ss + a.m - m0) * 4));
+  R.sar = make_rsrc(a.r_scales + m0 * 4, (uint32_t)(((steps - 1) * a.ld_rs + a.m - m0) * 4));
+  R.sws = make_rsrc(a.ws_scales + n0 * 4, (uint32_t)(((steps - 1) * a.ld_wss + a.n - n0) * 4));
+  R.swd = make_rsrc(a.wd_scales + n0 * 4, (uint32_t)(((steps - 1) * a.ld_wds + a.n - n0) * 4));
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 16 * (wave + 8 * j) + lrow;
-    O.as[j] = (uint32_t)(row * a.ld_sd + lchunk * 16);
-    O.ar[j] = (uint32_t)(row * a.ld_rc + lchunk * 16);
-    O.w[j] = (uint32_t)(row * a.ld_wc + lchunk * 16);
-    // scale load t = wave + 8 j: array t / (rows / 64) in the order sas, sar, sws, swd
-    int t = wave + 8 * j;
-    int64_t ld;
-    if (t < BM / 64) ld = a.ld_ss;
-    else if ((t -= BM / 64) < BM / 64) ld = a.ld_rs;
-    else if ((t -= BM / 64) < BN / 64) ld = a.ld_wss;
-    else { t -= BN / 64; ld = a.ld_wds; }
-    O.sc[j] = (uint32_t)((64 * t + lane) * ld);
+  for (int j = 0; j < P::kChunkPer; ++j) {
+    int q = wave + NW * j;
+    int64_t ld = a.ld_sd;
+    if (q >= P::kA && q < 2 * P::kA) { q -= P::kA; ld = a.ld_rc; }
+    else if (q >= 2 * P::kA) { q -= 2 * P::kA; ld = a.ld_wc; }
+    O.chunk[j] = (uint32_t)((16 * q + lrow) * ld + lchunk * 16);
   }
+#pragma unroll
+  for (int j = 0; j < P::kScalePer; ++j) {
+    int t = wave + NW * j;
+    if (t >= TBM / 64 && (t -= TBM / 64) >= TBM / 64 && (t -= TBM / 64) >= TBN / 64) t -= TBN / 64;
+    O.scale[j] = (uint32_t)((64 * t + lane) * 4);
+  }
+  O.ld_ss = (uint32_t)(a.ld_ss * 4);
+  O.ld_rs = (uint32_t)(a.ld_rs * 4);
+  O.ld_wss = (uint32_t)(a.ld_wss * 4);
+  O.ld_wds = (uint32_t)(a.ld_wds * 4);
 }
 
-template <int BN>
-__device__ __forceinline__ void issue_stage(const DRsrc &R, const DOffs &O, int wave, int kt,
-                                            const DStage<BN> &S) {
-  using P = DPlan<BN>;
+template <int TBM, int TBN, int NW>
+__device__ __forceinline__ void issue_stage(const DRsrc &R, const DOffs<TBM, TBN, NW> &O, int wave,
+                                            int kt, const DStage<TBM, TBN> &S) {
+  using P = DPlan<TBM, TBN, NW>;
+  using St = DStage<TBM, TBN>;
   const uint32_t base = lds_addr(&S);
-  const uint32_t kc = (uint32_t)kt * 64u, ks = (uint32_t)kt * 4u;
+  const uint32_t kc = (uint32_t)kt * 64u;
+  constexpr uint32_t oar = offsetof(St, ar), ow = offsetof(St, w);
+  constexpr uint32_t osas = offsetof(St, sas), osar = offsetof(St, sar);
+  constexpr uint32_t osws = offsetof(St, sws), oswd = offsetof(St, swd);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = wave + 8 * j;
-    b2l16(R.as, O.as[j], kc, base + q * 1024);
-    b2l16(R.ar, O.ar[j], kc, base + kOffAr + q * 1024);
-    if (q < P::kW) b2l16(R.w, O.w[j], kc, base + kOffW + q * 1024);
+  for (int j = 0; j < P::kChunkPer; ++j) {
+    const int q = wave + NW * j;
+    if (q < P::kA) b2l16(R.as, O.chunk[j], kc, base + q * 1024);
+    else if (q < 2 * P::kA) b2l16(R.ar, O.chunk[j], kc, base + oar + (q - P::kA) * 1024);
+    else if (q < 2 * P::kA + P::kW) b2l16(R.w, O.chunk[j], kc, base + ow + (q - 2 * P::kA) * 1024);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int t = wave + 8 * j;
+  for (int j = 0; j < P::kScalePer; ++j) {
+    int t = wave + NW * j;
     if (t >= P::kS) continue;
-    const uint32_t sbase = base + kOffW + BN * 64;
-    if (t < BM / 64) {
-      b2l4(R.sas, O.sc[j], ks, sbase + 256 * t);
-    } else if ((t -= BM / 64) < BM / 64) {
-      b2l4(R.sar, O.sc[j], ks, sbase + 4 * BM + 256 * t);
-    } else if ((t -= BM / 64) < BN / 64) {
-      b2l4(R.sws, O.sc[j], ks, sbase + 8 * BM + 256 * t);
-    } else {
-      t -= BN / 64;
-      b2l4(R.swd, O.sc[j], ks, sbase + 8 * BM + 4 * BN + 256 * t);
-    }
+    if (t < TBM / 64) b2l4(R.sas, O.scale[j], kt * O.ld_ss, base + osas + 256 * t);
+    else if ((t -= TBM / 64) < TBM / 64) b2l4(R.sar, O.scale[j], kt * O.ld_rs, base + osar + 256 * t);
+    else if ((t -= TBM / 64) < TBN / 64) b2l4(R.sws, O.scale[j], kt * O.ld_wss, base + osws + 256 * t);
+    else b2l4(R.swd, O.scale[j], kt * O.ld_wds, base + oswd + 256 * (t - TBN / 64));
   }
 }
 
-template <int BN>
-__device__ __forceinline__ void compute_stage(const DStage<BN> &S, v16f (&acc)[2][BN / 64], int wm,
-                                              int wn, int h, int li) {
-  constexpr int TN = BN / 64;
+// One 128-k step of wavefront (wm, wn): 64 rows x TBN/2 columns.
+template <int TBM, int TBN>
+__device__ __forceinline__ void compute_stage(const DStage<TBM, TBN> &S, v16f (&acc)[2][TBN / 64],
+                                              int wm, int wn, int h, int li) {
+  constexpr int TN = TBN / 64;
   int sas[2], sar[2], sws[TN], swd[TN];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -406,7 +424,7 @@ __device__ __forceinline__ void compute_stage(const DStage<BN> &S, v16f (&acc)[2
   }
 #pragma unroll
   for (int jt = 0; jt < TN; ++jt) {
-    const int r = wn * (BN / 2) + jt * 32 + li;
+    const int r = wn * (TBN / 2) + jt * 32 + li;
     sws[jt] = (int)(S.sws[r] >> (16 * h));
     swd[jt] = (int)(S.swd[r] >> (16 * h));
   }
@@ -422,52 +440,51 @@ __device__ __forceinline__ void compute_stage(const DStage<BN> &S, v16f (&acc)[2
     }
 #pragma unroll
     for (int jt = 0; jt < TN; ++jt) {
-      const int r = wn * (BN / 2) + jt * 32 + li;
+      const int r = wn * (TBN / 2) + jt * 32 + li;
       fb[jt] = as_operand(S.w[lds_slot(r, c)]);
     }
+    // backbone MFMAs for every tile first, then the residual ones: 2 TN
+    // independent accumulators between two updates of the same tile
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int path = 0; path < 2; ++path)
 #pragma unroll
-      for (int jt = 0; jt < TN; ++jt) {
-        if (s == 0) {
-          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fas[it], fb[jt], acc[it][jt], 4, 4, 0, sas[it], 0, sws[jt]);
-          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              far[it], fb[jt], acc[it][jt], 4, 4, 0, sar[it], 0, swd[jt]);
-        } else {
-          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fas[it], fb[jt], acc[it][jt], 4, 4, 1, sas[it], 1, sws[jt]);
-          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              far[it], fb[jt], acc[it][jt], 4, 4, 1, sar[it], 1, swd[jt]);
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int jt = 0; jt < TN; ++jt) {
+          const v8i fa = path == 0 ? fas[it] : far[it];
+          const int sa = path == 0 ? sas[it] : sar[it];
+          const int sw = path == 0 ? sws[jt] : swd[jt];
+          if (s == 0)
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jt], acc[it][jt], 4, 4, 0, sa, 0, sw);
+          else
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jt], acc[it][jt], 4, 4, 1, sa, 1, sw);
         }
-      }
   }
 }
 
-// Wait until this wave's loads of the current stage have landed (the next
-// stage's, if issued, may still be in flight), then make all waves' loads visible.
-template <int BN>
-__device__ __forceinline__ void stage_ready(bool next_in_flight) {
-  if (next_in_flight)
-    __builtin_amdgcn_s_waitcnt(0x3F70 | (DPlan<BN>::kMinPerWave & 0xF) |
-                               ((DPlan<BN>::kMinPerWave >> 4) << 14));
-  else
-    __builtin_amdgcn_s_waitcnt(0x3F70);   // vmcnt(0)
-  // a bare barrier: the loads above are the only memory traffic to order, and
-  // the memory clobber keeps the compiler from moving LDS reads across it
-  asm volatile("s_barrier" ::: "memory");
+// vmcnt(n) with lgkmcnt and expcnt left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x3F70 | (N & 0xF) | ((N >> 4) << 14));
 }
 
-template <int BN>
-__global__ __launch_bounds__(kThreads) void dual_gemm_dense_kernel(GemmArgs a) {
-  constexpr int TN = BN / 64;
-  __shared__ DStage<BN> st[3];
+// A bare barrier: the explicit vmcnt wait before it is the only ordering the
+// stage needs, and the memory clobber keeps LDS reads from moving across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int TBM, int TBN, int NW, int STAGES>
+__global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a) {
+  static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
+  constexpr int TN = TBN / 64;
+  using P = DPlan<TBM, TBN, NW>;
+  __shared__ DStage<TBM, TBN> st[STAGES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, li = lane & 31;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int64_t m0 = (int64_t)blockIdx.y * TBM, n0 = (int64_t)blockIdx.x * TBN;
 
   v16f acc[2][TN];
 #pragma unroll
@@ -479,25 +496,32 @@ __global__ __launch_bounds__(kThreads) void dual_gemm_dense_kernel(GemmArgs a) {
 
   const int ksteps = (int)(a.k / BK);
   DRsrc R;
-  DOffs O;
-  plan_loads<BN>(a, m0, n0, wave, lane, R, O);
-  issue_stage<BN>(R, O, wave, 0, st[0]);
-  if (ksteps > 1) issue_stage<BN>(R, O, wave, 1, st[1]);
+  DOffs<TBM, TBN, NW> O;
+  plan_loads<TBM, TBN, NW>(a, m0, n0, wave, lane, R, O);
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < ksteps) issue_stage<TBM, TBN, NW>(R, O, wave, p, st[p]);
 
-  int cur = 0;                  // stage of step kt; (cur + 2) % 3 is free once all waves pass the barrier
+  int cur = 0;
   for (int kt = 0; kt < ksteps; ++kt) {
-    stage_ready<BN>(kt + 1 < ksteps);
-    const int nxt = cur == 0 ? 2 : cur - 1;
-    if (kt + 2 < ksteps) issue_stage<BN>(R, O, wave, kt + 2, st[nxt]);
-    compute_stage<BN>(st[cur], acc, wm, wn, h, li);
-    cur = cur == 2 ? 0 : cur + 1;
+    // stages kt + 1 .. kt + STAGES - 2 may stay in flight
+    const int ahead = min(ksteps - 1 - kt, STAGES - 2);
+    if (STAGES == 3 && ahead >= 1) wait_vmcnt<P::kMinPerWave>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + STAGES - 1 < ksteps) {
+      const int nxt = cur == 0 ? STAGES - 1 : cur - 1;
+      issue_stage<TBM, TBN, NW>(R, O, wave, kt + STAGES - 1, st[nxt]);
+    }
+    compute_stage<TBM, TBN>(st[cur], acc, wm, wn, h, li);
+    cur = cur == STAGES - 1 ? 0 : cur + 1;
   }
 
 #pragma unroll
   for (int it = 0; it < 2; ++it)
 #pragma unroll
     for (int jt = 0; jt < TN; ++jt) {
-      const int64_t col = n0 + wn * (BN / 2) + jt * 32 + li;
+      const int64_t col = n0 + wn * (TBN / 2) + jt * 32 + li;
       if (col >= a.n) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -507,25 +531,40 @@ __global__ __launch_bounds__(kThreads) void dual_gemm_dense_kernel(GemmArgs a) {
     }
 }
 
+template <int TBM, int TBN, int NW, int STAGES>
+void launch_dense(const GemmArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)((a.n + TBN - 1) / TBN), (unsigned)((a.m + TBM - 1) / TBM)), block(64 * NW);
+  dual_gemm_dense_kernel<TBM, TBN, NW, STAGES><<<grid, block, 0, s>>>(a);
+}
+
 template <int BN>
 void launch_bn(const GemmArgs &a, bool dense, hipStream_t s) {
   dim3 grid((unsigned)((a.n + BN - 1) / BN), (unsigned)((a.m + BM - 1) / BM)), block(kThreads);
   if (dense)
-    dual_gemm_dense_kernel<BN><<<grid, block, 0, s>>>(a);
+    dual_gemm_mx_kernel<BN, true><<<grid, block, 0, s>>>(a);
   else
     dual_gemm_mx_kernel<BN, false><<<grid, block, 0, s>>>(a);
 }
 
 }  // namespace
 
-// Tile width: fill the 256 CUs with as few, as large tiles as possible.
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s) {
-  const int64_t mt = (a.m + BM - 1) / BM;
-  auto tiles = [&](int bn) { return mt * ((a.n + bn - 1) / bn); };
-  if (tiles(192) >= 256 || tiles(128) > 256)
-    launch_bn<192>(a, dense_expanded, s);
-  else
-    launch_bn<128>(a, dense_expanded, s);
+  const bool kstep_scales = a.ss_kstep && a.rs_kstep && a.wss_kstep && a.wds_kstep;
+  if (dense_expanded && kstep_scales) {
+    // 128 x BN tiles, two workgroups per CU; the widest tile that still gives
+    // every CU two tiles
+    const int64_t mt = (a.m + 127) / 128;
+    if (mt * ((a.n + 191) / 192) >= 512)
+      launch_dense<128, 192, 4, 2>(a, s);
+    else
+      launch_dense<128, 128, 4, 3>(a, s);
+  } else {
+    const int64_t mt = (a.m + BM - 1) / BM;
+    if (mt * ((a.n + 191) / 192) >= 256 || mt * ((a.n + 127) / 128) > 256)
+      launch_bn<192>(a, dense_expanded, s);
+    else
+      launch_bn<128>(a, dense_expanded, s);
+  }
   return hipGetLastError();
 }
 

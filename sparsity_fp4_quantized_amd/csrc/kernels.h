@@ -19,6 +19,7 @@ struct PrepArgs {
   uint8_t *r_scales; int64_t ld_rs;
   uint8_t *s_dense;  int64_t ld_sd;   // optional
   float *tensor_scale;                // NVFP4: [0] scale, [1] amax
+  int s_kstep, r_kstep;               // scale arrays in the k-step-major layout
 };
 
 struct QuantArgs {
@@ -27,6 +28,7 @@ struct QuantArgs {
   uint8_t *codes;  int64_t ld_c;
   uint8_t *scales; int64_t ld_s;
   float *tensor_scale;                // NVFP4
+  int kstep;                          // scales in the k-step-major layout
 };
 
 struct GemmArgs {
@@ -43,6 +45,7 @@ struct GemmArgs {
   const float *w_tensor_scale;              // NVFP4
   float *y;                int64_t ld_y;
   int64_t m, n, k;
+  int ss_kstep, rs_kstep, wss_kstep, wds_kstep;   // per scale view: k-step-major layout
 };
 
 hipError_t launch_prepare_mx(const PrepArgs &a, hipStream_t s);

@@ -356,6 +356,21 @@ __device__ __forceinline__ void quantize_block_nv(const float xf[32], float s_t,
 
 // ---------------------------------------------------------------- stores
 
+// Scale bytes of the lane's 32 k (block b): MXFP4 one byte, NVFP4 two.
+// Row-major: byte offset row * ld + b (MX) or 2 b (NV).  K-step-major: step
+// t = b / 4 holds 4 (MX) or 8 (NV) bytes per row, rows contiguous.
+template <int FMT>
+__device__ __forceinline__ void store_scale(uint8_t *base, int64_t ld, bool kstep, int64_t row,
+                                            int64_t b, uint32_t v) {
+  if (FMT == 0) {
+    const int64_t off = kstep ? ((b >> 2) * ld + row) * 4 + (b & 3) : row * ld + b;
+    base[off] = (uint8_t)v;
+  } else {
+    const int64_t off = kstep ? ((b >> 2) * ld + row) * 8 + 2 * (b & 3) : row * ld + 2 * b;
+    *reinterpret_cast<uint16_t *>(base + off) = (uint16_t)v;
+  }
+}
+
 template <int FMT>
 __device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int64_t b,
                                             const BlockOut &o) {
@@ -366,13 +381,8 @@ __device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int6
   if (a.s_dense)
     *reinterpret_cast<uint4 *>(a.s_dense + row * a.ld_sd + 16 * b) =
         make_uint4(o.s_dense[0], o.s_dense[1], o.s_dense[2], o.s_dense[3]);
-  if (FMT == 0) {
-    a.s_scales[row * a.ld_ss + b] = (uint8_t)o.s_scale;
-    a.r_scales[row * a.ld_rs + b] = (uint8_t)o.r_scale;
-  } else {
-    *reinterpret_cast<uint16_t *>(a.s_scales + row * a.ld_ss + 2 * b) = (uint16_t)o.s_scale;
-    *reinterpret_cast<uint16_t *>(a.r_scales + row * a.ld_rs + 2 * b) = (uint16_t)o.r_scale;
-  }
+  store_scale<FMT>(a.s_scales, a.ld_ss, a.s_kstep, row, b, o.s_scale);
+  store_scale<FMT>(a.r_scales, a.ld_rs, a.r_kstep, row, b, o.r_scale);
 }
 
 __device__ __forceinline__ float nv_tensor_scale(const float *ts) {
@@ -616,10 +626,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(QuantArgs a) {
     nv_codes(v, S, q);
   }
   *reinterpret_cast<uint4 *>(a.codes + row * a.ld_c + 16 * b) = make_uint4(q[0], q[1], q[2], q[3]);
-  if (FMT == 0)
-    a.scales[row * a.ld_s + b] = (uint8_t)scales;
-  else
-    *reinterpret_cast<uint16_t *>(a.scales + row * a.ld_s + 2 * b) = (uint16_t)scales;
+  store_scale<FMT>(a.scales, a.ld_s, a.kstep, row, b, scales);
 }
 
 template <int FMT>

@@ -21,18 +21,29 @@ bool valid_format(sharq_format f) { return f == SHARQ_MXFP4 || f == SHARQ_NVFP4;
 
 sharq_status from_hip(hipError_t e) { return e == hipSuccess ? SHARQ_OK : SHARQ_ERR_DEVICE; }
 
-// Checks of one scale array: [rows, k/blk] bytes; `dword` asks for 4-byte
-// access (GEMM), otherwise NVFP4 needs 2-byte access (two blocks per lane).
-sharq_status check_scales(sharq_format f, const uint8_t *p, int64_t ld, int64_t k, bool dword) {
-  if (!p) return SHARQ_ERR_NULL;
-  if (ld < k / block_of(f)) return SHARQ_ERR_SHAPE;
+// Checks of one scale array of `rows` rows.  ROW_MAJOR: [rows, k/blk] bytes;
+// `dword` asks for 4-byte access (GEMM), otherwise NVFP4 needs 2-byte access
+// (two blocks per lane).  KSTEP_MAJOR: ld counts rows per 128-k step.
+sharq_status check_scales(sharq_format f, const sharq_fp4_view *v, int64_t rows, int64_t k,
+                          bool dword) {
+  if (!v->scales) return SHARQ_ERR_NULL;
+  if (v->reserved != 0) return SHARQ_ERR_SHAPE;
+  if (v->scale_layout == SHARQ_SCALES_KSTEP_MAJOR) {
+    if (k % 128 || v->ld_scales < rows) return SHARQ_ERR_SHAPE;
+    if (!aligned(v->scales, f == SHARQ_MXFP4 ? 4 : 8)) return SHARQ_ERR_ALIGN;
+    return SHARQ_OK;
+  }
+  if (v->scale_layout != SHARQ_SCALES_ROW_MAJOR) return SHARQ_ERR_UNSUPPORTED;
+  if (v->ld_scales < k / block_of(f)) return SHARQ_ERR_SHAPE;
   if (dword) {
-    if (!aligned(p, 4) || ld % 4) return SHARQ_ERR_ALIGN;
+    if (!aligned(v->scales, 4) || v->ld_scales % 4) return SHARQ_ERR_ALIGN;
   } else if (f == SHARQ_NVFP4) {
-    if (!aligned(p, 2) || ld % 2) return SHARQ_ERR_ALIGN;
+    if (!aligned(v->scales, 2) || v->ld_scales % 2) return SHARQ_ERR_ALIGN;
   }
   return SHARQ_OK;
 }
+
+int kstep(const sharq_fp4_view *v) { return v->scale_layout == SHARQ_SCALES_KSTEP_MAJOR ? 1 : 0; }
 
 }  // namespace
 
@@ -70,14 +81,14 @@ sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int
   if (n < 1 || k < 32 || k % 32 || ld_w < k || w_out->ld_codes < k / 2) return SHARQ_ERR_SHAPE;
   if (ld_w % 8 || !aligned(w_bf16, 16) || !aligned(w_out->codes, 16) || w_out->ld_codes % 16)
     return SHARQ_ERR_ALIGN;
-  sharq_status st = check_scales(fmt, w_out->scales, w_out->ld_scales, k, false);
+  sharq_status st = check_scales(fmt, w_out, n, k, false);
   if (st != SHARQ_OK) return st;
   if (fmt == SHARQ_NVFP4) {
     if (!w_out->tensor_scale) return SHARQ_ERR_NULL;
     if (!aligned(w_out->tensor_scale, 4)) return SHARQ_ERR_ALIGN;
   }
   QuantArgs a{w_bf16, ld_w, n, k, w_out->codes, w_out->ld_codes, w_out->scales, w_out->ld_scales,
-              w_out->tensor_scale};
+              w_out->tensor_scale, kstep(w_out)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(fmt == SHARQ_MXFP4 ? sharq::launch_quantize_weight_mx(a, s)
                                      : sharq::launch_quantize_weight_nv(a, s));
@@ -98,9 +109,9 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
   if (!aligned(sp->meta, 4) || sp->ld_meta % 4) return SHARQ_ERR_ALIGN;
   if (!aligned(rs->codes, 16) || rs->ld_codes % 16) return SHARQ_ERR_ALIGN;
   if (sp->dense_codes && (!aligned(sp->dense_codes, 16) || sp->ld_dense % 16)) return SHARQ_ERR_ALIGN;
-  sharq_status st = check_scales(fmt, sp->scales, sp->ld_scales, k, false);
+  sharq_status st = check_scales(fmt, sp, m, k, false);
   if (st != SHARQ_OK) return st;
-  st = check_scales(fmt, rs->scales, rs->ld_scales, k, false);
+  st = check_scales(fmt, rs, m, k, false);
   if (st != SHARQ_OK) return st;
   if (fmt == SHARQ_NVFP4) {
     if (!sp->tensor_scale) return SHARQ_ERR_NULL;
@@ -110,7 +121,7 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
   PrepArgs a{x_bf16, ld_x, m, k, gamma_bf16, eps,
              sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->scales, sp->ld_scales,
              rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
-             sp->dense_codes, sp->ld_dense, sp->tensor_scale};
+             sp->dense_codes, sp->ld_dense, sp->tensor_scale, kstep(sp), kstep(rs)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(fmt == SHARQ_MXFP4 ? sharq::launch_prepare_mx(a, s)
                                      : sharq::launch_prepare_nv(a, s));
@@ -147,10 +158,10 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
     return SHARQ_ERR_ALIGN;
   if (!aligned(y, 4)) return SHARQ_ERR_ALIGN;
   sharq_status st;
-  if ((st = check_scales(fmt, sp->scales, sp->ld_scales, k, true)) != SHARQ_OK) return st;
-  if ((st = check_scales(fmt, rs->scales, rs->ld_scales, k, true)) != SHARQ_OK) return st;
-  if ((st = check_scales(fmt, wsv->scales, wsv->ld_scales, k, true)) != SHARQ_OK) return st;
-  if ((st = check_scales(fmt, wdv->scales, wdv->ld_scales, k, true)) != SHARQ_OK) return st;
+  if ((st = check_scales(fmt, sp, m, k, true)) != SHARQ_OK) return st;
+  if ((st = check_scales(fmt, rs, m, k, true)) != SHARQ_OK) return st;
+  if ((st = check_scales(fmt, wsv, n, k, true)) != SHARQ_OK) return st;
+  if ((st = check_scales(fmt, wdv, n, k, true)) != SHARQ_OK) return st;
   if (fmt == SHARQ_NVFP4) {
     if (!sp->tensor_scale || !wsv->tensor_scale) return SHARQ_ERR_NULL;
     if (!aligned(sp->tensor_scale, 4) || !aligned(wsv->tensor_scale, 4)) return SHARQ_ERR_ALIGN;
@@ -158,7 +169,8 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
   GemmArgs a{sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->dense_codes, sp->ld_dense,
              sp->scales, sp->ld_scales, rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
              wsv->codes, wsv->ld_codes, wsv->scales, wsv->ld_scales, wdv->scales, wdv->ld_scales,
-             sp->tensor_scale, wsv->tensor_scale, y, ld_y, m, n, k};
+             sp->tensor_scale, wsv->tensor_scale, y, ld_y, m, n, k,
+             kstep(sp), kstep(rs), kstep(wsv), kstep(wdv)};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fmt == SHARQ_MXFP4) return from_hip(sharq::launch_dual_gemm_mx(a, dense_expanded, s));
   hipError_t e = sharq::launch_dual_gemm_nv(a, (int)variant, s);

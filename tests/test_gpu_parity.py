@@ -29,12 +29,13 @@ def host(t) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def check_prep(fmt, x_bits, gamma_bits, eps=1e-5, dense=True, label=""):
+def check_prep(fmt, x_bits, gamma_bits, eps=1e-5, dense=True, label="", layout=None):
     ref = oracle.prepare(fmt, x_bits, gamma_bits, eps, dense_backbone=True)
     sp, rs = sq.prepare(dev16(x_bits), None if gamma_bits is None else dev16(gamma_bits), eps,
-                        fmt=fmt, dense_backbone=dense)
-    got = {"meta": host(sp.meta), "s_codes": host(sp.codes), "s_scales": host(sp.scales),
-           "r_codes": host(rs.codes), "r_scales": host(rs.scales)}
+                        fmt=fmt, dense_backbone=dense, scale_layout=layout)
+    got = {"meta": host(sp.meta), "s_codes": host(sp.codes),
+           "s_scales": host(sq.scales_row_major(sp)),
+           "r_codes": host(rs.codes), "r_scales": host(sq.scales_row_major(rs))}
     if dense:
         got["s_dense"] = host(sp.dense_codes)
     for key, val in got.items():
@@ -50,17 +51,35 @@ def check_prep(fmt, x_bits, gamma_bits, eps=1e-5, dense=True, label=""):
     return ref, sp, rs
 
 
-def to_dev_prep(fmt, p):
+def dev_scales(rowmajor: np.ndarray, fmt, layout):
+    """Row-major [rows, k/blk] scale bytes as a device array in `layout`."""
+    if layout == sq.SCALES_KSTEP_MAJOR:
+        rows, nb = rowmajor.shape
+        per = 128 // sq.BLOCK[fmt]
+        rowmajor = np.ascontiguousarray(rowmajor.reshape(rows, nb // per, per).transpose(1, 0, 2))
+    return torch.from_numpy(np.ascontiguousarray(rowmajor)).to(DEV)
+
+
+def to_dev_weight(fmt, q, layout=sq.SCALES_KSTEP_MAJOR):
+    n, kh = q["codes"].shape
+    w = sq.FP4Tensor(fmt, n, kh * 2, torch.from_numpy(q["codes"]).to(DEV),
+                     dev_scales(q["scales"], fmt, layout), scale_layout=layout)
+    if fmt == sq.NVFP4:
+        w.tensor_scale = torch.tensor([q["tensor_scale"][0], 0.0], dtype=torch.float32, device=DEV)
+    return w
+
+
+def to_dev_prep(fmt, p, layout=sq.SCALES_KSTEP_MAJOR):
     """Oracle preparation outputs as device FP4 tensors (GEMM-only tests)."""
     m, kq = p["s_codes"].shape
     k = kq * 4
     sp = sq.FP4Tensor(fmt, m, k, torch.from_numpy(p["s_codes"]).to(DEV),
-                      torch.from_numpy(p["s_scales"]).to(DEV),
-                      meta=torch.from_numpy(p["meta"]).to(DEV))
+                      dev_scales(p["s_scales"], fmt, layout),
+                      meta=torch.from_numpy(p["meta"]).to(DEV), scale_layout=layout)
     if "s_dense" in p:
         sp.dense_codes = torch.from_numpy(p["s_dense"]).to(DEV)
     rs = sq.FP4Tensor(fmt, m, k, torch.from_numpy(p["r_codes"]).to(DEV),
-                      torch.from_numpy(p["r_scales"]).to(DEV))
+                      dev_scales(p["r_scales"], fmt, layout), scale_layout=layout)
     if fmt == sq.NVFP4:
         ts = torch.tensor([p["tensor_scale"][0], 0.0], dtype=torch.float32, device=DEV)
         sp.tensor_scale = ts
@@ -88,6 +107,15 @@ def test_prepare_mx_shapes(m, k, norm):
 def test_prepare_mx_workloads(name):
     w = si.WORKLOADS[name]
     check_prep(sq.MXFP4, si.workload_x(w), si.workload_gamma(w), label=name)
+
+
+@pytest.mark.parametrize("fmt,norm", [(0, True), (0, False), (1, True), (1, False)])
+def test_prepare_scale_layouts(fmt, norm):
+    """Both scale layouts hold the same bytes."""
+    x = si.activations("student_t4", 21, 512, 5, 50.0, seed=44 + fmt)
+    g = si.gamma(512, 6) if norm else None
+    for layout in (sq.SCALES_ROW_MAJOR, sq.SCALES_KSTEP_MAJOR):
+        check_prep(fmt, x, g, label=f"layout {layout}", layout=layout)
 
 
 def test_prepare_mx_degenerate_rows():
@@ -143,9 +171,11 @@ def test_prepare_deterministic():
 def test_quantize_weight(fmt, n, k):
     w = si.weights(n, k, seed=n + k)
     ref = oracle.quantize_weight(fmt, w)
-    got = sq.quantize_weight(dev16(w), fmt)
-    assert np.array_equal(host(got.codes), ref["codes"])
-    assert np.array_equal(host(got.scales), ref["scales"])
+    layouts = [sq.SCALES_ROW_MAJOR] + ([sq.SCALES_KSTEP_MAJOR] if k % 128 == 0 else [])
+    for layout in layouts:
+        got = sq.quantize_weight(dev16(w), fmt, scale_layout=layout)
+        assert np.array_equal(host(got.codes), ref["codes"])
+        assert np.array_equal(host(sq.scales_row_major(got)), ref["scales"])
     if fmt == sq.NVFP4:
         assert host(got.tensor_scale)[0] == ref["tensor_scale"][0]
 
@@ -161,28 +191,34 @@ def _gemm_case(m, n, k, seed, fmt=sq.MXFP4, norm=True):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 256), (37, 75, 256), (130, 200, 384), (1, 1, 128),
-                                   (257, 129, 1024), (64, 512, 4096)])
+                                   (257, 129, 1024), (64, 512, 4096), (300, 1000, 640),
+                                   (129, 193, 128), (512, 192, 256)])
 def test_dual_gemm_mx_vs_oracle(m, n, k):
     x, w, g, p, q = _gemm_case(m, n, k, seed=m + 7 * n + k)
     ref = oracle.dual_gemm(sq.MXFP4, p, q)
-    sp, rs = to_dev_prep(sq.MXFP4, p)
-    wq = sq.FP4Tensor(sq.MXFP4, n, k, torch.from_numpy(q["codes"]).to(DEV),
-                      torch.from_numpy(q["scales"]).to(DEV))
-    for variant in (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED):
-        y = host(sq.dual_gemm(sp, rs, wq, variant=variant))
-        err = normwise(y, ref)
-        assert err <= GEMM_TOL, (variant, err)
+    for layout in (sq.SCALES_KSTEP_MAJOR, sq.SCALES_ROW_MAJOR):
+        sp, rs = to_dev_prep(sq.MXFP4, p, layout)
+        wq = to_dev_weight(sq.MXFP4, q, layout)
+        for variant in (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED):
+            y = host(sq.dual_gemm(sp, rs, wq, variant=variant))
+            err = normwise(y, ref)
+            assert err <= GEMM_TOL, (layout, variant, err)
 
 
 def test_dual_gemm_variants_bitwise_equal():
     x, w, g, p, q = _gemm_case(200, 300, 512, seed=3)
-    sp, rs = to_dev_prep(sq.MXFP4, p)
-    wq = sq.FP4Tensor(sq.MXFP4, 300, 512, torch.from_numpy(q["codes"]).to(DEV),
-                      torch.from_numpy(q["scales"]).to(DEV))
+    sp, rs = to_dev_prep(sq.MXFP4, p, sq.SCALES_ROW_MAJOR)
+    wq = to_dev_weight(sq.MXFP4, q, sq.SCALES_ROW_MAJOR)
     a = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS)
     b = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DENSE_EXPANDED)
     c = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS)
     assert torch.equal(a, b) and torch.equal(a, c)
+    # the k-step-major pipeline: deterministic run to run
+    sp2, rs2 = to_dev_prep(sq.MXFP4, p, sq.SCALES_KSTEP_MAJOR)
+    wq2 = to_dev_weight(sq.MXFP4, q, sq.SCALES_KSTEP_MAJOR)
+    d = sq.dual_gemm(sp2, rs2, wq2, variant=sq.GEMM_DENSE_EXPANDED)
+    e = sq.dual_gemm(sp2, rs2, wq2, variant=sq.GEMM_DENSE_EXPANDED)
+    assert torch.equal(d, e)
 
 
 def test_dual_gemm_exact_special_case():
@@ -218,10 +254,12 @@ def test_end_to_end_workloads(name, samples):
     x, W, g = si.workload_x(w), si.workload_w(w), si.workload_gamma(w)
     p = oracle.prepare(sq.MXFP4, x, g)
     q = oracle.quantize_weight(sq.MXFP4, W)
-    sp, rs = sq.prepare(dev16(x), None if g is None else dev16(g))
+    sp, rs = sq.prepare(dev16(x), None if g is None else dev16(g), dense_backbone=True)
     wq = sq.quantize_weight(dev16(W))
     y = host(sq.dual_gemm(sp, rs, wq))
+    y2 = host(sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS))
     if samples is None:
+        assert normwise(y2, oracle.dual_gemm(sq.MXFP4, p, q)) <= GEMM_TOL
         ref = oracle.dual_gemm(sq.MXFP4, p, q)
         assert normwise(y, ref) <= GEMM_TOL
         return
@@ -236,13 +274,13 @@ def test_end_to_end_workloads(name, samples):
     got = y[rows, cols]
     # normalize by the largest |Y| over the sample (the full max is at least this)
     assert normwise(got, ref) <= GEMM_TOL
+    assert normwise(y2[rows, cols], ref) <= GEMM_TOL
 
 
 def test_sparse_mfma_unsupported_for_mxfp4():
     x, w, g, p, q = _gemm_case(16, 128, 128, seed=9)
     sp, rs = to_dev_prep(sq.MXFP4, p)
-    wq = sq.FP4Tensor(sq.MXFP4, 128, 128, torch.from_numpy(q["codes"]).to(DEV),
-                      torch.from_numpy(q["scales"]).to(DEV))
+    wq = to_dev_weight(sq.MXFP4, q)
     with pytest.raises(sq.SharqError) as e:
         sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA)
     assert e.value.status == sq.ERR_UNSUPPORTED
