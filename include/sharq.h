@@ -186,15 +186,21 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
  * own scales pointer (the path-specific scale view; for MXFP4 the values must
  * be the weight's scales, and both usually alias one buffer).
  * Variants: DECOMPRESS reads the 2:4 backbone (codes + meta) and expands it
- * while staging; DENSE_EXPANDED reads sparse->dense_codes instead; AUTO is
- * DENSE_EXPANDED when sparse->dense_codes is non-NULL, else DECOMPRESS.  SPARSE_MFMA: gfx950 has
- * no structured-sparse MFMA for FP4 operands, so it returns
- * SHARQ_ERR_UNSUPPORTED for MXFP4.
+ * to dense codes inside the GEMM; DENSE_EXPANDED reads sparse->dense_codes
+ * instead; AUTO is DENSE_EXPANDED when sparse->dense_codes is non-NULL, else
+ * DECOMPRESS.  SPARSE_MFMA (NVFP4 only) feeds the 2:4 backbone codes and
+ * indices to the structured-sparse fp16 MFMA; gfx950 has no
+ * structured-sparse MFMA for FP4 operands, so it returns
+ * SHARQ_ERR_UNSUPPORTED for MXFP4.  The 2:4 indices must be as
+ * sharq_prepare writes them (the two kept positions of a group distinct).
+ * NVFP4 runs on fp16 MFMAs (2:4 and dense): each operand element
+ * q * e4m3 scale is exact in fp16.
  * Requirements: m, n >= 1; k >= 128, k % 128 == 0; ld_y >= n; codes 16-byte
  * aligned with ld % 16 == 0 (backbone codes too;
  * meta ld % 8 == 0 and 8-byte aligned); scales ROW_MAJOR 4-byte aligned with
  * ld % 4 == 0, or KSTEP_MAJOR with ld >= rows (the fast path: all four views
- * KSTEP_MAJOR); y 4-byte aligned.
+ * KSTEP_MAJOR); y 4-byte aligned; every code, meta and scale array spans
+ * less than 4 GiB (rows x ld), else SHARQ_ERR_SHAPE.
  */
 sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sparse,
                              const sharq_fp4_view *resid, const sharq_fp4_view *w_sparse_view,

@@ -1,6 +1,468 @@
-// NVFP4-style dual GEMM (emulated scales): not built yet.
+// Dual-path NVFP4-style GEMM of the SharQ path, for gfx950.
+//
+// "SharQ: Bridging Activation Sparsity and FP4 Quantization for LLM
+// Inference" (arXiv:2606.26587), abstract, sentences 4 and 5 (sparse FP4 GEMM
+// on the backbone, dense FP4 GEMM on the residual, one weight payload read
+// through path-specific scale views) and sentence 7 (the NVFP4 format):
+//
+//   Y = s_tA s_tW (deq(backbone) W^T + deq(residual) W^T),  fp32 out,
+//
+// where deq gives q * sb per element (q an E2M1 value, sb the E4M3 scale of
+// its 16-element block) and s_tA, s_tW are the fp32 tensor scales.
+//
+// gfx950 has no block-scaled MFMA that takes E4M3 scales, so each wavefront
+// turns its operand fragments into fp16 on the fly: q * sb has at most six
+// significant bits and lies in [2^-10, 2688], so it is exact in fp16.  The
+// FP4 codes are decoded with v_cvt_scalef32_pk_f16_fp4 at scale 1 and
+// multiplied by the block scale (decoded from E4M3 with
+// v_cvt_scalef32_pk_f16_fp8) with v_pk_mul_f16; both steps are exact.  The
+// products accumulate in fp32 on v_mfma_f32_32x32x16_f16 and the tensor
+// scales multiply the fp32 sum once, in the epilogue.
+//
+// Backbone variants: dense codes (the dense view the preparation writes),
+// 2:4 codes expanded to dense codes in registers, or 2:4 codes fed straight
+// to the structured-sparse v_smfmac_f32_32x32x32_f16 together with the 2:4
+// indices, which skips the zero half of the backbone: half the backbone
+// MFMA issue time and half its dequantization work.
+//
+// Data movement is the one of the MXFP4 dense pipeline: every operand tile
+// and every scale tile goes global -> LDS with buffer_load ... lds, STAGES - 1
+// K steps (128 k each) ahead, into a ring of LDS stages; loads past the end
+// of an operand return 0.  A workgroup of four wavefronts owns 128 x TBN of
+// Y; wavefront (wm, wn) owns 64 rows x TBN / 2 columns (2 x TBN / 64 MFMA
+// tiles of 32 x 32).
+//
+// k assignment inside a 128-k step (any assignment works as long as the A
+// and B fragments of one MFMA use the same one): lane half h (h = lane / 32)
+// holds k in [64h, 64h + 64); slice s (0..7) of it is k = 64h + 8s + i,
+// i = 0..7, i.e. code bytes 32h + 4s .. 32h + 4s + 3 of the row and the block
+// scale 4h + s / 2.
+// The sparse MFMA t (t = 0..3) takes the B fragments of slices 2t and 2t + 1
+// (16 B values a lane).  Its A lane half a holds four 2:4 groups, group g
+// matching B lane half g / 2, B values 8a + 4 (g & 1) .. + 3, so that in the
+// row's numbering of 2:4 groups (32 a step) they are 4t + 2a, 4t + 2a + 1,
+// 16 + 4t + 2a and 16 + 4t + 2a + 1; blocks t and 4 + t scale them.  The
+// index operand holds one nibble (two 2-bit positions) per group, group g at
+// bits 4g; a 32-bit index word serves two MFMAs, 16 bits each.
+#include <stddef.h>
+
+#include "fp4_device.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace sharq {
-hipError_t launch_dual_gemm_nv(const GemmArgs &, int, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+using namespace gemm;
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v16h __attribute__((ext_vector_type(16)));
+
+// how the backbone reaches the MFMAs
+constexpr int kBBDense = 0;    // dense codes
+constexpr int kBBExpand = 1;   // 2:4 codes + indices, expanded to dense codes
+constexpr int kBBSparse = 2;   // 2:4 codes + indices, structured-sparse MFMA
+
+template <int TBM, int TBN, int BB, bool SH>
+struct NStage {
+  // backbone: dense rows of 64 bytes (chunk-swizzled) or 2:4 codes, 32 bytes a row
+  u32x4 as[BB == kBBDense ? TBM * 4 : TBM * 2];
+  u32x4 am[BB == kBBDense ? 1 : TBM];   // 2:4 indices, 16 bytes a row
+  u32x4 ar[TBM * 4];
+  u32x4 w[TBN * 4];
+  // E4M3 scales, two words (8 blocks) a row
+  uint32_t sas[TBM * 2], sar[TBM * 2], sws[TBN * 2], swd[SH ? 4 : TBN * 2];
+};
+
+// Load plan of one stage.  Loads, in order: backbone (16-row dense chunk
+// loads, or 32-row code loads then 64-row index loads), residual and W
+// (16-row chunk loads), then the scale words (32 rows a load) of the
+// backbone, the residual, the sparse-path and the dense-path W view (the
+// last one only when the two views differ).  Wavefront w issues loads
+// w, w + NW, ...
+template <int TBM, int TBN, int NW, int BB, bool SH>
+struct NPlan {
+  static constexpr int kAS = BB == kBBDense ? TBM / 16 : TBM / 32;
+  static constexpr int kAM = BB == kBBDense ? 0 : TBM / 64;
+  static constexpr int kAR = TBM / 16, kW = TBN / 16;
+  static constexpr int kSA = TBM / 32, kSW = TBN / 32, kSWD = SH ? 0 : TBN / 32;
+  static constexpr int b1 = kAS, b2 = b1 + kAM, b3 = b2 + kAR, b4 = b3 + kW;
+  static constexpr int b5 = b4 + kSA, b6 = b5 + kSA, b7 = b6 + kSW, kTotal = b7 + kSWD;
+  static constexpr int kPer = (kTotal + NW - 1) / NW;
+  static constexpr int kMinPerWave = kTotal / NW;   // waitcnt allowance per stage
+};
+
+struct NRsrc {
+  i32x4 as, am, ar, w, sas, sar, sws, swd;
+};
+
+template <int KPER>
+struct NOffs {
+  uint32_t voff[KPER];      // per-lane byte offset of each load in its operand
+  uint32_t step_sa, step_sr, step_sws, step_swd;   // scale bytes per 128-k step
+};
+
+// Scale array of one operand: resource from row r0, per-lane offset of scale
+// word d (row d / 2, half d & 1) and the bytes per K step.  K-step-major:
+// step t of row r at (t * ld + r) * 8; row-major: at r * ld + 8 t.
+__device__ __forceinline__ i32x4 scale_rsrc(const uint8_t *p, int64_t ld, int kstep, int64_t rows,
+                                            int64_t r0, int64_t steps) {
+  if (kstep) return make_rsrc(p + r0 * 8, (uint32_t)(((steps - 1) * ld + rows - r0) * 8));
+  return make_rsrc(p + r0 * ld, (uint32_t)((rows - r0) * ld));
+}
+__device__ __forceinline__ uint32_t scale_voff(int64_t ld, int kstep, int d) {
+  const int row = d >> 1, half = d & 1;
+  return kstep ? (uint32_t)(row * 8 + half * 4) : (uint32_t)(row * ld + half * 4);
+}
+__device__ __forceinline__ uint32_t scale_step(int64_t ld, int kstep) {
+  return kstep ? (uint32_t)(ld * 8) : 8u;
+}
+
+template <int TBM, int TBN, int NW, int BB, bool SH>
+__device__ __forceinline__ void nv_plan(const GemmArgs &a, int64_t m0, int64_t n0, int wave,
+                                        int lane, NRsrc &R, NOffs<NPlan<TBM, TBN, NW, BB, SH>::kPer> &O) {
+  using P = NPlan<TBM, TBN, NW, BB, SH>;
+  const int64_t steps = a.k / BK;
+  if (BB == kBBDense) {
+    R.as = make_rsrc(a.s_dense + m0 * a.ld_sd, (uint32_t)((a.m - m0) * a.ld_sd));
+  } else {
+    R.as = make_rsrc(a.s_codes + m0 * a.ld_sc, (uint32_t)((a.m - m0) * a.ld_sc));
+    R.am = make_rsrc(a.meta + m0 * a.ld_meta, (uint32_t)((a.m - m0) * a.ld_meta));
+  }
+  R.ar = make_rsrc(a.r_codes + m0 * a.ld_rc, (uint32_t)((a.m - m0) * a.ld_rc));
+  R.w = make_rsrc(a.w_codes + n0 * a.ld_wc, (uint32_t)((a.n - n0) * a.ld_wc));
+  R.sas = scale_rsrc(a.s_scales, a.ld_ss, a.ss_kstep, a.m, m0, steps);
+  R.sar = scale_rsrc(a.r_scales, a.ld_rs, a.rs_kstep, a.m, m0, steps);
+  R.sws = scale_rsrc(a.ws_scales, a.ld_wss, a.wss_kstep, a.n, n0, steps);
+  if (!SH) R.swd = scale_rsrc(a.wd_scales, a.ld_wds, a.wds_kstep, a.n, n0, steps);
+  O.step_sa = scale_step(a.ld_ss, a.ss_kstep);
+  O.step_sr = scale_step(a.ld_rs, a.rs_kstep);
+  O.step_sws = scale_step(a.ld_wss, a.wss_kstep);
+  O.step_swd = SH ? 0u : scale_step(a.ld_wds, a.wds_kstep);
+  // dense chunk loads: lane l -> row l / 4 of the 16, logical chunk placed at
+  // LDS slot l (the lds_slot swizzle)
+  const int drow = lane >> 2, dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+  for (int j = 0; j < P::kPer; ++j) {
+    const int q = wave + NW * j;
+    uint32_t v = 0;
+    if (q < P::b1) {
+      if (BB == kBBDense) v = (uint32_t)((16 * q + drow) * a.ld_sd + dchunk * 16);
+      else v = (uint32_t)((32 * q + (lane >> 1)) * a.ld_sc + (lane & 1) * 16);
+    } else if (q < P::b2) {
+      v = (uint32_t)((64 * (q - P::b1) + lane) * a.ld_meta);
+    } else if (q < P::b3) {
+      v = (uint32_t)((16 * (q - P::b2) + drow) * a.ld_rc + dchunk * 16);
+    } else if (q < P::b4) {
+      v = (uint32_t)((16 * (q - P::b3) + drow) * a.ld_wc + dchunk * 16);
+    } else if (q < P::b5) {
+      v = scale_voff(a.ld_ss, a.ss_kstep, 64 * (q - P::b4) + lane);
+    } else if (q < P::b6) {
+      v = scale_voff(a.ld_rs, a.rs_kstep, 64 * (q - P::b5) + lane);
+    } else if (q < P::b7) {
+      v = scale_voff(a.ld_wss, a.wss_kstep, 64 * (q - P::b6) + lane);
+    } else if (q < P::kTotal) {
+      v = scale_voff(a.ld_wds, a.wds_kstep, 64 * (q - P::b7) + lane);
+    }
+    O.voff[j] = v;
+  }
+}
+
+template <int TBM, int TBN, int NW, int BB, bool SH>
+__device__ __forceinline__ void nv_issue(const NRsrc &R, const NOffs<NPlan<TBM, TBN, NW, BB, SH>::kPer> &O,
+                                         int wave, int kt, const NStage<TBM, TBN, BB, SH> &S) {
+  using P = NPlan<TBM, TBN, NW, BB, SH>;
+  using St = NStage<TBM, TBN, BB, SH>;
+  const uint32_t base = lds_addr(&S);
+  constexpr uint32_t oam = offsetof(St, am), oar = offsetof(St, ar), ow = offsetof(St, w);
+  constexpr uint32_t osas = offsetof(St, sas), osar = offsetof(St, sar);
+  constexpr uint32_t osws = offsetof(St, sws), oswd = offsetof(St, swd);
+  const uint32_t t = (uint32_t)kt;
+#pragma unroll
+  for (int j = 0; j < P::kPer; ++j) {
+    const int q = wave + NW * j;
+    if (q < P::b1) b2l16(R.as, O.voff[j], t * (BB == kBBDense ? 64u : 32u), base + q * 1024);
+    else if (q < P::b2) b2l16(R.am, O.voff[j], t * 16u, base + oam + (q - P::b1) * 1024);
+    else if (q < P::b3) b2l16(R.ar, O.voff[j], t * 64u, base + oar + (q - P::b2) * 1024);
+    else if (q < P::b4) b2l16(R.w, O.voff[j], t * 64u, base + ow + (q - P::b3) * 1024);
+    else if (q < P::b5) b2l4(R.sas, O.voff[j], t * O.step_sa, base + osas + (q - P::b4) * 256);
+    else if (q < P::b6) b2l4(R.sar, O.voff[j], t * O.step_sr, base + osar + (q - P::b5) * 256);
+    else if (q < P::b7) b2l4(R.sws, O.voff[j], t * O.step_sws, base + osws + (q - P::b6) * 256);
+    else if (q < P::kTotal) b2l4(R.swd, O.voff[j], t * O.step_swd, base + oswd + (q - P::b7) * 256);
+  }
+}
+
+// E4M3 scale bytes 2p, 2p + 1 of a scale word, as fp16 (exact)
+template <int P>
+__device__ __forceinline__ v2h e4m3_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, P != 0);
+}
+
+// Eight FP4 codes (one word, k in order) times a block scale, as fp16 (exact).
+template <int HALF>
+__device__ __forceinline__ v8h deq8(uint32_t c, v2h sc) {
+  const v2h s = HALF ? v2h{sc.y, sc.y} : v2h{sc.x, sc.x};
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * s;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * s;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * s;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * s;
+  return v8h{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ v16h cat16(v8h a, v8h b) {
+  return v16h{a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7],
+              b[0], b[1], b[2], b[3], b[4], b[5], b[6], b[7]};
+}
+
+__device__ __forceinline__ uint32_t word(const u32x4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// One 128-k step of wavefront (wm, wn): 64 rows x TBN/2 columns.
+template <int TBM, int TBN, int BB, bool SH>
+__device__ __forceinline__ void nv_compute(const NStage<TBM, TBN, BB, SH> &S,
+                                           v16f (&acc)[2][TBN / 64], int wm, int wn, int h, int li) {
+  constexpr int TN = TBN / 64;
+  // scale words: lane half h takes word h of each row (blocks 4h .. 4h + 3);
+  // pair p holds blocks 4h + 2p, 4h + 2p + 1
+  v2h sa_s[2][2], sa_r[2][2], sw_s[TN][2], sw_d[TN][2];
+  int ra[2], cb[TN];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    ra[it] = wm * 64 + it * 32 + li;
+    const uint32_t ws = S.sas[2 * ra[it] + h], wr = S.sar[2 * ra[it] + h];
+    sa_s[it][0] = e4m3_pair<0>(ws);
+    sa_s[it][1] = e4m3_pair<1>(ws);
+    sa_r[it][0] = e4m3_pair<0>(wr);
+    sa_r[it][1] = e4m3_pair<1>(wr);
+  }
+#pragma unroll
+  for (int jt = 0; jt < TN; ++jt) {
+    cb[jt] = wn * (TBN / 2) + jt * 32 + li;
+    const uint32_t ws = S.sws[2 * cb[jt] + h];
+    sw_s[jt][0] = e4m3_pair<0>(ws);
+    sw_s[jt][1] = e4m3_pair<1>(ws);
+    if (!SH) {
+      const uint32_t wd = S.swd[2 * cb[jt] + h];
+      sw_d[jt][0] = e4m3_pair<0>(wd);
+      sw_d[jt][1] = e4m3_pair<1>(wd);
+    }
+  }
+  // 2:4 backbone.  Expanded: the lane's 16 code bytes (64 dense k) and 8
+  // index bytes.  Sparse MFMA: the row's 32 code bytes and 16 index bytes,
+  // regrouped below into the lane's MFMA operands.
+  u32x4 sc[2], sc1[2], smx[2];
+  u32x2 sm[2];
+  v2h ssp[2][4];
+  if (BB == kBBExpand) {
+    const uint32_t *am = reinterpret_cast<const uint32_t *>(S.am);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      sc[it] = S.as[2 * ra[it] + h];
+      sm[it] = u32x2{am[4 * ra[it] + 2 * h], am[4 * ra[it] + 2 * h + 1]};
+    }
+  } else if (BB == kBBSparse) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      sc[it] = S.as[2 * ra[it]];
+      sc1[it] = S.as[2 * ra[it] + 1];
+      smx[it] = S.am[ra[it]];
+      // block scales 0..7 of the row, as fp16 pairs
+      const uint32_t w0 = S.sas[2 * ra[it]], w1 = S.sas[2 * ra[it] + 1];
+      ssp[it][0] = e4m3_pair<0>(w0);
+      ssp[it][1] = e4m3_pair<1>(w0);
+      ssp[it][2] = e4m3_pair<0>(w1);
+      ssp[it][3] = e4m3_pair<1>(w1);
+    }
+  }
+  // byte selectors: codes of groups (2h, 2h + 1) of two words; index bytes
+  // h, 2 + h of two words, interleaved
+  const uint32_t sel_codes = h ? 0x07060302u : 0x05040100u;
+  const uint32_t sel_index = h ? 0x07030501u : 0x06020400u;
+  (void)sel_codes;
+  (void)sel_index;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int cc = 2 * h + q;       // dense chunk: slices 4q .. 4q + 3
+    u32x4 ca[2], cr[2], cw[TN];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      cr[it] = S.ar[lds_slot(ra[it], cc)];
+      if (BB == kBBDense) {
+        ca[it] = S.as[lds_slot(ra[it], cc)];
+      } else if (BB == kBBExpand) {
+        uint32_t d[4];
+        expand8(word(sc[it], 2 * q), word(sc[it], 2 * q + 1), q ? sm[it].y : sm[it].x, d);
+        ca[it] = u32x4{d[0], d[1], d[2], d[3]};
+      }
+    }
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) cw[jt] = S.w[lds_slot(cb[jt], cc)];
+
+    v8h fb_prev[TN], fbd_prev[TN];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      v8h fb[TN], fbd[TN], fa[2], fr[2];
+#pragma unroll
+      for (int jt = 0; jt < TN; ++jt) {
+        const uint32_t c = word(cw[jt], s4);
+        fb[jt] = (s4 >> 1) ? deq8<1>(c, sw_s[jt][q]) : deq8<0>(c, sw_s[jt][q]);
+        if (!SH) fbd[jt] = (s4 >> 1) ? deq8<1>(c, sw_d[jt][q]) : deq8<0>(c, sw_d[jt][q]);
+        else fbd[jt] = fb[jt];
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const uint32_t cres = word(cr[it], s4);
+        fr[it] = (s4 >> 1) ? deq8<1>(cres, sa_r[it][q]) : deq8<0>(cres, sa_r[it][q]);
+        if (BB != kBBSparse) {
+          const uint32_t cbb = word(ca[it], s4);
+          fa[it] = (s4 >> 1) ? deq8<1>(cbb, sa_s[it][q]) : deq8<0>(cbb, sa_s[it][q]);
+        }
+      }
+      if (BB != kBBSparse) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+          for (int jt = 0; jt < TN; ++jt)
+            acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[it], fb[jt], acc[it][jt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int jt = 0; jt < TN; ++jt)
+          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[it], fbd[jt], acc[it][jt], 0, 0, 0);
+      if (BB == kBBSparse) {
+        if (s4 & 1) {
+          // sparse MFMA t over slices s4 - 1, s4
+          const int t = 2 * q + (s4 >> 1), p = t & 1;
+          v8h fs[2];
+          int idx[2];
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const uint32_t c = __builtin_amdgcn_perm(word(sc1[it], t), word(sc[it], t), sel_codes);
+            const v2h lo = ssp[it][t >> 1], hi = ssp[it][2 + (t >> 1)];
+            const v2h s0 = p ? v2h{lo.y, lo.y} : v2h{lo.x, lo.x};
+            const v2h s1 = p ? v2h{hi.y, hi.y} : v2h{hi.x, hi.x};
+            const v2h g0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * s0;
+            const v2h g1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * s0;
+            const v2h g2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * s1;
+            const v2h g3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * s1;
+            fs[it] = v8h{g0.x, g0.y, g1.x, g1.y, g2.x, g2.y, g3.x, g3.y};
+            idx[it] = (int)__builtin_amdgcn_perm(word(smx[it], 2 + (t >> 1)), word(smx[it], t >> 1), sel_index);
+          }
+#pragma unroll
+          for (int jt = 0; jt < TN; ++jt) {
+            const v16h b = cat16(fb_prev[jt], fb[jt]);
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+              if (p == 0)
+                acc[it][jt] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(fs[it], b, acc[it][jt], idx[it], 0, 0);
+              else
+                acc[it][jt] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(fs[it], b, acc[it][jt], idx[it], 0, 1);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int jt = 0; jt < TN; ++jt) fb_prev[jt] = fb[jt];
+        }
+      }
+      (void)fbd_prev;
+    }
+  }
+}
+
+template <int TBM, int TBN, int NW, int STAGES, int BB, bool SH>
+__global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a) {
+  static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
+  static_assert(TBM % 64 == 0 && TBN % 64 == 0, "tile shape");
+  constexpr int TN = TBN / 64;
+  using P = NPlan<TBM, TBN, NW, BB, SH>;
+  __shared__ NStage<TBM, TBN, BB, SH> st[STAGES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, li = lane & 31;
+  const int64_t m0 = (int64_t)blockIdx.y * TBM, n0 = (int64_t)blockIdx.x * TBN;
+
+  v16f acc[2][TN];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int ksteps = (int)(a.k / BK);
+  NRsrc R;
+  NOffs<P::kPer> O;
+  nv_plan<TBM, TBN, NW, BB, SH>(a, m0, n0, wave, lane, R, O);
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < ksteps) nv_issue<TBM, TBN, NW, BB, SH>(R, O, wave, p, st[p]);
+
+  int cur = 0;
+  for (int kt = 0; kt < ksteps; ++kt) {
+    // stages kt + 1 .. kt + STAGES - 2 may stay in flight
+    const int ahead = min(ksteps - 1 - kt, STAGES - 2);
+    if (STAGES == 3 && ahead >= 1) wait_vmcnt<P::kMinPerWave>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + STAGES - 1 < ksteps) {
+      const int nxt = cur == 0 ? STAGES - 1 : cur - 1;
+      nv_issue<TBM, TBN, NW, BB, SH>(R, O, wave, kt + STAGES - 1, st[nxt]);
+    }
+    nv_compute<TBM, TBN, BB, SH>(st[cur], acc, wm, wn, h, li);
+    cur = cur == STAGES - 1 ? 0 : cur + 1;
+  }
+
+  const float ts = a.a_tensor_scale[0] * a.w_tensor_scale[0];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) {
+      const int64_t col = n0 + wn * (TBN / 2) + jt * 32 + li;
+      if (col >= a.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < a.m) a.y[row * a.ld_y + col] = acc[it][jt][r] * ts;
+      }
+    }
+}
+
+template <int TBN, int STAGES, int BB>
+void launch_nv(const GemmArgs &a, bool shared, hipStream_t s) {
+  dim3 grid((unsigned)((a.n + TBN - 1) / TBN), (unsigned)((a.m + 127) / 128)), block(256);
+  if (shared)
+    dual_gemm_nv_kernel<128, TBN, 4, STAGES, BB, true><<<grid, block, 0, s>>>(a);
+  else
+    dual_gemm_nv_kernel<128, TBN, 4, STAGES, BB, false><<<grid, block, 0, s>>>(a);
+}
+
+template <int BB>
+void launch_bb(const GemmArgs &a, bool shared, hipStream_t s) {
+  // 128 x 256 tiles (two workgroups a CU) when there are enough of them
+  const int64_t mt = (a.m + 127) / 128;
+  if (mt * ((a.n + 255) / 256) >= 512)
+    launch_nv<256, 2, BB>(a, shared, s);
+  else
+    launch_nv<128, 3, BB>(a, shared, s);
+}
+
+}  // namespace
+
+hipError_t launch_dual_gemm_nv(const GemmArgs &a, int variant, hipStream_t s) {
+  // one W scale view serves both paths when the two views are the same array
+  const bool shared = a.ws_scales == a.wd_scales && a.ld_wss == a.ld_wds && a.wss_kstep == a.wds_kstep;
+  switch (variant) {
+    case 1: launch_bb<kBBExpand>(a, shared, s); break;
+    case 2: launch_bb<kBBDense>(a, shared, s); break;
+    case 3: launch_bb<kBBSparse>(a, shared, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace sharq

@@ -45,6 +45,14 @@ sharq_status check_scales(sharq_format f, const sharq_fp4_view *v, int64_t rows,
 
 int kstep(const sharq_fp4_view *v) { return v->scale_layout == SHARQ_SCALES_KSTEP_MAJOR ? 1 : 0; }
 
+// The scale array of `rows` rows spans less than 4 GiB.
+bool scales_fit(sharq_format f, const sharq_fp4_view *v, int64_t rows, int64_t k) {
+  const int64_t lim = (int64_t)1 << 32;
+  if (v->scale_layout == SHARQ_SCALES_KSTEP_MAJOR)
+    return (k / 128) * v->ld_scales * (128 / block_of(f)) < lim;
+  return rows * v->ld_scales < lim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,11 +179,17 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
              wsv->codes, wsv->ld_codes, wsv->scales, wsv->ld_scales, wdv->scales, wdv->ld_scales,
              sp->tensor_scale, wsv->tensor_scale, y, ld_y, m, n, k,
              kstep(sp), kstep(rs), kstep(wsv), kstep(wdv)};
+  // the kernels address every operand with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 32;
+  if (m * rs->ld_codes >= lim || n * wsv->ld_codes >= lim ||
+      (dense_expanded ? m * sp->ld_dense : m * sp->ld_codes) >= lim ||
+      (!dense_expanded && m * sp->ld_meta >= lim) || !scales_fit(fmt, sp, m, k) ||
+      !scales_fit(fmt, rs, m, k) || !scales_fit(fmt, wsv, n, k) || !scales_fit(fmt, wdv, n, k))
+    return SHARQ_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fmt == SHARQ_MXFP4) return from_hip(sharq::launch_dual_gemm_mx(a, dense_expanded, s));
-  hipError_t e = sharq::launch_dual_gemm_nv(a, (int)variant, s);
-  if (e == hipErrorNotSupported) return SHARQ_ERR_UNSUPPORTED;
-  return from_hip(e);
+  const int v = variant == SHARQ_GEMM_SPARSE_MFMA ? 3 : dense_expanded ? 2 : 1;
+  return from_hip(sharq::launch_dual_gemm_nv(a, v, s));
 }
 
 }  // extern "C"

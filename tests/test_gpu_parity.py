@@ -277,6 +277,102 @@ def test_end_to_end_workloads(name, samples):
     assert normwise(y2[rows, cols], ref) <= GEMM_TOL
 
 
+NV_VARIANTS = (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED, sq.GEMM_SPARSE_MFMA)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 256, 256), (37, 75, 256), (1, 1, 128), (130, 200, 384),
+                                   (257, 129, 1024), (64, 512, 4096), (300, 1000, 640),
+                                   (129, 193, 128), (512, 768, 256)])
+def test_dual_gemm_nv_vs_oracle(m, n, k):
+    """NVFP4-style dual GEMM, all three backbone variants, both scale layouts."""
+    x, w, g, p, q = _gemm_case(m, n, k, seed=3 * m + n + k, fmt=sq.NVFP4)
+    ref = oracle.dual_gemm(sq.NVFP4, p, q)
+    for layout in (sq.SCALES_KSTEP_MAJOR, sq.SCALES_ROW_MAJOR):
+        sp, rs = to_dev_prep(sq.NVFP4, p, layout)
+        wq = to_dev_weight(sq.NVFP4, q, layout)
+        for variant in NV_VARIANTS:
+            y = host(sq.dual_gemm(sp, rs, wq, variant=variant))
+            err = normwise(y, ref)
+            assert err <= GEMM_TOL, (layout, variant, err)
+
+
+def test_dual_gemm_nv_dense_and_expanded_bitwise_equal():
+    """The expanded 2:4 backbone and the dense view feed identical MFMAs."""
+    x, w, g, p, q = _gemm_case(200, 600, 512, seed=11, fmt=sq.NVFP4)
+    sp, rs = to_dev_prep(sq.NVFP4, p)
+    wq = to_dev_weight(sq.NVFP4, q)
+    a = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS)
+    b = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DENSE_EXPANDED)
+    c = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA)
+    d = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA)
+    assert torch.equal(a, b)
+    assert torch.equal(c, d)
+
+
+def _zeroed(p, which):
+    """Copy of oracle preparation outputs with one path's codes set to 0 (+0.0)."""
+    z = dict(p)
+    if which == "backbone":
+        z["s_codes"] = np.zeros_like(p["s_codes"])
+        if "s_dense" in p:
+            z["s_dense"] = np.zeros_like(p["s_dense"])
+    else:
+        z["r_codes"] = np.zeros_like(p["r_codes"])
+    return z
+
+
+@pytest.mark.parametrize("fmt", [sq.MXFP4, sq.NVFP4])
+def test_dual_gemm_path_specific_weight_views(fmt):
+    """Distinct scale views of one W payload: the backbone product reads the
+    sparse-path view, the residual product the dense-path view."""
+    m, n, k = 96, 320, 512
+    x, w, g, p, q = _gemm_case(m, n, k, seed=21, fmt=fmt)
+    q2 = dict(q)
+    rng = np.random.default_rng(4)
+    if fmt == sq.MXFP4:
+        q2["scales"] = (q["scales"].astype(np.int32) + rng.integers(-2, 3, q["scales"].shape)).clip(1, 254).astype(np.uint8)
+    else:   # positive finite E4M3 bytes
+        q2["scales"] = rng.integers(0x08, 0x70, q["scales"].shape).astype(np.uint8)
+    ref = (oracle.dual_gemm(fmt, _zeroed(p, "residual"), q).astype(np.float64)
+           + oracle.dual_gemm(fmt, _zeroed(p, "backbone"), q2))
+    variants = NV_VARIANTS if fmt == sq.NVFP4 else (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)
+    for layout in (sq.SCALES_KSTEP_MAJOR, sq.SCALES_ROW_MAJOR):
+        sp, rs = to_dev_prep(fmt, p, layout)
+        wq = to_dev_weight(fmt, q, layout)
+        wd = dev_scales(q2["scales"], fmt, layout)
+        for variant in variants:
+            y = host(sq.dual_gemm(sp, rs, wq, variant=variant, w_dense_scales=wd))
+            assert normwise(y, ref) <= GEMM_TOL, (layout, variant)
+
+
+@pytest.mark.parametrize("name,samples", [("tiny", None), ("nvfp4_prefill", 4096)])
+def test_end_to_end_nv_workloads(name, samples):
+    """NVFP4-style prepare + weight quantization + dual GEMM on the GPU vs the
+    oracle's, every variant."""
+    w = si.WORKLOADS[name]
+    x, W, g = si.workload_x(w), si.workload_w(w), si.workload_gamma(w)
+    p = oracle.prepare(sq.NVFP4, x, g)
+    q = oracle.quantize_weight(sq.NVFP4, W)
+    sp, rs = sq.prepare(dev16(x), None if g is None else dev16(g), fmt=sq.NVFP4, dense_backbone=True)
+    wq = sq.quantize_weight(dev16(W), fmt=sq.NVFP4)
+    ys = [host(sq.dual_gemm(sp, rs, wq, variant=v)) for v in NV_VARIANTS]
+    if samples is None:
+        ref = oracle.dual_gemm(sq.NVFP4, p, q)
+        for v, y in zip(NV_VARIANTS, ys):
+            assert normwise(y, ref) <= GEMM_TOL, v
+        return
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.integers(0, w.m, samples))
+    cols = rng.integers(0, w.n, samples)
+    rows[:4] = [0, 0, w.m - 1, w.m - 1]
+    cols[:4] = [0, w.n - 1, 0, w.n - 1]
+    order = np.argsort(rows, kind="stable")
+    rows, cols = rows[order], cols[order]
+    ref = oracle.dual_gemm_pairs(sq.NVFP4, p, q, rows, cols)
+    for v, y in zip(NV_VARIANTS, ys):
+        assert normwise(y[rows, cols], ref) <= GEMM_TOL, v
+
+
 def test_sparse_mfma_unsupported_for_mxfp4():
     x, w, g, p, q = _gemm_case(16, 128, 128, seed=9)
     sp, rs = to_dev_prep(sq.MXFP4, p)
