@@ -146,18 +146,7 @@ def main():
     for i in range(nsets):
         xi = x0.clone()
         wq = sq.quantize_weight(W0.clone() if i else W0, w.fmt)
-        lay = sq.default_scale_layout(w.k)
-        sp = sq.FP4Tensor(w.fmt, w.m, w.k, torch.empty((w.m, w.k // 4), dtype=torch.uint8, device=dev),
-                          sq.alloc_scales(w.fmt, w.m, w.k, lay, dev),
-                          meta=torch.empty((w.m, w.k // 8), dtype=torch.uint8, device=dev),
-                          scale_layout=lay)
-        rs = sq.FP4Tensor(w.fmt, w.m, w.k, torch.empty((w.m, w.k // 2), dtype=torch.uint8, device=dev),
-                          sq.alloc_scales(w.fmt, w.m, w.k, lay, dev), scale_layout=lay)
-        if w.fmt == sq.NVFP4:
-            sp.tensor_scale = torch.zeros(2, dtype=torch.float32, device=dev)
-            rs.tensor_scale = sp.tensor_scale
-        if not args.no_dense_view:
-            sp.dense_codes = torch.empty((w.m, w.k // 2), dtype=torch.uint8, device=dev)
+        sp, rs = sq.alloc_prepared(w.fmt, w.m, w.k, dev, dense_backbone=not args.no_dense_view)
         y = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
         sets.append((xi, wq, sp, rs, y))
     torch.cuda.synchronize()

@@ -66,20 +66,23 @@ typedef enum {
 } sharq_gemm_variant;
 
 /*
- * Layout of a block-scale array (sharq_fp4_view.scale_layout).
- *   ROW_MAJOR:   the scale byte of row r, k-block j sits at scales[r * ld_scales + j].
- *   KSTEP_MAJOR: k is cut into steps of 128; the scale bytes of row r in step t
- *                (4 for MXFP4, 8 for NVFP4, in k order) are contiguous, rows of a
- *                step are contiguous: the bytes start at
- *                scales + (t * ld_scales + r) * (128 / block); ld_scales >= rows
- *                counts rows per step.  Needs k % 128 == 0.  This is the view the
- *                GEMM reads fastest: 64 rows of one step are 256 (MX) or 512 (NV)
- *                contiguous bytes.
+ * Layout of every array of one operand view (sharq_fp4_view.layout): codes,
+ * meta, dense_codes and scales alike.
+ *   ROW_MAJOR:   row r of an array starts at array + r * ld (ld in bytes) and
+ *                holds the row's bytes in k order (see sharq_fp4_view).
+ *   KSTEP_MAJOR: k is cut into steps of 128; the bytes of row r that belong to
+ *                step t are contiguous, and so are the rows of one step: they
+ *                start at array + (t * ld + r) * b, where b is the array's bytes
+ *                per row and step (dense codes 64, 2:4 codes 32, meta 16, scales
+ *                4 for MXFP4 and 8 for NVFP4) and ld >= rows counts rows per
+ *                step.  Needs k % 128 == 0.  This is the layout the GEMM
+ *                streams fastest: 16 rows of one step are 1 KiB of contiguous
+ *                codes, so every cache line it fetches is used whole.
  */
 typedef enum {
-    SHARQ_SCALES_ROW_MAJOR = 0,
-    SHARQ_SCALES_KSTEP_MAJOR = 1
-} sharq_scale_layout;
+    SHARQ_LAYOUT_ROW_MAJOR = 0,
+    SHARQ_LAYOUT_KSTEP_MAJOR = 1
+} sharq_layout;
 
 /* Which array sharq_bytes sizes. */
 enum {
@@ -90,17 +93,18 @@ enum {
 };
 
 /*
- * One FP4 operand view.  Rows are K-contiguous; all pointers are device pointers.
+ * One FP4 operand view; all pointers are device pointers, every array in the
+ * layout `layout` names.  Per row, in k order:
  *
- *   codes        dense operand: [rows, k/2], two E2M1 codes per byte, the lower
- *                k in the low nibble.  2:4 backbone: [rows, k/4], one byte per
+ *   codes        dense operand: k/2 bytes, two E2M1 codes per byte, the lower
+ *                k in the low nibble.  2:4 backbone: k/4 bytes, one byte per
  *                group of four k: the code of the lower kept index in the low
  *                nibble, the code of the higher kept index in the high nibble.
- *   meta         backbone only (else NULL): [rows, k/8]; per group of four k the
+ *   meta         backbone only (else NULL): k/8 bytes; per group of four k the
  *                nibble i0 | i1 << 2 (kept indices, i0 < i1); group 2j sits in
  *                the low nibble of byte j.
  *   scales       E8M0 bytes (MXFP4, one per 32 k) or E4M3 bytes (NVFP4, one per
- *                16 k) of every row, in the layout `scale_layout` names.
+ *                16 k).
  *   dense_codes  optional backbone in the dense layout of `codes` (zeros at the
  *                dropped positions); written by sharq_prepare when non-NULL and
  *                read by SHARQ_GEMM_DENSE_EXPANDED.  NULL otherwise.
@@ -114,12 +118,29 @@ typedef struct sharq_fp4_view {
     int64_t ld_meta;
     uint8_t *scales;
     int64_t ld_scales;
-    int32_t scale_layout;   /* sharq_scale_layout */
+    int32_t layout;         /* sharq_layout, for every array of the view */
     int32_t reserved;       /* must be 0 */
     uint8_t *dense_codes;
     int64_t ld_dense;
     float *tensor_scale;
 } sharq_fp4_view;
+
+/*
+ * Requirements on a view of `rows` rows (checked by every entry point,
+ * SHARQ_ERR_SHAPE / SHARQ_ERR_ALIGN otherwise):
+ *   ROW_MAJOR:   each ld at least the array's row length in bytes (codes k/2,
+ *                or k/4 for 2:4 codes, meta k/8, dense_codes k/2, scales k/32
+ *                for MXFP4 and k/16 for NVFP4); codes and dense_codes 16-byte
+ *                aligned with ld % 16 == 0 (2:4 codes written by sharq_prepare:
+ *                8 and 8; read by the GEMM: 16 and 16); meta 4-byte aligned
+ *                with ld % 4 == 0 (read by the GEMM: 8 and 8); scales 4-byte
+ *                aligned with ld % 4 == 0 for the GEMM, 2-byte and even for
+ *                NVFP4 writers.
+ *   KSTEP_MAJOR: k % 128 == 0; each ld >= rows; codes, meta and dense_codes
+ *                16-byte aligned; scales 4-byte (MXFP4) or 8-byte (NVFP4)
+ *                aligned.
+ *   reserved == 0.
+ */
 
 /*
  * Quantize a weight matrix W [n, k] (bf16, row stride ld_w) to one FP4
@@ -133,12 +154,11 @@ typedef struct sharq_fp4_view {
  *          scale byte = E4M3(amax_block / (6 s_t)) (nearest even, saturating
  *          at 448), S = e4m3(byte) * s_t, codes = E2M1(w / S); every step is
  *          one fp32 operation.
- * Writes w_out->codes [n, k/2], w_out->scales, and for NVFP4
- * w_out->tensor_scale[0..1].  meta and dense_codes are ignored.
+ * Writes w_out->codes (dense, n rows), w_out->scales, and for NVFP4
+ * w_out->tensor_scale[0..1], in the layout w_out->layout names.  meta and
+ * dense_codes are ignored.
  * Requirements: n >= 1, k >= 32, k % 32 == 0, ld_w >= k, ld_w % 8 == 0;
- * w_bf16 and codes 16-byte aligned; ld_codes >= k/2 and % 16 == 0; scales:
- * ROW_MAJOR ld_scales >= k/blk (NVFP4: 2-byte aligned, ld even); KSTEP_MAJOR
- * k % 128 == 0, ld_scales >= n, 4-byte (MX) or 8-byte (NV) aligned.
+ * w_bf16 16-byte aligned; w_out as the view requirements above state.
  */
 sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int64_t n,
                                    int64_t k, int64_t ld_w, const sharq_fp4_view *w_out,
@@ -164,11 +184,8 @@ sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int
  * sparse_out->tensor_scale[0..1] (resid_out->tensor_scale must be NULL or the
  * same pointer: one tensor scale serves both paths).
  * Requirements: m >= 1; k >= 32, k % 32 == 0; k <= 16384 when gamma is given;
- * ld_x >= k, ld_x % 8 == 0; x 16-byte aligned; sparse codes 8-byte aligned with
- * ld % 8 == 0; meta 4-byte aligned with ld % 4 == 0; residual codes and
- * dense_codes 16-byte aligned with ld % 16 == 0; scales as for
- * sharq_quantize_weight (with m rows); every ld at least the row length it
- * describes.
+ * ld_x >= k, ld_x % 8 == 0; x 16-byte aligned; both views as the view
+ * requirements above state (m rows), with the same layout.
  */
 sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
                            int64_t ld_x, const uint16_t *gamma_bf16, float eps,
@@ -183,8 +200,10 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
  * to the fp32 sum.
  * The weight is passed as two views of ONE payload: w_sparse_view->codes must
  * equal w_dense_view->codes (otherwise SHARQ_ERR_SHAPE); each view brings its
- * own scales pointer (the path-specific scale view; for MXFP4 the values must
- * be the weight's scales, and both usually alias one buffer).
+ * own scales pointer (the path-specific scale view: the backbone product
+ * reads w_sparse_view->scales, the residual product w_dense_view->scales;
+ * usually both alias the weight's scales).  Both weight views must name the
+ * same layout.
  * Variants: DECOMPRESS reads the 2:4 backbone (codes + meta) and expands it
  * to dense codes inside the GEMM; DENSE_EXPANDED reads sparse->dense_codes
  * instead; AUTO is DENSE_EXPANDED when sparse->dense_codes is non-NULL, else
@@ -195,12 +214,10 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
  * sharq_prepare writes them (the two kept positions of a group distinct).
  * NVFP4 runs on fp16 MFMAs (2:4 and dense): each operand element
  * q * e4m3 scale is exact in fp16.
- * Requirements: m, n >= 1; k >= 128, k % 128 == 0; ld_y >= n; codes 16-byte
- * aligned with ld % 16 == 0 (backbone codes too;
- * meta ld % 8 == 0 and 8-byte aligned); scales ROW_MAJOR 4-byte aligned with
- * ld % 4 == 0, or KSTEP_MAJOR with ld >= rows (the fast path: all four views
- * KSTEP_MAJOR); y 4-byte aligned; every code, meta and scale array spans
- * less than 4 GiB (rows x ld), else SHARQ_ERR_SHAPE.
+ * Requirements: m, n >= 1; k >= 128, k % 128 == 0; ld_y >= n; y 4-byte
+ * aligned; the four views as the view requirements above state (m rows for
+ * the activations, n for the weight); every array spans less than 4 GiB.
+ * Fastest when every view is KSTEP_MAJOR.
  */
 sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sparse,
                              const sharq_fp4_view *resid, const sharq_fp4_view *w_sparse_view,
@@ -216,7 +233,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 2
+#define SHARQ_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -29,8 +29,11 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_DEVICE = range(6)
 
 BYTES_DENSE_CODES, BYTES_SPARSE_CODES, BYTES_META, BYTES_SCALES = range(4)
 
-SCALES_ROW_MAJOR = 0
-SCALES_KSTEP_MAJOR = 1
+LAYOUT_ROW_MAJOR = 0
+LAYOUT_KSTEP_MAJOR = 1
+
+# bytes per row and 128-k step of each array of an operand (k-step-major layout)
+BPS_CODES, BPS_SPARSE_CODES, BPS_META = 64, 32, 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsharq.so")
@@ -38,7 +41,7 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 # every symbol include/sharq.h declares
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_dual_gemm", "sharq_bytes",
            "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class SharqError(RuntimeError):
@@ -53,7 +56,7 @@ class FP4ViewC(ctypes.Structure):
         ("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
         ("meta", ctypes.c_void_p), ("ld_meta", ctypes.c_int64),
         ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64),
-        ("scale_layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("dense_codes", ctypes.c_void_p), ("ld_dense", ctypes.c_int64),
         ("tensor_scale", ctypes.c_void_p),
     ]
@@ -138,81 +141,96 @@ def _bits16(t):
     return t
 
 
+def scale_bps(fmt: int) -> int:
+    """Scale bytes per row and 128-k step."""
+    return 128 // BLOCK[fmt]
+
+
+def _ld_of(t, layout: int, bps: int) -> int:
+    """ld of one array: bytes per row (row-major) or rows per step (k-step-major)."""
+    if layout == LAYOUT_KSTEP_MAJOR:
+        if t.dim() != 3 or t.shape[2] != bps or t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != bps):
+            raise ValueError(f"k-step-major array must be [k/128, rows, {bps}], contiguous within a step")
+        return t.stride(0) // bps if t.shape[0] > 1 else t.shape[1]
+    return _ld(t)
+
+
 @dataclasses.dataclass
 class FP4Tensor:
     """Device buffers of one FP4 operand (see ``sharq_fp4_view``).
 
-    scales: uint8 [rows, k/blk] (row-major) or [k/128, rows, 128/blk]
-    (k-step-major, the layout the GEMM reads fastest)."""
+    Every array is in ``layout``: row-major [rows, bytes per row], or
+    k-step-major [k/128, rows, bytes per row and step] (codes 64, 2:4 codes
+    32, meta 16, scales 4 (MXFP4) or 8 (NVFP4)), the layout the GEMM streams
+    fastest.  ``codes`` is 2:4-compressed when ``meta`` is set."""
     fmt: int
     rows: int
     k: int
-    codes: object                   # uint8 [rows, k/2] or [rows, k/4] (backbone)
+    codes: object
     scales: object
-    meta: object = None             # uint8 [rows, k/8] (backbone)
-    dense_codes: object = None      # uint8 [rows, k/2] (optional backbone view)
+    meta: object = None             # 2:4 indices (backbone)
+    dense_codes: object = None      # optional dense backbone view
     tensor_scale: object = None     # float32 [2] (NVFP4)
-    scale_layout: int = SCALES_ROW_MAJOR
+    layout: int = LAYOUT_ROW_MAJOR
 
     def view(self) -> FP4ViewC:
         v = FP4ViewC()
+        L = self.layout
+        v.layout = L
         v.codes = _ptr(self.codes)
-        v.ld_codes = _ld(self.codes)
+        v.ld_codes = _ld_of(self.codes, L, BPS_SPARSE_CODES if self.meta is not None else BPS_CODES)
         if self.meta is not None:
             v.meta = _ptr(self.meta)
-            v.ld_meta = _ld(self.meta)
+            v.ld_meta = _ld_of(self.meta, L, BPS_META)
         v.scales = _ptr(self.scales)
-        v.scale_layout = self.scale_layout
-        if self.scale_layout == SCALES_KSTEP_MAJOR:
-            sc = self.scales                     # [k/128, rows, 128/blk]
-            if sc.stride(2) != 1 or (sc.shape[1] > 1 and sc.stride(1) != sc.shape[2]):
-                raise ValueError("k-step-major scales must be contiguous within a step")
-            # rows per k step
-            v.ld_scales = sc.stride(0) // sc.shape[2] if sc.shape[0] > 1 else sc.shape[1]
-        else:
-            v.ld_scales = _ld(self.scales)
+        v.ld_scales = _ld_of(self.scales, L, scale_bps(self.fmt))
         if self.dense_codes is not None:
             v.dense_codes = _ptr(self.dense_codes)
-            v.ld_dense = _ld(self.dense_codes)
+            v.ld_dense = _ld_of(self.dense_codes, L, BPS_CODES)
         if self.tensor_scale is not None:
             v.tensor_scale = _ptr(self.tensor_scale)
         return v
 
+    def row_major(self, name: str):
+        """Array `name` as a [rows, bytes per row] tensor (a copy if k-step-major)."""
+        return row_major(getattr(self, name), self.layout, self.rows)
 
-def _alloc(rows, cols, device, dtype=None):
+
+def row_major(arr, layout: int, rows: int):
+    if layout == LAYOUT_KSTEP_MAJOR:
+        return arr.permute(1, 0, 2)[:rows].reshape(rows, -1)
+    return arr
+
+
+def default_layout(k: int) -> int:
+    return LAYOUT_KSTEP_MAJOR if k % 128 == 0 else LAYOUT_ROW_MAJOR
+
+
+def alloc_array(rows: int, k: int, bps: int, layout: int, device):
+    """Uninitialized array of `rows` rows with `bps` bytes per row and 128-k step."""
     torch = _torch()
-    return torch.empty((rows, cols), dtype=dtype or torch.uint8, device=device)
-
-
-def default_scale_layout(k: int) -> int:
-    return SCALES_KSTEP_MAJOR if k % 128 == 0 else SCALES_ROW_MAJOR
+    if layout == LAYOUT_KSTEP_MAJOR:
+        return torch.empty((k // 128, rows, bps), dtype=torch.uint8, device=device)
+    return torch.empty((rows, k * bps // 128), dtype=torch.uint8, device=device)
 
 
 def alloc_scales(fmt: int, rows: int, k: int, layout: int, device):
-    """Scale array of `rows` rows in the given layout."""
-    torch = _torch()
-    blk = BLOCK[fmt]
-    if layout == SCALES_KSTEP_MAJOR:
-        return torch.empty((k // 128, rows, 128 // blk), dtype=torch.uint8, device=device)
-    return torch.empty((rows, k // blk), dtype=torch.uint8, device=device)
+    return alloc_array(rows, k, scale_bps(fmt), layout, device)
 
 
 def scales_row_major(t: FP4Tensor):
     """The operand's scales as a [rows, k/blk] tensor (a copy if k-step-major)."""
-    if t.scale_layout == SCALES_KSTEP_MAJOR:
-        return t.scales.permute(1, 0, 2).reshape(t.rows, -1)
-    return t.scales
+    return t.row_major("scales")
 
 
-def quantize_weight(w, fmt: int = MXFP4, scale_layout: Optional[int] = None,
-                    stream=None) -> FP4Tensor:
+def quantize_weight(w, fmt: int = MXFP4, layout: Optional[int] = None, stream=None) -> FP4Tensor:
     """One FP4 payload of W [n, k] (both GEMM paths read it)."""
     torch = _torch()
     w = _bits16(w)
     n, k = w.shape
-    layout = default_scale_layout(k) if scale_layout is None else scale_layout
-    out = FP4Tensor(fmt, n, k, _alloc(n, k // 2, w.device),
-                    alloc_scales(fmt, n, k, layout, w.device), scale_layout=layout)
+    L = default_layout(k) if layout is None else layout
+    out = FP4Tensor(fmt, n, k, alloc_array(n, k, BPS_CODES, L, w.device),
+                    alloc_scales(fmt, n, k, L, w.device), layout=L)
     if fmt == NVFP4:
         out.tensor_scale = torch.zeros(2, dtype=torch.float32, device=w.device)
     v = out.view()
@@ -221,23 +239,30 @@ def quantize_weight(w, fmt: int = MXFP4, scale_layout: Optional[int] = None,
     return out
 
 
-def prepare(x, gamma=None, eps: float = 1e-5, fmt: int = MXFP4, dense_backbone: bool = False,
-            scale_layout: Optional[int] = None, stream=None):
-    """Fused preparation of X [m, k]: returns (backbone, residual) FP4 operands."""
+def alloc_prepared(fmt: int, m: int, k: int, device, dense_backbone: bool = False,
+                   layout: Optional[int] = None):
+    """Uninitialized (backbone, residual) operands for sharq_prepare."""
     torch = _torch()
+    L = default_layout(k) if layout is None else layout
+    sp = FP4Tensor(fmt, m, k, alloc_array(m, k, BPS_SPARSE_CODES, L, device),
+                   alloc_scales(fmt, m, k, L, device), meta=alloc_array(m, k, BPS_META, L, device),
+                   layout=L)
+    if dense_backbone:
+        sp.dense_codes = alloc_array(m, k, BPS_CODES, L, device)
+    rs = FP4Tensor(fmt, m, k, alloc_array(m, k, BPS_CODES, L, device),
+                   alloc_scales(fmt, m, k, L, device), layout=L)
+    if fmt == NVFP4:
+        sp.tensor_scale = torch.zeros(2, dtype=torch.float32, device=device)
+        rs.tensor_scale = sp.tensor_scale
+    return sp, rs
+
+
+def prepare(x, gamma=None, eps: float = 1e-5, fmt: int = MXFP4, dense_backbone: bool = False,
+            layout: Optional[int] = None, stream=None):
+    """Fused preparation of X [m, k]: returns (backbone, residual) FP4 operands."""
     x = _bits16(x)
     m, k = x.shape
-    dev = x.device
-    layout = default_scale_layout(k) if scale_layout is None else scale_layout
-    sp = FP4Tensor(fmt, m, k, _alloc(m, k // 4, dev), alloc_scales(fmt, m, k, layout, dev),
-                   meta=_alloc(m, k // 8, dev), scale_layout=layout)
-    if dense_backbone:
-        sp.dense_codes = _alloc(m, k // 2, dev)
-    rs = FP4Tensor(fmt, m, k, _alloc(m, k // 2, dev), alloc_scales(fmt, m, k, layout, dev),
-                   scale_layout=layout)
-    if fmt == NVFP4:
-        sp.tensor_scale = torch.zeros(2, dtype=torch.float32, device=dev)
-        rs.tensor_scale = sp.tensor_scale
+    sp, rs = alloc_prepared(fmt, m, k, x.device, dense_backbone, layout)
     prepare_into(x, gamma, eps, sp, rs, stream)
     return sp, rs
 

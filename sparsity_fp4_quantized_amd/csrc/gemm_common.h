@@ -39,6 +39,31 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
   return r;
 }
 
+// One operand array streamed global -> LDS: a buffer resource over its bytes
+// from row r0 on (reads past the end return 0), the byte stride between rows
+// within a step and the byte stride between 128-k steps.  `bps` is the
+// array's bytes per row and step; row-major arrays have ld bytes per row,
+// k-step-major ones ld rows per step.
+struct OpStream {
+  i32x4 rsrc;
+  uint32_t row_stride, step;
+};
+
+__device__ __forceinline__ OpStream op_stream(const uint8_t *p, int64_t ld, int ksm, int64_t rows,
+                                              int64_t r0, int64_t steps, int64_t bps) {
+  OpStream s;
+  if (ksm) {
+    s.rsrc = make_rsrc(p + r0 * bps, (uint32_t)(((steps - 1) * ld + rows - r0) * bps));
+    s.row_stride = (uint32_t)bps;
+    s.step = (uint32_t)(ld * bps);
+  } else {
+    s.rsrc = make_rsrc(p + r0 * ld, (uint32_t)((rows - r0) * ld));
+    s.row_stride = (uint32_t)ld;
+    s.step = (uint32_t)bps;
+  }
+  return s;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
@@ -64,6 +89,35 @@ __device__ __forceinline__ void wait_vmcnt() {
 // A bare barrier: the explicit vmcnt wait before it is the only ordering the
 // stage needs, and the memory clobber keeps LDS reads from moving across it.
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Workgroup -> output tile.  Workgroups go to the 8 XCDs round robin (XCD =
+// id % 8) and each XCD has its own L2, so XCD x takes a contiguous run of
+// tile numbers.  Tiles are numbered in bands of GM tile rows, down the rows
+// of a band first, so that a run covers a compact block of tile rows and
+// columns: the A rows and W columns of one XCD's tiles stay in its L2.  A
+// bijection of [0, gm * gn) for any grid.
+__device__ __forceinline__ void xcd_tile(uint32_t id, uint32_t gm, uint32_t gn, uint32_t GM,
+                                         uint32_t &tm, uint32_t &tn) {
+  const uint32_t T = gm * gn, per = T / 8, rem = T % 8;
+  const uint32_t x = id % 8, local = id / 8;
+  const uint32_t t = x * per + min(x, rem) + local;
+  const uint32_t band = t / (GM * gn), within = t - band * GM * gn;
+  const uint32_t rows = min(GM, gm - band * GM);
+  tm = band * GM + within % rows;
+  tn = within / rows;
+}
+
+// Host side: tile rows per band for a gm x gn grid of TBM x TBN tiles, so
+// that each XCD's block of tiles reads about as many A bytes (TBM k per tile
+// row, both paths) as W bytes (TBN k / 2 per tile column).
+inline uint32_t xcd_band_rows(int64_t gm, int64_t gn, int tbm, int tbn) {
+  const double per = (double)(gm * gn) / 8.0;
+  double want = per * tbn / (2.0 * tbm);
+  uint32_t GM = 1;
+  while (GM < gm && (double)(2 * GM) * (2 * GM) <= want * 2.0) GM *= 2;
+  (void)gn;
+  return GM;
+}
 
 // Expand eight 2:4 groups (8 code bytes, 4 meta bytes) into 32 dense codes.
 __device__ __forceinline__ void expand8(uint32_t c_lo, uint32_t c_hi, uint32_t meta, uint32_t out[4]) {

@@ -63,10 +63,9 @@ struct Smem {
 };
 
 // The 32-bit word of E8M0 scales of row r for 128-k step kt.
-__device__ __forceinline__ uint32_t scale_word(const uint8_t *p, int64_t ld, int kstep, int64_t r,
+__device__ __forceinline__ uint32_t scale_word(const uint8_t *p, int64_t ld, int ksm, int64_t r,
                                                int kt) {
-  const int64_t off = kstep ? ((int64_t)kt * ld + r) * 4 : r * ld + (int64_t)kt * 4;
-  return *reinterpret_cast<const uint32_t *>(p + off);
+  return *reinterpret_cast<const uint32_t *>(p + arr_off(r, kt, ld, ksm, 4));
 }
 
 template <int BN, bool kDense>
@@ -78,16 +77,16 @@ __device__ __forceinline__ void load_stage(const GemmArgs &a, int64_t m0, int64_
   for (int j = 0; j < 2; ++j) {
     const int c = tid + kThreads * j, row = c >> 2, part = c & 3;
     const int64_t gm = m0 + row;
-    st.ar[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.r_codes + gm * a.ld_rc + kt * 64 + part * 16) : z;
+    st.ar[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.r_codes + arr_off(gm, kt, a.ld_rc, a.r_ksm, 64) + part * 16) : z;
     if (kDense)
-      st.as[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.s_dense + gm * a.ld_sd + kt * 64 + part * 16) : z;
+      st.as[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.s_dense + arr_off(gm, kt, a.ld_sd, a.s_ksm, 64) + part * 16) : z;
   }
   if (!kDense) {
     const int row = tid >> 1, half = tid & 1;
     const int64_t gm = m0 + row;
     if (gm < a.m) {
-      st.as[0] = *reinterpret_cast<const u32x4 *>(a.s_codes + gm * a.ld_sc + kt * 32 + half * 16);
-      u32x2 mv = *reinterpret_cast<const u32x2 *>(a.meta + gm * a.ld_meta + kt * 16 + half * 8);
+      st.as[0] = *reinterpret_cast<const u32x4 *>(a.s_codes + arr_off(gm, kt, a.ld_sc, a.s_ksm, 32) + half * 16);
+      u32x2 mv = *reinterpret_cast<const u32x2 *>(a.meta + arr_off(gm, kt, a.ld_meta, a.s_ksm, 16) + half * 8);
       st.as[1] = u32x4{mv.x, mv.y, 0u, 0u};
     } else {
       st.as[0] = z;
@@ -100,18 +99,18 @@ __device__ __forceinline__ void load_stage(const GemmArgs &a, int64_t m0, int64_
     if (c < Stage<BN, kDense>::kWChunks) {
       const int row = c >> 2, part = c & 3;
       const int64_t gn = n0 + row;
-      st.w[j] = gn < a.n ? *reinterpret_cast<const u32x4 *>(a.w_codes + gn * a.ld_wc + kt * 64 + part * 16) : z;
+      st.w[j] = gn < a.n ? *reinterpret_cast<const u32x4 *>(a.w_codes + arr_off(gn, kt, a.ld_wc, a.w_ksm, 64) + part * 16) : z;
     }
   }
   // scale words: threads [0, 256) the two A paths of row tid; [256, 256 + BN) the two W views
   if (tid < BM) {
     const int64_t gm = m0 + tid;
-    st.sc[0] = gm < a.m ? scale_word(a.s_scales, a.ld_ss, a.ss_kstep, gm, kt) : 0u;
-    st.sc[1] = gm < a.m ? scale_word(a.r_scales, a.ld_rs, a.rs_kstep, gm, kt) : 0u;
+    st.sc[0] = gm < a.m ? scale_word(a.s_scales, a.ld_ss, a.s_ksm, gm, kt) : 0u;
+    st.sc[1] = gm < a.m ? scale_word(a.r_scales, a.ld_rs, a.r_ksm, gm, kt) : 0u;
   } else if (tid < BM + BN) {
     const int64_t gn = n0 + (tid - BM);
-    st.sc[0] = gn < a.n ? scale_word(a.ws_scales, a.ld_wss, a.wss_kstep, gn, kt) : 0u;
-    st.sc[1] = gn < a.n ? scale_word(a.wd_scales, a.ld_wds, a.wds_kstep, gn, kt) : 0u;
+    st.sc[0] = gn < a.n ? scale_word(a.ws_scales, a.ld_wss, a.w_ksm, gn, kt) : 0u;
+    st.sc[1] = gn < a.n ? scale_word(a.wd_scales, a.ld_wds, a.w_ksm, gn, kt) : 0u;
   }
 }
 
@@ -276,14 +275,13 @@ struct DPlan {
 };
 
 struct DRsrc {
-  i32x4 as, ar, w, sas, sar, sws, swd;
+  OpStream as, ar, w, sas, sar, sws, swd;
 };
 
 template <int TBM, int TBN, int NW>
 struct DOffs {
   uint32_t chunk[DPlan<TBM, TBN, NW>::kChunkPer];
   uint32_t scale[DPlan<TBM, TBN, NW>::kScalePer];
-  uint32_t ld_ss, ld_rs, ld_wss, ld_wds;   // bytes per 128-k step of each scale view
 };
 
 template <int TBM, int TBN, int NW>
@@ -291,35 +289,35 @@ __device__ __forceinline__ void plan_loads(const GemmArgs &a, int64_t m0, int64_
                                            int lane, DRsrc &R, DOffs<TBM, TBN, NW> &O) {
   using P = DPlan<TBM, TBN, NW>;
   const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  R.as = make_rsrc(a.s_dense + m0 * a.ld_sd, (uint32_t)((a.m - m0) * a.ld_sd));
-  R.ar = make_rsrc(a.r_codes + m0 * a.ld_rc, (uint32_t)((a.m - m0) * a.ld_rc));
-  R.w = make_rsrc(a.w_codes + n0 * a.ld_wc, (uint32_t)((a.n - n0) * a.ld_wc));
-  // k-step-major scales: step t of row r at (t * ld + r) * 4; the resource
-  // starts at the tile's first row and ends at the array's last row of the
-  // last step, so rows past M (N) of the last step read 0
   const int64_t steps = a.k / BK;
-  R.sas = make_rsrc(a.s_scales + m0 * 4, (uint32_t)(((steps - 1) * a.ld_ss + a.m - m0) * 4));
-  R.sar = make_rsrc(a.r_scales + m0 * 4, (uint32_t)(((steps - 1) * a.ld_rs + a.m - m0) * 4));
-  R.sws = make_rsrc(a.ws_scales + n0 * 4, (uint32_t)(((steps - 1) * a.ld_wss + a.n - n0) * 4));
-  R.swd = make_rsrc(a.wd_scales + n0 * 4, (uint32_t)(((steps - 1) * a.ld_wds + a.n - n0) * 4));
+  R.as = op_stream(a.s_dense, a.ld_sd, a.s_ksm, a.m, m0, steps, 64);
+  R.ar = op_stream(a.r_codes, a.ld_rc, a.r_ksm, a.m, m0, steps, 64);
+  R.w = op_stream(a.w_codes, a.ld_wc, a.w_ksm, a.n, n0, steps, 64);
+  R.sas = op_stream(a.s_scales, a.ld_ss, a.s_ksm, a.m, m0, steps, 4);
+  R.sar = op_stream(a.r_scales, a.ld_rs, a.r_ksm, a.m, m0, steps, 4);
+  R.sws = op_stream(a.ws_scales, a.ld_wss, a.w_ksm, a.n, n0, steps, 4);
+  R.swd = op_stream(a.wd_scales, a.ld_wds, a.w_ksm, a.n, n0, steps, 4);
 #pragma unroll
   for (int j = 0; j < P::kChunkPer; ++j) {
     int q = wave + NW * j;
-    int64_t ld = a.ld_sd;
-    if (q >= P::kA && q < 2 * P::kA) { q -= P::kA; ld = a.ld_rc; }
-    else if (q >= 2 * P::kA) { q -= 2 * P::kA; ld = a.ld_wc; }
-    O.chunk[j] = (uint32_t)((16 * q + lrow) * ld + lchunk * 16);
+    uint32_t rs = R.as.row_stride;
+    if (q >= P::kA && q < 2 * P::kA) { q -= P::kA; rs = R.ar.row_stride; }
+    else if (q >= 2 * P::kA) { q -= 2 * P::kA; rs = R.w.row_stride; }
+    O.chunk[j] = (uint32_t)(16 * q + lrow) * rs + lchunk * 16;
   }
 #pragma unroll
   for (int j = 0; j < P::kScalePer; ++j) {
     int t = wave + NW * j;
-    if (t >= TBM / 64 && (t -= TBM / 64) >= TBM / 64 && (t -= TBM / 64) >= TBN / 64) t -= TBN / 64;
-    O.scale[j] = (uint32_t)((64 * t + lane) * 4);
+    uint32_t rs = R.sas.row_stride;
+    if (t >= TBM / 64) {
+      t -= TBM / 64; rs = R.sar.row_stride;
+      if (t >= TBM / 64) {
+        t -= TBM / 64; rs = R.sws.row_stride;
+        if (t >= TBN / 64) { t -= TBN / 64; rs = R.swd.row_stride; }
+      }
+    }
+    O.scale[j] = (uint32_t)(64 * t + lane) * rs;
   }
-  O.ld_ss = (uint32_t)(a.ld_ss * 4);
-  O.ld_rs = (uint32_t)(a.ld_rs * 4);
-  O.ld_wss = (uint32_t)(a.ld_wss * 4);
-  O.ld_wds = (uint32_t)(a.ld_wds * 4);
 }
 
 template <int TBM, int TBN, int NW>
@@ -328,25 +326,26 @@ __device__ __forceinline__ void issue_stage(const DRsrc &R, const DOffs<TBM, TBN
   using P = DPlan<TBM, TBN, NW>;
   using St = DStage<TBM, TBN>;
   const uint32_t base = lds_addr(&S);
-  const uint32_t kc = (uint32_t)kt * 64u;
+  const uint32_t t = (uint32_t)kt;
   constexpr uint32_t oar = offsetof(St, ar), ow = offsetof(St, w);
   constexpr uint32_t osas = offsetof(St, sas), osar = offsetof(St, sar);
   constexpr uint32_t osws = offsetof(St, sws), oswd = offsetof(St, swd);
 #pragma unroll
   for (int j = 0; j < P::kChunkPer; ++j) {
     const int q = wave + NW * j;
-    if (q < P::kA) b2l16(R.as, O.chunk[j], kc, base + q * 1024);
-    else if (q < 2 * P::kA) b2l16(R.ar, O.chunk[j], kc, base + oar + (q - P::kA) * 1024);
-    else if (q < 2 * P::kA + P::kW) b2l16(R.w, O.chunk[j], kc, base + ow + (q - 2 * P::kA) * 1024);
+    if (q < P::kA) b2l16(R.as.rsrc, O.chunk[j], t * R.as.step, base + q * 1024);
+    else if (q < 2 * P::kA) b2l16(R.ar.rsrc, O.chunk[j], t * R.ar.step, base + oar + (q - P::kA) * 1024);
+    else if (q < 2 * P::kA + P::kW)
+      b2l16(R.w.rsrc, O.chunk[j], t * R.w.step, base + ow + (q - 2 * P::kA) * 1024);
   }
 #pragma unroll
   for (int j = 0; j < P::kScalePer; ++j) {
-    int t = wave + NW * j;
-    if (t >= P::kS) continue;
-    if (t < TBM / 64) b2l4(R.sas, O.scale[j], kt * O.ld_ss, base + osas + 256 * t);
-    else if ((t -= TBM / 64) < TBM / 64) b2l4(R.sar, O.scale[j], kt * O.ld_rs, base + osar + 256 * t);
-    else if ((t -= TBM / 64) < TBN / 64) b2l4(R.sws, O.scale[j], kt * O.ld_wss, base + osws + 256 * t);
-    else b2l4(R.swd, O.scale[j], kt * O.ld_wds, base + oswd + 256 * (t - TBN / 64));
+    int q = wave + NW * j;
+    if (q >= P::kS) continue;
+    if (q < TBM / 64) b2l4(R.sas.rsrc, O.scale[j], t * R.sas.step, base + osas + 256 * q);
+    else if ((q -= TBM / 64) < TBM / 64) b2l4(R.sar.rsrc, O.scale[j], t * R.sar.step, base + osar + 256 * q);
+    else if ((q -= TBM / 64) < TBN / 64) b2l4(R.sws.rsrc, O.scale[j], t * R.sws.step, base + osws + 256 * q);
+    else b2l4(R.swd.rsrc, O.scale[j], t * R.swd.step, base + oswd + 256 * (q - TBN / 64));
   }
 }
 
@@ -403,7 +402,7 @@ __device__ __forceinline__ void compute_stage(const DStage<TBM, TBN> &S, v16f (&
 }
 
 template <int TBM, int TBN, int NW, int STAGES>
-__global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, uint32_t band) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
   constexpr int TN = TBN / 64;
   using P = DPlan<TBM, TBN, NW>;
@@ -413,7 +412,9 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, li = lane & 31;
-  const int64_t m0 = (int64_t)blockIdx.y * TBM, n0 = (int64_t)blockIdx.x * TBN;
+  uint32_t tm, tn;
+  xcd_tile(blockIdx.x, (uint32_t)((a.m + TBM - 1) / TBM), (uint32_t)((a.n + TBN - 1) / TBN), band, tm, tn);
+  const int64_t m0 = (int64_t)tm * TBM, n0 = (int64_t)tn * TBN;
 
   v16f acc[2][TN];
 #pragma unroll
@@ -462,8 +463,9 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a) {
 
 template <int TBM, int TBN, int NW, int STAGES>
 void launch_dense(const GemmArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)((a.n + TBN - 1) / TBN), (unsigned)((a.m + TBM - 1) / TBM)), block(64 * NW);
-  dual_gemm_dense_kernel<TBM, TBN, NW, STAGES><<<grid, block, 0, s>>>(a);
+  const int64_t gm = (a.m + TBM - 1) / TBM, gn = (a.n + TBN - 1) / TBN;
+  dual_gemm_dense_kernel<TBM, TBN, NW, STAGES>
+      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN));
 }
 
 template <int BN>
@@ -478,15 +480,15 @@ void launch_bn(const GemmArgs &a, bool dense, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s) {
-  const bool kstep_scales = a.ss_kstep && a.rs_kstep && a.wss_kstep && a.wds_kstep;
-  if (dense_expanded && kstep_scales) {
-    // 128 x BN tiles, two workgroups per CU; the widest tile that still gives
-    // every CU two tiles
+  if (dense_expanded) {
+    // 128-row tiles, two LDS stages: 128 x 192 (two workgroups a CU) when
+    // that still gives every CU two tiles and K is short; else 128 x 128
+    // (three a CU), whose smaller K step keeps more loads in flight per CU
     const int64_t mt = (a.m + 127) / 128;
-    if (mt * ((a.n + 191) / 192) >= 512)
+    if (mt * ((a.n + 191) / 192) >= 512 && a.k <= 8192)
       launch_dense<128, 192, 4, 2>(a, s);
     else
-      launch_dense<128, 128, 4, 3>(a, s);
+      launch_dense<128, 128, 4, 2>(a, s);
   } else {
     const int64_t mt = (a.m + BM - 1) / BM;
     if (mt * ((a.n + 191) / 192) >= 256 || mt * ((a.n + 127) / 128) > 256)

@@ -94,30 +94,13 @@ struct NPlan {
 };
 
 struct NRsrc {
-  i32x4 as, am, ar, w, sas, sar, sws, swd;
+  OpStream as, am, ar, w, sas, sar, sws, swd;
 };
 
 template <int KPER>
 struct NOffs {
   uint32_t voff[KPER];      // per-lane byte offset of each load in its operand
-  uint32_t step_sa, step_sr, step_sws, step_swd;   // scale bytes per 128-k step
 };
-
-// Scale array of one operand: resource from row r0, per-lane offset of scale
-// word d (row d / 2, half d & 1) and the bytes per K step.  K-step-major:
-// step t of row r at (t * ld + r) * 8; row-major: at r * ld + 8 t.
-__device__ __forceinline__ i32x4 scale_rsrc(const uint8_t *p, int64_t ld, int kstep, int64_t rows,
-                                            int64_t r0, int64_t steps) {
-  if (kstep) return make_rsrc(p + r0 * 8, (uint32_t)(((steps - 1) * ld + rows - r0) * 8));
-  return make_rsrc(p + r0 * ld, (uint32_t)((rows - r0) * ld));
-}
-__device__ __forceinline__ uint32_t scale_voff(int64_t ld, int kstep, int d) {
-  const int row = d >> 1, half = d & 1;
-  return kstep ? (uint32_t)(row * 8 + half * 4) : (uint32_t)(row * ld + half * 4);
-}
-__device__ __forceinline__ uint32_t scale_step(int64_t ld, int kstep) {
-  return kstep ? (uint32_t)(ld * 8) : 8u;
-}
 
 template <int TBM, int TBN, int NW, int BB, bool SH>
 __device__ __forceinline__ void nv_plan(const GemmArgs &a, int64_t m0, int64_t n0, int wave,
@@ -125,45 +108,38 @@ __device__ __forceinline__ void nv_plan(const GemmArgs &a, int64_t m0, int64_t n
   using P = NPlan<TBM, TBN, NW, BB, SH>;
   const int64_t steps = a.k / BK;
   if (BB == kBBDense) {
-    R.as = make_rsrc(a.s_dense + m0 * a.ld_sd, (uint32_t)((a.m - m0) * a.ld_sd));
+    R.as = op_stream(a.s_dense, a.ld_sd, a.s_ksm, a.m, m0, steps, 64);
   } else {
-    R.as = make_rsrc(a.s_codes + m0 * a.ld_sc, (uint32_t)((a.m - m0) * a.ld_sc));
-    R.am = make_rsrc(a.meta + m0 * a.ld_meta, (uint32_t)((a.m - m0) * a.ld_meta));
+    R.as = op_stream(a.s_codes, a.ld_sc, a.s_ksm, a.m, m0, steps, 32);
+    R.am = op_stream(a.meta, a.ld_meta, a.s_ksm, a.m, m0, steps, 16);
   }
-  R.ar = make_rsrc(a.r_codes + m0 * a.ld_rc, (uint32_t)((a.m - m0) * a.ld_rc));
-  R.w = make_rsrc(a.w_codes + n0 * a.ld_wc, (uint32_t)((a.n - n0) * a.ld_wc));
-  R.sas = scale_rsrc(a.s_scales, a.ld_ss, a.ss_kstep, a.m, m0, steps);
-  R.sar = scale_rsrc(a.r_scales, a.ld_rs, a.rs_kstep, a.m, m0, steps);
-  R.sws = scale_rsrc(a.ws_scales, a.ld_wss, a.wss_kstep, a.n, n0, steps);
-  if (!SH) R.swd = scale_rsrc(a.wd_scales, a.ld_wds, a.wds_kstep, a.n, n0, steps);
-  O.step_sa = scale_step(a.ld_ss, a.ss_kstep);
-  O.step_sr = scale_step(a.ld_rs, a.rs_kstep);
-  O.step_sws = scale_step(a.ld_wss, a.wss_kstep);
-  O.step_swd = SH ? 0u : scale_step(a.ld_wds, a.wds_kstep);
+  R.ar = op_stream(a.r_codes, a.ld_rc, a.r_ksm, a.m, m0, steps, 64);
+  R.w = op_stream(a.w_codes, a.ld_wc, a.w_ksm, a.n, n0, steps, 64);
+  R.sas = op_stream(a.s_scales, a.ld_ss, a.s_ksm, a.m, m0, steps, 8);
+  R.sar = op_stream(a.r_scales, a.ld_rs, a.r_ksm, a.m, m0, steps, 8);
+  R.sws = op_stream(a.ws_scales, a.ld_wss, a.w_ksm, a.n, n0, steps, 8);
+  if (!SH) R.swd = op_stream(a.wd_scales, a.ld_wds, a.w_ksm, a.n, n0, steps, 8);
   // dense chunk loads: lane l -> row l / 4 of the 16, logical chunk placed at
-  // LDS slot l (the lds_slot swizzle)
+  // LDS slot l (the lds_slot swizzle); scale word d of a load: row d / 2, half d & 1
   const int drow = lane >> 2, dchunk = (lane & 3) ^ ((lane >> 4) & 3);
 #pragma unroll
   for (int j = 0; j < P::kPer; ++j) {
     const int q = wave + NW * j;
     uint32_t v = 0;
     if (q < P::b1) {
-      if (BB == kBBDense) v = (uint32_t)((16 * q + drow) * a.ld_sd + dchunk * 16);
-      else v = (uint32_t)((32 * q + (lane >> 1)) * a.ld_sc + (lane & 1) * 16);
+      if (BB == kBBDense) v = (uint32_t)(16 * q + drow) * R.as.row_stride + dchunk * 16;
+      else v = (uint32_t)(32 * q + (lane >> 1)) * R.as.row_stride + (lane & 1) * 16;
     } else if (q < P::b2) {
-      v = (uint32_t)((64 * (q - P::b1) + lane) * a.ld_meta);
+      v = (uint32_t)(64 * (q - P::b1) + lane) * R.am.row_stride;
     } else if (q < P::b3) {
-      v = (uint32_t)((16 * (q - P::b2) + drow) * a.ld_rc + dchunk * 16);
+      v = (uint32_t)(16 * (q - P::b2) + drow) * R.ar.row_stride + dchunk * 16;
     } else if (q < P::b4) {
-      v = (uint32_t)((16 * (q - P::b3) + drow) * a.ld_wc + dchunk * 16);
-    } else if (q < P::b5) {
-      v = scale_voff(a.ld_ss, a.ss_kstep, 64 * (q - P::b4) + lane);
-    } else if (q < P::b6) {
-      v = scale_voff(a.ld_rs, a.rs_kstep, 64 * (q - P::b5) + lane);
-    } else if (q < P::b7) {
-      v = scale_voff(a.ld_wss, a.wss_kstep, 64 * (q - P::b6) + lane);
+      v = (uint32_t)(16 * (q - P::b3) + drow) * R.w.row_stride + dchunk * 16;
     } else if (q < P::kTotal) {
-      v = scale_voff(a.ld_wds, a.wds_kstep, 64 * (q - P::b7) + lane);
+      const int d = 64 * (q < P::b5 ? q - P::b4 : q < P::b6 ? q - P::b5 : q < P::b7 ? q - P::b6 : q - P::b7) + lane;
+      const uint32_t rs = q < P::b5 ? R.sas.row_stride : q < P::b6 ? R.sar.row_stride
+                          : q < P::b7 ? R.sws.row_stride : R.swd.row_stride;
+      v = (uint32_t)(d >> 1) * rs + (d & 1) * 4;
     }
     O.voff[j] = v;
   }
@@ -182,14 +158,14 @@ __device__ __forceinline__ void nv_issue(const NRsrc &R, const NOffs<NPlan<TBM, 
 #pragma unroll
   for (int j = 0; j < P::kPer; ++j) {
     const int q = wave + NW * j;
-    if (q < P::b1) b2l16(R.as, O.voff[j], t * (BB == kBBDense ? 64u : 32u), base + q * 1024);
-    else if (q < P::b2) b2l16(R.am, O.voff[j], t * 16u, base + oam + (q - P::b1) * 1024);
-    else if (q < P::b3) b2l16(R.ar, O.voff[j], t * 64u, base + oar + (q - P::b2) * 1024);
-    else if (q < P::b4) b2l16(R.w, O.voff[j], t * 64u, base + ow + (q - P::b3) * 1024);
-    else if (q < P::b5) b2l4(R.sas, O.voff[j], t * O.step_sa, base + osas + (q - P::b4) * 256);
-    else if (q < P::b6) b2l4(R.sar, O.voff[j], t * O.step_sr, base + osar + (q - P::b5) * 256);
-    else if (q < P::b7) b2l4(R.sws, O.voff[j], t * O.step_sws, base + osws + (q - P::b6) * 256);
-    else if (q < P::kTotal) b2l4(R.swd, O.voff[j], t * O.step_swd, base + oswd + (q - P::b7) * 256);
+    if (q < P::b1) b2l16(R.as.rsrc, O.voff[j], t * R.as.step, base + q * 1024);
+    else if (q < P::b2) b2l16(R.am.rsrc, O.voff[j], t * R.am.step, base + oam + (q - P::b1) * 1024);
+    else if (q < P::b3) b2l16(R.ar.rsrc, O.voff[j], t * R.ar.step, base + oar + (q - P::b2) * 1024);
+    else if (q < P::b4) b2l16(R.w.rsrc, O.voff[j], t * R.w.step, base + ow + (q - P::b3) * 1024);
+    else if (q < P::b5) b2l4(R.sas.rsrc, O.voff[j], t * R.sas.step, base + osas + (q - P::b4) * 256);
+    else if (q < P::b6) b2l4(R.sar.rsrc, O.voff[j], t * R.sar.step, base + osar + (q - P::b5) * 256);
+    else if (q < P::b7) b2l4(R.sws.rsrc, O.voff[j], t * R.sws.step, base + osws + (q - P::b6) * 256);
+    else if (q < P::kTotal) b2l4(R.swd.rsrc, O.voff[j], t * R.swd.step, base + oswd + (q - P::b7) * 256);
   }
 }
 
@@ -373,7 +349,7 @@ __device__ __forceinline__ void nv_compute(const NStage<TBM, TBN, BB, SH> &S,
 }
 
 template <int TBM, int TBN, int NW, int STAGES, int BB, bool SH>
-__global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a, uint32_t band) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
   static_assert(TBM % 64 == 0 && TBN % 64 == 0, "tile shape");
   constexpr int TN = TBN / 64;
@@ -384,7 +360,9 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, li = lane & 31;
-  const int64_t m0 = (int64_t)blockIdx.y * TBM, n0 = (int64_t)blockIdx.x * TBN;
+  uint32_t tm, tn;
+  xcd_tile(blockIdx.x, (uint32_t)((a.m + TBM - 1) / TBM), (uint32_t)((a.n + TBN - 1) / TBN), band, tm, tn);
+  const int64_t m0 = (int64_t)tm * TBM, n0 = (int64_t)tn * TBN;
 
   v16f acc[2][TN];
 #pragma unroll
@@ -434,11 +412,13 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a) {
 
 template <int TBN, int STAGES, int BB>
 void launch_nv(const GemmArgs &a, bool shared, hipStream_t s) {
-  dim3 grid((unsigned)((a.n + TBN - 1) / TBN), (unsigned)((a.m + 127) / 128)), block(256);
+  const int64_t gm = (a.m + 127) / 128, gn = (a.n + TBN - 1) / TBN;
+  const dim3 grid((unsigned)(gm * gn)), block(256);
+  const uint32_t band = xcd_band_rows(gm, gn, 128, TBN);
   if (shared)
-    dual_gemm_nv_kernel<128, TBN, 4, STAGES, BB, true><<<grid, block, 0, s>>>(a);
+    dual_gemm_nv_kernel<128, TBN, 4, STAGES, BB, true><<<grid, block, 0, s>>>(a, band);
   else
-    dual_gemm_nv_kernel<128, TBN, 4, STAGES, BB, false><<<grid, block, 0, s>>>(a);
+    dual_gemm_nv_kernel<128, TBN, 4, STAGES, BB, false><<<grid, block, 0, s>>>(a, band);
 }
 
 template <int BB>
@@ -455,7 +435,7 @@ void launch_bb(const GemmArgs &a, bool shared, hipStream_t s) {
 
 hipError_t launch_dual_gemm_nv(const GemmArgs &a, int variant, hipStream_t s) {
   // one W scale view serves both paths when the two views are the same array
-  const bool shared = a.ws_scales == a.wd_scales && a.ld_wss == a.ld_wds && a.wss_kstep == a.wds_kstep;
+  const bool shared = a.ws_scales == a.wd_scales && a.ld_wss == a.ld_wds;
   switch (variant) {
     case 1: launch_bb<kBBExpand>(a, shared, s); break;
     case 2: launch_bb<kBBDense>(a, shared, s); break;

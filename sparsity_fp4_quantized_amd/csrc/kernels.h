@@ -19,7 +19,7 @@ struct PrepArgs {
   uint8_t *r_scales; int64_t ld_rs;
   uint8_t *s_dense;  int64_t ld_sd;   // optional
   float *tensor_scale;                // NVFP4: [0] scale, [1] amax
-  int s_kstep, r_kstep;               // scale arrays in the k-step-major layout
+  int s_ksm, r_ksm;                   // backbone / residual view k-step-major (every array)
 };
 
 struct QuantArgs {
@@ -28,7 +28,7 @@ struct QuantArgs {
   uint8_t *codes;  int64_t ld_c;
   uint8_t *scales; int64_t ld_s;
   float *tensor_scale;                // NVFP4
-  int kstep;                          // scales in the k-step-major layout
+  int ksm;                            // codes and scales k-step-major
 };
 
 struct GemmArgs {
@@ -45,8 +45,15 @@ struct GemmArgs {
   const float *w_tensor_scale;              // NVFP4
   float *y;                int64_t ld_y;
   int64_t m, n, k;
-  int ss_kstep, rs_kstep, wss_kstep, wds_kstep;   // per scale view: k-step-major layout
+  int s_ksm, r_ksm, w_ksm;   // per operand (codes, meta, dense view, scales): k-step-major
 };
+
+// Offset of the bytes of row r in 128-k step t of an operand array with `bps`
+// bytes per row and step: row-major (ld bytes per row) or k-step-major (ld
+// rows per step).
+__host__ __device__ inline int64_t arr_off(int64_t r, int64_t t, int64_t ld, int ksm, int64_t bps) {
+  return ksm ? (t * ld + r) * bps : r * ld + t * bps;
+}
 
 hipError_t launch_prepare_mx(const PrepArgs &a, hipStream_t s);
 hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s);

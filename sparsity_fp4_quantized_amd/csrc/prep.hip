@@ -356,33 +356,33 @@ __device__ __forceinline__ void quantize_block_nv(const float xf[32], float s_t,
 
 // ---------------------------------------------------------------- stores
 
-// Scale bytes of the lane's 32 k (block b): MXFP4 one byte, NVFP4 two.
-// Row-major: byte offset row * ld + b (MX) or 2 b (NV).  K-step-major: step
-// t = b / 4 holds 4 (MX) or 8 (NV) bytes per row, rows contiguous.
+// Stores of the lane's 32 k (block b of row `row`): every array of a view in
+// its layout (arr_off: row-major, or k-step-major with 4 blocks of 32 k per
+// 128-k step).  Scales: MXFP4 one byte, NVFP4 two.
 template <int FMT>
-__device__ __forceinline__ void store_scale(uint8_t *base, int64_t ld, bool kstep, int64_t row,
+__device__ __forceinline__ void store_scale(uint8_t *base, int64_t ld, int ksm, int64_t row,
                                             int64_t b, uint32_t v) {
   if (FMT == 0) {
-    const int64_t off = kstep ? ((b >> 2) * ld + row) * 4 + (b & 3) : row * ld + b;
-    base[off] = (uint8_t)v;
+    base[arr_off(row, b >> 2, ld, ksm, 4) + (b & 3)] = (uint8_t)v;
   } else {
-    const int64_t off = kstep ? ((b >> 2) * ld + row) * 8 + 2 * (b & 3) : row * ld + 2 * b;
-    *reinterpret_cast<uint16_t *>(base + off) = (uint16_t)v;
+    *reinterpret_cast<uint16_t *>(base + arr_off(row, b >> 2, ld, ksm, 8) + 2 * (b & 3)) = (uint16_t)v;
   }
 }
 
 template <int FMT>
 __device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int64_t b,
                                             const BlockOut &o) {
-  *reinterpret_cast<uint2 *>(a.s_codes + row * a.ld_sc + 8 * b) = make_uint2(o.s_comp[0], o.s_comp[1]);
-  *reinterpret_cast<uint32_t *>(a.meta + row * a.ld_meta + 4 * b) = o.meta;
-  *reinterpret_cast<uint4 *>(a.r_codes + row * a.ld_rc + 16 * b) =
+  const int64_t t = b >> 2, q = b & 3;
+  *reinterpret_cast<uint2 *>(a.s_codes + arr_off(row, t, a.ld_sc, a.s_ksm, 32) + 8 * q) =
+      make_uint2(o.s_comp[0], o.s_comp[1]);
+  *reinterpret_cast<uint32_t *>(a.meta + arr_off(row, t, a.ld_meta, a.s_ksm, 16) + 4 * q) = o.meta;
+  *reinterpret_cast<uint4 *>(a.r_codes + arr_off(row, t, a.ld_rc, a.r_ksm, 64) + 16 * q) =
       make_uint4(o.r_codes[0], o.r_codes[1], o.r_codes[2], o.r_codes[3]);
   if (a.s_dense)
-    *reinterpret_cast<uint4 *>(a.s_dense + row * a.ld_sd + 16 * b) =
+    *reinterpret_cast<uint4 *>(a.s_dense + arr_off(row, t, a.ld_sd, a.s_ksm, 64) + 16 * q) =
         make_uint4(o.s_dense[0], o.s_dense[1], o.s_dense[2], o.s_dense[3]);
-  store_scale<FMT>(a.s_scales, a.ld_ss, a.s_kstep, row, b, o.s_scale);
-  store_scale<FMT>(a.r_scales, a.ld_rs, a.r_kstep, row, b, o.r_scale);
+  store_scale<FMT>(a.s_scales, a.ld_ss, a.s_ksm, row, b, o.s_scale);
+  store_scale<FMT>(a.r_scales, a.ld_rs, a.r_ksm, row, b, o.r_scale);
 }
 
 __device__ __forceinline__ float nv_tensor_scale(const float *ts) {
@@ -489,13 +489,24 @@ __global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chu
   store_block<FMT>(a, row, b, o);
 }
 
-// NVFP4 tensor amax of x_n (one atomic max per wave; fp32 bit patterns of
-// non-negative values order like unsigned integers).
-__device__ __forceinline__ void wave_amax_atomic(uint32_t am, float *ts) {
+// NVFP4 tensor amax of x_n.  fp32 bit patterns of non-negative values order
+// like unsigned integers; each workgroup reduces its share (grid-stride) and
+// issues at most one atomic max, so that few atomics meet at the one address.
+__device__ __forceinline__ void block_amax_atomic(uint32_t am, float *ts) {
+  __shared__ uint32_t wmax[8];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int *>(ts + 1), am);
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) wmax[wave] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int i = 0; i < nw; ++i) m = max(m, wmax[i]);
+    if (m) atomicMax(reinterpret_cast<unsigned int *>(ts + 1), m);
+  }
 }
+
+constexpr unsigned kAmaxGrid = 2048;   // workgroups of the amax passes (at most)
 
 template <int WPR>
 __global__ __launch_bounds__(512) void amax_norm_kernel(PrepArgs a) {
@@ -503,40 +514,43 @@ __global__ __launch_bounds__(512) void amax_norm_kernel(PrepArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int riw = wave / WPR, wir = wave - riw * WPR;
-  const int64_t row = (int64_t)blockIdx.x * RPW + riw;
   const int64_t nblk = a.k / 32;
   const int64_t b = (int64_t)wir * 64 + lane;
-  const bool has = row < a.m && b < nblk;
-  const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
-  uint32_t xw[16];
-  float xf[32];
-  load32_cached(a.x + lrow * a.ld_x + 32 * lb, xw);
-  unpack32(xw, xf);
-  float s = block_sumsq(xf);
-  float r = row_rms<WPR>(has ? s : 0.0f, riw, wir, a.k, a.eps);
+  const int64_t groups = (a.m + RPW - 1) / RPW;
   uint32_t am = 0;
-  if (has) {
-    normalize32(xf, xw, a.gamma + 32 * b, r);
+  for (int64_t gi = blockIdx.x; gi < groups; gi += gridDim.x) {
+    const int64_t row = gi * RPW + riw;
+    const bool has = row < a.m && b < nblk;
+    const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
+    uint32_t xw[16];
+    float xf[32];
+    load32_cached(a.x + lrow * a.ld_x + 32 * lb, xw);
+    unpack32(xw, xf);
+    float s = block_sumsq(xf);
+    float r = row_rms<WPR>(has ? s : 0.0f, riw, wir, a.k, a.eps);
+    if (has) {
+      normalize32(xf, xw, a.gamma + 32 * b, r);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) am = max(am, __float_as_uint(xf[i]) & 0x7FFFFFFFu);
+      for (int i = 0; i < 32; ++i) am = max(am, __float_as_uint(xf[i]) & 0x7FFFFFFFu);
+    }
+    __syncthreads();   // the row reduction's LDS is reused by the next row group
   }
-  if (row < a.m) wave_amax_atomic(am, a.tensor_scale);
+  block_amax_atomic(am, a.tensor_scale);
 }
 
 __global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *x, int64_t ld, int64_t m,
                                                         int64_t k, float *ts) {
-  const int64_t nblk = k / 32;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nblk = k / 32, total = m * nblk;
   uint32_t am = 0;
-  if (gid < m * nblk) {
+  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total;
+       gid += (int64_t)gridDim.x * 256) {
     const int64_t row = gid / nblk, b = gid - row * nblk;
     uint32_t xw[16];
     load32_cached(x + row * ld + 32 * b, xw);
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = max(am, max(xw[i] & 0x7FFFu, (xw[i] >> 16) & 0x7FFFu));
-    am <<= 16;
   }
-  wave_amax_atomic(am, ts);
+  block_amax_atomic(am << 16, ts);
 }
 
 __global__ void zero_amax_kernel(float *ts) { ts[1] = 0.0f; }
@@ -545,7 +559,7 @@ template <int FMT, int WPR>
 void launch_norm(const PrepArgs &a, hipStream_t s) {
   constexpr int RPW = WPR <= 4 ? 4 / WPR : 1;
   const dim3 grid((unsigned)((a.m + RPW - 1) / RPW)), block(64 * WPR * RPW);
-  if (FMT == 1) amax_norm_kernel<WPR><<<grid, block, 0, s>>>(a);
+  if (FMT == 1) amax_norm_kernel<WPR><<<dim3(min(grid.x, kAmaxGrid)), block, 0, s>>>(a);
   prep_norm_kernel<FMT, WPR><<<grid, block, 0, s>>>(a);
 }
 
@@ -566,7 +580,8 @@ hipError_t launch_prepare(const PrepArgs &a, hipStream_t s) {
       default: launch_norm<FMT, 8>(a, s); break;
     }
   } else {
-    if (FMT == 1) amax_flat_kernel<<<flat_grid, 256, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.tensor_scale);
+    if (FMT == 1)
+      amax_flat_kernel<<<dim3(min(flat_grid.x, kAmaxGrid)), 256, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.tensor_scale);
     const uint32_t chunks = (uint32_t)((a.k / 32 + 63) / 64);
     const uint64_t waves = (uint64_t)a.m * chunks;
     prep_flat_kernel<FMT><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a, chunks);
@@ -625,8 +640,9 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(QuantArgs a) {
     scales = sb0 | (sb1 << 8);
     nv_codes(v, S, q);
   }
-  *reinterpret_cast<uint4 *>(a.codes + row * a.ld_c + 16 * b) = make_uint4(q[0], q[1], q[2], q[3]);
-  store_scale<FMT>(a.scales, a.ld_s, a.kstep, row, b, scales);
+  *reinterpret_cast<uint4 *>(a.codes + arr_off(row, b >> 2, a.ld_c, a.ksm, 64) + 16 * (b & 3)) =
+      make_uint4(q[0], q[1], q[2], q[3]);
+  store_scale<FMT>(a.scales, a.ld_s, a.ksm, row, b, scales);
 }
 
 template <int FMT>
@@ -635,7 +651,7 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t s) {
   dim3 grid((unsigned)((total + 255) / 256)), block(256);
   if (FMT == 1) {
     zero_amax_kernel<<<1, 1, 0, s>>>(a.tensor_scale);
-    amax_flat_kernel<<<grid, block, 0, s>>>(a.w, a.ld_w, a.n, a.k, a.tensor_scale);
+    amax_flat_kernel<<<dim3(min(grid.x, kAmaxGrid)), block, 0, s>>>(a.w, a.ld_w, a.n, a.k, a.tensor_scale);
   }
   quant_weight_kernel<FMT><<<grid, block, 0, s>>>(a);
   return hipGetLastError();

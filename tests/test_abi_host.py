@@ -43,11 +43,19 @@ FAKE = 1 << 20     # aligned, never dereferenced: validation fails first
 
 
 def view(codes=FAKE, ld_codes=128, meta=FAKE, ld_meta=32, scales=FAKE, ld_scales=8,
-         dense=None, ld_dense=0, ts=None):
+         dense=None, ld_dense=0, ts=None, layout=0, reserved=0):
     v = sq.FP4ViewC()
     v.codes, v.ld_codes, v.meta, v.ld_meta = codes, ld_codes, meta, ld_meta
     v.scales, v.ld_scales, v.dense_codes, v.ld_dense, v.tensor_scale = scales, ld_scales, dense, ld_dense, ts
+    v.layout, v.reserved = layout, reserved
     return v
+
+
+def ksm(rows=16, **kw):
+    """A k-step-major view: every ld counts rows per 128-k step."""
+    args = dict(ld_codes=rows, ld_meta=rows, ld_scales=rows, layout=sq.LAYOUT_KSTEP_MAJOR)
+    args.update(kw)
+    return view(**args)
 
 
 def prep(fmt=0, x=FAKE, m=16, k=256, ld_x=256, gamma=None, sp=None, rs=None):
@@ -75,8 +83,15 @@ def prep(fmt=0, x=FAKE, m=16, k=256, ld_x=256, gamma=None, sp=None, rs=None):
     (dict(fmt=1), sq.ERR_SHAPE),           # NVFP4 needs k/16 scales per row
     (dict(fmt=1, sp=view(ld_codes=64, ld_scales=16), rs=view(meta=None, ld_scales=16)),
      sq.ERR_NULL),                         # NVFP4 without a tensor-scale buffer
+    (dict(sp=ksm(), rs=view(meta=None)), sq.ERR_SHAPE),    # the two views differ in layout
+    (dict(k=160, ld_x=160, sp=ksm(), rs=ksm(meta=None)), sq.ERR_SHAPE),   # k % 128
+    (dict(sp=ksm(ld_codes=8), rs=ksm(meta=None)), sq.ERR_SHAPE),          # ld < rows
+    (dict(sp=ksm(meta=FAKE + 8), rs=ksm(meta=None)), sq.ERR_ALIGN),
+    (dict(sp=view(ld_codes=64, reserved=1)), sq.ERR_SHAPE),
+    (dict(sp=view(ld_codes=64, layout=5)), sq.ERR_UNSUPPORTED),
 ])
 def test_prepare_validation(kwargs, status):
+    assert prep(**kwargs) == status
     assert prep(**kwargs) == status
 
 
@@ -104,6 +119,11 @@ def gemm(fmt=0, m=16, n=256, k=256, y=FAKE, ld_y=256, variant=0, sp=None, rs=Non
     (dict(sp=view(ld_codes=72)), sq.ERR_ALIGN),
     (dict(y=FAKE + 1), sq.ERR_ALIGN),
     (dict(fmt=1), sq.ERR_SHAPE),      # NVFP4 needs k/16 scales per row (ld 8 < 16)
+    (dict(ws=ksm(256, meta=None), wd=view(meta=None)), sq.ERR_SHAPE),   # W views' layouts differ
+    (dict(sp=ksm(8), rs=ksm(meta=None), ws=ksm(256, meta=None), wd=ksm(256, meta=None)),
+     sq.ERR_SHAPE),                   # rows per step < m
+    (dict(sp=ksm(scales=FAKE + 2), rs=ksm(meta=None), ws=ksm(256, meta=None), wd=ksm(256, meta=None)),
+     sq.ERR_ALIGN),
 ])
 def test_gemm_validation(kwargs, status):
     assert gemm(**kwargs) == status
@@ -118,6 +138,10 @@ def test_quantize_weight_validation():
     assert L.sharq_quantize_weight(0, FAKE + 4, 16, 256, 256, ctypes.byref(v), None) == sq.ERR_ALIGN
     nv = view(meta=None, ld_scales=16)
     assert L.sharq_quantize_weight(1, FAKE, 16, 256, 256, ctypes.byref(nv), None) == sq.ERR_NULL
+    k1 = ksm(meta=None, codes=FAKE + 8)
+    assert L.sharq_quantize_weight(0, FAKE, 16, 256, 256, ctypes.byref(k1), None) == sq.ERR_ALIGN
+    k2 = ksm(meta=None)
+    assert L.sharq_quantize_weight(0, FAKE, 16, 160, 160, ctypes.byref(k2), None) == sq.ERR_SHAPE
 
 
 def test_binding_refuses_without_library(monkeypatch, tmp_path):

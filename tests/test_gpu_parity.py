@@ -32,12 +32,12 @@ def host(t) -> np.ndarray:
 def check_prep(fmt, x_bits, gamma_bits, eps=1e-5, dense=True, label="", layout=None):
     ref = oracle.prepare(fmt, x_bits, gamma_bits, eps, dense_backbone=True)
     sp, rs = sq.prepare(dev16(x_bits), None if gamma_bits is None else dev16(gamma_bits), eps,
-                        fmt=fmt, dense_backbone=dense, scale_layout=layout)
-    got = {"meta": host(sp.meta), "s_codes": host(sp.codes),
-           "s_scales": host(sq.scales_row_major(sp)),
-           "r_codes": host(rs.codes), "r_scales": host(sq.scales_row_major(rs))}
+                        fmt=fmt, dense_backbone=dense, layout=layout)
+    got = {"meta": host(sp.row_major("meta")), "s_codes": host(sp.row_major("codes")),
+           "s_scales": host(sp.row_major("scales")),
+           "r_codes": host(rs.row_major("codes")), "r_scales": host(rs.row_major("scales"))}
     if dense:
-        got["s_dense"] = host(sp.dense_codes)
+        got["s_dense"] = host(sp.row_major("dense_codes"))
     for key, val in got.items():
         want = ref[key]
         if not np.array_equal(val, want):
@@ -51,35 +51,38 @@ def check_prep(fmt, x_bits, gamma_bits, eps=1e-5, dense=True, label="", layout=N
     return ref, sp, rs
 
 
-def dev_scales(rowmajor: np.ndarray, fmt, layout):
-    """Row-major [rows, k/blk] scale bytes as a device array in `layout`."""
-    if layout == sq.SCALES_KSTEP_MAJOR:
+def to_layout(rowmajor: np.ndarray, bps: int, layout):
+    """Row-major [rows, steps * bps] array as a device array in `layout`."""
+    if layout == sq.LAYOUT_KSTEP_MAJOR:
         rows, nb = rowmajor.shape
-        per = 128 // sq.BLOCK[fmt]
-        rowmajor = np.ascontiguousarray(rowmajor.reshape(rows, nb // per, per).transpose(1, 0, 2))
+        rowmajor = rowmajor.reshape(rows, nb // bps, bps).transpose(1, 0, 2)
     return torch.from_numpy(np.ascontiguousarray(rowmajor)).to(DEV)
 
 
-def to_dev_weight(fmt, q, layout=sq.SCALES_KSTEP_MAJOR):
+def dev_scales(rowmajor: np.ndarray, fmt, layout):
+    return to_layout(rowmajor, sq.scale_bps(fmt), layout)
+
+
+def to_dev_weight(fmt, q, layout=sq.LAYOUT_KSTEP_MAJOR):
     n, kh = q["codes"].shape
-    w = sq.FP4Tensor(fmt, n, kh * 2, torch.from_numpy(q["codes"]).to(DEV),
-                     dev_scales(q["scales"], fmt, layout), scale_layout=layout)
+    w = sq.FP4Tensor(fmt, n, kh * 2, to_layout(q["codes"], sq.BPS_CODES, layout),
+                     dev_scales(q["scales"], fmt, layout), layout=layout)
     if fmt == sq.NVFP4:
         w.tensor_scale = torch.tensor([q["tensor_scale"][0], 0.0], dtype=torch.float32, device=DEV)
     return w
 
 
-def to_dev_prep(fmt, p, layout=sq.SCALES_KSTEP_MAJOR):
+def to_dev_prep(fmt, p, layout=sq.LAYOUT_KSTEP_MAJOR):
     """Oracle preparation outputs as device FP4 tensors (GEMM-only tests)."""
     m, kq = p["s_codes"].shape
     k = kq * 4
-    sp = sq.FP4Tensor(fmt, m, k, torch.from_numpy(p["s_codes"]).to(DEV),
+    sp = sq.FP4Tensor(fmt, m, k, to_layout(p["s_codes"], sq.BPS_SPARSE_CODES, layout),
                       dev_scales(p["s_scales"], fmt, layout),
-                      meta=torch.from_numpy(p["meta"]).to(DEV), scale_layout=layout)
+                      meta=to_layout(p["meta"], sq.BPS_META, layout), layout=layout)
     if "s_dense" in p:
-        sp.dense_codes = torch.from_numpy(p["s_dense"]).to(DEV)
-    rs = sq.FP4Tensor(fmt, m, k, torch.from_numpy(p["r_codes"]).to(DEV),
-                      dev_scales(p["r_scales"], fmt, layout), scale_layout=layout)
+        sp.dense_codes = to_layout(p["s_dense"], sq.BPS_CODES, layout)
+    rs = sq.FP4Tensor(fmt, m, k, to_layout(p["r_codes"], sq.BPS_CODES, layout),
+                      dev_scales(p["r_scales"], fmt, layout), layout=layout)
     if fmt == sq.NVFP4:
         ts = torch.tensor([p["tensor_scale"][0], 0.0], dtype=torch.float32, device=DEV)
         sp.tensor_scale = ts
@@ -110,11 +113,11 @@ def test_prepare_mx_workloads(name):
 
 
 @pytest.mark.parametrize("fmt,norm", [(0, True), (0, False), (1, True), (1, False)])
-def test_prepare_scale_layouts(fmt, norm):
-    """Both scale layouts hold the same bytes."""
+def test_prepare_layouts(fmt, norm):
+    """Both layouts hold the same bytes."""
     x = si.activations("student_t4", 21, 512, 5, 50.0, seed=44 + fmt)
     g = si.gamma(512, 6) if norm else None
-    for layout in (sq.SCALES_ROW_MAJOR, sq.SCALES_KSTEP_MAJOR):
+    for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR):
         check_prep(fmt, x, g, label=f"layout {layout}", layout=layout)
 
 
@@ -137,11 +140,12 @@ def test_prepare_padded_row_stride():
     g = si.gamma(k, seed=5)
     xt = dev16(x)[:, :k]
     assert xt.stride(0) == ld
-    sp, rs = sq.prepare(xt, dev16(g), 1e-5)
     ref = oracle.prepare(sq.MXFP4, np.ascontiguousarray(x[:, :k]), g)
-    assert np.array_equal(host(sp.codes), ref["s_codes"])
-    assert np.array_equal(host(rs.codes), ref["r_codes"])
-    assert np.array_equal(host(sp.meta), ref["meta"])
+    for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR):
+        sp, rs = sq.prepare(xt, dev16(g), 1e-5, layout=layout)
+        assert np.array_equal(host(sp.row_major("codes")), ref["s_codes"])
+        assert np.array_equal(host(rs.row_major("codes")), ref["r_codes"])
+        assert np.array_equal(host(sp.row_major("meta")), ref["meta"])
 
 
 def test_prepare_nv_small():
@@ -171,11 +175,11 @@ def test_prepare_deterministic():
 def test_quantize_weight(fmt, n, k):
     w = si.weights(n, k, seed=n + k)
     ref = oracle.quantize_weight(fmt, w)
-    layouts = [sq.SCALES_ROW_MAJOR] + ([sq.SCALES_KSTEP_MAJOR] if k % 128 == 0 else [])
+    layouts = [sq.LAYOUT_ROW_MAJOR] + ([sq.LAYOUT_KSTEP_MAJOR] if k % 128 == 0 else [])
     for layout in layouts:
-        got = sq.quantize_weight(dev16(w), fmt, scale_layout=layout)
-        assert np.array_equal(host(got.codes), ref["codes"])
-        assert np.array_equal(host(sq.scales_row_major(got)), ref["scales"])
+        got = sq.quantize_weight(dev16(w), fmt, layout=layout)
+        assert np.array_equal(host(got.row_major("codes")), ref["codes"])
+        assert np.array_equal(host(got.row_major("scales")), ref["scales"])
     if fmt == sq.NVFP4:
         assert host(got.tensor_scale)[0] == ref["tensor_scale"][0]
 
@@ -196,7 +200,7 @@ def _gemm_case(m, n, k, seed, fmt=sq.MXFP4, norm=True):
 def test_dual_gemm_mx_vs_oracle(m, n, k):
     x, w, g, p, q = _gemm_case(m, n, k, seed=m + 7 * n + k)
     ref = oracle.dual_gemm(sq.MXFP4, p, q)
-    for layout in (sq.SCALES_KSTEP_MAJOR, sq.SCALES_ROW_MAJOR):
+    for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
         sp, rs = to_dev_prep(sq.MXFP4, p, layout)
         wq = to_dev_weight(sq.MXFP4, q, layout)
         for variant in (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED):
@@ -207,15 +211,15 @@ def test_dual_gemm_mx_vs_oracle(m, n, k):
 
 def test_dual_gemm_variants_bitwise_equal():
     x, w, g, p, q = _gemm_case(200, 300, 512, seed=3)
-    sp, rs = to_dev_prep(sq.MXFP4, p, sq.SCALES_ROW_MAJOR)
-    wq = to_dev_weight(sq.MXFP4, q, sq.SCALES_ROW_MAJOR)
+    sp, rs = to_dev_prep(sq.MXFP4, p, sq.LAYOUT_ROW_MAJOR)
+    wq = to_dev_weight(sq.MXFP4, q, sq.LAYOUT_ROW_MAJOR)
     a = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS)
     b = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DENSE_EXPANDED)
     c = sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS)
     assert torch.equal(a, b) and torch.equal(a, c)
     # the k-step-major pipeline: deterministic run to run
-    sp2, rs2 = to_dev_prep(sq.MXFP4, p, sq.SCALES_KSTEP_MAJOR)
-    wq2 = to_dev_weight(sq.MXFP4, q, sq.SCALES_KSTEP_MAJOR)
+    sp2, rs2 = to_dev_prep(sq.MXFP4, p, sq.LAYOUT_KSTEP_MAJOR)
+    wq2 = to_dev_weight(sq.MXFP4, q, sq.LAYOUT_KSTEP_MAJOR)
     d = sq.dual_gemm(sp2, rs2, wq2, variant=sq.GEMM_DENSE_EXPANDED)
     e = sq.dual_gemm(sp2, rs2, wq2, variant=sq.GEMM_DENSE_EXPANDED)
     assert torch.equal(d, e)
@@ -287,7 +291,7 @@ def test_dual_gemm_nv_vs_oracle(m, n, k):
     """NVFP4-style dual GEMM, all three backbone variants, both scale layouts."""
     x, w, g, p, q = _gemm_case(m, n, k, seed=3 * m + n + k, fmt=sq.NVFP4)
     ref = oracle.dual_gemm(sq.NVFP4, p, q)
-    for layout in (sq.SCALES_KSTEP_MAJOR, sq.SCALES_ROW_MAJOR):
+    for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
         sp, rs = to_dev_prep(sq.NVFP4, p, layout)
         wq = to_dev_weight(sq.NVFP4, q, layout)
         for variant in NV_VARIANTS:
@@ -336,7 +340,7 @@ def test_dual_gemm_path_specific_weight_views(fmt):
     ref = (oracle.dual_gemm(fmt, _zeroed(p, "residual"), q).astype(np.float64)
            + oracle.dual_gemm(fmt, _zeroed(p, "backbone"), q2))
     variants = NV_VARIANTS if fmt == sq.NVFP4 else (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)
-    for layout in (sq.SCALES_KSTEP_MAJOR, sq.SCALES_ROW_MAJOR):
+    for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
         sp, rs = to_dev_prep(fmt, p, layout)
         wq = to_dev_weight(fmt, q, layout)
         wd = dev_scales(q2["scales"], fmt, layout)
