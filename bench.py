@@ -13,9 +13,22 @@ the 256 MB last-level cache.
 Prints ONE JSON line.  `value` is the step's throughput in algorithmic
 TFLOP/s (3*M*N*K: the backbone GEMM multiplies two of every four k, the
 residual GEMM all of them).  `roofline` describes the dominant kernel (the
-dual GEMM) against the dense MXFP4 MFMA peak; `roofline_prep` the
-preparation kernel against HBM bandwidth.  `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+dual GEMM) against the dense MFMA peak of its operand type (HBM bandwidth
+for the decode shape, whose GEMM streams the weight once); `roofline_prep`
+the preparation kernel(s) against HBM bandwidth.  Kernel durations are the
+means of HIP event pairs around each launch inside the timed region.
+`traffic` is the HBM bytes per launch measured with rocprofv3 counters
+(FETCH_SIZE and WRITE_SIZE, scaled by what the same counters read for a
+device copy of known size), read from profiles/traffic.json when it was
+taken on the current kernel source, else null.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload.
+
+Traffic measurement (two counter runs, then the conversion on any host):
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o pmc -- \
+      python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --calibrate-copy [--workload W]
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR_W -o pmc -- \
+      python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --calibrate-copy [--workload W]
+  python3 bench.py --traffic-from DIR_F DIR_W [--workload W] [--variant V]
 """
 from __future__ import annotations
 
@@ -39,6 +52,7 @@ PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
 LLC_BYTES = 256 << 20            # MI355X Infinity Cache
 
 PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 256 << 20           # the counter-calibration copy
 
 
 def prep_bytes_per_elem(fmt: int) -> float:
@@ -61,6 +75,99 @@ def source_hash(*names) -> str:
         with open(os.path.join(ROOT, "sparsity_fp4_quantized_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_sources(fmt: int):
+    gemm = "gemm_mx.hip" if fmt == si.MXFP4 else "gemm_nv.hip"
+    return ((gemm, "gemm_common.h", "fp4_device.h", "kernels.h"),
+            ("prep.hip", "fp4_device.h", "kernels.h"))
+
+
+def traffic_key(kind: str, w: si.Workload, variant: int, dense_view: bool) -> str:
+    if kind == "dual_gemm":
+        return f"dual_gemm/{w.name}/v{variant}"
+    return f"prepare/{w.name}/{'dense' if dense_view else 'nodense'}"
+
+
+def _pmc_rows(d: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no rocprofv3 counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows, counter: str):
+    """{dispatch id: (kernel name, grid size, counter value summed over instances)}"""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        name, grid, val = r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])
+        if key in out:
+            out[key] = (name, grid, out[key][2] + val)
+        else:
+            out[key] = (name, grid, val)
+    return out
+
+
+def traffic_convert(args, w: si.Workload):
+    """Counter runs -> HBM bytes per launch of the GEMM and of one preparation
+    (all its kernels), each counter scaled by its reading for the copy."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", args.traffic_from[0]), ("WRITE_SIZE", args.traffic_from[1])):
+        disp = _per_dispatch(_pmc_rows(d), counter)
+        copies = [v for v in disp.values() if "copyBuffer" in v[0]]
+        if not copies:
+            raise SystemExit(f"{d}: no calibration copy (run the bench with --calibrate-copy)")
+        # the calibration copy is by far the largest copy of the run
+        factor = COPY_BYTES / (max(c[2] for c in copies) * 1024.0)
+        # one step = the preparation kernels, then the GEMM; other kernels
+        # (weight quantization, copies) break a run of preparation kernels
+        gemm, prep, pending = [], [], []
+        for key in sorted(disp):
+            name, _, val = disp[key]
+            if "dual_gemm" in name:
+                gemm.append(val)
+                if pending:
+                    prep.append(sum(pending))
+                pending = []
+            elif "prep_" in name or "amax" in name:
+                pending.append(val)
+            else:
+                pending = []
+        res[counter] = {"factor": factor, "gemm_kib": float(np.mean(gemm)),
+                        "prep_kib": float(np.mean(prep)), "launches": len(gemm)}
+    f, wr = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    gemm_src, prep_src = kernel_sources(w.fmt)
+    entries = {
+        traffic_key("dual_gemm", w, args.variant, not args.no_dense_view): {
+            "source_hash": source_hash(*gemm_src),
+            "fetch_kib": round(f["gemm_kib"], 1), "write_kib": round(wr["gemm_kib"], 1),
+            "bytes_per_launch": round(f["gemm_kib"] * 1024 * f["factor"] + wr["gemm_kib"] * 1024 * wr["factor"]),
+            "launches": f["launches"]},
+        traffic_key("prepare", w, args.variant, not args.no_dense_view): {
+            "source_hash": source_hash(*prep_src),
+            "fetch_kib": round(f["prep_kib"], 1), "write_kib": round(wr["prep_kib"], 1),
+            "bytes_per_launch": round(f["prep_kib"] * 1024 * f["factor"] + wr["prep_kib"] * 1024 * wr["factor"])},
+    }
+    path = os.path.join(PROFILES, "traffic.json")
+    d = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            d = json.load(fh)
+    d["copy_calibration"] = {"bytes": COPY_BYTES, "fetch_factor": round(f["factor"], 4),
+                             "write_factor": round(wr["factor"], 4)}
+    d.update(entries)
+    with open(path, "w") as fh:
+        json.dump(d, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(entries))
 
 
 def traffic_from_profiles(kernel_key: str, src_hash: str):
@@ -120,7 +227,14 @@ def main():
     ap.add_argument("--no-dense-view", action="store_true",
                     help="prepare writes only the 2:4 backbone; the GEMM expands it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help=f"run one {COPY_BYTES >> 20} MiB device copy first (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="convert two rocprofv3 --pmc runs into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_convert(args, si.WORKLOADS[args.workload])
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the SharQ path here "
@@ -156,6 +270,13 @@ def main():
         sq.prepare_into(xi, g, 1e-5, sp, rs)
         sq.dual_gemm(sp, rs, wq, variant=args.variant, out=y)
 
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -178,30 +299,10 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     step_ms_events = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in range(args.steps)]))
 
-    # per-kernel average launch duration: the same launches back to back on the
-    # same stream, one event pair around each batch
-    def batch_ms(fn, reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(reps):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
-
-    reps = max(20, args.steps)
-
-    def prep_only(i):
-        xi, wq, sp, rs, y = sets[i % nsets]
-        sq.prepare_into(xi, g, 1e-5, sp, rs)
-
-    def gemm_only(i):
-        xi, wq, sp, rs, y = sets[i % nsets]
-        sq.dual_gemm(sp, rs, wq, variant=args.variant, out=y)
-
-    prep_ms = batch_ms(prep_only, reps)
-    gemm_ms = batch_ms(gemm_only, reps)
+    # per-kernel average launch duration, from the event pairs around each
+    # launch inside the timed region
+    prep_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]))
+    gemm_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]))
 
     flops = 3.0 * w.m * w.n * w.k
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -210,10 +311,25 @@ def main():
     prep_gbps = pbytes / (prep_ms * 1e-3) / 1e9
     peak = PEAK_FP4_TFLOPS if w.fmt == sq.MXFP4 else PEAK_BF16_TFLOPS
 
-    gemm_src = source_hash("gemm_mx.hip", "fp4_device.h", "kernels.h")
-    prep_src = source_hash("prep.hip", "fp4_device.h", "kernels.h")
-    gemm_traffic = traffic_from_profiles(f"dual_gemm/{w.name}/v{args.variant}", gemm_src)
-    prep_traffic = traffic_from_profiles(f"prepare/{w.name}", prep_src)
+    gemm_src, prep_src = kernel_sources(w.fmt)
+    dense_view = not args.no_dense_view
+    gemm_traffic = traffic_from_profiles(traffic_key("dual_gemm", w, args.variant, dense_view),
+                                         source_hash(*gemm_src))
+    prep_traffic = traffic_from_profiles(traffic_key("prepare", w, args.variant, dense_view),
+                                         source_hash(*prep_src))
+    gbytes = gemm_bytes(w)
+    if w.m <= 64:
+        # decode: the GEMM streams W once; HBM bandwidth bounds it
+        gemm_gbps = gbytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "dual_gemm", "achieved": round(gemm_gbps, 1),
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": gemm_traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
+                    "algorithmic_bytes_per_launch": gbytes, "algorithmic_flops_per_launch": flops}
+    else:
+        roofline = {"bound": "mfma", "kernel": "dual_gemm", "achieved": round(gemm_tflops, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
+                    "traffic": gemm_traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
+                    "algorithmic_flops_per_launch": flops}
 
     out = {
         "metric": "dual-path FP4 GEMM TFLOP/s + prep GB/s (Llama-8B shapes), % of roofline",
@@ -226,7 +342,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4" if w.fmt == sq.MXFP4 else "nvfp4-emulated",
+        "dtype": "mxfp4" if w.fmt == sq.MXFP4 else "nvfp4 operands, fp16 mfma",
         "data": "synthetic (seeded Llama-3.1-8B-shaped activations with outlier channels, "
                 "N(0,0.02) weights)",
         "config": {"workload": f"{w.name}: X {w.m}x{w.k} bf16, W {w.n}x{w.k}, "
@@ -235,16 +351,13 @@ def main():
                    "m": w.m, "n": w.n, "k": w.k, "gemm_variant": args.variant,
                    "backbone_dense_view": not args.no_dense_view,
                    "buffer_sets": nsets},
-        "roofline": {"bound": "mfma", "kernel": "dual_gemm", "achieved": round(gemm_tflops, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
-                     "traffic": gemm_traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
-                     "algorithmic_flops_per_launch": flops},
+        "roofline": roofline,
         "roofline_prep": {"bound": "hbm", "kernel": "prepare", "achieved": round(prep_gbps, 1),
                           "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                           "frac": round(prep_gbps / PEAK_HBM_GBPS, 4), "traffic": prep_traffic,
                           "avg_launch_us": round(prep_ms * 1e3, 3),
                           "algorithmic_bytes_per_launch": pbytes},
-        "gemm_bytes_per_launch": gemm_bytes(w),
+        "gemm_bytes_per_launch": gbytes,
         "step_ms_events": round(step_ms_events, 5),
     }
     if not args.no_cpu_baseline:
