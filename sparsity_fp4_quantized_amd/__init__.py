@@ -173,7 +173,20 @@ class FP4Tensor:
     tensor_scale: object = None     # float32 [2] (NVFP4)
     layout: int = LAYOUT_ROW_MAJOR
 
+    def __setattr__(self, name, value):
+        # any change of a field drops the cached C view
+        object.__setattr__(self, "_vc", None)
+        object.__setattr__(self, name, value)
+
     def view(self) -> FP4ViewC:
+        """The C view (built once, then cached until a field changes)."""
+        vc = getattr(self, "_vc", None)
+        if vc is None:
+            vc = self._build_view()
+            object.__setattr__(self, "_vc", vc)
+        return vc
+
+    def _build_view(self) -> FP4ViewC:
         v = FP4ViewC()
         L = self.layout
         v.layout = L
@@ -287,9 +300,11 @@ def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AU
         out = torch.empty((m, n), dtype=torch.float32, device=w.codes.device)
     wv_s = w.view()
     if w_dense_scales is not None:
-        wv_d = dataclasses.replace(w, scales=w_dense_scales).view()
+        wv_d = FP4ViewC.from_buffer_copy(wv_s)
+        wv_d.scales = _ptr(w_dense_scales)
+        wv_d.ld_scales = _ld_of(w_dense_scales, w.layout, scale_bps(w.fmt))
     else:
-        wv_d = w.view()
+        wv_d = wv_s
     vs, vr = sp.view(), rs.view()
     _check(lib().sharq_dual_gemm(sp.fmt, ctypes.byref(vs), ctypes.byref(vr), ctypes.byref(wv_s),
                                  ctypes.byref(wv_d), m, n, k, out.data_ptr(), _ld(out),

@@ -477,10 +477,235 @@ void launch_bn(const GemmArgs &a, bool dense, hipStream_t s) {
     dual_gemm_mx_kernel<BN, false><<<grid, block, 0, s>>>(a);
 }
 
+// ---------------------------------------------------------------------------
+// Skinny kernel for m <= 32 (decode): the GEMM streams W once and is bound by
+// HBM bandwidth, not by the MFMAs.  A workgroup of NW wavefronts owns all
+// rows (padded to 32 with zeros) x 32 columns; its wavefronts split K (128-k
+// steps w, w + NW, ...), each loading its fragments straight from global
+// memory (W streams once; A is small and stays in L2), and the NW partial
+// tiles are summed through LDS as a fixed pairwise tree.  Many short
+// wavefronts keep more loads in flight than a few long ones.  Lane (h, li):
+// row / column li, k blocks 2h (first MFMA) and 2h + 1 (second), as in the
+// tiled kernels.
+struct SkFrag {
+  u32x4 fs[2], fr[2], fw[2];
+  int sas, sar, sws, swd;
+};
+
+template <bool kDense>
+__device__ __forceinline__ void sk_load(const GemmArgs &a, int kt, int h, bool row_ok, bool col_ok,
+                                        int64_t r, int64_t c, SkFrag &F) {
+  const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int chunk = 2 * h + s;
+    F.fr[s] = row_ok ? *reinterpret_cast<const u32x4 *>(a.r_codes + arr_off(r, kt, a.ld_rc, a.r_ksm, 64) + chunk * 16) : z;
+    F.fw[s] = col_ok ? *reinterpret_cast<const u32x4 *>(a.w_codes + arr_off(c, kt, a.ld_wc, a.w_ksm, 64) + chunk * 16) : z;
+    if (kDense) {
+      F.fs[s] = row_ok ? *reinterpret_cast<const u32x4 *>(a.s_dense + arr_off(r, kt, a.ld_sd, a.s_ksm, 64) + chunk * 16) : z;
+    } else if (row_ok) {
+      const u32x2 cb = *reinterpret_cast<const u32x2 *>(a.s_codes + arr_off(r, kt, a.ld_sc, a.s_ksm, 32) + chunk * 8);
+      const uint32_t mb = *reinterpret_cast<const uint32_t *>(a.meta + arr_off(r, kt, a.ld_meta, a.s_ksm, 16) + chunk * 4);
+      uint32_t d[4];
+      expand8(cb.x, cb.y, mb, d);
+      F.fs[s] = u32x4{d[0], d[1], d[2], d[3]};
+    } else {
+      F.fs[s] = z;
+    }
+  }
+  F.sas = row_ok ? (int)(scale_word(a.s_scales, a.ld_ss, a.s_ksm, r, kt) >> (16 * h)) : 0;
+  F.sar = row_ok ? (int)(scale_word(a.r_scales, a.ld_rs, a.r_ksm, r, kt) >> (16 * h)) : 0;
+  F.sws = col_ok ? (int)(scale_word(a.ws_scales, a.ld_wss, a.w_ksm, c, kt) >> (16 * h)) : 0;
+  F.swd = col_ok ? (int)(scale_word(a.wd_scales, a.ld_wds, a.w_ksm, c, kt) >> (16 * h)) : 0;
+}
+
+__device__ __forceinline__ void sk_mfma(const SkFrag &F, v16f &acc) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(F.fs[0]), as_operand(F.fw[0]), acc, 4, 4, 0, F.sas, 0, F.sws);
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(F.fr[0]), as_operand(F.fw[0]), acc, 4, 4, 0, F.sar, 0, F.swd);
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(F.fs[1]), as_operand(F.fw[1]), acc, 4, 4, 1, F.sas, 1, F.sws);
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(F.fr[1]), as_operand(F.fw[1]), acc, 4, 4, 1, F.sar, 1, F.swd);
+}
+
+template <bool kDense, int U, int NW>
+__global__ __launch_bounds__(64 * NW) void dual_gemm_skinny_kernel(GemmArgs a) {
+  __shared__ float part[NW][64][17];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const bool row_ok = li < a.m;
+  const int64_t col = n0 + li;
+  const bool col_ok = col < a.n;
+  const int64_t r = row_ok ? li : 0, c = col_ok ? col : 0;
+  const int ksteps = (int)(a.k / BK);
+
+  v16f acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+
+  // wavefront w takes 128-k steps w, w + NW, ...; U steps' loads in flight
+  // before their MFMAs
+  int kt = wave;
+  for (; kt + NW * (U - 1) < ksteps; kt += NW * U) {
+    SkFrag F[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) sk_load<kDense>(a, kt + NW * u, h, row_ok, col_ok, r, c, F[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) sk_mfma(F[u], acc);
+  }
+  for (; kt < ksteps; kt += NW) {
+    SkFrag F;
+    sk_load<kDense>(a, kt, h, row_ok, col_ok, r, c, F);
+    sk_mfma(F, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part[wave][lane][i] = acc[i];
+  __syncthreads();
+  // thread t sums (lane t % 64, accumulator slots (t / 64) * 16 / NW ..) over
+  // the wavefronts as a fixed pairwise tree
+  constexpr int SLOTS = 16 / NW;
+  static_assert(SLOTS >= 1 && 16 % NW == 0, "NW divides 16");
+  const int l = tid & 63, q = tid >> 6;
+  const int64_t ocol = n0 + (l & 31);
+  if (ocol < a.n) {
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int i = SLOTS * q + j;
+      const int row = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
+      float v[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v[w] = part[w][l][i];
+#pragma unroll
+      for (int width = NW / 2; width >= 1; width >>= 1)
+#pragma unroll
+        for (int w = 0; w < width; ++w) v[w] = v[2 * w] + v[2 * w + 1];
+      if (row < a.m) a.y[row * a.ld_y + ocol] = v[0];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel for m <= 32: the GEMM streams W once and is bound by HBM
+// bandwidth.  A workgroup of four wavefronts owns all rows (padded to 32 with
+// zeros) x 128 columns, one 32 x 32 MFMA tile per wavefront, over the whole
+// K.  W, both A operands and the four scale arrays go global -> LDS with
+// buffer_load ... lds through a ring of STAGES 128-k steps (STAGES - 1 in
+// flight), which keeps far more bytes in flight than loads into registers.
+// Lane (h, li): row / column li, k blocks 2h (first MFMA) and 2h + 1.
+template <int STAGES>
+struct KStage {
+  u32x4 w[128 * 4];            // 128 W rows x 64 bytes (chunk-swizzled)
+  u32x4 as[32 * 4], ar[32 * 4];
+  uint32_t sws[128], swd[128], sas[64], sar[64];   // A scale rows 32..63 stay unused
+};
+
+template <int STAGES>
+__global__ __launch_bounds__(256) void dual_gemm_decode_kernel(GemmArgs a) {
+  __shared__ KStage<STAGES> st[STAGES];
+  using St = KStage<STAGES>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int64_t n0 = (int64_t)blockIdx.x * 128;
+  const int64_t steps = a.k / BK;
+  const int ksteps = (int)steps;
+
+  // streams and this wavefront's loads: W chunk groups 2w, 2w + 1 (16 rows
+  // each); wave 0 the backbone rows and scales, wave 1 the residual's, waves
+  // 2 and 3 the two W scale views
+  const OpStream sw = op_stream(a.w_codes, a.ld_wc, a.w_ksm, a.n, n0, steps, 64);
+  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t vw0 = (uint32_t)(16 * (2 * wave) + lrow) * sw.row_stride + lchunk * 16;
+  const uint32_t vw1 = (uint32_t)(16 * (2 * wave + 1) + lrow) * sw.row_stride + lchunk * 16;
+  OpStream sa, ss;
+  uint32_t osa = 0, oss = 0;
+  if (wave == 0) {
+    sa = op_stream(a.s_dense, a.ld_sd, a.s_ksm, a.m, 0, steps, 64);
+    ss = op_stream(a.s_scales, a.ld_ss, a.s_ksm, a.m, 0, steps, 4);
+    osa = offsetof(St, as); oss = offsetof(St, sas);
+  } else if (wave == 1) {
+    sa = op_stream(a.r_codes, a.ld_rc, a.r_ksm, a.m, 0, steps, 64);
+    ss = op_stream(a.r_scales, a.ld_rs, a.r_ksm, a.m, 0, steps, 4);
+    osa = offsetof(St, ar); oss = offsetof(St, sar);
+  } else {
+    ss = wave == 2 ? op_stream(a.ws_scales, a.ld_wss, a.w_ksm, a.n, n0, steps, 4)
+                   : op_stream(a.wd_scales, a.ld_wds, a.w_ksm, a.n, n0, steps, 4);
+    oss = wave == 2 ? offsetof(St, sws) : offsetof(St, swd);
+  }
+  const uint32_t va0 = (uint32_t)lrow * sa.row_stride + lchunk * 16;
+  const uint32_t va1 = (uint32_t)(16 + lrow) * sa.row_stride + lchunk * 16;
+  const uint32_t vs0 = (uint32_t)lane * ss.row_stride;
+  const uint32_t vs1 = (uint32_t)(64 + lane) * ss.row_stride;
+
+  auto issue = [&](int kt, const St &S) {
+    const uint32_t base = lds_addr(&S), t = (uint32_t)kt;
+    b2l16(sw.rsrc, vw0, t * sw.step, base + offsetof(St, w) + (2 * wave) * 1024);
+    b2l16(sw.rsrc, vw1, t * sw.step, base + offsetof(St, w) + (2 * wave + 1) * 1024);
+    if (wave < 2) {
+      b2l16(sa.rsrc, va0, t * sa.step, base + osa);
+      b2l16(sa.rsrc, va1, t * sa.step, base + osa + 1024);
+      b2l4(ss.rsrc, vs0, t * ss.step, base + oss);
+    } else {
+      b2l4(ss.rsrc, vs0, t * ss.step, base + oss);
+      b2l4(ss.rsrc, vs1, t * ss.step, base + oss + 256);
+    }
+  };
+
+  v16f acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < ksteps) issue(p, st[p]);
+
+  const int wc = 32 * wave + li;     // the lane's W row within the tile
+  int cur = 0;
+  for (int kt = 0; kt < ksteps; ++kt) {
+    // stages kt + 1 .. kt + STAGES - 2 may stay in flight (4 or 5 loads each)
+    if (kt + STAGES - 2 < ksteps) wait_vmcnt<4 * (STAGES - 2)>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + STAGES - 1 < ksteps) issue(kt + STAGES - 1, st[cur == 0 ? STAGES - 1 : cur - 1]);
+    const St &S = st[cur];
+    const int sas = (int)(S.sas[li] >> (16 * h)), sar = (int)(S.sar[li] >> (16 * h));
+    const int sws = (int)(S.sws[wc] >> (16 * h)), swd = (int)(S.swd[wc] >> (16 * h));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int c = 2 * h + s;
+      const v8i fs = as_operand(S.as[lds_slot(li, c)]);
+      const v8i fr = as_operand(S.ar[lds_slot(li, c)]);
+      const v8i fw = as_operand(S.w[lds_slot(wc, c)]);
+      if (s == 0) {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fs, fw, acc, 4, 4, 0, sas, 0, sws);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr, fw, acc, 4, 4, 0, sar, 0, swd);
+      } else {
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fs, fw, acc, 4, 4, 1, sas, 1, sws);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr, fw, acc, 4, 4, 1, sar, 1, swd);
+      }
+    }
+    cur = cur == STAGES - 1 ? 0 : cur + 1;
+  }
+  const int64_t col = n0 + wc;
+  if (col < a.n) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < a.m) a.y[row * a.ld_y + col] = acc[r];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s) {
-  if (dense_expanded) {
+  if (a.m <= 32 && dense_expanded) {
+    // decode: W streams through LDS, four 128-k steps in flight
+    dual_gemm_decode_kernel<4><<<dim3((unsigned)((a.n + 127) / 128)), dim3(256), 0, s>>>(a);
+  } else if (a.m <= 32) {
+    // decode with the 2:4 backbone expanded in registers: split-K over four
+    // wavefronts, fragments loaded straight from global memory
+    dual_gemm_skinny_kernel<false, 1, 4><<<dim3((unsigned)((a.n + 31) / 32)), dim3(256), 0, s>>>(a);
+  } else if (dense_expanded) {
     // 128-row tiles, two LDS stages: 128 x 192 (two workgroups a CU) when
     // that still gives every CU two tiles and K is short; else 128 x 128
     // (three a CU), whose smaller K step keeps more loads in flight per CU

@@ -196,7 +196,8 @@ def _gemm_case(m, n, k, seed, fmt=sq.MXFP4, norm=True):
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 256), (37, 75, 256), (130, 200, 384), (1, 1, 128),
                                    (257, 129, 1024), (64, 512, 4096), (300, 1000, 640),
-                                   (129, 193, 128), (512, 192, 256)])
+                                   (129, 193, 128), (512, 192, 256), (32, 300, 640), (7, 96, 1152),
+                                   (33, 64, 384)])
 def test_dual_gemm_mx_vs_oracle(m, n, k):
     x, w, g, p, q = _gemm_case(m, n, k, seed=m + 7 * n + k)
     ref = oracle.dual_gemm(sq.MXFP4, p, q)
