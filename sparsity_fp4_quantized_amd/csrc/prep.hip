@@ -254,17 +254,40 @@ __device__ __forceinline__ void quantize_block_mx(const uint32_t xw[16], const f
 
 // ---------------------------------------------------------------- NVFP4 block
 
+// fl32(v / S) from y = fl32(1 / S): q0 = fl32(v y) is within an ulp of v / S,
+// r = fma(-q0, S, v) is then exact, and fma(r, y, q0) is the correctly rounded
+// quotient (Markstein's correction of a faithful quotient with a correctly
+// rounded reciprocal).  Valid while neither y nor the quotient leaves the
+// normal range: S in [2^-100, 2^100] and |v / S| < 8 here.
+__device__ __forceinline__ float div_rn(float v, float S, float y) {
+  const float q0 = v * y;
+  const float r = __builtin_fmaf(-q0, S, v);
+  return __builtin_fmaf(r, y, q0);
+}
+
 // E2M1 codes of fl32(v / S) for 32 values (two 16-blocks with scales S[0], S[1]),
 // signed zeros when S == 0; packed two per byte.
 __device__ __forceinline__ void nv_codes(const float v[32], const float S[2], uint32_t out[4]) {
   uint32_t w[4] = {0u, 0u, 0u, 0u};
+  float y[2];
+  bool fast[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    fast[b] = S[b] >= 0x1p-100f && S[b] <= 0x1p100f;
+    y[b] = 1.0f / S[b];
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float s = S[i >> 3];
     float t0 = v[2 * i], t1 = v[2 * i + 1];
     // S == 0: keep only the sign (the conversion of +-0 keeps it)
-    t0 = s == 0.0f ? __uint_as_float(__float_as_uint(t0) & 0x80000000u) : t0 / s;
-    t1 = s == 0.0f ? __uint_as_float(__float_as_uint(t1) & 0x80000000u) : t1 / s;
+    if (fast[i >> 3]) {
+      t0 = div_rn(t0, s, y[i >> 3]);
+      t1 = div_rn(t1, s, y[i >> 3]);
+    } else {
+      t0 = s == 0.0f ? __uint_as_float(__float_as_uint(t0) & 0x80000000u) : t0 / s;
+      t1 = s == 0.0f ? __uint_as_float(__float_as_uint(t1) & 0x80000000u) : t1 / s;
+    }
     uint32_t &x = w[i >> 2];
     switch (i & 3) {
       case 0: x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, t0, t1, 1.0f, 0); break;
@@ -502,7 +525,9 @@ __device__ __forceinline__ void block_amax_atomic(uint32_t am, float *ts) {
   if (threadIdx.x == 0) {
     uint32_t m = 0;
     for (int i = 0; i < nw; ++i) m = max(m, wmax[i]);
-    if (m) atomicMax(reinterpret_cast<unsigned int *>(ts + 1), m);
+    // the value only grows: skip the atomic when memory already holds >= m
+    unsigned int *p = reinterpret_cast<unsigned int *>(ts + 1);
+    if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
   }
 }
 
