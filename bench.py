@@ -184,6 +184,48 @@ def traffic_from_profiles(kernel_key: str, src_hash: str):
     return e.get("bytes_per_launch")
 
 
+def yardsticks(w: si.Workload, torch, dev) -> dict:
+    """What plain work of the same size takes on this GPU (context, not targets):
+    a device copy that reads 2 B and writes 1 B per element of X (the
+    preparation's traffic), and the vendor MXFP4 GEMM (hipBLASLt through
+    torch._scaled_mm) on the dual GEMM folded into one GEMM with K' = 2K.
+    Each is the mean of 20 back-to-back launches between two events."""
+    out = {}
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    n_el = w.m * w.k
+    src = torch.empty(2 * n_el, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(n_el, dtype=torch.uint8, device=dev)
+    # reads both halves of src (2 B / element), writes dst (1 B / element)
+    us = timed(lambda: torch.maximum(src[:n_el], src[n_el:], out=dst))
+    out["copy_like_prep"] = {"us": round(us, 3), "bytes": 3 * n_el,
+                             "GB/s": round(3 * n_el / (us * 1e-6) / 1e9, 1)}
+    del src, dst
+    if w.fmt == si.MXFP4 and w.m > 64:
+        try:
+            K2 = 2 * w.k
+            a = torch.randint(0, 255, (w.m, K2 // 2), dtype=torch.uint8, device=dev).view(torch.float4_e2m1fn_x2)
+            b = torch.randint(0, 255, (w.n, K2 // 2), dtype=torch.uint8, device=dev).view(torch.float4_e2m1fn_x2)
+            sa = torch.full((w.m, K2 // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+            sb = torch.full((w.n, K2 // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+            us = timed(lambda: torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.float32))
+            out["vendor_mxfp4_gemm_folded"] = {"us": round(us, 3), "m": w.m, "n": w.n, "k": K2,
+                                               "dense_TFLOP/s": round(2.0 * w.m * w.n * K2 / (us * 1e-6) / 1e12, 1)}
+        except Exception as e:  # not every torch build routes MX formats to hipBLASLt
+            out["vendor_mxfp4_gemm_folded"] = {"error": str(e)[:200]}
+    return out
+
+
 def cpu_baseline(w: si.Workload, x, W, g, seconds: float = 12.0) -> dict:
     """The CPU oracle (single thread, as committed) on a bounded sample of the
     workload; reported in the same unit as `value` by projecting the sample's
@@ -229,6 +271,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help=f"run one {COPY_BYTES >> 20} MiB device copy first (counter calibration)")
+    ap.add_argument("--no-yardsticks", action="store_true",
+                    help="skip the plain-copy and vendor FP4 GEMM reference timings")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="convert two rocprofv3 --pmc runs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -329,7 +373,10 @@ def main():
         roofline = {"bound": "mfma", "kernel": "dual_gemm", "achieved": round(gemm_tflops, 2),
                     "peak": peak, "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
                     "traffic": gemm_traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
-                    "algorithmic_flops_per_launch": flops}
+                    "algorithmic_flops_per_launch": flops,
+                    "executed_TFLOP/s": round((1.0 if (w.fmt == sq.NVFP4 and args.variant == 3) else 4.0 / 3.0)
+                                              * gemm_tflops, 2),
+                    "dense_equivalent_TFLOP/s": round(2.0 / 3.0 * gemm_tflops, 2)}
 
     out = {
         "metric": "dual-path FP4 GEMM TFLOP/s + prep GB/s (Llama-8B shapes), % of roofline",
@@ -360,6 +407,8 @@ def main():
         "gemm_bytes_per_launch": gbytes,
         "step_ms_events": round(step_ms_events, 5),
     }
+    if not args.no_yardsticks:
+        out["yardsticks"] = yardsticks(w, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x_np, W_np, g_np)
     print(json.dumps(out), flush=True)

@@ -97,6 +97,21 @@ __device__ __forceinline__ float swz_xor(float v) {
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (XOR << 10)));
 }
 
+// Sum over each aligned group of L lanes (L a power of two <= 64), as a
+// perfect binary tree of adjacent pairs; every lane of a group gets the sum.
+template <int L>
+__device__ __forceinline__ float lane_tree_sum(float v) {
+  if (L >= 2) v = v + swz_xor<1>(v);
+  if (L >= 4) v = v + swz_xor<2>(v);
+  if (L >= 8) v = v + swz_xor<4>(v);
+  if (L >= 16) v = v + swz_xor<8>(v);
+  if (L >= 32) v = v + swz_xor<16>(v);
+  if (L >= 64)
+    v = v + __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) & 63) << 2,
+                                                        __float_as_int(v)));
+  return v;
+}
+
 __device__ __forceinline__ float wave_tree_sum(float v) {
   v = v + swz_xor<1>(v);
   v = v + swz_xor<2>(v);
@@ -418,15 +433,17 @@ __device__ __forceinline__ float nv_tensor_scale(const float *ts) {
 // Row reduction: `s` is the lane's block sum of squares (0 for lanes past the
 // row end); every thread of the workgroup calls this.  Returns
 // r = 1 / sqrt(ss / k + eps) of the lane's row.
+// `buf` alternates between calls of one loop, so that a wavefront writing the
+// next row's partial sums never overwrites values another is still reading.
 template <int WPR>
-__device__ __forceinline__ float row_rms(float s, int riw, int wir, int64_t k, float eps) {
-  __shared__ float part[4 * kMaxWavesPerRow];
+__device__ __forceinline__ float row_rms(float s, int riw, int wir, int64_t k, float eps, int buf = 0) {
+  __shared__ float part[2][4 * kMaxWavesPerRow];
   s = wave_tree_sum(s);
-  if ((threadIdx.x & 63) == 0) part[riw * kMaxWavesPerRow + wir] = s;
+  if ((threadIdx.x & 63) == 0) part[buf][riw * kMaxWavesPerRow + wir] = s;
   __syncthreads();
   float c[kMaxWavesPerRow];
 #pragma unroll
-  for (int i = 0; i < kMaxWavesPerRow; ++i) c[i] = i < WPR ? part[riw * kMaxWavesPerRow + i] : 0.0f;
+  for (int i = 0; i < kMaxWavesPerRow; ++i) c[i] = i < WPR ? part[buf][riw * kMaxWavesPerRow + i] : 0.0f;
 #pragma unroll
   for (int w = kMaxWavesPerRow / 2; w >= 1; w >>= 1) {
 #pragma unroll
@@ -439,63 +456,91 @@ __device__ __forceinline__ float row_rms(float s, int riw, int wir, int64_t k, f
 }
 
 // x_n = bf16((x * r) * gamma): returns the bf16 pairs and overwrites xf with x_n.
-__device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const uint16_t *g,
+__device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const float gf[32],
                                             float r) {
-  uint32_t gw[16];
-  load32_cached(g, gw);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float lo = (xf[2 * i] * r) * bf16_lo(gw[i]);
-    float hi = (xf[2 * i + 1] * r) * bf16_hi(gw[i]);
+    float lo = (xf[2 * i] * r) * gf[2 * i];
+    float hi = (xf[2 * i + 1] * r) * gf[2 * i + 1];
     xw[i] = pack_bf16x2(lo, hi);
     xf[2 * i] = bf16_lo(xw[i]);
     xf[2 * i + 1] = bf16_hi(xw[i]);
   }
 }
 
+__device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const uint16_t *g,
+                                            float r) {
+  uint32_t gw[16];
+  float gf[32];
+  load32_cached(g, gw);
+  unpack32(gw, gf);
+  normalize32(xf, xw, gf, r);
+}
+
 // ---------------------------------------------------------------- kernels
 
-// Workgroup = RPW rows x WPR waves; wave (riw, wir), lane -> block wir * 64 + lane.
-// Lanes past the row end (or past the last row) load a valid block of X and
-// contribute +0 to the sum of squares; they store nothing.
-template <int FMT, int WPR>
-__global__ __launch_bounds__(512) void prep_norm_kernel(PrepArgs a) {
-  constexpr int RPW = WPR <= 4 ? 4 / WPR : 1;
+// Workgroup = R rows x W wavefronts: lane l of wavefront w takes row q = l / L
+// (L = 64 / R lanes per row) and block w * L + l % L, so a wavefront stores R
+// consecutive rows of each 128-k step next to each other in the k-step-major
+// layout (R = 1 keeps a row's blocks contiguous for the row-major layout).
+// The row's sum of squares is the oracle's perfect binary tree: the lane's 32
+// values, then adjacent lanes of the row (butterfly over L lanes), then the W
+// wavefronts in LDS (padded to a power of two with zeros).  Lanes past the row
+// end (or past the last row) load a valid block of X and contribute +0; they
+// store nothing.
+template <int FMT, int R, int W>
+__global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
+  constexpr int L = 64 / R;
+  __shared__ float part[R][W];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int riw = wave / WPR, wir = wave - riw * WPR;
-  const int64_t row = (int64_t)blockIdx.x * RPW + riw;
+  const int q = lane / L;
+  const int64_t row = (int64_t)blockIdx.x * R + q;
   const int64_t nblk = a.k / 32;
-  const int64_t b = (int64_t)wir * 64 + lane;
+  const int64_t b = (int64_t)wave * L + lane % L;
   const bool has = row < a.m && b < nblk;
   const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
   uint32_t xw[16];
   float xf[32];
   load32(a.x + lrow * a.ld_x + 32 * lb, xw);
   unpack32(xw, xf);
-  float s = block_sumsq(xf);
-  float r = row_rms<WPR>(has ? s : 0.0f, riw, wir, a.k, a.eps);
+  float s = lane_tree_sum<L>(has ? block_sumsq(xf) : 0.0f);
+  if (lane % L == 0) part[q][wave] = s;
+  __syncthreads();
+  float c[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) c[i] = part[q][i];
+#pragma unroll
+  for (int w = W / 2; w >= 1; w >>= 1) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) c[i] = c[2 * i] + c[2 * i + 1];
+  }
+  const float r = 1.0f / __builtin_sqrtf(c[0] / (float)a.k + a.eps);
   if (!has) return;
   normalize32(xf, xw, a.gamma + 32 * b, r);
   BlockOut o;
   if (FMT == 0) {
     quantize_block_mx(xw, xf, o);
   } else {
-    float s_t = nv_tensor_scale(a.tensor_scale);
+    const float s_t = nv_tensor_scale(a.tensor_scale);
     if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
     quantize_block_nv(xf, s_t, o);
   }
   store_block<FMT>(a, row, b, o);
 }
 
-// No normalization: blocks are independent.  Each wavefront takes 64
-// consecutive blocks of one row (chunk c of row r, wave-uniform).
-template <int FMT>
+// No normalization: blocks are independent.  A wavefront takes R rows x
+// 64 / R consecutive blocks: R = 16 (one 128-k step of 16 consecutive rows)
+// makes every store of the k-step-major layout 16 rows contiguous; R = 1 (64
+// blocks of one row) does the same for the row-major layout.
+template <int FMT, int R>
 __global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chunks) {
+  constexpr int L = 64 / R;
   const uint32_t w = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t row32 = w / chunks;
-  const int64_t row = row32;
-  const int64_t b = (int64_t)(w - row32 * chunks) * 64 + (threadIdx.x & 63);
+  const int lane = threadIdx.x & 63;
+  const uint32_t rg = w / chunks;
+  const int64_t row = (int64_t)rg * R + lane / L;
+  const int64_t b = (int64_t)(w - rg * chunks) * L + lane % L;
   if (row >= a.m || b >= a.k / 32) return;
   uint32_t xw[16];
   float xf[32];
@@ -580,36 +625,64 @@ __global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *x, int64
 
 __global__ void zero_amax_kernel(float *ts) { ts[1] = 0.0f; }
 
-template <int FMT, int WPR>
+template <int FMT, int R, int W>
 void launch_norm(const PrepArgs &a, hipStream_t s) {
+  prep_norm_kernel<FMT, R, W><<<dim3((unsigned)((a.m + R - 1) / R)), dim3(64 * W), 0, s>>>(a);
+}
+
+template <int WPR>
+void launch_amax_norm(const PrepArgs &a, hipStream_t s) {
   constexpr int RPW = WPR <= 4 ? 4 / WPR : 1;
-  const dim3 grid((unsigned)((a.m + RPW - 1) / RPW)), block(64 * WPR * RPW);
-  if (FMT == 1) amax_norm_kernel<WPR><<<dim3(min(grid.x, kAmaxGrid)), block, 0, s>>>(a);
-  prep_norm_kernel<FMT, WPR><<<grid, block, 0, s>>>(a);
+  const unsigned groups = (unsigned)((a.m + RPW - 1) / RPW);
+  amax_norm_kernel<WPR><<<dim3(min(groups, kAmaxGrid)), dim3(64 * WPR * RPW), 0, s>>>(a);
+}
+
+// W = nblk / (64 / R) wavefronts per row group, rounded up to a power of two <= 8.
+template <int FMT, int R>
+void launch_norm_w(const PrepArgs &a, int64_t nblk, hipStream_t s) {
+  const int64_t w = (nblk + 64 / R - 1) / (64 / R);
+  if (w <= 1) launch_norm<FMT, R, 1>(a, s);
+  else if (w <= 2) launch_norm<FMT, R, 2>(a, s);
+  else if (w <= 4) launch_norm<FMT, R, 4>(a, s);
+  else launch_norm<FMT, R, 8>(a, s);
 }
 
 template <int FMT>
 hipError_t launch_prepare(const PrepArgs &a, hipStream_t s) {
-  const int64_t total = a.m * (a.k / 32);
-  const dim3 flat_grid((unsigned)((total + 255) / 256));
+  const int64_t nblk = a.k / 32;
+  const bool ksm = a.s_ksm != 0;
   if (FMT == 1) zero_amax_kernel<<<1, 1, 0, s>>>(a.tensor_scale);
   if (a.gamma) {
-    switch ((a.k / 32 + 63) / 64) {   // wavefronts per row
-      case 1: launch_norm<FMT, 1>(a, s); break;
-      case 2: launch_norm<FMT, 2>(a, s); break;
-      case 3: launch_norm<FMT, 3>(a, s); break;
-      case 4: launch_norm<FMT, 4>(a, s); break;
-      case 5: launch_norm<FMT, 5>(a, s); break;
-      case 6: launch_norm<FMT, 6>(a, s); break;
-      case 7: launch_norm<FMT, 7>(a, s); break;
-      default: launch_norm<FMT, 8>(a, s); break;
+    if (FMT == 1) {
+      switch ((nblk + 63) / 64) {   // wavefronts per row of the pre-pass
+        case 1: launch_amax_norm<1>(a, s); break;
+        case 2: launch_amax_norm<2>(a, s); break;
+        case 3: launch_amax_norm<3>(a, s); break;
+        case 4: launch_amax_norm<4>(a, s); break;
+        case 5: launch_amax_norm<5>(a, s); break;
+        case 6: launch_amax_norm<6>(a, s); break;
+        case 7: launch_amax_norm<7>(a, s); break;
+        default: launch_amax_norm<8>(a, s); break;
+      }
     }
+    // one row per wavefront group: measured faster than R = 2 or 4 rows for
+    // both layouts (smaller workgroups keep more wavefronts resident)
+    launch_norm_w<FMT, 1>(a, nblk, s);
   } else {
-    if (FMT == 1)
+    if (FMT == 1) {
+      const int64_t total = a.m * nblk;
+      const dim3 flat_grid((unsigned)((total + 255) / 256));
       amax_flat_kernel<<<dim3(min(flat_grid.x, kAmaxGrid)), 256, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.tensor_scale);
-    const uint32_t chunks = (uint32_t)((a.k / 32 + 63) / 64);
-    const uint64_t waves = (uint64_t)a.m * chunks;
-    prep_flat_kernel<FMT><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a, chunks);
+    }
+    if (ksm) {
+      const uint32_t chunks = (uint32_t)((nblk + 3) / 4);
+      const uint64_t waves = (uint64_t)((a.m + 15) / 16) * chunks;
+      prep_flat_kernel<FMT, 16><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a, chunks);
+    } else {
+      const uint32_t chunks = (uint32_t)((nblk + 63) / 64);
+      const uint64_t waves = (uint64_t)a.m * chunks;
+      prep_flat_kernel<FMT, 1><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a, chunks);
+    }
   }
   return hipGetLastError();
 }
