@@ -15,8 +15,10 @@ TFLOP/s (3*M*N*K: the backbone GEMM multiplies two of every four k, the
 residual GEMM all of them).  `roofline` describes the dominant kernel (the
 dual GEMM) against the dense MFMA peak of its operand type (HBM bandwidth
 for the decode shape, whose GEMM streams the weight once); `roofline_prep`
-the preparation kernel(s) against HBM bandwidth.  Kernel durations are the
-means of HIP event pairs around each launch inside the timed region.
+the preparation kernel(s) against HBM bandwidth.  The timed region holds the
+steps only, with one HIP event pair around it; each kernel's average launch
+duration comes from the same launches of that kernel run back to back over
+the same buffer sets, one event pair around the batch.
 `traffic` is the HBM bytes per launch measured with rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, scaled by what the same counters read for a
 device copy of known size), read from profiles/traffic.json when it was
@@ -218,7 +220,7 @@ def yardsticks(w: si.Workload, torch, dev) -> dict:
             b = torch.randint(0, 255, (w.n, K2 // 2), dtype=torch.uint8, device=dev).view(torch.float4_e2m1fn_x2)
             sa = torch.full((w.m, K2 // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
             sb = torch.full((w.n, K2 // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
-            us = timed(lambda: torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.float32))
+            us = timed(lambda: torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.bfloat16))
             out["vendor_mxfp4_gemm_folded"] = {"us": round(us, 3), "m": w.m, "n": w.n, "k": K2,
                                                "dense_TFLOP/s": round(2.0 * w.m * w.n * K2 / (us * 1e-6) / 1e12, 1)}
         except Exception as e:  # not every torch build routes MX formats to hipBLASLt
@@ -325,28 +327,45 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, synchronized on both sides
+    # timed region: exactly `steps` steps, synchronized on both sides, with one
+    # event pair around it (events between kernels would add ~4 us each)
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_start.record(stream)
     for i in range(args.steps):
-        xi, wq, sp, rs, y = sets[i % nsets]
-        ev[i][0].record(stream)
-        sq.prepare_into(xi, g, 1e-5, sp, rs)
-        ev[i][1].record(stream)
-        sq.dual_gemm(sp, rs, wq, variant=args.variant, out=y)
-        ev[i][2].record(stream)
+        step(i)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     ms_per_step = wall * 1e3 / args.steps
-    step_ms_events = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in range(args.steps)]))
+    step_ms_events = e_start.elapsed_time(e_end) / args.steps
 
-    # per-kernel average launch duration, from the event pairs around each
-    # launch inside the timed region
-    prep_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]))
-    gemm_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]))
+    # per-kernel average launch duration: the timed region's launches of one
+    # kernel, back to back on the same stream over the same buffer sets, one
+    # event pair around the batch
+    def batch_ms(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def prep_only(i):
+        xi, wq, sp, rs, y = sets[i % nsets]
+        sq.prepare_into(xi, g, 1e-5, sp, rs)
+
+    def gemm_only(i):
+        xi, wq, sp, rs, y = sets[i % nsets]
+        sq.dual_gemm(sp, rs, wq, variant=args.variant, out=y)
+
+    prep_ms = batch_ms(prep_only, args.steps)
+    gemm_ms = batch_ms(gemm_only, args.steps)
 
     flops = 3.0 * w.m * w.n * w.k
     value = flops / (ms_per_step * 1e-3) / 1e12
