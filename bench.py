@@ -129,17 +129,19 @@ def traffic_convert(args, w: si.Workload):
             raise SystemExit(f"{d}: no calibration copy (run the bench with --calibrate-copy)")
         # the calibration copy is by far the largest copy of the run
         factor = COPY_BYTES / (max(c[2] for c in copies) * 1024.0)
-        # one step = the preparation kernels, then the GEMM; other kernels
-        # (weight quantization, copies) break a run of preparation kernels
+        # one preparation = its prep_* kernel plus the NVFP4 amax kernels
+        # launched right before it; any other kernel (the weight
+        # quantization's amax pass included) drops the pending amax kernels
         gemm, prep, pending = [], [], []
         for key in sorted(disp):
             name, _, val = disp[key]
             if "dual_gemm" in name:
                 gemm.append(val)
-                if pending:
-                    prep.append(sum(pending))
                 pending = []
-            elif "prep_" in name or "amax" in name:
+            elif "prep_" in name:
+                prep.append(sum(pending) + val)
+                pending = []
+            elif "amax" in name:
                 pending.append(val)
             else:
                 pending = []
