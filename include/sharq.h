@@ -59,7 +59,7 @@ typedef enum {
 } sharq_format;
 
 typedef enum {
-    SHARQ_GEMM_AUTO = 0,           /* the default variant for the format */
+    SHARQ_GEMM_AUTO = 0,           /* the format's default (see sharq_dual_gemm) */
     SHARQ_GEMM_DECOMPRESS = 1,     /* backbone expanded from its 2:4 form to dense FP4 while staged in LDS */
     SHARQ_GEMM_DENSE_EXPANDED = 2, /* backbone read from the dense view written by sharq_prepare */
     SHARQ_GEMM_SPARSE_MFMA = 3     /* backbone on the structured-sparse MFMA (see sharq_dual_gemm) */
@@ -206,8 +206,9 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
  * same layout.
  * Variants: DECOMPRESS reads the 2:4 backbone (codes + meta) and expands it
  * to dense codes inside the GEMM; DENSE_EXPANDED reads sparse->dense_codes
- * instead; AUTO is DENSE_EXPANDED when sparse->dense_codes is non-NULL, else
- * DECOMPRESS.  SPARSE_MFMA (NVFP4 only) feeds the 2:4 backbone codes and
+ * instead; AUTO is, for MXFP4, DENSE_EXPANDED when sparse->dense_codes is
+ * non-NULL, else DECOMPRESS, and for NVFP4 SPARSE_MFMA.  SPARSE_MFMA (NVFP4
+ * only) feeds the 2:4 backbone codes and
  * indices to the structured-sparse fp16 MFMA; gfx950 has no
  * structured-sparse MFMA for FP4 operands, so it returns
  * SHARQ_ERR_UNSUPPORTED for MXFP4.  The 2:4 indices must be as

@@ -1,19 +1,23 @@
-"""Build the HIP library libsharq.so (gfx950) in-tree with hipcc."""
+"""Build the HIP library libsharq.so (gfx950) in-tree with hipcc.
+
+Each source compiles to its own object (in parallel, with its own extra
+flags), then one hipcc link writes libsharq.so."""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsharq.so")
-SOURCES = ["sharq_abi.cpp", "prep.hip", "gemm_mx.hip", "gemm_nv.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # bit-exact quantization: no contraction into FMA, IEEE fp32 division and
     # square root, fp32 denormals kept
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -23,17 +27,35 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
+# source -> extra flags.  The NVFP4 GEMM keeps its MFMA accumulators in VGPRs:
+# its 2:4 MFMA (v_smfmac) accumulates in VGPRs only, so accumulators in AGPRs
+# were copied between the two register files around every sparse MFMA, and
+# the dense kernels fit two wavefronts per SIMD only without AGPRs.
+SOURCES = {
+    "sharq_abi.cpp": [],
+    "prep.hip": [],
+    "gemm_mx.hip": [],
+    "gemm_nv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
-def sources():
-    return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
 
-
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *sources()]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    jobs = []
+    for src, extra in SOURCES.items():
+        obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+        jobs.append(([HIPCC, *FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], obj))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *[obj for _, obj in jobs]], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -423,9 +423,10 @@ void launch_nv(const GemmArgs &a, bool shared, hipStream_t s) {
 
 template <int BB>
 void launch_bb(const GemmArgs &a, bool shared, hipStream_t s) {
-  // 128 x 256 tiles (two workgroups a CU) when there are enough of them
+  // 128 x 256 tiles when there are enough of them; the 2:4 MFMA variant
+  // holds more operands and runs fastest on 128 x 128 tiles (three stages)
   const int64_t mt = (a.m + 127) / 128;
-  if (mt * ((a.n + 255) / 256) >= 512)
+  if (BB != kBBSparse && mt * ((a.n + 255) / 256) >= 512)
     launch_nv<256, 2, BB>(a, shared, s);
   else
     launch_nv<128, 3, BB>(a, shared, s);

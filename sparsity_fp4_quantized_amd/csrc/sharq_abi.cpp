@@ -161,8 +161,10 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
   if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
     return SHARQ_ERR_SHAPE;
   if (fmt == SHARQ_MXFP4 && variant == SHARQ_GEMM_SPARSE_MFMA) return SHARQ_ERR_UNSUPPORTED;
-  // AUTO reads the dense backbone view when the caller has one (no expansion
-  // work in the GEMM), else the 2:4 form
+  // AUTO: NVFP4 runs the 2:4 backbone on the structured-sparse MFMA (its
+  // fastest variant); MXFP4 reads the dense backbone view when the caller has
+  // one (no expansion work in the GEMM), else the 2:4 form
+  if (fmt == SHARQ_NVFP4 && variant == SHARQ_GEMM_AUTO) variant = SHARQ_GEMM_SPARSE_MFMA;
   const bool dense_expanded = variant == SHARQ_GEMM_DENSE_EXPANDED ||
                               (variant == SHARQ_GEMM_AUTO && sp->dense_codes != nullptr);
   if (dense_expanded) {
