@@ -282,6 +282,45 @@ def test_end_to_end_workloads(name, samples):
     assert normwise(y2[rows, cols], ref) <= GEMM_TOL
 
 
+def _padded(t, layout, extra_rows=0, extra_bytes=0):
+    """A copy of device array `t` inside a larger buffer: row-major arrays get
+    `extra_bytes` of padding per row, k-step-major ones `extra_rows` rows per step."""
+    if layout == sq.LAYOUT_KSTEP_MAJOR:
+        steps, rows, bps = t.shape
+        big = torch.full((steps, rows + extra_rows, bps), 0xA5, dtype=torch.uint8, device=DEV)
+        big[:, :rows] = t
+        return big[:, :rows]
+    rows, nb = t.shape
+    big = torch.full((rows, nb + extra_bytes), 0xA5, dtype=torch.uint8, device=DEV)
+    big[:, :nb] = t
+    return big[:, :nb]
+
+
+@pytest.mark.parametrize("fmt", [sq.MXFP4, sq.NVFP4])
+@pytest.mark.parametrize("m,n,k", [(96, 160, 384), (20, 200, 256)])
+def test_dual_gemm_padded_leading_dims(fmt, m, n, k):
+    """Operands inside larger buffers (padding filled with 0xA5): row-major
+    rows longer than the data, k-step-major steps with more rows than the
+    operand; the GEMM must read only the described bytes."""
+    x, w, g, p, q = _gemm_case(m, n, k, seed=m + n, fmt=fmt)
+    ref = oracle.dual_gemm(fmt, p, q)
+    variants = NV_VARIANTS if fmt == sq.NVFP4 else (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)
+    for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR):
+        sp, rs = to_dev_prep(fmt, p, layout)
+        wq = to_dev_weight(fmt, q, layout)
+        pad = dict(extra_rows=24, extra_bytes=48)
+        for t in (sp, rs, wq):
+            t.codes = _padded(t.codes, layout, **pad)
+            t.scales = _padded(t.scales, layout, **pad)
+        sp.meta = _padded(sp.meta, layout, **pad)
+        sp.dense_codes = _padded(sp.dense_codes, layout, **pad)
+        out = torch.full((m, n + 8), float("nan"), dtype=torch.float32, device=DEV)
+        for variant in variants:
+            y = host(sq.dual_gemm(sp, rs, wq, variant=variant, out=out[:, :n]))
+            assert normwise(y, ref) <= GEMM_TOL, (layout, variant)
+        assert np.isnan(host(out)[:, n:]).all()        # nothing written past n
+
+
 NV_VARIANTS = (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED, sq.GEMM_SPARSE_MFMA)
 
 
