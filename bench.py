@@ -227,7 +227,42 @@ def yardsticks(w: si.Workload, torch, dev) -> dict:
                                                "dense_TFLOP/s": round(2.0 * w.m * w.n * K2 / (us * 1e-6) / 1e12, 1)}
         except Exception as e:  # not every torch build routes MX formats to hipBLASLt
             out["vendor_mxfp4_gemm_folded"] = {"error": str(e)[:200]}
+    if w.fmt == si.MXFP4 and w.m > 64:
+        out["mfma_fp4_random_operands"] = mfma_yardstick(torch, dev)
     return out
+
+
+def mfma_yardstick(torch, dev) -> dict:
+    """A kernel doing nothing but FP4 scaled MFMAs on random operands (two
+    workgroups of four wavefronts per CU, as the tiled dual GEMM): its
+    FLOP/s and the engine clock it ran at (s_memtime against the 100 MHz
+    s_memrealtime), i.e. the MFMA rate this GPU sustains on FP4 data."""
+    import ctypes
+    path = os.path.join(ROOT, "sparsity_fp4_quantized_amd", "libsharq_yardstick.so")
+    L = ctypes.CDLL(path)
+    L.sharq_yardstick_mfma_fp4.restype = ctypes.c_int
+    L.sharq_yardstick_mfma_fp4.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    wgs, iters = 512, 4000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    ticks = torch.empty(2 * wgs, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for label, rnd in (("random", 1), ("constant", 0)):
+        for _ in range(2):   # the second launch is the one reported
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = L.sharq_yardstick_mfma_fp4(wgs, iters, rnd, out.data_ptr(), ticks.data_ptr(), stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                return {"error": f"launch returned {rc}"}
+        t = ticks.view(wgs, 2).double().sum(0).cpu().numpy()
+        flops = wgs * 4 * iters * 24 * 2.0 * 32 * 32 * 64
+        us = e0.elapsed_time(e1) * 1e3
+        res[label] = {"us": round(us, 1), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                      "clock_MHz": round(100.0 * t[1] / t[0])}
+    return res
 
 
 def cpu_baseline(w: si.Workload, x, W, g, seconds: float = 12.0) -> dict:

@@ -1,7 +1,9 @@
-"""Build the HIP library libsharq.so (gfx950) in-tree with hipcc.
+"""Build the HIP library libsharq.so (gfx950) in-tree with hipcc, and the
+measurement library libsharq_yardstick.so that bench.py's MFMA yardstick
+loads (not part of the sharq ABI).
 
 Each source compiles to its own object (in parallel, with its own extra
-flags), then one hipcc link writes libsharq.so."""
+flags), then one hipcc link per library."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -13,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsharq.so")
+YARDSTICK_LIB = os.path.join(HERE, "libsharq_yardstick.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -37,6 +40,7 @@ SOURCES = {
     "gemm_mx.hip": [],
     "gemm_nv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
+YARDSTICK_SOURCES = {"yardstick.hip": []}
 
 
 def _run(cmd, verbose):
@@ -48,15 +52,18 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     jobs = []
-    for src, extra in SOURCES.items():
-        obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-        jobs.append(([HIPCC, *FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], obj))
+    for srcs in (SOURCES, YARDSTICK_SOURCES):
+        for src, extra in srcs.items():
+            obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+            jobs.append(([HIPCC, *FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], obj))
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_run, cmd, verbose) for cmd, _ in jobs]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *[obj for _, obj in jobs]], verbose)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (YARDSTICK_LIB, YARDSTICK_SOURCES)):
+        objs = [os.path.join(OBJ, os.path.splitext(src)[0] + ".o") for src in srcs]
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

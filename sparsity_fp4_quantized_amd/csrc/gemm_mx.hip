@@ -333,7 +333,15 @@ __device__ __forceinline__ void issue_stage(const DRsrc &R, const DOffs<TBM, TBN
 #pragma unroll
   for (int j = 0; j < P::kChunkPer; ++j) {
     const int q = wave + NW * j;
-    if (q < P::kA) b2l16(R.as.rsrc, O.chunk[j], t * R.as.step, base + q * 1024);
+    // loads NW j .. NW j + NW - 1 go to one operand when the operand
+    // boundaries are multiples of NW: resolved at compile time
+    const int q0 = NW * j;
+    if (q0 + NW <= P::kA) b2l16(R.as.rsrc, O.chunk[j], t * R.as.step, base + q * 1024);
+    else if (q0 >= P::kA && q0 + NW <= 2 * P::kA)
+      b2l16(R.ar.rsrc, O.chunk[j], t * R.ar.step, base + oar + (q - P::kA) * 1024);
+    else if (q0 >= 2 * P::kA && q0 + NW <= 2 * P::kA + P::kW)
+      b2l16(R.w.rsrc, O.chunk[j], t * R.w.step, base + ow + (q - 2 * P::kA) * 1024);
+    else if (q < P::kA) b2l16(R.as.rsrc, O.chunk[j], t * R.as.step, base + q * 1024);
     else if (q < 2 * P::kA) b2l16(R.ar.rsrc, O.chunk[j], t * R.ar.step, base + oar + (q - P::kA) * 1024);
     else if (q < 2 * P::kA + P::kW)
       b2l16(R.w.rsrc, O.chunk[j], t * R.w.step, base + ow + (q - 2 * P::kA) * 1024);
@@ -367,21 +375,36 @@ __device__ __forceinline__ void compute_stage(const DStage<TBM, TBN> &S, v16f (&
     sws[jt] = (int)(S.sws[r] >> (16 * h));
     swd[jt] = (int)(S.swd[r] >> (16 * h));
   }
+  u32x4 ras[2][2], rar[2][2], rb[2][TN];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    v8i fas[2], far[2], fb[TN];
     const int c = 2 * h + s;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int r = wm * 64 + it * 32 + li;
-      fas[it] = as_operand(S.as[lds_slot(r, c)]);
-      far[it] = as_operand(S.ar[lds_slot(r, c)]);
+      ras[s][it] = S.as[lds_slot(r, c)];
+      rar[s][it] = S.ar[lds_slot(r, c)];
     }
 #pragma unroll
     for (int jt = 0; jt < TN; ++jt) {
       const int r = wn * (TBN / 2) + jt * 32 + li;
-      fb[jt] = as_operand(S.w[lds_slot(r, c)]);
+      rb[s][jt] = S.w[lds_slot(r, c)];
     }
+  }
+  // every LDS read of the step is issued before the first MFMA (left to
+  // itself the compiler reuses one register set and waits on each A
+  // fragment just before its MFMAs)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v8i fas[2], far[2], fb[TN];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      fas[it] = as_operand(ras[s][it]);
+      far[it] = as_operand(rar[s][it]);
+    }
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) fb[jt] = as_operand(rb[s][jt]);
     // backbone MFMAs for every tile first, then the residual ones: 2 TN
     // independent accumulators between two updates of the same tile
 #pragma unroll
