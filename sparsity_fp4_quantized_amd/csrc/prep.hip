@@ -35,25 +35,15 @@ constexpr int kMaxWavesPerRow = 8;     // K <= 16384 with normalization
 
 // ---------------------------------------------------------------- helpers
 
-// X is read exactly once: non-temporal loads keep it out of the way of the
-// outputs and of the next kernel's operands.
+// 32 bf16 values (64 bytes) as four 16-byte loads.  Plain loads: a
+// wavefront's four loads cover each 128-byte line between them, and the L1
+// serves the later ones; non-temporal loads (which skip it) fetched every line
+// again for each load and made the preparation 10-28% slower.
 __device__ __forceinline__ void load32(const uint16_t *p, uint32_t w[16]) {
   const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    u32x4 t = __builtin_nontemporal_load(q + i);
-    w[4 * i + 0] = t.x;
-    w[4 * i + 1] = t.y;
-    w[4 * i + 2] = t.z;
-    w[4 * i + 3] = t.w;
-  }
-}
-
-__device__ __forceinline__ void load32_cached(const uint16_t *p, uint32_t w[16]) {
-  const uint4 *q = reinterpret_cast<const uint4 *>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 t = q[i];
+    const u32x4 t = q[i];
     w[4 * i + 0] = t.x;
     w[4 * i + 1] = t.y;
     w[4 * i + 2] = t.z;
@@ -472,7 +462,7 @@ __device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const
                                             float r) {
   uint32_t gw[16];
   float gf[32];
-  load32_cached(g, gw);
+  load32(g, gw);
   unpack32(gw, gf);
   normalize32(xf, xw, gf, r);
 }
@@ -594,7 +584,7 @@ __global__ __launch_bounds__(512) void amax_norm_kernel(PrepArgs a) {
     const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
     uint32_t xw[16];
     float xf[32];
-    load32_cached(a.x + lrow * a.ld_x + 32 * lb, xw);
+    load32(a.x + lrow * a.ld_x + 32 * lb, xw);
     unpack32(xw, xf);
     float s = block_sumsq(xf);
     float r = row_rms<WPR>(has ? s : 0.0f, riw, wir, a.k, a.eps);
@@ -616,7 +606,7 @@ __global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *x, int64
        gid += (int64_t)gridDim.x * 256) {
     const int64_t row = gid / nblk, b = gid - row * nblk;
     uint32_t xw[16];
-    load32_cached(x + row * ld + 32 * b, xw);
+    load32(x + row * ld + 32 * b, xw);
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = max(am, max(xw[i] & 0x7FFFu, (xw[i] >> 16) & 0x7FFFu));
   }
