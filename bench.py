@@ -465,6 +465,10 @@ def main():
     }
     if not args.no_yardsticks:
         out["yardsticks"] = yardsticks(w, torch, dev)
+        mf = out["yardsticks"].get("mfma_fp4_random_operands", {}).get("random")
+        if mf and "executed_TFLOP/s" in roofline:
+            # executed MFMA rate against the rate FP4 MFMAs alone sustain on data
+            roofline["executed_vs_fp4_mfma_yardstick"] = round(roofline["executed_TFLOP/s"] / mf["TFLOP/s"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x_np, W_np, g_np)
     print(json.dumps(out), flush=True)

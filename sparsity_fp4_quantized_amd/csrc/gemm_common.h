@@ -15,8 +15,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256, BK = 128;
-constexpr int kThreads = 512;
+constexpr int BK = 128;   // k per pipeline step
 
 __device__ __forceinline__ v8i as_operand(u32x4 v) {
   v8i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
@@ -120,20 +119,30 @@ inline uint32_t xcd_band_rows(int64_t gm, int64_t gn, int tbm, int tbn) {
 }
 
 // Expand eight 2:4 groups (8 code bytes, 4 meta bytes) into 32 dense codes.
+// Output word q holds groups 2q and 2q + 1, one per 16-bit half, so both are
+// placed at once with packed 16-bit shifts: the two code bytes go to bytes 0
+// and 2 (v_perm), their low nibbles (code at i0) and high nibbles (code at
+// i1) are shifted left by 4 i0 and 4 i1 of their own group.  The meta byte q
+// (i0 | i1 << 2 of group 2q, the same of group 2q + 1 in the high nibble) is
+// copied to bytes 0 and 2 and shifted right by 0 and 4 per half, which lines
+// up 4 i1 in bits 2-3 and i0 in bits 0-1 of each half.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_shl16(uint32_t v, uint32_t s) {
+  const u16x2 r = __builtin_bit_cast(u16x2, v) << __builtin_bit_cast(u16x2, s);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ void expand8(uint32_t c_lo, uint32_t c_hi, uint32_t meta, uint32_t out[4]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const int g = 2 * q + gg;
-      const uint32_t cb = ((g < 4 ? c_lo : c_hi) >> (8 * (g & 3))) & 0xFFu;
-      const uint32_t s0 = ((meta >> (4 * g)) & 3u) << 2;
-      const uint32_t s1 = ((meta >> (4 * g + 2)) & 3u) << 2;
-      const uint32_t d16 = ((cb & 15u) << s0) | ((cb >> 4) << s1);
-      word |= d16 << (16 * gg);
-    }
-    out[q] = word;
+    const uint32_t k = 2u * (q & 1);
+    const uint32_t x = __builtin_amdgcn_perm(0u, q < 2 ? c_lo : c_hi, k | 0x0C00u | ((k + 1u) << 16) | 0x0C000000u);
+    const uint32_t lo = x & 0x000F000Fu, hi = (x >> 4) & 0x000F000Fu;
+    const uint32_t y = __builtin_amdgcn_perm(0u, meta, (uint32_t)q | 0x0C00u | ((uint32_t)q << 16) | 0x0C000000u);
+    const u16x2 zv = __builtin_bit_cast(u16x2, y) >> u16x2{0, 4};
+    const uint32_t z = __builtin_bit_cast(uint32_t, zv);
+    out[q] = pk_shl16(lo, (z & 0x00030003u) << 2) | pk_shl16(hi, z & 0x000C000Cu);
   }
 }
 

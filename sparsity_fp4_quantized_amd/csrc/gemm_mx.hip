@@ -16,15 +16,14 @@
 // Each K step stages the W tile once and feeds it to the MFMAs of both paths,
 // which accumulate into the same registers.
 //
-// Tiling: a workgroup of 8 wavefronts (2 per SIMD) owns a BM x BN tile of Y
-// (BM = 256); wavefront (wm, wn) of the 4 x 2 grid owns 64 rows x BN/2
-// columns, i.e. 2 x BN/64 MFMA tiles of 32 x 32.  K advances 128 per step
-// (one 32-bit word of four E8M0 scales per row).  The LDS holds two stages;
-// global loads of step k+1 are issued before the MFMAs of step k and written
-// to the other stage after them, with one barrier per step.  LDS rows are 64
-// bytes (four 16-byte chunks); chunk c of row r sits at c ^ ((r >> 2) & 3),
-// so sixteen lanes reading one chunk of sixteen consecutive rows hit sixteen
-// different bank groups.
+// Kernels: dual_gemm_dense_kernel (prefill, backbone in the dense layout the
+// preparation wrote), dual_gemm_decomp_kernel (prefill, the 2:4 backbone
+// expanded in LDS), dual_gemm_decode_kernel and dual_gemm_skinny_kernel (m <=
+// 32, bound by streaming W).  The prefill kernels stage 128-k steps of every
+// operand in LDS with direct global -> LDS loads; LDS rows are 64 bytes (four
+// 16-byte chunks) and chunk c of row r sits at c ^ ((r >> 2) & 3), so sixteen
+// lanes reading one chunk of sixteen consecutive rows hit sixteen different
+// bank groups.
 //
 // Operand layout of the 32x32x64 FP4 MFMA (lane l, h = l / 32): A row l % 32
 // and B column l % 32, 32 consecutive k (16 bytes) per lane; the lane's scale
@@ -43,204 +42,6 @@ namespace sharq {
 namespace {
 
 using namespace gemm;
-
-template <int BN, bool kDense>
-struct Stage {
-  static constexpr int kWChunks = BN * 4;                      // 16-byte chunks of the W tile
-  static constexpr int kWPer = (kWChunks + kThreads - 1) / kThreads;
-  u32x4 ar[2];        // residual tile: 256 rows x 4 chunks -> 2 per thread
-  u32x4 as[2];        // backbone: dense chunks, or [0] = 16 code bytes + [1].xy = 8 meta bytes
-  u32x4 w[kWPer];
-  uint32_t sc[2];     // scale words (see load)
-};
-
-template <int BN>
-struct Smem {
-  u32x4 as[2][BM * 4];
-  u32x4 ar[2][BM * 4];
-  u32x4 w[2][BN * 4];
-  uint32_t sas[2][BM], sar[2][BM], sws[2][BN], swd[2][BN];
-};
-
-// The 32-bit word of E8M0 scales of row r for 128-k step kt.
-__device__ __forceinline__ uint32_t scale_word(const uint8_t *p, int64_t ld, int ksm, int64_t r,
-                                               int kt) {
-  return *reinterpret_cast<const uint32_t *>(p + arr_off(r, kt, ld, ksm, 4));
-}
-
-template <int BN, bool kDense>
-__device__ __forceinline__ void load_stage(const GemmArgs &a, int64_t m0, int64_t n0, int kt,
-                                           Stage<BN, kDense> &st) {
-  const int tid = threadIdx.x;
-  const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = tid + kThreads * j, row = c >> 2, part = c & 3;
-    const int64_t gm = m0 + row;
-    st.ar[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.r_codes + arr_off(gm, kt, a.ld_rc, a.r_ksm, 64) + part * 16) : z;
-    if (kDense)
-      st.as[j] = gm < a.m ? *reinterpret_cast<const u32x4 *>(a.s_dense + arr_off(gm, kt, a.ld_sd, a.s_ksm, 64) + part * 16) : z;
-  }
-  if (!kDense) {
-    const int row = tid >> 1, half = tid & 1;
-    const int64_t gm = m0 + row;
-    if (gm < a.m) {
-      st.as[0] = *reinterpret_cast<const u32x4 *>(a.s_codes + arr_off(gm, kt, a.ld_sc, a.s_ksm, 32) + half * 16);
-      u32x2 mv = *reinterpret_cast<const u32x2 *>(a.meta + arr_off(gm, kt, a.ld_meta, a.s_ksm, 16) + half * 8);
-      st.as[1] = u32x4{mv.x, mv.y, 0u, 0u};
-    } else {
-      st.as[0] = z;
-      st.as[1] = u32x4{0x44444444u, 0x44444444u, 0u, 0u};
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < Stage<BN, kDense>::kWPer; ++j) {
-    const int c = tid + kThreads * j;
-    if (c < Stage<BN, kDense>::kWChunks) {
-      const int row = c >> 2, part = c & 3;
-      const int64_t gn = n0 + row;
-      st.w[j] = gn < a.n ? *reinterpret_cast<const u32x4 *>(a.w_codes + arr_off(gn, kt, a.ld_wc, a.w_ksm, 64) + part * 16) : z;
-    }
-  }
-  // scale words: threads [0, 256) the two A paths of row tid; [256, 256 + BN) the two W views
-  if (tid < BM) {
-    const int64_t gm = m0 + tid;
-    st.sc[0] = gm < a.m ? scale_word(a.s_scales, a.ld_ss, a.s_ksm, gm, kt) : 0u;
-    st.sc[1] = gm < a.m ? scale_word(a.r_scales, a.ld_rs, a.r_ksm, gm, kt) : 0u;
-  } else if (tid < BM + BN) {
-    const int64_t gn = n0 + (tid - BM);
-    st.sc[0] = gn < a.n ? scale_word(a.ws_scales, a.ld_wss, a.w_ksm, gn, kt) : 0u;
-    st.sc[1] = gn < a.n ? scale_word(a.wd_scales, a.ld_wds, a.w_ksm, gn, kt) : 0u;
-  }
-}
-
-template <int BN, bool kDense>
-__device__ __forceinline__ void store_stage(Smem<BN> &sm, int buf, const Stage<BN, kDense> &st) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = tid + kThreads * j, row = c >> 2, part = c & 3;
-    sm.ar[buf][lds_slot(row, part)] = st.ar[j];
-    if (kDense) sm.as[buf][lds_slot(row, part)] = st.as[j];
-  }
-  if (!kDense) {
-    const int row = tid >> 1, half = tid & 1;
-    uint32_t d0[4], d1[4];
-    expand8(st.as[0].x, st.as[0].y, st.as[1].x, d0);
-    expand8(st.as[0].z, st.as[0].w, st.as[1].y, d1);
-    sm.as[buf][lds_slot(row, 2 * half)] = u32x4{d0[0], d0[1], d0[2], d0[3]};
-    sm.as[buf][lds_slot(row, 2 * half + 1)] = u32x4{d1[0], d1[1], d1[2], d1[3]};
-  }
-#pragma unroll
-  for (int j = 0; j < Stage<BN, kDense>::kWPer; ++j) {
-    const int c = tid + kThreads * j;
-    if (c < Stage<BN, kDense>::kWChunks) {
-      const int row = c >> 2, part = c & 3;
-      sm.w[buf][lds_slot(row, part)] = st.w[j];
-    }
-  }
-  if (tid < BM) {
-    sm.sas[buf][tid] = st.sc[0];
-    sm.sar[buf][tid] = st.sc[1];
-  } else if (tid < BM + BN) {
-    sm.sws[buf][tid - BM] = st.sc[0];
-    sm.swd[buf][tid - BM] = st.sc[1];
-  }
-}
-
-template <int BN, bool kDense>
-__global__ __launch_bounds__(kThreads) void dual_gemm_mx_kernel(GemmArgs a) {
-  constexpr int TN = BN / 64;           // 32-column MFMA tiles per wavefront
-  __shared__ Smem<BN> sm;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, li = lane & 31;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-
-  v16f acc[2][TN];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int ksteps = (int)(a.k / BK);
-  Stage<BN, kDense> st;
-  load_stage<BN, kDense>(a, m0, n0, 0, st);
-  store_stage<BN, kDense>(sm, 0, st);
-  __syncthreads();
-
-  for (int kt = 0; kt < ksteps; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < ksteps;
-    if (more) load_stage<BN, kDense>(a, m0, n0, kt + 1, st);
-
-    // scale words of this lane's rows / columns, shifted to k blocks 2h, 2h + 1
-    int sas[2], sar[2], sws[TN], swd[TN];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int r = wm * 64 + it * 32 + li;
-      sas[it] = (int)(sm.sas[buf][r] >> (16 * h));
-      sar[it] = (int)(sm.sar[buf][r] >> (16 * h));
-    }
-#pragma unroll
-    for (int jt = 0; jt < TN; ++jt) {
-      const int r = wn * (BN / 2) + jt * 32 + li;
-      sws[jt] = (int)(sm.sws[buf][r] >> (16 * h));
-      swd[jt] = (int)(sm.swd[buf][r] >> (16 * h));
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8i fas[2], far[2], fb[TN];
-      const int c = 2 * h + s;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int r = wm * 64 + it * 32 + li;
-        fas[it] = as_operand(sm.as[buf][lds_slot(r, c)]);
-        far[it] = as_operand(sm.ar[buf][lds_slot(r, c)]);
-      }
-#pragma unroll
-      for (int jt = 0; jt < TN; ++jt) {
-        const int r = wn * (BN / 2) + jt * 32 + li;
-        fb[jt] = as_operand(sm.w[buf][lds_slot(r, c)]);
-      }
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int jt = 0; jt < TN; ++jt) {
-          if (s == 0) {
-            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fas[it], fb[jt], acc[it][jt], 4, 4, 0, sas[it], 0, sws[jt]);
-            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                far[it], fb[jt], acc[it][jt], 4, 4, 0, sar[it], 0, swd[jt]);
-          } else {
-            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fas[it], fb[jt], acc[it][jt], 4, 4, 1, sas[it], 1, sws[jt]);
-            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                far[it], fb[jt], acc[it][jt], 4, 4, 1, sar[it], 1, swd[jt]);
-          }
-        }
-    }
-    if (more) store_stage<BN, kDense>(sm, buf ^ 1, st);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int jt = 0; jt < TN; ++jt) {
-      const int64_t col = n0 + wn * (BN / 2) + jt * 32 + li;
-      if (col >= a.n) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < a.m) a.y[row * a.ld_y + col] = acc[it][jt][r];
-      }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Dense-operand pipeline: the backbone is read in its dense layout, so all
@@ -358,9 +159,18 @@ __device__ __forceinline__ void issue_stage(const DRsrc &R, const DOffs<TBM, TBN
 }
 
 // One 128-k step of wavefront (wm, wn): 64 rows x TBN/2 columns.
-template <int TBM, int TBN>
-__device__ __forceinline__ void compute_stage(const DStage<TBM, TBN> &S, v16f (&acc)[2][TBN / 64],
-                                              int wm, int wn, int h, int li) {
+// Side work of a step that runs under its MFMAs: pre() issues its LDS reads
+// with the step's, post() its arithmetic and LDS writes, interleaved with the
+// MFMAs.
+struct NoSide {
+  static constexpr int kValuPerMfma = 0;
+  __device__ __forceinline__ void pre() {}
+  __device__ __forceinline__ void post() {}
+};
+
+template <int TBM, int TBN, class Stage, class Side = NoSide>
+__device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN / 64],
+                                              int wm, int wn, int h, int li, Side side = Side()) {
   constexpr int TN = TBN / 64;
   int sas[2], sar[2], sws[TN], swd[TN];
 #pragma unroll
@@ -391,6 +201,7 @@ __device__ __forceinline__ void compute_stage(const DStage<TBM, TBN> &S, v16f (&
       rb[s][jt] = S.w[lds_slot(r, c)];
     }
   }
+  side.pre();
   // every LDS read of the step is issued before the first MFMA (left to
   // itself the compiler reuses one register set and waits on each A
   // fragment just before its MFMAs)
@@ -421,6 +232,15 @@ __device__ __forceinline__ void compute_stage(const DStage<TBM, TBN> &S, v16f (&
           else
             acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb[jt], acc[it][jt], 4, 4, 1, sa, 1, sw);
         }
+  }
+  if (Side::kValuPerMfma > 0) {
+    side.post();
+    // one MFMA, then kValuPerMfma VALU instructions of the side work, ...
+#pragma unroll
+    for (int i = 0; i < 4 * TN * 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, Side::kValuPerMfma, 0);
+    }
   }
 }
 
@@ -491,14 +311,241 @@ void launch_dense(const GemmArgs &a, hipStream_t s) {
       <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN));
 }
 
-template <int BN>
-void launch_bn(const GemmArgs &a, bool dense, hipStream_t s) {
-  dim3 grid((unsigned)((a.n + BN - 1) / BN), (unsigned)((a.m + BM - 1) / BM)), block(kThreads);
-  if (dense)
-    dual_gemm_mx_kernel<BN, true><<<grid, block, 0, s>>>(a);
-  else
-    dual_gemm_mx_kernel<BN, false><<<grid, block, 0, s>>>(a);
+// ---------------------------------------------------------------------------
+// Prefill with the 2:4 backbone as the preparation wrote it (DECOMPRESS): the
+// tiled kernel above, with the backbone streamed compressed (codes 32 and meta
+// 16 bytes per row and 128-k step instead of 64 dense bytes) and expanded once
+// per workgroup in LDS.  At step kt the workgroup computes step kt from stage
+// kt % 2, and meanwhile (a) streams step kt + 1's residual, W and scales into
+// stage (kt + 1) % 2, (b) streams step kt + 2's compressed backbone into the
+// compressed area of stage kt % 2 (step kt's was expanded a step earlier),
+// and (c) expands step kt + 1's compressed backbone, which landed during step
+// kt - 1, into the dense area of stage (kt + 1) % 2.  One barrier a step.
+// Every wavefront issues the same loads each step (padding loads read
+// nothing: an empty buffer resource), so the loop has no branch; the steps
+// past the end are fetched the same way and never used.
+template <int TBM, int TBN>
+struct XStage {
+  u32x4 as[TBM * 4];           // dense backbone, expanded in LDS
+  u32x4 ar[TBM * 4];
+  u32x4 w[TBN * 4];
+  uint32_t sas[TBM], sar[TBM], sws[TBN], swd[TBN];
+  uint8_t codes[TBM * 32];     // compressed backbone: 32 code bytes a row
+  uint8_t meta[TBM * 16];      // 16 meta bytes a row
+  u32x4 spare[64];             // destination of padding loads
+};
+
+template <int TBM, int TBN, int NW>
+struct XPlan {
+  static constexpr int kChunks = TBM / 32 + TBM / 64 + TBM / 16 + TBN / 16;   // 16-byte loads
+  static constexpr int kScales = 2 * (TBM / 64) + 2 * (TBN / 64);             // 4-byte loads
+  static constexpr int kChunkPer = (kChunks + NW - 1) / NW, kScalePer = (kScales + NW - 1) / NW;
+  static constexpr int kPerWave = kChunkPer + kScalePer;
+};
+
+// One load of this wavefront: resource, bytes per step, the lane's offset at
+// step 0, its LDS offset within a stage, and which step it fetches at step
+// kt (kt + 1 + ahead).
+struct XLoad {
+  i32x4 rsrc;
+  uint32_t step, voff, lds, ahead;
+};
+
+template <int TBM, int TBN, int NW>
+__device__ __forceinline__ void decomp_plan(const GemmArgs &a, int64_t m0, int64_t n0, int wave, int lane,
+                                            XLoad (&L)[XPlan<TBM, TBN, NW>::kPerWave]) {
+  using P = XPlan<TBM, TBN, NW>;
+  using St = XStage<TBM, TBN>;
+  const int64_t steps = a.k / BK;
+  const OpStream sc = op_stream(a.s_codes, a.ld_sc, a.s_ksm, a.m, m0, steps, 32);
+  const OpStream sm = op_stream(a.meta, a.ld_meta, a.s_ksm, a.m, m0, steps, 16);
+  const OpStream ar = op_stream(a.r_codes, a.ld_rc, a.r_ksm, a.m, m0, steps, 64);
+  const OpStream w = op_stream(a.w_codes, a.ld_wc, a.w_ksm, a.n, n0, steps, 64);
+  const OpStream sas = op_stream(a.s_scales, a.ld_ss, a.s_ksm, a.m, m0, steps, 4);
+  const OpStream sar = op_stream(a.r_scales, a.ld_rs, a.r_ksm, a.m, m0, steps, 4);
+  const OpStream sws = op_stream(a.ws_scales, a.ld_wss, a.w_ksm, a.n, n0, steps, 4);
+  const OpStream swd = op_stream(a.wd_scales, a.ld_wds, a.w_ksm, a.n, n0, steps, 4);
+  const i32x4 none = make_rsrc(a.w_codes, 0u);
+  constexpr int NC = TBM / 32, NM = TBM / 64, NA = TBM / 16, NB = TBN / 16;
+  // 16-byte loads: compressed codes (32 rows of 32 bytes each), meta (64 rows
+  // of 16 bytes), residual and W (16 rows of 64 bytes, chunk-swizzled)
+#pragma unroll
+  for (int j = 0; j < P::kChunkPer; ++j) {
+    const int q = wave + NW * j;
+    const int op = q < NC ? 0 : q < NC + NM ? 1 : q < NC + NM + NA ? 2 : q < NC + NM + NA + NB ? 3 : 4;
+    const int i = op == 0 ? q : op == 1 ? q - NC : op == 2 ? q - NC - NM : q - NC - NM - NA;
+    const OpStream o = op == 0 ? sc : op == 1 ? sm : op == 2 ? ar : w;
+    uint32_t voff, lds;
+    if (op == 0) {
+      voff = (uint32_t)(32 * i + (lane >> 1)) * o.row_stride + (lane & 1) * 16;
+      lds = (uint32_t)offsetof(St, codes) + (uint32_t)i * 1024;
+    } else if (op == 1) {
+      voff = (uint32_t)(64 * i + lane) * o.row_stride;
+      lds = (uint32_t)offsetof(St, meta) + (uint32_t)i * 1024;
+    } else {
+      const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+      voff = (uint32_t)(16 * i + lrow) * o.row_stride + lchunk * 16;
+      lds = (op == 2 ? (uint32_t)offsetof(St, ar) : (uint32_t)offsetof(St, w)) + (uint32_t)i * 1024;
+    }
+    const bool real = op < 4;
+    L[j].rsrc = real ? o.rsrc : none;
+    L[j].step = real ? o.step : 0u;
+    L[j].voff = real ? voff : 0u;
+    L[j].lds = real ? lds : (uint32_t)offsetof(St, spare);
+    L[j].ahead = op < 2 ? 1u : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < P::kScalePer; ++j) {
+    const int q = wave + NW * j;
+    constexpr int TA = TBM / 64, T = TBN / 64;
+    const int op = q < TA ? 0 : q < 2 * TA ? 1 : q < 2 * TA + T ? 2 : q < 2 * TA + 2 * T ? 3 : 4;
+    const int i = op == 0 ? q : op == 1 ? q - TA : op == 2 ? q - 2 * TA : q - 2 * TA - T;
+    const OpStream o = op == 0 ? sas : op == 1 ? sar : op == 2 ? sws : swd;
+    const uint32_t lds = op == 0 ? (uint32_t)offsetof(St, sas) : op == 1 ? (uint32_t)offsetof(St, sar)
+                       : op == 2 ? (uint32_t)offsetof(St, sws) : (uint32_t)offsetof(St, swd);
+    const bool real = op < 4;
+    XLoad &d = L[P::kChunkPer + j];
+    d.rsrc = real ? o.rsrc : none;
+    d.step = real ? o.step : 0u;
+    d.voff = real ? (uint32_t)(64 * i + lane) * o.row_stride : 0u;
+    d.lds = real ? lds + (uint32_t)i * 256 : (uint32_t)offsetof(St, spare);
+    d.ahead = 0u;
+  }
 }
+
+// The loads of step kt: each fetches step kt + 1 + ahead into stage
+// (kt + 1 + ahead) % 2.  kRawOnly: only the compressed backbone's, for step
+// kt + 2 (the prologue's step 0).
+template <int TBM, int TBN, int NW, bool kRawOnly = false>
+__device__ __forceinline__ void decomp_issue(const XLoad (&L)[XPlan<TBM, TBN, NW>::kPerWave], int kt,
+                                             uint32_t base0, uint32_t base1) {
+  using P = XPlan<TBM, TBN, NW>;
+#pragma unroll
+  for (int j = 0; j < P::kPerWave; ++j) {
+    if (kRawOnly && !L[j].ahead) continue;
+    // (uniform values; readfirstlane keeps them in scalar registers)
+    const uint32_t t = (uint32_t)kt + 1u + L[j].ahead;
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)(t * L[j].step));
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(((t & 1u) ? base1 : base0) + L[j].lds));
+    if (j < P::kChunkPer) b2l16(L[j].rsrc, L[j].voff, soff, lds);
+    else b2l4(L[j].rsrc, L[j].voff, soff, lds);
+  }
+}
+
+// The workgroup expands a stage's compressed backbone into its dense area:
+// unit u = 16 dense bytes (chunk u % 4 of row u / 4) from 8 code bytes and 4
+// meta bytes.
+template <int TBM, int TBN, int NW>
+__device__ __forceinline__ void decomp_expand(XStage<TBM, TBN> &S, int tid) {
+#pragma unroll
+  for (int i = 0; i < TBM * 4 / (64 * NW); ++i) {
+    const int u = tid + 64 * NW * i, r = u >> 2, c = u & 3;
+    const u32x2 cb = *reinterpret_cast<const u32x2 *>(S.codes + r * 32 + 8 * c);
+    const uint32_t mb = *reinterpret_cast<const uint32_t *>(S.meta + r * 16 + 4 * c);
+    uint32_t d[4];
+    expand8(cb.x, cb.y, mb, d);
+    S.as[lds_slot(r, c)] = u32x4{d[0], d[1], d[2], d[3]};
+  }
+}
+
+// Expansion of one stage's compressed backbone as side work of the MFMAs.
+template <int TBM, int TBN, int NW>
+struct ExpandSide {
+  static constexpr int kUnits = TBM * 4 / (64 * NW);
+  static constexpr int kValuPerMfma = 6;
+  XStage<TBM, TBN> *S;
+  int tid;
+  u32x2 cb[kUnits];
+  uint32_t mb[kUnits];
+  __device__ __forceinline__ void pre() {
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const int u = tid + 64 * NW * i, r = u >> 2, c = u & 3;
+      cb[i] = *reinterpret_cast<const u32x2 *>(S->codes + r * 32 + 8 * c);
+      mb[i] = *reinterpret_cast<const uint32_t *>(S->meta + r * 16 + 4 * c);
+    }
+  }
+  __device__ __forceinline__ void post() {
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+      const int u = tid + 64 * NW * i, r = u >> 2, c = u & 3;
+      uint32_t d[4];
+      expand8(cb[i].x, cb[i].y, mb[i], d);
+      S->as[lds_slot(r, c)] = u32x4{d[0], d[1], d[2], d[3]};
+    }
+  }
+};
+
+template <int TBM, int TBN, int NW>
+__global__ __launch_bounds__(64 * NW) void dual_gemm_decomp_kernel(GemmArgs a, uint32_t band) {
+  static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
+  constexpr int TN = TBN / 64;
+  using P = XPlan<TBM, TBN, NW>;
+  __shared__ XStage<TBM, TBN> st[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, li = lane & 31;
+  uint32_t tm, tn;
+  xcd_tile(blockIdx.x, (uint32_t)((a.m + TBM - 1) / TBM), (uint32_t)((a.n + TBN - 1) / TBN), band, tm, tn);
+  const int64_t m0 = (int64_t)tm * TBM, n0 = (int64_t)tn * TBN;
+
+  v16f acc[2][TN];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int ksteps = (int)(a.k / BK);
+  XLoad L[P::kPerWave];
+  decomp_plan<TBM, TBN, NW>(a, m0, n0, wave, lane, L);
+  const uint32_t base0 = lds_addr(&st[0]), base1 = lds_addr(&st[1]);
+  // prologue: step 0's compressed backbone, then step 0's other operands and
+  // step 1's compressed backbone
+  decomp_issue<TBM, TBN, NW, true>(L, -2, base0, base1);
+  decomp_issue<TBM, TBN, NW>(L, -1, base0, base1);
+  wait_vmcnt<0>();
+  stage_barrier();
+  decomp_expand<TBM, TBN, NW>(st[0], tid);
+
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int cur = kt & 1;
+    // every load issued at step kt - 1 has landed (step kt's operands, step
+    // kt + 1's compressed backbone); the barrier also publishes step kt's
+    // expansion and frees stage (kt + 1) % 2 and step kt's compressed area
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    stage_barrier();
+    decomp_issue<TBM, TBN, NW>(L, kt, base0, base1);
+    compute_stage<TBM, TBN>(st[cur], acc, wm, wn, h, li, ExpandSide<TBM, TBN, NW>{&st[cur ^ 1], tid});
+  }
+  // no loads may land in LDS after the workgroup ends
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) {
+      const int64_t col = n0 + wn * (TBN / 2) + jt * 32 + li;
+      if (col >= a.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < a.m) a.y[row * a.ld_y + col] = acc[it][jt][r];
+      }
+    }
+}
+
+template <int TBM, int TBN, int NW>
+void launch_decomp(const GemmArgs &a, hipStream_t s) {
+  const int64_t gm = (a.m + TBM - 1) / TBM, gn = (a.n + TBN - 1) / TBN;
+  dual_gemm_decomp_kernel<TBM, TBN, NW>
+      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN));
+}
+
 
 // ---------------------------------------------------------------------------
 // Skinny kernel for m <= 32 (decode): the GEMM streams W once and is bound by
@@ -510,6 +557,12 @@ void launch_bn(const GemmArgs &a, bool dense, hipStream_t s) {
 // wavefronts keep more loads in flight than a few long ones.  Lane (h, li):
 // row / column li, k blocks 2h (first MFMA) and 2h + 1 (second), as in the
 // tiled kernels.
+// The 32-bit word of E8M0 scales of row r for 128-k step kt.
+__device__ __forceinline__ uint32_t scale_word(const uint8_t *p, int64_t ld, int ksm, int64_t r,
+                                               int kt) {
+  return *reinterpret_cast<const uint32_t *>(p + arr_off(r, kt, ld, ksm, 4));
+}
+
 struct SkFrag {
   u32x4 fs[2], fr[2], fw[2];
   int sas, sar, sws, swd;
@@ -738,11 +791,15 @@ hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream
     else
       launch_dense<128, 128, 4, 2>(a, s);
   } else {
-    const int64_t mt = (a.m + BM - 1) / BM;
-    if (mt * ((a.n + 191) / 192) >= 256 || mt * ((a.n + 127) / 128) > 256)
-      launch_bn<192>(a, dense_expanded, s);
+    // the same tiles; 128 x 256 when that still gives every CU a tile: the
+    // expansion's cost per step does not grow with TBN, the MFMAs' does
+    const int64_t mt = (a.m + 127) / 128;
+    if (mt * ((a.n + 191) / 192) >= 512 && a.k <= 8192)
+      launch_decomp<128, 192, 4>(a, s);
+    else if (mt * ((a.n + 255) / 256) >= 256)
+      launch_decomp<128, 256, 4>(a, s);
     else
-      launch_bn<128>(a, dense_expanded, s);
+      launch_decomp<128, 128, 4>(a, s);
   }
   return hipGetLastError();
 }

@@ -210,6 +210,31 @@ def test_dual_gemm_mx_vs_oracle(m, n, k):
             assert err <= GEMM_TOL, (layout, variant, err)
 
 
+@pytest.mark.parametrize("m,n,k", [(2000, 6100, 384), (2000, 4000, 640), (2048, 4096, 128)])
+def test_dual_gemm_mx_large_tile_configs(m, n, k):
+    """Shapes that take the tile configurations of the large workloads
+    (128 x 192 for both variants; 128 x 128 dense and 128 x 256 expanding),
+    with ragged edges, against the oracle at every 32-row and 32-column tile
+    edge plus random outputs."""
+    x, w, g, p, q = _gemm_case(m, n, k, seed=m + n + k)
+    rng = np.random.default_rng(m + n)
+    er = np.concatenate([np.arange(0, m, 32), np.arange(31, m, 32), [m - 1]])
+    ec = np.concatenate([np.arange(0, n, 32), np.arange(31, n, 32), [n - 1]])
+    rows = np.concatenate([er, rng.integers(0, m, 4000), rng.integers(0, m, ec.size)])
+    cols = np.concatenate([rng.integers(0, n, er.size), rng.integers(0, n, 4000), ec])
+    order = np.argsort(rows, kind="stable")
+    rows, cols = rows[order], cols[order]
+    ref = oracle.dual_gemm_pairs(sq.MXFP4, p, q, rows, cols)
+    for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
+        sp, rs = to_dev_prep(sq.MXFP4, p, layout)
+        wq = to_dev_weight(sq.MXFP4, q, layout)
+        ys = [host(sq.dual_gemm(sp, rs, wq, variant=v)) for v in (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)]
+        for v, y in zip(("decompress", "dense"), ys):
+            assert np.isfinite(y).all(), (layout, v)
+            err = normwise(y[rows, cols], ref)
+            assert err <= GEMM_TOL, (layout, v, err)
+
+
 def test_dual_gemm_variants_bitwise_equal():
     x, w, g, p, q = _gemm_case(200, 300, 512, seed=3)
     sp, rs = to_dev_prep(sq.MXFP4, p, sq.LAYOUT_ROW_MAJOR)
