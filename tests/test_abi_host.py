@@ -26,6 +26,17 @@ def test_exports_every_declared_symbol():
     assert L.sharq_abi_version() == sq.ABI_VERSION
 
 
+def test_yardstick_library_loads():
+    """bench.py's measurement library (not part of the ABI) is built beside the
+    product library and exports its one entry point."""
+    path = os.path.join(os.path.dirname(sq.LIB_PATH), "libsharq_yardstick.so")
+    L = ctypes.CDLL(path)
+    assert hasattr(L, "sharq_yardstick_mfma_fp4")
+    # invalid arguments are refused before any launch
+    L.sharq_yardstick_mfma_fp4.restype = ctypes.c_int
+    assert L.sharq_yardstick_mfma_fp4(0, 1, 1, None, None, None) != 0
+
+
 def test_status_strings_and_sizes():
     for s in range(6):
         assert sq.status_str(s)
