@@ -172,6 +172,9 @@ template <int TBM, int TBN, class Stage, class Side = NoSide>
 __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN / 64],
                                               int wm, int wn, int h, int li, Side side = Side()) {
   constexpr int TN = TBN / 64;
+  // the step's LDS reads are issued at raised wavefront priority, so that they
+  // go out ahead of the MFMAs another wavefront of the SIMD is issuing
+  __builtin_amdgcn_s_setprio(1);
   int sas[2], sar[2], sws[TN], swd[TN];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -205,6 +208,8 @@ __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN
   // every LDS read of the step is issued before the first MFMA (left to
   // itself the compiler reuses one register set and waits on each A
   // fragment just before its MFMAs)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
