@@ -73,6 +73,7 @@ struct NStage {
   u32x4 w[TBN * 4];
   // E4M3 scales, two words (8 blocks) a row
   uint32_t sas[TBM * 2], sar[TBM * 2], sws[TBN * 2], swd[SH ? 4 : TBN * 2];
+  u32x4 spare[64];             // destination of padding loads
 };
 
 // Load plan of one stage.  Loads, in order: backbone (16-row dense chunk
@@ -80,21 +81,27 @@ struct NStage {
 // (16-row chunk loads), then the scale words (32 rows a load) of the
 // backbone, the residual, the sparse-path and the dense-path W view (the
 // last one only when the two views differ).  Wavefront w issues loads
-// w, w + NW, ...
+// w, w + NW, ...  Every operand's count is a multiple of NW (the index loads
+// are padded with loads through an empty resource into a spare area), so
+// load j of every wavefront belongs to the same operand and the issue
+// compiles without branches.
 template <int TBM, int TBN, int NW, int BB, bool SH>
 struct NPlan {
   static constexpr int kAS = BB == kBBDense ? TBM / 16 : TBM / 32;
   static constexpr int kAM = BB == kBBDense ? 0 : TBM / 64;
+  static constexpr int kAMp = (kAM + NW - 1) / NW * NW;
   static constexpr int kAR = TBM / 16, kW = TBN / 16;
   static constexpr int kSA = TBM / 32, kSW = TBN / 32, kSWD = SH ? 0 : TBN / 32;
-  static constexpr int b1 = kAS, b2 = b1 + kAM, b3 = b2 + kAR, b4 = b3 + kW;
+  static constexpr int b1 = kAS, b2 = b1 + kAMp, b3 = b2 + kAR, b4 = b3 + kW;
   static constexpr int b5 = b4 + kSA, b6 = b5 + kSA, b7 = b6 + kSW, kTotal = b7 + kSWD;
-  static constexpr int kPer = (kTotal + NW - 1) / NW;
-  static constexpr int kMinPerWave = kTotal / NW;   // waitcnt allowance per stage
+  static_assert(kAS % NW == 0 && kAR % NW == 0 && kW % NW == 0 && kSA % NW == 0 && kSW % NW == 0 &&
+                kSWD % NW == 0, "operand load counts are multiples of NW");
+  static constexpr int kPer = kTotal / NW;   // loads per wavefront and stage
 };
 
 struct NRsrc {
   OpStream as, am, ar, w, sas, sar, sws, swd;
+  i32x4 none;
 };
 
 template <int KPER>
@@ -119,32 +126,35 @@ __device__ __forceinline__ void nv_plan(const GemmArgs &a, int64_t m0, int64_t n
   R.sar = op_stream(a.r_scales, a.ld_rs, a.r_ksm, a.m, m0, steps, 8);
   R.sws = op_stream(a.ws_scales, a.ld_wss, a.w_ksm, a.n, n0, steps, 8);
   if (!SH) R.swd = op_stream(a.wd_scales, a.ld_wds, a.w_ksm, a.n, n0, steps, 8);
+  R.none = make_rsrc(a.w_codes, 0u);
   // dense chunk loads: lane l -> row l / 4 of the 16, logical chunk placed at
   // LDS slot l (the lds_slot swizzle); scale word d of a load: row d / 2, half d & 1
   const int drow = lane >> 2, dchunk = (lane & 3) ^ ((lane >> 4) & 3);
 #pragma unroll
   for (int j = 0; j < P::kPer; ++j) {
-    const int q = wave + NW * j;
+    const int q0 = NW * j, q = wave + q0;
     uint32_t v = 0;
-    if (q < P::b1) {
+    if (q0 < P::b1) {
       if (BB == kBBDense) v = (uint32_t)(16 * q + drow) * R.as.row_stride + dchunk * 16;
       else v = (uint32_t)(32 * q + (lane >> 1)) * R.as.row_stride + (lane & 1) * 16;
-    } else if (q < P::b2) {
-      v = (uint32_t)(64 * (q - P::b1) + lane) * R.am.row_stride;
-    } else if (q < P::b3) {
+    } else if (q0 < P::b2) {
+      v = q - P::b1 < P::kAM ? (uint32_t)(64 * (q - P::b1) + lane) * R.am.row_stride : 0u;
+    } else if (q0 < P::b3) {
       v = (uint32_t)(16 * (q - P::b2) + drow) * R.ar.row_stride + dchunk * 16;
-    } else if (q < P::b4) {
+    } else if (q0 < P::b4) {
       v = (uint32_t)(16 * (q - P::b3) + drow) * R.w.row_stride + dchunk * 16;
-    } else if (q < P::kTotal) {
-      const int d = 64 * (q < P::b5 ? q - P::b4 : q < P::b6 ? q - P::b5 : q < P::b7 ? q - P::b6 : q - P::b7) + lane;
-      const uint32_t rs = q < P::b5 ? R.sas.row_stride : q < P::b6 ? R.sar.row_stride
-                          : q < P::b7 ? R.sws.row_stride : R.swd.row_stride;
+    } else {
+      const int d = 64 * (q0 < P::b5 ? q - P::b4 : q0 < P::b6 ? q - P::b5 : q0 < P::b7 ? q - P::b6 : q - P::b7) + lane;
+      const uint32_t rs = q0 < P::b5 ? R.sas.row_stride : q0 < P::b6 ? R.sar.row_stride
+                          : q0 < P::b7 ? R.sws.row_stride : R.swd.row_stride;
       v = (uint32_t)(d >> 1) * rs + (d & 1) * 4;
     }
     O.voff[j] = v;
   }
 }
 
+// The conditions on q0 = NW j are compile-time constants: every load is
+// unconditional.
 template <int TBM, int TBN, int NW, int BB, bool SH>
 __device__ __forceinline__ void nv_issue(const NRsrc &R, const NOffs<NPlan<TBM, TBN, NW, BB, SH>::kPer> &O,
                                          int wave, int kt, const NStage<TBM, TBN, BB, SH> &S) {
@@ -153,19 +163,31 @@ __device__ __forceinline__ void nv_issue(const NRsrc &R, const NOffs<NPlan<TBM, 
   const uint32_t base = lds_addr(&S);
   constexpr uint32_t oam = offsetof(St, am), oar = offsetof(St, ar), ow = offsetof(St, w);
   constexpr uint32_t osas = offsetof(St, sas), osar = offsetof(St, sar);
-  constexpr uint32_t osws = offsetof(St, sws), oswd = offsetof(St, swd);
+  constexpr uint32_t osws = offsetof(St, sws), oswd = offsetof(St, swd), osp = offsetof(St, spare);
   const uint32_t t = (uint32_t)kt;
 #pragma unroll
   for (int j = 0; j < P::kPer; ++j) {
-    const int q = wave + NW * j;
-    if (q < P::b1) b2l16(R.as.rsrc, O.voff[j], t * R.as.step, base + q * 1024);
-    else if (q < P::b2) b2l16(R.am.rsrc, O.voff[j], t * R.am.step, base + oam + (q - P::b1) * 1024);
-    else if (q < P::b3) b2l16(R.ar.rsrc, O.voff[j], t * R.ar.step, base + oar + (q - P::b2) * 1024);
-    else if (q < P::b4) b2l16(R.w.rsrc, O.voff[j], t * R.w.step, base + ow + (q - P::b3) * 1024);
-    else if (q < P::b5) b2l4(R.sas.rsrc, O.voff[j], t * R.sas.step, base + osas + (q - P::b4) * 256);
-    else if (q < P::b6) b2l4(R.sar.rsrc, O.voff[j], t * R.sar.step, base + osar + (q - P::b5) * 256);
-    else if (q < P::b7) b2l4(R.sws.rsrc, O.voff[j], t * R.sws.step, base + osws + (q - P::b6) * 256);
-    else if (q < P::kTotal) b2l4(R.swd.rsrc, O.voff[j], t * R.swd.step, base + oswd + (q - P::b7) * 256);
+    const int q0 = NW * j, q = wave + q0;
+    if (q0 < P::b1) {
+      b2l16(R.as.rsrc, O.voff[j], t * R.as.step, base + q * 1024);
+    } else if (q0 < P::b2) {
+      // index loads padded to NW: the padding ones read nothing into the spare area
+      const bool real = q - P::b1 < P::kAM;
+      b2l16(real ? R.am.rsrc : R.none, O.voff[j], real ? t * R.am.step : 0u,
+            base + (real ? oam + (q - P::b1) * 1024 : osp));
+    } else if (q0 < P::b3) {
+      b2l16(R.ar.rsrc, O.voff[j], t * R.ar.step, base + oar + (q - P::b2) * 1024);
+    } else if (q0 < P::b4) {
+      b2l16(R.w.rsrc, O.voff[j], t * R.w.step, base + ow + (q - P::b3) * 1024);
+    } else if (q0 < P::b5) {
+      b2l4(R.sas.rsrc, O.voff[j], t * R.sas.step, base + osas + (q - P::b4) * 256);
+    } else if (q0 < P::b6) {
+      b2l4(R.sar.rsrc, O.voff[j], t * R.sar.step, base + osar + (q - P::b5) * 256);
+    } else if (q0 < P::b7) {
+      b2l4(R.sws.rsrc, O.voff[j], t * R.sws.step, base + osws + (q - P::b6) * 256);
+    } else {
+      b2l4(R.swd.rsrc, O.voff[j], t * R.swd.step, base + oswd + (q - P::b7) * 256);
+    }
   }
 }
 
@@ -200,6 +222,8 @@ template <int TBM, int TBN, int BB, bool SH>
 __device__ __forceinline__ void nv_compute(const NStage<TBM, TBN, BB, SH> &S,
                                            v16f (&acc)[2][TBN / 64], int wm, int wn, int h, int li) {
   constexpr int TN = TBN / 64;
+  // the step's LDS reads go out at raised wavefront priority
+  __builtin_amdgcn_s_setprio(1);
   // scale words: lane half h takes word h of each row (blocks 4h .. 4h + 3);
   // pair p holds blocks 4h + 2p, 4h + 2p + 1
   v2h sa_s[2][2], sa_r[2][2], sw_s[TN][2], sw_d[TN][2];
@@ -258,15 +282,37 @@ __device__ __forceinline__ void nv_compute(const NStage<TBM, TBN, BB, SH> &S,
   const uint32_t sel_index = h ? 0x07030501u : 0x06020400u;
   (void)sel_codes;
   (void)sel_index;
+  // With 128-column tiles every LDS read of the step goes first (both
+  // halves), then the arithmetic; 256-column tiles have no registers to spare
+  // for that and read each half just before its arithmetic.
+  constexpr bool kHoist = TN <= 2;
+  u32x4 caq[2][2], crq[2][2], cwq[2][TN];
+  auto read_half = [&](int q) {
+    const int cc = 2 * h + q;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      crq[q][it] = S.ar[lds_slot(ra[it], cc)];
+      if (BB == kBBDense) caq[q][it] = S.as[lds_slot(ra[it], cc)];
+    }
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) cwq[q][jt] = S.w[lds_slot(cb[jt], cc)];
+  };
+  if (kHoist) {
+    read_half(0);
+    read_half(1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int cc = 2 * h + q;       // dense chunk: slices 4q .. 4q + 3
+    if (!kHoist) read_half(q);
     u32x4 ca[2], cr[2], cw[TN];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      cr[it] = S.ar[lds_slot(ra[it], cc)];
+      cr[it] = crq[q][it];
       if (BB == kBBDense) {
-        ca[it] = S.as[lds_slot(ra[it], cc)];
+        ca[it] = caq[q][it];
       } else if (BB == kBBExpand) {
         uint32_t d[4];
         expand8(word(sc[it], 2 * q), word(sc[it], 2 * q + 1), q ? sm[it].y : sm[it].x, d);
@@ -274,7 +320,7 @@ __device__ __forceinline__ void nv_compute(const NStage<TBM, TBN, BB, SH> &S,
       }
     }
 #pragma unroll
-    for (int jt = 0; jt < TN; ++jt) cw[jt] = S.w[lds_slot(cb[jt], cc)];
+    for (int jt = 0; jt < TN; ++jt) cw[jt] = cwq[q][jt];
 
     v8h fb_prev[TN], fbd_prev[TN];
 #pragma unroll
@@ -384,7 +430,7 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a, uint3
   for (int kt = 0; kt < ksteps; ++kt) {
     // stages kt + 1 .. kt + STAGES - 2 may stay in flight
     const int ahead = min(ksteps - 1 - kt, STAGES - 2);
-    if (STAGES == 3 && ahead >= 1) wait_vmcnt<P::kMinPerWave>();
+    if (STAGES == 3 && ahead >= 1) wait_vmcnt<P::kPer>();
     else wait_vmcnt<0>();
     stage_barrier();
     if (kt + STAGES - 1 < ksteps) {
