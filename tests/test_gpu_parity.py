@@ -365,6 +365,31 @@ def test_dual_gemm_nv_vs_oracle(m, n, k):
             assert err <= GEMM_TOL, (layout, variant, err)
 
 
+def _random_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 300)), int(rng.integers(1, 400)), 128 * int(rng.integers(1, 5)))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("fmt", [sq.MXFP4, sq.NVFP4])
+def test_dual_gemm_random_shapes(fmt):
+    """Seeded random shapes (m 1-299, n 1-399, k 128-512, both layouts, every
+    variant): ragged tiles in every position, the decode / prefill switch at
+    m = 32 and single-step K."""
+    variants = NV_VARIANTS if fmt == sq.NVFP4 else (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)
+    for i, (m, n, k) in enumerate(_random_shapes(11 + fmt, 10)):
+        x, w, g, p, q = _gemm_case(m, n, k, seed=1000 + i, fmt=fmt, norm=bool(i % 2))
+        ref = oracle.dual_gemm(fmt, p, q)
+        layout = (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR)[i % 2]
+        sp, rs = to_dev_prep(fmt, p, layout)
+        wq = to_dev_weight(fmt, q, layout)
+        for variant in variants:
+            y = host(sq.dual_gemm(sp, rs, wq, variant=variant))
+            assert np.isfinite(y).all(), (m, n, k, layout, variant)
+            err = normwise(y, ref)
+            assert err <= GEMM_TOL, (m, n, k, layout, variant, err)
+
+
 def test_dual_gemm_nv_dense_and_expanded_bitwise_equal():
     """The expanded 2:4 backbone and the dense view feed identical MFMAs."""
     x, w, g, p, q = _gemm_case(200, 600, 512, seed=11, fmt=sq.NVFP4)
