@@ -121,6 +121,16 @@ def test_prepare_layouts(fmt, norm):
         check_prep(fmt, x, g, label=f"layout {layout}", layout=layout)
 
 
+@pytest.mark.parametrize("m,k", [(1030, 4096), (600, 2048), (530, 8192), (1027, 8192)])
+def test_prepare_mx_row_groups(m, k):
+    """Row counts that take the normalized preparation's 4- and 2-row
+    wavefront groups (ragged last group), in both layouts."""
+    x = si.activations("student_t4", m, k, max(1, k // 100), 50.0, seed=m + k)
+    g = si.gamma(k, seed=k + 1)
+    for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR):
+        check_prep(sq.MXFP4, x, g, label=f"m{m} k{k} layout {layout}", layout=layout)
+
+
 def test_prepare_mx_degenerate_rows():
     k = 256
     x = np.zeros((6, k), np.float32)
