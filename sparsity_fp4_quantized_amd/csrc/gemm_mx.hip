@@ -718,13 +718,18 @@ __global__ __launch_bounds__(256) void dual_gemm_decode_kernel(GemmArgs a) {
   const uint32_t vs0 = (uint32_t)lane * ss.row_stride;
   const uint32_t vs1 = (uint32_t)(64 + lane) * ss.row_stride;
 
+  // A rows 16..31 exist only for m > 16: with m <= 16 their load would read
+  // nothing (past the end) and only cost issue slots; the rows' LDS then holds
+  // stale codes whose scales are 0 (rows past m load as zeros), and those
+  // output rows are never stored
+  const bool two_a = a.m > 16;
   auto issue = [&](int kt, const St &S) {
     const uint32_t base = lds_addr(&S), t = (uint32_t)kt;
     b2l16(sw.rsrc, vw0, t * sw.step, base + offsetof(St, w) + (2 * wave) * 1024);
     b2l16(sw.rsrc, vw1, t * sw.step, base + offsetof(St, w) + (2 * wave + 1) * 1024);
     if (wave < 2) {
       b2l16(sa.rsrc, va0, t * sa.step, base + osa);
-      b2l16(sa.rsrc, va1, t * sa.step, base + osa + 1024);
+      if (two_a) b2l16(sa.rsrc, va1, t * sa.step, base + osa + 1024);
       b2l4(ss.rsrc, vs0, t * ss.step, base + oss);
     } else {
       b2l4(ss.rsrc, vs0, t * ss.step, base + oss);
