@@ -469,6 +469,12 @@ def main():
         if mf and "executed_TFLOP/s" in roofline:
             # executed MFMA rate against the rate FP4 MFMAs alone sustain on data
             roofline["executed_vs_fp4_mfma_yardstick"] = round(roofline["executed_TFLOP/s"] / mf["TFLOP/s"], 4)
+            # the published peak assumes the 2.4 GHz peak engine clock; the
+            # same peak at the clock the yardstick ran at under FP4 MFMA load
+            sclk = mf["clock_MHz"]
+            roofline["sclk_MHz_under_fp4_mfma_load"] = sclk
+            roofline["peak_at_that_sclk"] = round(peak * sclk / 2400.0, 1)
+            roofline["frac_at_that_sclk"] = round(roofline["achieved"] / (peak * sclk / 2400.0), 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x_np, W_np, g_np)
     print(json.dumps(out), flush=True)
