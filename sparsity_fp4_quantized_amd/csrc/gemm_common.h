@@ -107,14 +107,18 @@ __device__ __forceinline__ void xcd_tile(uint32_t id, uint32_t gm, uint32_t gn, 
 }
 
 // Host side: tile rows per band for a gm x gn grid of TBM x TBN tiles, so
-// that each XCD's block of tiles reads about as many A bytes (TBM k per tile
-// row, both paths) as W bytes (TBN k / 2 per tile column).
-inline uint32_t xcd_band_rows(int64_t gm, int64_t gn, int tbm, int tbn) {
+// that the tiles an XCD runs at one time read about as many A bytes (TBM k
+// per tile row, both paths) as W bytes (TBN k / 2 per tile column).  At one
+// time an XCD runs its 32 CUs x `resident` workgroups, or its whole share of
+// the grid if that is smaller; with several waves of tiles a band as tall as
+// the whole share made each wave's block of tiles tall and narrow (the
+// NVFP4-style GEMM fetched twice the bytes from beyond the L2).
+inline uint32_t xcd_band_rows(int64_t gm, int64_t gn, int tbm, int tbn, int resident) {
   const double per = (double)(gm * gn) / 8.0;
-  double want = per * tbn / (2.0 * tbm);
+  const double at_once = per < 32.0 * resident ? per : 32.0 * resident;
+  const double want = at_once * tbn / (2.0 * tbm);
   uint32_t GM = 1;
   while (GM < gm && (double)(2 * GM) * (2 * GM) <= want * 2.0) GM *= 2;
-  (void)gn;
   return GM;
 }
 

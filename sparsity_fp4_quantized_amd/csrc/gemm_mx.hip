@@ -313,7 +313,7 @@ template <int TBM, int TBN, int NW, int STAGES>
 void launch_dense(const GemmArgs &a, hipStream_t s) {
   const int64_t gm = (a.m + TBM - 1) / TBM, gn = (a.n + TBN - 1) / TBN;
   dual_gemm_dense_kernel<TBM, TBN, NW, STAGES>
-      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN));
+      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, TBN <= 128 ? 3 : 2));
 }
 
 // ---------------------------------------------------------------------------
@@ -548,7 +548,7 @@ template <int TBM, int TBN, int NW>
 void launch_decomp(const GemmArgs &a, hipStream_t s) {
   const int64_t gm = (a.m + TBM - 1) / TBM, gn = (a.n + TBN - 1) / TBN;
   dual_gemm_decomp_kernel<TBM, TBN, NW>
-      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN));
+      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, TBN >= 256 ? 1 : 2));
 }
 
 

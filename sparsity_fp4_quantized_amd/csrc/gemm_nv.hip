@@ -460,7 +460,7 @@ template <int TBN, int STAGES, int BB>
 void launch_nv(const GemmArgs &a, bool shared, hipStream_t s) {
   const int64_t gm = (a.m + 127) / 128, gn = (a.n + TBN - 1) / TBN;
   const dim3 grid((unsigned)(gm * gn)), block(256);
-  const uint32_t band = xcd_band_rows(gm, gn, 128, TBN);
+  const uint32_t band = xcd_band_rows(gm, gn, 128, TBN, TBN >= 256 ? 1 : 2);   // workgroups a CU holds
   if (shared)
     dual_gemm_nv_kernel<128, TBN, 4, STAGES, BB, true><<<grid, block, 0, s>>>(a, band);
   else
