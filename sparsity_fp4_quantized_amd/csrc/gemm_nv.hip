@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a, uint3
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < a.m) a.y[row * a.ld_y + col] = acc[it][jt][r] * ts;
+        if (row < a.m) __builtin_nontemporal_store(acc[it][jt][r] * ts, &a.y[row * a.ld_y + col]);
       }
     }
 }

@@ -28,6 +28,7 @@ namespace sharq {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -387,30 +388,45 @@ __device__ __forceinline__ void quantize_block_nv(const float xf[32], float s_t,
 // Stores of the lane's 32 k (block b of row `row`): every array of a view in
 // its layout (arr_off: row-major, or k-step-major with 4 blocks of 32 k per
 // 128-k step).  Scales: MXFP4 one byte, NVFP4 two.
-template <int FMT>
+//
+// NT: non-temporal stores, for kernels whose wavefronts write whole 128-byte
+// lines (four or sixteen rows of a k-step, or 64 blocks of one row).  The GEMM
+// that reads these arrays runs after this kernel and mostly on other XCDs, so
+// kept in this XCD's L2 they are only dirty lines to write back at the
+// kernel's end (measured: down_prefill 21.9 -> 17.3 us, qkv_prefill -3%).
+// With one row per wavefront a store of the k-step-major arrays writes
+// sixteen pieces of 2-32 bytes, and non-temporal partial lines made the
+// NVFP4 preparation 40% slower: those kernels store normally.
+template <bool NT, class T>
+__device__ __forceinline__ void put(T v, T *p) {
+  if (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int FMT, bool NT>
 __device__ __forceinline__ void store_scale(uint8_t *base, int64_t ld, int ksm, int64_t row,
                                             int64_t b, uint32_t v) {
   if (FMT == 0) {
-    base[arr_off(row, b >> 2, ld, ksm, 4) + (b & 3)] = (uint8_t)v;
+    put<NT>((uint8_t)v, base + arr_off(row, b >> 2, ld, ksm, 4) + (b & 3));
   } else {
-    *reinterpret_cast<uint16_t *>(base + arr_off(row, b >> 2, ld, ksm, 8) + 2 * (b & 3)) = (uint16_t)v;
+    put<NT>((uint16_t)v, reinterpret_cast<uint16_t *>(base + arr_off(row, b >> 2, ld, ksm, 8) + 2 * (b & 3)));
   }
 }
 
-template <int FMT>
+template <int FMT, bool NT>
 __device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int64_t b,
                                             const BlockOut &o) {
   const int64_t t = b >> 2, q = b & 3;
-  *reinterpret_cast<uint2 *>(a.s_codes + arr_off(row, t, a.ld_sc, a.s_ksm, 32) + 8 * q) =
-      make_uint2(o.s_comp[0], o.s_comp[1]);
-  *reinterpret_cast<uint32_t *>(a.meta + arr_off(row, t, a.ld_meta, a.s_ksm, 16) + 4 * q) = o.meta;
-  *reinterpret_cast<uint4 *>(a.r_codes + arr_off(row, t, a.ld_rc, a.r_ksm, 64) + 16 * q) =
-      make_uint4(o.r_codes[0], o.r_codes[1], o.r_codes[2], o.r_codes[3]);
+  put<NT>(u32x2{o.s_comp[0], o.s_comp[1]},
+          reinterpret_cast<u32x2 *>(a.s_codes + arr_off(row, t, a.ld_sc, a.s_ksm, 32) + 8 * q));
+  put<NT>(o.meta, reinterpret_cast<uint32_t *>(a.meta + arr_off(row, t, a.ld_meta, a.s_ksm, 16) + 4 * q));
+  put<NT>(u32x4{o.r_codes[0], o.r_codes[1], o.r_codes[2], o.r_codes[3]},
+          reinterpret_cast<u32x4 *>(a.r_codes + arr_off(row, t, a.ld_rc, a.r_ksm, 64) + 16 * q));
   if (a.s_dense)
-    *reinterpret_cast<uint4 *>(a.s_dense + arr_off(row, t, a.ld_sd, a.s_ksm, 64) + 16 * q) =
-        make_uint4(o.s_dense[0], o.s_dense[1], o.s_dense[2], o.s_dense[3]);
-  store_scale<FMT>(a.s_scales, a.ld_ss, a.s_ksm, row, b, o.s_scale);
-  store_scale<FMT>(a.r_scales, a.ld_rs, a.r_ksm, row, b, o.r_scale);
+    put<NT>(u32x4{o.s_dense[0], o.s_dense[1], o.s_dense[2], o.s_dense[3]},
+            reinterpret_cast<u32x4 *>(a.s_dense + arr_off(row, t, a.ld_sd, a.s_ksm, 64) + 16 * q));
+  store_scale<FMT, NT>(a.s_scales, a.ld_ss, a.s_ksm, row, b, o.s_scale);
+  store_scale<FMT, NT>(a.r_scales, a.ld_rs, a.r_ksm, row, b, o.r_scale);
 }
 
 __device__ __forceinline__ float nv_tensor_scale(const float *ts) {
@@ -516,7 +532,7 @@ __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
     if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
     quantize_block_nv(xf, s_t, o);
   }
-  store_block<FMT>(a, row, b, o);
+  store_block<FMT, (R >= 4)>(a, row, b, o);
 }
 
 // No normalization: blocks are independent.  A wavefront takes R rows x
@@ -544,7 +560,7 @@ __global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chu
     if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
     quantize_block_nv(xf, s_t, o);
   }
-  store_block<FMT>(a, row, b, o);
+  store_block<FMT, true>(a, row, b, o);
 }
 
 // NVFP4 tensor amax of x_n.  fp32 bit patterns of non-negative values order
@@ -738,7 +754,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(QuantArgs a) {
   }
   *reinterpret_cast<uint4 *>(a.codes + arr_off(row, b >> 2, a.ld_c, a.ksm, 64) + 16 * (b & 3)) =
       make_uint4(q[0], q[1], q[2], q[3]);
-  store_scale<FMT>(a.scales, a.ld_s, a.ksm, row, b, scales);
+  store_scale<FMT, false>(a.scales, a.ld_s, a.ksm, row, b, scales);
 }
 
 template <int FMT>
