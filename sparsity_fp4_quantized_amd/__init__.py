@@ -280,24 +280,44 @@ def prepare(x, gamma=None, eps: float = 1e-5, fmt: int = MXFP4, dense_backbone: 
     return sp, rs
 
 
-def prepare_into(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None):
-    """sharq_prepare into caller-provided buffers (nothing is allocated)."""
+class BoundCall:
+    """One library call with its arguments marshalled once (pointers, sizes,
+    views and the stream, taken when it is bound): calling it only crosses into
+    the library, which launches the kernels.  For loops that run the same
+    buffers again and again; the tensors it was bound to must stay alive and
+    keep their storage."""
+    __slots__ = ("_fn", "_args", "_where", "_keep")
+
+    def __init__(self, fn, args, where, keep):
+        self._fn, self._args, self._where, self._keep = fn, args, where, keep
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != OK:
+            raise SharqError(status, self._where)
+
+
+def bind_prepare(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None) -> BoundCall:
+    """sharq_prepare into caller-provided buffers, bound for repeated calls."""
     x = _bits16(x)
     g = None if gamma is None else _bits16(gamma)
     m, k = x.shape
     vs, vr = sp.view(), rs.view()
-    _check(lib().sharq_prepare(sp.fmt, x.data_ptr(), m, k, _ld(x), _ptr(g), float(eps),
-                               ctypes.byref(vs), ctypes.byref(vr), _stream_ptr(stream)),
-           "sharq_prepare")
+    args = (ctypes.c_int(sp.fmt), ctypes.c_void_p(x.data_ptr()), ctypes.c_int64(m), ctypes.c_int64(k),
+            ctypes.c_int64(_ld(x)), ctypes.c_void_p(_ptr(g)), ctypes.c_float(float(eps)),
+            ctypes.byref(vs), ctypes.byref(vr), _stream_ptr(stream))
+    return BoundCall(lib().sharq_prepare, args, "sharq_prepare", (x, g, sp, rs, vs, vr))
 
 
-def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AUTO,
-              w_dense_scales=None, out=None, stream=None):
-    """Y = deq(backbone) deq(W)^T + deq(residual) deq(W)^T, fp32 [m, n]."""
-    torch = _torch()
+def prepare_into(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None):
+    """sharq_prepare into caller-provided buffers (nothing is allocated)."""
+    bind_prepare(x, gamma, eps, sp, rs, stream)()
+
+
+def bind_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, out, variant: int = GEMM_AUTO,
+                   w_dense_scales=None, stream=None) -> BoundCall:
+    """sharq_dual_gemm into `out` (fp32 [m, n]), bound for repeated calls."""
     m, k, n = sp.rows, sp.k, w.rows
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=w.codes.device)
     wv_s = w.view()
     if w_dense_scales is not None:
         wv_d = FP4ViewC.from_buffer_copy(wv_s)
@@ -306,7 +326,18 @@ def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AU
     else:
         wv_d = wv_s
     vs, vr = sp.view(), rs.view()
-    _check(lib().sharq_dual_gemm(sp.fmt, ctypes.byref(vs), ctypes.byref(vr), ctypes.byref(wv_s),
-                                 ctypes.byref(wv_d), m, n, k, out.data_ptr(), _ld(out),
-                                 variant, _stream_ptr(stream)), "sharq_dual_gemm")
+    args = (ctypes.c_int(sp.fmt), ctypes.byref(vs), ctypes.byref(vr), ctypes.byref(wv_s), ctypes.byref(wv_d),
+            ctypes.c_int64(m), ctypes.c_int64(n), ctypes.c_int64(k), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_int64(_ld(out)), ctypes.c_int(variant), _stream_ptr(stream))
+    return BoundCall(lib().sharq_dual_gemm, args, "sharq_dual_gemm",
+                     (sp, rs, w, out, w_dense_scales, vs, vr, wv_s, wv_d))
+
+
+def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AUTO,
+              w_dense_scales=None, out=None, stream=None):
+    """Y = deq(backbone) deq(W)^T + deq(residual) deq(W)^T, fp32 [m, n]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((sp.rows, w.rows), dtype=torch.float32, device=w.codes.device)
+    bind_dual_gemm(sp, rs, w, out, variant, w_dense_scales, stream)()
     return out

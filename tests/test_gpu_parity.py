@@ -179,6 +179,31 @@ def test_prepare_deterministic():
         assert torch.equal(t1, t2)
 
 
+
+def test_bound_calls_match_one_shot_calls():
+    """bind_prepare / bind_dual_gemm (arguments marshalled once, as bench.py
+    runs them) give the bytes of the one-shot calls, call after call, and
+    write into the buffers they were bound to."""
+    w = si.WORKLOADS["qkv_prefill"]
+    x = dev16(si.workload_x(w, m=300))
+    g = dev16(si.workload_gamma(w))
+    wq = sq.quantize_weight(dev16(si.workload_w(w, n=200)))
+    sp0, rs0 = sq.prepare(x, g, dense_backbone=True)
+    y0 = sq.dual_gemm(sp0, rs0, wq)
+    sp, rs = sq.alloc_prepared(sq.MXFP4, 300, w.k, DEV, dense_backbone=True)
+    y = torch.full_like(y0, float("nan"))
+    prep, gemm = sq.bind_prepare(x, g, 1e-5, sp, rs), sq.bind_dual_gemm(sp, rs, wq, y)
+    for _ in range(3):
+        prep()
+        gemm()
+        torch.cuda.synchronize()
+        for t1, t2 in [(sp.codes, sp0.codes), (sp.meta, sp0.meta), (sp.scales, sp0.scales),
+                       (sp.dense_codes, sp0.dense_codes), (rs.codes, rs0.codes), (rs.scales, rs0.scales)]:
+            assert torch.equal(t1, t2)
+        assert torch.equal(y, y0)
+        y.fill_(float("nan"))
+
+
 # ------------------------------------------------------------ weights
 @pytest.mark.parametrize("fmt,n,k", [(0, 256, 256), (0, 6144, 4096), (0, 33, 96), (1, 256, 256),
                                      (1, 1000, 4096)])
