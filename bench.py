@@ -298,6 +298,109 @@ def cpu_baseline(w: si.Workload, x, W, g, seconds: float = 12.0) -> dict:
                        f"per-row and per-output rates: {step_s:.1f} s")}
 
 
+CHAIN_LAYERS = 3     # weight copies cycled, so that no linear's W stays in the 256 MB cache
+
+
+def chain_main(args):
+    """Decoder-layer linear chain: Llama-3.1-8B's QKV -> O -> gate+up -> down,
+    at prefill (2048 tokens) and decode (16 tokens), with SharQ (preparation +
+    dual GEMM, MXFP4, fp32 Y) against the vendor GEMMs on the same shapes:
+    bf16 (torch.nn.functional.linear -> hipBLASLt, bf16 out) and FP8 E4M3
+    with per-tensor scales (torch._scaled_mm, bf16 out), the latter also with
+    the activation's dynamic quantization (amax, scale, cast) counted.  The
+    baselines get no RMSNorm, SharQ's preparation includes it where the layer
+    has one.  Speed only: accuracy needs the model's weights.  Weights: one
+    seeded N(0, 0.02) draw per linear, and CHAIN_LAYERS row-rotated copies that
+    the timed loop cycles through.  Prints one JSON line."""
+    import torch
+    import torch.nn.functional as F
+    import sparsity_fp4_quantized_amd as sq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    reps, warm = max(args.steps // 4, 10), max(args.warmup // 4, 5)
+    fp8 = torch.float8_e4m3fn
+    one = torch.ones((), dtype=torch.float32, device=dev)
+
+    def batch_us(fn):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    # weights: bf16, FP8 (per-tensor scale) and the SharQ payload, per layer copy
+    wts = {}
+    for lin in si.LAYER_LINEARS:
+        w = si.layer_workload(lin, 16)
+        W0 = torch.from_numpy(si.workload_w(w).view(np.int16)).to(dev).view(torch.bfloat16)
+        copies = [torch.roll(W0, shifts=7 * l, dims=0).contiguous() for l in range(CHAIN_LAYERS)]
+        ws = [(Wl.abs().amax().float() / 448.0) for Wl in copies]
+        w8 = [(Wl.float() / sc).to(fp8) for Wl, sc in zip(copies, ws)]
+        wq = [sq.quantize_weight(Wl.view(torch.int16)) for Wl in copies]
+        wts[lin] = (copies, w8, ws, wq)
+    torch.cuda.synchronize()
+
+    result = {"metric": "Llama-3.1-8B decoder-layer linear chain (QKV, O, gate+up, down) time",
+              "unit": "us", "higher_is_better": False, "layers_cycled": CHAIN_LAYERS,
+              "steps": reps, "warmup": warm, "data": "synthetic (seeded activations, N(0,0.02) weights)"}
+    for phase, m in (("prefill", 2048), ("decode", 16)):
+        runs = {"sharq": [], "bf16": [], "fp8": [], "fp8_with_act_quant": []}
+        per = {}
+        for lin in si.LAYER_LINEARS:
+            w = si.layer_workload(lin, m)
+            copies, w8, ws, wq = wts[lin]
+            x = torch.from_numpy(si.workload_x(w).view(np.int16)).to(dev)
+            g = None if not w.norm else torch.from_numpy(si.workload_gamma(w).view(np.int16)).to(dev)
+            xb = x.view(torch.bfloat16)
+            xs = xb.abs().amax().float() / 448.0
+            x8 = (xb.float() / xs).to(fp8)
+            sp, rs = sq.alloc_prepared(sq.MXFP4, m, w.k, dev, dense_backbone=True)
+            y = torch.empty((m, w.n), dtype=torch.float32, device=dev)
+            calls = [(sq.bind_prepare(x, g, 1e-5, sp, rs), sq.bind_dual_gemm(sp, rs, wq[l], y))
+                     for l in range(CHAIN_LAYERS)]
+
+            def sharq(i, calls=calls):
+                p, q = calls[i % CHAIN_LAYERS]
+                p()
+                q()
+
+            def bf16(i, xb=xb, copies=copies):
+                F.linear(xb, copies[i % CHAIN_LAYERS])
+
+            def f8(i, x8=x8, xs=xs, w8=w8, ws=ws):
+                torch._scaled_mm(x8, w8[i % CHAIN_LAYERS].t(), xs, ws[i % CHAIN_LAYERS], out_dtype=torch.bfloat16)
+
+            def f8q(i, xb=xb, w8=w8, ws=ws):
+                s_ = xb.abs().amax().float() / 448.0
+                q8 = (xb / s_).to(fp8)
+                torch._scaled_mm(q8, w8[i % CHAIN_LAYERS].t(), s_, ws[i % CHAIN_LAYERS], out_dtype=torch.bfloat16)
+
+            fns = {"sharq": sharq, "bf16": bf16, "fp8": f8, "fp8_with_act_quant": f8q}
+            per[lin] = {}
+            for k, fn in fns.items():
+                try:
+                    per[lin][k] = round(batch_us(fn), 2)
+                    if runs[k] is not None:
+                        runs[k].append(fn)
+                except (RuntimeError, TypeError) as e:   # a torch build without this vendor path
+                    per[lin][k] = {"error": str(e)[:200]}
+                    runs[k] = None
+        chain = {}
+        for k, fns in runs.items():
+            if fns is not None and len(fns) == len(si.LAYER_LINEARS):
+                chain[k] = round(batch_us(lambda i, fns=fns: [fn(i) for fn in fns]), 2)
+        speed = {f"sharq_speedup_vs_{k}": round(chain[k] / chain["sharq"], 3) for k in chain if k != "sharq"}
+        result[phase] = {"m": m, "chain_us": chain, "per_linear_us": per, **speed}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +417,8 @@ def main():
                     help=f"run one {COPY_BYTES >> 20} MiB device copy first (counter calibration)")
     ap.add_argument("--no-yardsticks", action="store_true",
                     help="skip the plain-copy and vendor FP4 GEMM reference timings")
+    ap.add_argument("--chain", action="store_true",
+                    help="time the decoder-layer linear chain (SharQ vs bf16 / FP8 vendor GEMMs) instead")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="convert two rocprofv3 --pmc runs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -321,6 +426,9 @@ def main():
         traffic_convert(args, si.WORKLOADS[args.workload])
         return
 
+    if args.chain and args.gpus == 1:
+        chain_main(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the SharQ path here "
               "is single-GPU, and its sharding is described, not run.", file=sys.stderr)

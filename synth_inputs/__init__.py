@@ -61,6 +61,28 @@ WORKLOADS = {
 }
 
 
+# The four linear layers of one Llama-3.1-8B decoder layer, in order, for the
+# layer-chain benchmark: (K, N, input distribution, outlier channels, outlier
+# factor, RMSNorm before it).  QKV and gate+up read the residual stream
+# through an RMSNorm (heavy-tailed, with outlier channels, as qkv_prefill);
+# O reads the attention output (no norm; plain normal values); down reads
+# SiLU(gate) * up (as down_prefill).
+LAYER_LINEARS = {
+    "qkv": (4096, 6144, "student_t4", 41, 50.0, True),
+    "o": (4096, 4096, "normal", 0, 1.0, False),
+    "gate_up": (4096, 28672, "student_t4", 41, 50.0, True),
+    "down": (14336, 4096, "silu_like", 72, 30.0, False),
+}
+
+
+def layer_workload(linear: str, m: int, fmt: int = MXFP4) -> Workload:
+    """One linear of the decoder-layer chain with m tokens (2048: prefill, 16:
+    decode); seeds 20 + i for X and 1020 + i for W, i the linear's position."""
+    i = list(LAYER_LINEARS).index(linear)
+    k, n, dist, n_out, factor, norm = LAYER_LINEARS[linear]
+    return Workload(f"layer_{linear}_m{m}", m, k, n, dist, n_out, factor, norm, fmt, 20 + i, 1020 + i)
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values (finite) to bfloat16, nearest-even, as uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)

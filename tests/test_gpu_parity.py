@@ -310,12 +310,9 @@ def test_dual_gemm_exact_special_case():
     assert np.array_equal(y, ref)
 
 
-@pytest.mark.parametrize("name,samples", [("tiny", None), ("qkv_prefill", 4096),
-                                          ("down_prefill", 4096), ("decode_gate_up", 8192)])
-def test_end_to_end_workloads(name, samples):
-    """prepare + dual GEMM on the GPU vs the oracle's, at the full workload size
-    (sampled outputs for the large ones)."""
-    w = si.WORKLOADS[name]
+def _check_end_to_end(w, samples):
+    """prepare + dual GEMM (dense view and DECOMPRESS) on the GPU vs the
+    oracle's, at the workload's full size (sampled outputs when `samples`)."""
     x, W, g = si.workload_x(w), si.workload_w(w), si.workload_gamma(w)
     p = oracle.prepare(sq.MXFP4, x, g)
     q = oracle.quantize_weight(sq.MXFP4, W)
@@ -324,8 +321,8 @@ def test_end_to_end_workloads(name, samples):
     y = host(sq.dual_gemm(sp, rs, wq))
     y2 = host(sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS))
     if samples is None:
-        assert normwise(y2, oracle.dual_gemm(sq.MXFP4, p, q)) <= GEMM_TOL
         ref = oracle.dual_gemm(sq.MXFP4, p, q)
+        assert normwise(y2, ref) <= GEMM_TOL
         assert normwise(y, ref) <= GEMM_TOL
         return
     rng = np.random.default_rng(0)
@@ -340,6 +337,20 @@ def test_end_to_end_workloads(name, samples):
     # normalize by the largest |Y| over the sample (the full max is at least this)
     assert normwise(got, ref) <= GEMM_TOL
     assert normwise(y2[rows, cols], ref) <= GEMM_TOL
+
+
+@pytest.mark.parametrize("name,samples", [("tiny", None), ("qkv_prefill", 4096),
+                                          ("down_prefill", 4096), ("decode_gate_up", 8192)])
+def test_end_to_end_workloads(name, samples):
+    _check_end_to_end(si.WORKLOADS[name], samples)
+
+
+@pytest.mark.parametrize("linear,m,samples", [("o", 2048, 4096), ("gate_up", 2048, 4096),
+                                              ("qkv", 16, None), ("o", 16, None), ("down", 16, None)])
+def test_layer_chain_linears(linear, m, samples):
+    """The decoder-layer chain's other shapes (bench.py --chain): O projection
+    (no norm, plain normal input), gate+up at prefill, and the decode shapes."""
+    _check_end_to_end(si.layer_workload(linear, m), samples)
 
 
 def _padded(t, layout, extra_rows=0, extra_bytes=0):
