@@ -71,6 +71,8 @@ def lib():
         L.oracle_nv_tensor_scale.restype = ctypes.c_float
         L.oracle_rmsnorm_row.argtypes = [P, P, I64, ctypes.c_float, P]
         L.oracle_rmsnorm_row.restype = None
+        L.oracle_residual_add.argtypes = [P, P, I64, P]
+        L.oracle_residual_add.restype = None
         L.oracle_mask_group.argtypes = [P, P, P]
         L.oracle_mask_group.restype = None
         L.oracle_normalize.argtypes = [P, I64, I64, P, ctypes.c_float, P]
@@ -189,6 +191,23 @@ def prepare(fmt: int, x: np.ndarray, gamma: Optional[np.ndarray] = None, eps: fl
     if rc != 0:
         raise ValueError("oracle_prepare: bad arguments")
     return out
+
+
+def residual_add(h: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """x = bf16(fl32(h) + fl32(o)), elementwise (bf16 bit patterns)."""
+    h, o = _u16(h), _u16(o)
+    assert h.shape == o.shape
+    x = np.empty_like(h)
+    lib().oracle_residual_add(_p(h), _p(o), h.size, _p(x))
+    return x
+
+
+def prepare_residual(fmt: int, h: np.ndarray, o: np.ndarray, gamma: np.ndarray, eps: float = 1e-5,
+                     dense_backbone: bool = False):
+    """Residual add, then the preparation operator on the sum: returns the new
+    residual stream x = bf16(h + o) and prepare(fmt, x, gamma)."""
+    x = residual_add(h, o)
+    return x, prepare(fmt, x, gamma, eps, dense_backbone)
 
 
 def quantize_weight(fmt: int, w: np.ndarray) -> dict:

@@ -208,6 +208,25 @@ void oracle_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t k, flo
     }
 }
 
+/*
+ * Residual add in front of the norm (the fused neighbouring step): the
+ * residual stream h and the sublayer output o, both bf16, are added in
+ * binary32 and the sum is rounded to bf16, which is what an unfused bf16 add
+ * computes; the result is the new residual stream and the input of the
+ * RMSNorm.  (The abstract, sentence 5, has the preparation absorb the layer
+ * normalization into one operator; in a pre-norm decoder layer the residual
+ * add is the step in front of it.)
+ */
+void oracle_residual_add(const uint16_t *h, const uint16_t *o, int64_t n, uint16_t *x)
+{
+    for (int64_t i = 0; i < n; i++) {
+        float a = oracle_bf16_to_f32(h[i]);
+        float b = oracle_bf16_to_f32(o[i]);
+        float sum = a + b;
+        x[i] = oracle_f32_to_bf16(sum);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* 2:4 magnitude mask                                                  */
 /* ------------------------------------------------------------------ */

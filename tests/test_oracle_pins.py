@@ -129,6 +129,74 @@ def test_bf16_rounding_matches_torch():
     assert (si.f32_to_bf16_bits(f) == want).all()
 
 
+# ------------------------------------------------------------ residual add
+def _bf16_pairs(rng, n):
+    """Random finite bf16 bit patterns with exponents that keep sums finite,
+    plus pairs that cancel and pairs whose sum falls on a bf16 tie."""
+    e = rng.integers(60, 190, (2, n)).astype(np.uint32)
+    sign = rng.integers(0, 2, (2, n)).astype(np.uint32)
+    mant = rng.integers(0, 128, (2, n)).astype(np.uint32)
+    b = ((sign << 15) | (e << 7) | mant).astype(np.uint16)
+    h, o = b[0], b[1]
+    o[:100] = h[:100] ^ 0x8000                       # x + (-x)
+    # 1 + 2^-8 (exactly between two bf16 values): ties to even either way
+    h[100:110], o[100:110] = 0x3F80, 0x3B80
+    h[110:120], o[110:120] = 0x3F81, 0x3B80
+    return h, o
+
+
+def _bf16_rne_exact(v: float) -> int:
+    """bf16 bits of the binary32 value v, rounded to 8 significant bits with
+    ties to even by way of math.frexp (not the oracle's bit trick)."""
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    m, e = math.frexp(abs(v))                  # |v| = m 2^e, m in [0.5, 1)
+    q = round(m * 256)                         # half to even
+    r = math.ldexp(q, e - 8)
+    return int(np.float32(math.copysign(r, v)).view(np.uint32) >> 16)
+
+
+def test_residual_add_vs_exact_sum():
+    """bf16(fl32(h + o)): the exact sum (binary64, exact for these exponent
+    ranges) rounded to binary32 by numpy, then to bf16 by an independent
+    half-to-even rounding."""
+    rng = np.random.default_rng(11)
+    h, o = _bf16_pairs(rng, 20000)
+    got = oracle.residual_add(h, o)
+    hf, of = si.bf16_bits_to_f32(h).astype(np.float64), si.bf16_bits_to_f32(o).astype(np.float64)
+    want = np.array([_bf16_rne_exact(float(np.float32(a + b))) for a, b in zip(hf, of)], np.uint16)
+    assert (got == want).all()
+    assert (got[:100] == 0).all()                  # x + (-x) = +0
+    assert (got[100:110] == 0x3F80).all() and (got[110:120] == 0x3F82).all()
+
+
+def test_residual_add_vs_torch_bf16_add():
+    """torch's CPU bf16 add (fp32 sum, rounded to bf16) on the same pairs."""
+    rng = np.random.default_rng(12)
+    h, o = _bf16_pairs(rng, 200000)
+    th = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16)
+    to = torch.from_numpy(o.view(np.int16)).view(torch.bfloat16)
+    want = (th + to).view(torch.int16).numpy().view(np.uint16)
+    assert (oracle.residual_add(h, o) == want).all()
+    assert (oracle.residual_add(o, h) == want).all()     # commutes
+
+
+def test_prepare_residual_with_zero_update_is_prepare():
+    """o = +0: the residual stream passes through (-0 becomes +0) and the
+    preparation is the plain one of h."""
+    w = si.WORKLOADS["qkv_prefill"]
+    h = si.workload_x(w, m=24)
+    h[0, :3] = [0x8000, 0x0000, 0x3F80]
+    g = si.gamma(w.k, 77)
+    x, p = oracle.prepare_residual(oracle.MXFP4, h, np.zeros_like(h), g, dense_backbone=True)
+    want_x = h.copy()
+    want_x[want_x == 0x8000] = 0
+    assert (x == want_x).all()
+    q = oracle.prepare(oracle.MXFP4, want_x, g, dense_backbone=True)
+    for key in q:
+        assert (p[key] == q[key]).all(), key
+
+
 # ------------------------------------------------------------ tree sum
 def _tree_recursive(q):
     n = len(q)
