@@ -392,12 +392,31 @@ def chain_main(args):
                 except (RuntimeError, TypeError) as e:   # a torch build without this vendor path
                     per[lin][k] = {"error": str(e)[:200]}
                     runs[k] = None
+        # the residual add in front of QKV's norm: fused into the preparation
+        # (one kernel) against torch's bf16 add followed by the preparation
+        w = si.layer_workload("qkv", m)
+        h = torch.from_numpy(si.workload_x(w).view(np.int16)).to(dev)
+        o = torch.from_numpy(si.activations("normal", m, w.k, 0, 1.0, 40).view(np.int16)).to(dev)
+        g = torch.from_numpy(si.workload_gamma(w).view(np.int16)).to(dev)
+        xsum = torch.empty_like(h)
+        sp, rs = sq.alloc_prepared(sq.MXFP4, m, w.k, dev, dense_backbone=True)
+        fused = sq.bind_prepare_residual(h, o, g, 1e-5, sp, rs, xsum)
+        plain = sq.bind_prepare(xsum, g, 1e-5, sp, rs)
+        hb, ob, xb_ = h.view(torch.bfloat16), o.view(torch.bfloat16), xsum.view(torch.bfloat16)
+
+        def unfused(i):
+            torch.add(hb, ob, out=xb_)
+            plain()
+
+        residual_add = {"fused_us": round(batch_us(lambda i: fused()), 2),
+                        "torch_add_then_prepare_us": round(batch_us(unfused), 2)}
         chain = {}
         for k, fns in runs.items():
             if fns is not None and len(fns) == len(si.LAYER_LINEARS):
                 chain[k] = round(batch_us(lambda i, fns=fns: [fn(i) for fn in fns]), 2)
         speed = {f"sharq_speedup_vs_{k}": round(chain[k] / chain["sharq"], 3) for k in chain if k != "sharq"}
-        result[phase] = {"m": m, "chain_us": chain, "per_linear_us": per, **speed}
+        result[phase] = {"m": m, "chain_us": chain, "per_linear_us": per, **speed,
+                         "qkv_residual_add_and_prepare": residual_add}
     print(json.dumps(result), flush=True)
 
 

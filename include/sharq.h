@@ -193,6 +193,29 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
                            void *stream);
 
 /*
+ * The preparation operator with the residual add in front of its norm fused
+ * in (the step the pre-norm decoder layer runs right before the norm that
+ * the abstract, sentence 5, has the preparation absorb):
+ *   x = bf16(h + o)   elementwise: the bf16 residual stream h [m, k] (row
+ *                     stride ld_h) plus the bf16 sublayer output o (ld_o),
+ *                     added in fp32 and rounded to nearest even;
+ * x is stored to x_out (bf16, ld_out) as the new residual stream, and
+ * sharq_prepare's steps 1-4 follow on x with gamma_bf16 (required) and eps.
+ * One HBM pass over h and o.  x_out may be h itself (with ld_out == ld_h) or
+ * o (with ld_out == ld_o); any other overlap is undefined.
+ * MXFP4 only (SHARQ_ERR_UNSUPPORTED for NVFP4, whose tensor-scale pre-pass
+ * would need the sum first).
+ * Requirements: as sharq_prepare with gamma given, and for h, o and x_out:
+ * ld >= k, ld % 8 == 0, 16-byte aligned.
+ */
+sharq_status sharq_prepare_residual(sharq_format fmt, const uint16_t *h_bf16, int64_t ld_h,
+                                    const uint16_t *o_bf16, int64_t ld_o, uint16_t *x_out_bf16,
+                                    int64_t ld_out, int64_t m, int64_t k,
+                                    const uint16_t *gamma_bf16, float eps,
+                                    const sharq_fp4_view *sparse_out,
+                                    const sharq_fp4_view *resid_out, void *stream);
+
+/*
  * Dual-path GEMM (abstract, sentences 4 and 5):
  *   Y = deq(backbone) * deq(W)^T + deq(residual) * deq(W)^T
  * accumulated in fp32 and stored as fp32 [m, n] (row stride ld_y).  NVFP4:
@@ -234,7 +257,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 3
+#define SHARQ_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

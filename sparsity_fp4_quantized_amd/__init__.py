@@ -39,9 +39,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 # every symbol include/sharq.h declares
-EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_dual_gemm", "sharq_bytes",
-           "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 3
+EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_dual_gemm",
+           "sharq_bytes", "sharq_status_str", "sharq_abi_version")
+ABI_VERSION = 4
 
 
 class SharqError(RuntimeError):
@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.sharq_quantize_weight.restype = ctypes.c_int
         L.sharq_prepare.argtypes = [ctypes.c_int, P, I64, I64, I64, P, ctypes.c_float, V, V, P]
         L.sharq_prepare.restype = ctypes.c_int
+        L.sharq_prepare_residual.argtypes = [ctypes.c_int, P, I64, P, I64, P, I64, I64, I64, P,
+                                             ctypes.c_float, V, V, P]
+        L.sharq_prepare_residual.restype = ctypes.c_int
         L.sharq_dual_gemm.argtypes = [ctypes.c_int, V, V, V, V, I64, I64, I64, P, I64,
                                       ctypes.c_int, P]
         L.sharq_dual_gemm.restype = ctypes.c_int
@@ -312,6 +315,37 @@ def bind_prepare(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None) -> Bo
 def prepare_into(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None):
     """sharq_prepare into caller-provided buffers (nothing is allocated)."""
     bind_prepare(x, gamma, eps, sp, rs, stream)()
+
+
+def bind_prepare_residual(h, o, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, out, stream=None) -> BoundCall:
+    """sharq_prepare_residual: out = bf16(h + o) (the new residual stream; may
+    be h or o itself), then the preparation of out, bound for repeated calls."""
+    h, o, out, g = _bits16(h), _bits16(o), _bits16(out), _bits16(gamma)
+    m, k = h.shape
+    if tuple(o.shape) != (m, k) or tuple(out.shape) != (m, k):
+        raise ValueError("h, o and out must have the same shape")
+    vs, vr = sp.view(), rs.view()
+    args = (ctypes.c_int(sp.fmt), ctypes.c_void_p(h.data_ptr()), ctypes.c_int64(_ld(h)),
+            ctypes.c_void_p(o.data_ptr()), ctypes.c_int64(_ld(o)), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_int64(_ld(out)), ctypes.c_int64(m), ctypes.c_int64(k), ctypes.c_void_p(g.data_ptr()),
+            ctypes.c_float(float(eps)), ctypes.byref(vs), ctypes.byref(vr), _stream_ptr(stream))
+    return BoundCall(lib().sharq_prepare_residual, args, "sharq_prepare_residual",
+                     (h, o, out, g, sp, rs, vs, vr))
+
+
+def prepare_residual(h, o, gamma, eps: float = 1e-5, dense_backbone: bool = False,
+                     layout: Optional[int] = None, out=None, stream=None):
+    """Residual add fused into the preparation (MXFP4): returns (x, backbone,
+    residual) with x = bf16(h + o) written to `out` (a new tensor when None;
+    pass h to update the residual stream in place)."""
+    torch = _torch()
+    h = _bits16(h)
+    m, k = h.shape
+    if out is None:
+        out = torch.empty_like(h)
+    sp, rs = alloc_prepared(MXFP4, m, k, h.device, dense_backbone, layout)
+    bind_prepare_residual(h, o, gamma, eps, sp, rs, out, stream)()
+    return out, sp, rs
 
 
 def bind_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, out, variant: int = GEMM_AUTO,

@@ -20,6 +20,10 @@ struct PrepArgs {
   uint8_t *s_dense;  int64_t ld_sd;   // optional
   float *tensor_scale;                // NVFP4: [0] scale, [1] amax
   int s_ksm, r_ksm;                   // backbone / residual view k-step-major (every array)
+  // residual add in front of the norm (MXFP4 with normalization only):
+  // x = bf16(x + add), written to x_out, then prepared; add == nullptr: none
+  const uint16_t *add = nullptr;  int64_t ld_add = 0;
+  uint16_t *x_out = nullptr;      int64_t ld_xout = 0;
 };
 
 struct QuantArgs {

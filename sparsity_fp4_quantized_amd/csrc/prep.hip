@@ -485,6 +485,16 @@ __device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const
 
 // ---------------------------------------------------------------- kernels
 
+// A lane's 32 bf16 values as four 16-byte stores.  Plain stores: each one
+// writes a quarter of 32 lines, and the L2 merges the four quarters before the
+// lines leave it; non-temporal, the partial lines went out one by one (the
+// residual-add preparation took 20.9 against 16.5 us on the qkv shape).
+__device__ __forceinline__ void store32(uint16_t *p, const uint32_t w[16]) {
+  u32x4 *q = reinterpret_cast<u32x4 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+}
+
 // Workgroup = R rows x W wavefronts: lane l of wavefront w takes row q = l / L
 // (L = 64 / R lanes per row) and block w * L + l % L, so a wavefront stores R
 // consecutive rows of each 128-k step next to each other in the k-step-major
@@ -493,8 +503,11 @@ __device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const
 // values, then adjacent lanes of the row (butterfly over L lanes), then the W
 // wavefronts in LDS (padded to a power of two with zeros).  Lanes past the row
 // end (or past the last row) load a valid block of X and contribute +0; they
-// store nothing.
-template <int FMT, int R, int W>
+// store nothing.  ADD: the residual add in front of the norm, x = bf16(x +
+// add) (the binary32 sum rounded to nearest even), stored to x_out as the new
+// residual stream and prepared in place of X; x_out may be X itself or
+// `add`, since every lane reads its block before it writes it.
+template <int FMT, int R, int W, bool ADD = false>
 __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
   constexpr int L = 64 / R;
   __shared__ float part[R][W];
@@ -508,10 +521,19 @@ __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
   const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
   // gamma's loads go out with X's, so that they land during the row
   // reduction rather than after it (-4% on the qkv shape)
-  uint32_t xw[16], gw[16];
+  uint32_t xw[16], gw[16], ow[16];
   float xf[32];
   load32(a.x + lrow * a.ld_x + 32 * lb, xw);
+  if (ADD) load32(a.add + lrow * a.ld_add + 32 * lb, ow);
   load32(a.gamma + 32 * lb, gw);
+  if (ADD) {
+    float of[32];
+    unpack32(xw, xf);
+    unpack32(ow, of);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xw[i] = pack_bf16x2(xf[2 * i] + of[2 * i], xf[2 * i + 1] + of[2 * i + 1]);
+    if (has) store32(a.x_out + row * a.ld_xout + 32 * b, xw);
+  }
   unpack32(xw, xf);
   float s = lane_tree_sum<L>(has ? block_sumsq(xf) : 0.0f);
   if (lane % L == 0) part[q][wave] = s;
@@ -638,9 +660,9 @@ __global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *x, int64
 
 __global__ void zero_amax_kernel(float *ts) { ts[1] = 0.0f; }
 
-template <int FMT, int R, int W>
+template <int FMT, int R, int W, bool ADD>
 void launch_norm(const PrepArgs &a, hipStream_t s) {
-  prep_norm_kernel<FMT, R, W><<<dim3((unsigned)((a.m + R - 1) / R)), dim3(64 * W), 0, s>>>(a);
+  prep_norm_kernel<FMT, R, W, ADD><<<dim3((unsigned)((a.m + R - 1) / R)), dim3(64 * W), 0, s>>>(a);
 }
 
 template <int WPR>
@@ -651,13 +673,25 @@ void launch_amax_norm(const PrepArgs &a, hipStream_t s) {
 }
 
 // W = nblk / (64 / R) wavefronts per row group, rounded up to a power of two <= 8.
-template <int FMT, int R>
+template <int FMT, int R, bool ADD>
 void launch_norm_w(const PrepArgs &a, int64_t nblk, hipStream_t s) {
   const int64_t w = (nblk + 64 / R - 1) / (64 / R);
-  if (w <= 1) launch_norm<FMT, R, 1>(a, s);
-  else if (w <= 2) launch_norm<FMT, R, 2>(a, s);
-  else if (w <= 4) launch_norm<FMT, R, 4>(a, s);
-  else launch_norm<FMT, R, 8>(a, s);
+  if (w <= 1) launch_norm<FMT, R, 1, ADD>(a, s);
+  else if (w <= 2) launch_norm<FMT, R, 2, ADD>(a, s);
+  else if (w <= 4) launch_norm<FMT, R, 4, ADD>(a, s);
+  else launch_norm<FMT, R, 8, ADD>(a, s);
+}
+
+// the residual-add kernels exist for MXFP4 only (the entry point refuses NVFP4)
+template <int FMT, int R>
+void launch_norm_rows(const PrepArgs &a, int64_t nblk, hipStream_t s) {
+  if constexpr (FMT == 0) {
+    if (a.add) {
+      launch_norm_w<FMT, R, true>(a, nblk, s);
+      return;
+    }
+  }
+  launch_norm_w<FMT, R, false>(a, nblk, s);
 }
 
 template <int FMT>
@@ -686,9 +720,9 @@ hipError_t launch_prepare(const PrepArgs &a, hipStream_t s) {
     // Few rows (decode) keep one row per group, so that there
     // are more workgroups; NVFP4 too: its arithmetic, not its memory traffic,
     // sets its time, and fewer, larger workgroups were slower.
-    if (FMT == 0 && a.m >= 1024 && nblk <= 8 * 16) launch_norm_w<FMT, 4>(a, nblk, s);
-    else if (FMT == 0 && a.m >= 512 && nblk <= 8 * 32) launch_norm_w<FMT, 2>(a, nblk, s);
-    else launch_norm_w<FMT, 1>(a, nblk, s);
+    if (FMT == 0 && a.m >= 1024 && nblk <= 8 * 16) launch_norm_rows<FMT, 4>(a, nblk, s);
+    else if (FMT == 0 && a.m >= 512 && nblk <= 8 * 32) launch_norm_rows<FMT, 2>(a, nblk, s);
+    else launch_norm_rows<FMT, 1>(a, nblk, s);
   } else {
     if (FMT == 1) {
       const int64_t total = a.m * nblk;

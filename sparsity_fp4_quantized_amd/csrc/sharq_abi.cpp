@@ -111,9 +111,15 @@ sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int
                                      : sharq::launch_quantize_weight_nv(a, s));
 }
 
-sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
-                           int64_t ld_x, const uint16_t *gamma_bf16, float eps,
-                           const sharq_fp4_view *sp, const sharq_fp4_view *rs, void *stream) {
+namespace {
+
+// Validation and launch shared by sharq_prepare and sharq_prepare_residual
+// (add == nullptr: no residual add).
+sharq_status prepare_common(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
+                            int64_t ld_x, const uint16_t *gamma_bf16, float eps,
+                            const sharq_fp4_view *sp, const sharq_fp4_view *rs,
+                            const uint16_t *add, int64_t ld_add, uint16_t *x_out, int64_t ld_out,
+                            void *stream) {
   if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
   if (!x_bf16 || !sp || !rs) return SHARQ_ERR_NULL;
   if (m < 1 || k < 32 || k % 32 || ld_x < k) return SHARQ_ERR_SHAPE;
@@ -139,9 +145,40 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
              sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->scales, sp->ld_scales,
              rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
              sp->dense_codes, sp->ld_dense, sp->tensor_scale, ksm(sp), ksm(rs)};
+  a.add = add;
+  a.ld_add = ld_add;
+  a.x_out = x_out;
+  a.ld_xout = ld_out;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(fmt == SHARQ_MXFP4 ? sharq::launch_prepare_mx(a, s)
                                      : sharq::launch_prepare_nv(a, s));
+}
+
+}  // namespace
+
+sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
+                           int64_t ld_x, const uint16_t *gamma_bf16, float eps,
+                           const sharq_fp4_view *sp, const sharq_fp4_view *rs, void *stream) {
+  return prepare_common(fmt, x_bf16, m, k, ld_x, gamma_bf16, eps, sp, rs, nullptr, 0, nullptr, 0,
+                        stream);
+}
+
+sharq_status sharq_prepare_residual(sharq_format fmt, const uint16_t *h_bf16, int64_t ld_h,
+                                    const uint16_t *o_bf16, int64_t ld_o, uint16_t *x_out_bf16,
+                                    int64_t ld_out, int64_t m, int64_t k,
+                                    const uint16_t *gamma_bf16, float eps,
+                                    const sharq_fp4_view *sp, const sharq_fp4_view *rs,
+                                    void *stream) {
+  if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
+  if (fmt != SHARQ_MXFP4) return SHARQ_ERR_UNSUPPORTED;
+  if (!h_bf16 || !o_bf16 || !x_out_bf16 || !gamma_bf16) return SHARQ_ERR_NULL;
+  if (ld_o < k || ld_out < k) return SHARQ_ERR_SHAPE;
+  if (ld_o % 8 || ld_out % 8 || !aligned(o_bf16, 16) || !aligned(x_out_bf16, 16)) return SHARQ_ERR_ALIGN;
+  // in place on h or o only with that array's own row stride
+  if ((x_out_bf16 == h_bf16 && ld_out != ld_h) || (x_out_bf16 == o_bf16 && ld_out != ld_o))
+    return SHARQ_ERR_SHAPE;
+  return prepare_common(fmt, h_bf16, m, k, ld_h, gamma_bf16, eps, sp, rs, o_bf16, ld_o, x_out_bf16,
+                        ld_out, stream);
 }
 
 sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,

@@ -106,6 +106,36 @@ def test_prepare_validation(kwargs, status):
     assert prep(**kwargs) == status
 
 
+def prep_res(fmt=0, h=FAKE, ld_h=256, o=FAKE, ld_o=256, out=FAKE, ld_out=256, m=16, k=256,
+             gamma=FAKE, sp=None, rs=None):
+    sp = sp or view(ld_codes=64)
+    rs = rs or view(meta=None)
+    return sq.lib().sharq_prepare_residual(fmt, h, ld_h, o, ld_o, out, ld_out, m, k, gamma, 1e-5,
+                                           ctypes.byref(sp), ctypes.byref(rs), None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(fmt=1), sq.ERR_UNSUPPORTED),     # NVFP4: the tensor-scale pre-pass would need the sum
+    (dict(fmt=7), sq.ERR_UNSUPPORTED),
+    (dict(gamma=None), sq.ERR_NULL),       # the norm is part of the fused step
+    (dict(h=None), sq.ERR_NULL),
+    (dict(o=None), sq.ERR_NULL),
+    (dict(out=None), sq.ERR_NULL),
+    (dict(ld_o=128), sq.ERR_SHAPE),
+    (dict(ld_out=128), sq.ERR_SHAPE),
+    (dict(ld_o=260), sq.ERR_ALIGN),
+    (dict(o=FAKE + 2), sq.ERR_ALIGN),
+    (dict(out=FAKE + 8), sq.ERR_ALIGN),
+    (dict(ld_out=264), sq.ERR_SHAPE),      # in place on h (out == h) with another row stride
+    (dict(o=FAKE + 4096, ld_out=264, out=FAKE + 4096), sq.ERR_SHAPE),   # in place on o likewise
+    (dict(h=FAKE + 2), sq.ERR_ALIGN),      # then every sharq_prepare check on h and the views
+    (dict(m=0), sq.ERR_SHAPE),
+    (dict(sp=view(ld_codes=63)), sq.ERR_SHAPE),
+])
+def test_prepare_residual_validation(kwargs, status):
+    assert prep_res(**kwargs) == status
+
+
 def gemm(fmt=0, m=16, n=256, k=256, y=FAKE, ld_y=256, variant=0, sp=None, rs=None, ws=None,
          wd=None):
     sp = sp or view(ld_codes=64)

@@ -204,6 +204,71 @@ def test_bound_calls_match_one_shot_calls():
         y.fill_(float("nan"))
 
 
+
+def _compare_prep(label, sp, rs, ref, dense=True):
+    got = {"meta": host(sp.row_major("meta")), "s_codes": host(sp.row_major("codes")),
+           "s_scales": host(sp.row_major("scales")),
+           "r_codes": host(rs.row_major("codes")), "r_scales": host(rs.row_major("scales"))}
+    if dense:
+        got["s_dense"] = host(sp.row_major("dense_codes"))
+    for key, val in got.items():
+        assert np.array_equal(val, ref[key]), (label, key, int((val != ref[key]).sum()))
+
+
+@pytest.mark.parametrize("m,k,where", [(2048, 4096, "new"), (600, 2048, "h"), (37, 4096, "o"),
+                                       (1027, 8192, "new"), (5, 256, "h")])
+def test_prepare_residual(m, k, where):
+    """Residual add fused into the preparation: the new residual stream and
+    every prepared array byte for byte against the oracle (four, two and one
+    rows per wavefront; written to a new tensor, or in place on h or on o)."""
+    h = si.activations("student_t4", m, k, 41 if k >= 4096 else 4, 50.0, seed=31)
+    o = si.activations("normal", m, k, 0, 1.0, seed=32)
+    g = si.gamma(k, 33)
+    x_ref, ref = oracle.prepare_residual(sq.MXFP4, h, o, g, dense_backbone=True)
+    dh, do = dev16(h), dev16(o)
+    out = {"new": None, "h": dh, "o": do}[where]
+    x, sp, rs = sq.prepare_residual(dh, do, dev16(g), dense_backbone=True, out=out)
+    assert np.array_equal(host(x).view(np.uint16), x_ref), "residual stream"
+    if where == "h":
+        assert np.array_equal(host(dh).view(np.uint16), x_ref)
+    _compare_prep(f"m{m} k{k} {where}", sp, rs, ref)
+
+
+def test_prepare_residual_padded_rows_untouched():
+    """Row strides above k: the padding of the output rows is never written."""
+    m, k, ld = 300, 4096, 4096 + 64
+    h = si.activations("student_t4", m, k, 41, 50.0, seed=34)
+    o = si.activations("normal", m, k, 0, 1.0, seed=35)
+    g = si.gamma(k, 36)
+    x_ref, ref = oracle.prepare_residual(sq.MXFP4, h, o, g, dense_backbone=True)
+    big = torch.full((m, ld), 0x7A5A, dtype=torch.int16, device=DEV)
+    hb = torch.full((m, ld), 0, dtype=torch.int16, device=DEV)
+    hb[:, :k] = dev16(h)
+    x, sp, rs = sq.prepare_residual(hb[:, :k], dev16(o), dev16(g), dense_backbone=True, out=big[:, :k])
+    got = host(big).view(np.uint16)
+    assert np.array_equal(got[:, :k], x_ref)
+    assert (got[:, k:] == 0x7A5A).all()
+    _compare_prep("padded", sp, rs, ref)
+
+
+def test_bound_prepare_residual_repeats():
+    """bind_prepare_residual called again on its own output (a residual stream
+    that keeps growing) matches the oracle step after step."""
+    m, k = 64, 4096
+    h = si.activations("student_t4", m, k, 41, 50.0, seed=37)
+    o = si.activations("normal", m, k, 0, 1.0, seed=38)
+    g = si.gamma(k, 39)
+    dh = dev16(h)
+    sp, rs = sq.alloc_prepared(sq.MXFP4, m, k, DEV, dense_backbone=True)
+    call = sq.bind_prepare_residual(dh, dev16(o), dev16(g), 1e-5, sp, rs, dh)
+    x = h
+    for step in range(3):
+        call()
+        x, ref = oracle.prepare_residual(sq.MXFP4, x, o, g, dense_backbone=True)
+        assert np.array_equal(host(dh).view(np.uint16), x), step
+        _compare_prep(f"step {step}", sp, rs, ref)
+
+
 # ------------------------------------------------------------ weights
 @pytest.mark.parametrize("fmt,n,k", [(0, 256, 256), (0, 6144, 4096), (0, 33, 96), (1, 256, 256),
                                      (1, 1000, 4096)])
