@@ -73,6 +73,10 @@ def lib():
         L.oracle_rmsnorm_row.restype = None
         L.oracle_residual_add.argtypes = [P, P, I64, P]
         L.oracle_residual_add.restype = None
+        L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+        L.oracle_silu_mul.argtypes = [P, I64, P, I64, I64, I64, P]
+        L.oracle_silu_mul.restype = None
         L.oracle_mask_group.argtypes = [P, P, P]
         L.oracle_mask_group.restype = None
         L.oracle_normalize.argtypes = [P, I64, I64, P, ctypes.c_float, P]
@@ -208,6 +212,29 @@ def prepare_residual(fmt: int, h: np.ndarray, o: np.ndarray, gamma: np.ndarray, 
     residual stream x = bf16(h + o) and prepare(fmt, x, gamma)."""
     x = residual_add(h, o)
     return x, prepare(fmt, x, gamma, eps, dense_backbone)
+
+
+def f64_to_bf16(v: float) -> int:
+    return lib().oracle_f64_to_bf16(float(v))
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """x = bf16(silu(g) * u) from fp32 gate and up [m, k] (one rounding of a
+    binary64 evaluation)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    assert g.shape == u.shape and g.ndim == 2
+    m, k = g.shape
+    x = np.empty((m, k), np.uint16)
+    lib().oracle_silu_mul(_p(g), k, _p(u), k, m, k, _p(x))
+    return x
+
+
+def prepare_silu_mul(fmt: int, g: np.ndarray, u: np.ndarray, dense_backbone: bool = False):
+    """SiLU(gate) * up, then the preparation operator without a norm (the
+    down projection's input): returns x and prepare(fmt, x)."""
+    x = silu_mul(g, u)
+    return x, prepare(fmt, x, None, 1e-5, dense_backbone)
 
 
 def quantize_weight(fmt: int, w: np.ndarray) -> dict:

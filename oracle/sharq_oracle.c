@@ -227,6 +227,45 @@ void oracle_residual_add(const uint16_t *h, const uint16_t *o, int64_t n, uint16
     }
 }
 
+/*
+ * bf16 nearest-even of a double: directly from the double for |v| >= 2^-126
+ * (8 significant bits, ties to even); below 2^-126, the bf16 subnormal range,
+ * through float (the double rounded to float, then to bf16).
+ */
+uint16_t oracle_f64_to_bf16(double v)
+{
+    if (v == 0.0)
+        return signbit(v) ? 0x8000u : 0u;
+    int e;
+    double m = frexp(fabs(v), &e);            /* |v| = m 2^e, m in [0.5, 1) */
+    if (e - 1 < -126)
+        return oracle_f32_to_bf16((float)v);
+    double q = rint(ldexp(m, 8));             /* 8 significant bits, nearest even */
+    double r = ldexp(q, e - 8);
+    return oracle_f32_to_bf16((float)(signbit(v) ? -r : r));   /* exact: r has 8 bits */
+}
+
+/*
+ * SiLU(gate) * up in front of the down projection (the other fused
+ * neighbouring step): the gate and up halves of the gate+up projection's
+ * fp32 output; x = bf16 of g / (1 + exp(-g)) * u evaluated in binary64 and
+ * rounded once.  The abstract leaves the MLP's arithmetic open; one rounding
+ * of a double evaluation is the plainest reading, and the one a GPU can
+ * reproduce exactly without matching this file's exp bit for bit.
+ */
+void oracle_silu_mul(const float *g, int64_t ld_g, const float *u, int64_t ld_u, int64_t m,
+                     int64_t k, uint16_t *x)
+{
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t i = 0; i < k; i++) {
+            double gd = (double)g[r * ld_g + i];
+            double ud = (double)u[r * ld_u + i];
+            double s = gd / (1.0 + exp(-gd));
+            double v = s * ud;
+            x[r * k + i] = oracle_f64_to_bf16(v);
+        }
+}
+
 /* ------------------------------------------------------------------ */
 /* 2:4 magnitude mask                                                  */
 /* ------------------------------------------------------------------ */

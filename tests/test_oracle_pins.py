@@ -197,6 +197,68 @@ def test_prepare_residual_with_zero_update_is_prepare():
         assert (p[key] == q[key]).all(), key
 
 
+# ------------------------------------------------------------ SiLU(gate) * up
+def _bf16_of_decimal(v) -> int:
+    """bf16 bits nearest (ties to even) to the Decimal v, in Decimal arithmetic."""
+    import decimal
+    if v == 0:
+        return 0x8000 if v.is_signed() else 0
+    a = abs(v)
+    e = a.adjusted() * 10 // 3 - 2                # a first guess of floor(log2 a)
+    two = decimal.Decimal(2)
+    while two ** (e + 1) <= a:
+        e += 1
+    while two ** e > a:
+        e -= 1
+    e = max(e, -126)                              # bf16 subnormals share 2^-133 steps
+    q = (a / two ** (e - 7)).quantize(decimal.Decimal(1), rounding=decimal.ROUND_HALF_EVEN)
+    r = float(q * two ** (e - 7))
+    bits = int(np.float32(r).view(np.uint32) >> 16)
+    return bits | (0x8000 if v < 0 else 0)
+
+
+def test_silu_mul_vs_decimal():
+    """x = bf16(silu(g) * u): against a 60-digit Decimal evaluation rounded to
+    bf16 by Decimal arithmetic, on random fp32 gates and ups over a wide range
+    (far from bf16 midpoints the two must agree exactly)."""
+    import decimal
+    decimal.getcontext().prec = 60
+    rng = np.random.default_rng(21)
+    g = np.concatenate([rng.normal(0, 3, 3000), rng.uniform(-40, 40, 1000), [0.0, -0.0, 1e-30, -88.0]])
+    u = np.concatenate([rng.normal(0, 1, 3000) * 10.0 ** rng.integers(-6, 4, 3000),
+                        rng.normal(0, 5, 1000), [3.0, 3.0, 2.0, 1.0]])
+    g, u = g.astype(np.float32)[None, :], u.astype(np.float32)[None, :]
+    got = oracle.silu_mul(g, u)[0]
+    one = decimal.Decimal(1)
+    for i in range(g.shape[1]):
+        gd, ud = decimal.Decimal(float(g[0, i])), decimal.Decimal(float(u[0, i]))
+        v = gd / (one + (-gd).exp()) * ud
+        assert got[i] == _bf16_of_decimal(v), (i, float(g[0, i]), float(u[0, i]), hex(got[i]))
+
+
+def test_silu_mul_closed_forms():
+    """silu(0) = 0 (the zero takes u's sign), u = 0 gives a zero with silu's
+    sign, and for g = 80 the gate's sigmoid is 1 in every format, so x is the
+    product g u rounded once."""
+    g = np.array([[0.0, 0.0, 2.0, -2.0, 80.0, 80.0, 95.0]], np.float32)
+    u = np.array([[3.0, -3.0, 0.0, 0.0, 1.5, -0.3, 1.0 / 3.0]], np.float32)
+    x = oracle.silu_mul(g, u)[0]
+    assert list(x[:4]) == [0x0000, 0x8000, 0x0000, 0x8000]
+    for i in range(4, 7):
+        want = _bf16_of_decimal(__import__("decimal").Decimal(float(g[0, i])) *
+                                __import__("decimal").Decimal(float(u[0, i])))
+        assert x[i] == want
+
+
+def test_f64_to_bf16_ties_and_binades():
+    assert oracle.f64_to_bf16(1.0 + 2.0 ** -8) == 0x3F80            # tie, even below
+    assert oracle.f64_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82        # tie, even above
+    assert oracle.f64_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81   # just past the tie
+    assert oracle.f64_to_bf16(2.0 - 2.0 ** -9) == 0x4000            # rounds up into the next binade
+    assert oracle.f64_to_bf16(-0.0) == 0x8000
+    assert oracle.f64_to_bf16(2.0 ** -130) == 0x0008                # bf16 subnormal
+
+
 # ------------------------------------------------------------ tree sum
 def _tree_recursive(q):
     n = len(q)
