@@ -410,13 +410,32 @@ def chain_main(args):
 
         residual_add = {"fused_us": round(batch_us(lambda i: fused()), 2),
                         "torch_add_then_prepare_us": round(batch_us(unfused), 2)}
+        # SiLU(gate) * up in front of down: fused into the preparation, reading
+        # the two halves of the gate+up projection's fp32 output, against
+        # torch's silu, multiply and bf16 cast followed by the preparation
+        F_ = si.LAYER_LINEARS["down"][0]
+        g_, u_ = si.gate_up_output(m, F_, 42)
+        gu = torch.from_numpy(np.concatenate([g_, u_], axis=1)).to(dev)
+        gate, up = gu[:, :F_], gu[:, F_:]
+        spd, rsd = sq.alloc_prepared(sq.MXFP4, m, F_, dev, dense_backbone=True)
+        xd = torch.empty((m, F_), dtype=torch.bfloat16, device=dev)
+        fused_s = sq.bind_prepare_silu_mul(gate, up, spd, rsd)
+        plain_s = sq.bind_prepare(xd.view(torch.int16), None, 1e-5, spd, rsd)
+
+        def unfused_s(i):
+            torch.mul(F.silu(gate), up, out=xd)
+            plain_s()
+
+        silu_mul = {"fused_us": round(batch_us(lambda i: fused_s()), 2),
+                    "torch_silu_mul_then_prepare_us": round(batch_us(unfused_s), 2)}
         chain = {}
         for k, fns in runs.items():
             if fns is not None and len(fns) == len(si.LAYER_LINEARS):
                 chain[k] = round(batch_us(lambda i, fns=fns: [fn(i) for fn in fns]), 2)
         speed = {f"sharq_speedup_vs_{k}": round(chain[k] / chain["sharq"], 3) for k in chain if k != "sharq"}
         result[phase] = {"m": m, "chain_us": chain, "per_linear_us": per, **speed,
-                         "qkv_residual_add_and_prepare": residual_add}
+                         "qkv_residual_add_and_prepare": residual_add,
+                         "down_silu_mul_and_prepare": silu_mul}
     print(json.dumps(result), flush=True)
 
 

@@ -216,6 +216,28 @@ sharq_status sharq_prepare_residual(sharq_format fmt, const uint16_t *h_bf16, in
                                     const sharq_fp4_view *resid_out, void *stream);
 
 /*
+ * The preparation operator with SiLU(gate) * up in front of it (the down
+ * projection's input in a gated MLP; no norm):
+ *   x = bf16(g / (1 + exp(-g)) * u)   elementwise over the fp32 gate g and up
+ *                                     u [m, k] (row strides ld_gate, ld_up;
+ *                                     e.g. the two halves of the gate+up
+ *                                     projection's fp32 output), evaluated in
+ *                                     binary64 and rounded once to nearest
+ *                                     even (the kernel evaluates in fp32 and
+ *                                     repeats in binary64 wherever fp32 could
+ *                                     round differently);
+ * then sharq_prepare's steps 2-4 on x (no normalization).  x itself is not
+ * written.  One HBM pass over g and u.  MXFP4 only.
+ * Requirements: m >= 1; k >= 32, k % 32 == 0; ld_gate, ld_up >= k and
+ * multiples of 4; gate and up 16-byte aligned; both views as sharq_prepare
+ * requires.  Inputs are finite with |x| below the bf16 maximum.
+ */
+sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t ld_gate,
+                                    const float *up, int64_t ld_up, int64_t m, int64_t k,
+                                    const sharq_fp4_view *sparse_out,
+                                    const sharq_fp4_view *resid_out, void *stream);
+
+/*
  * Dual-path GEMM (abstract, sentences 4 and 5):
  *   Y = deq(backbone) * deq(W)^T + deq(residual) * deq(W)^T
  * accumulated in fp32 and stored as fp32 [m, n] (row stride ld_y).  NVFP4:
@@ -257,7 +279,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 4
+#define SHARQ_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

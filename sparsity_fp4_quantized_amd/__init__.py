@@ -39,9 +39,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 # every symbol include/sharq.h declares
-EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_dual_gemm",
-           "sharq_bytes", "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 4
+EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_prepare_silu_mul",
+           "sharq_dual_gemm", "sharq_bytes", "sharq_status_str", "sharq_abi_version")
+ABI_VERSION = 5
 
 
 class SharqError(RuntimeError):
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare_residual.argtypes = [ctypes.c_int, P, I64, P, I64, P, I64, I64, I64, P,
                                              ctypes.c_float, V, V, P]
         L.sharq_prepare_residual.restype = ctypes.c_int
+        L.sharq_prepare_silu_mul.argtypes = [ctypes.c_int, P, I64, P, I64, I64, I64, V, V, P]
+        L.sharq_prepare_silu_mul.restype = ctypes.c_int
         L.sharq_dual_gemm.argtypes = [ctypes.c_int, V, V, V, V, I64, I64, I64, P, I64,
                                       ctypes.c_int, P]
         L.sharq_dual_gemm.restype = ctypes.c_int
@@ -346,6 +348,39 @@ def prepare_residual(h, o, gamma, eps: float = 1e-5, dense_backbone: bool = Fals
     sp, rs = alloc_prepared(MXFP4, m, k, h.device, dense_backbone, layout)
     bind_prepare_residual(h, o, gamma, eps, sp, rs, out, stream)()
     return out, sp, rs
+
+
+def _f32(t):
+    torch = _torch()
+    if t.dtype != torch.float32:
+        raise TypeError(f"expected a float32 tensor, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError("tensor must be on the GPU")
+    return t
+
+
+def bind_prepare_silu_mul(gate, up, sp: FP4Tensor, rs: FP4Tensor, stream=None) -> BoundCall:
+    """sharq_prepare_silu_mul: the preparation (no norm) of x = bf16(silu(gate)
+    * up), from fp32 gate and up [m, k], bound for repeated calls."""
+    gate, up = _f32(gate), _f32(up)
+    m, k = gate.shape
+    if tuple(up.shape) != (m, k):
+        raise ValueError("gate and up must have the same shape")
+    vs, vr = sp.view(), rs.view()
+    args = (ctypes.c_int(sp.fmt), ctypes.c_void_p(gate.data_ptr()), ctypes.c_int64(_ld(gate)),
+            ctypes.c_void_p(up.data_ptr()), ctypes.c_int64(_ld(up)), ctypes.c_int64(m), ctypes.c_int64(k),
+            ctypes.byref(vs), ctypes.byref(vr), _stream_ptr(stream))
+    return BoundCall(lib().sharq_prepare_silu_mul, args, "sharq_prepare_silu_mul", (gate, up, sp, rs, vs, vr))
+
+
+def prepare_silu_mul(gate, up, dense_backbone: bool = False, layout: Optional[int] = None, stream=None):
+    """SiLU(gate) * up fused into the preparation (MXFP4, no norm): returns the
+    (backbone, residual) operands of the down projection.  gate and up may be
+    the two column halves of the gate+up projection's fp32 output."""
+    m, k = gate.shape
+    sp, rs = alloc_prepared(MXFP4, m, k, gate.device, dense_backbone, layout)
+    bind_prepare_silu_mul(gate, up, sp, rs, stream)()
+    return sp, rs
 
 
 def bind_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, out, variant: int = GEMM_AUTO,

@@ -24,6 +24,10 @@ struct PrepArgs {
   // x = bf16(x + add), written to x_out, then prepared; add == nullptr: none
   const uint16_t *add = nullptr;  int64_t ld_add = 0;
   uint16_t *x_out = nullptr;      int64_t ld_xout = 0;
+  // SiLU(gate) * up in front of the preparation (MXFP4, no norm): fp32 gate
+  // and up [m, k] replace x
+  const float *gate = nullptr;    int64_t ld_gate = 0;
+  const float *up = nullptr;      int64_t ld_up = 0;
 };
 
 struct QuantArgs {
@@ -60,6 +64,7 @@ __host__ __device__ inline int64_t arr_off(int64_t r, int64_t t, int64_t ld, int
 }
 
 hipError_t launch_prepare_mx(const PrepArgs &a, hipStream_t s);
+hipError_t launch_prepare_silu_mx(const PrepArgs &a, hipStream_t s);
 hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s);

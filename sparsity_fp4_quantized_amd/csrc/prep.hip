@@ -592,6 +592,82 @@ __global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chu
   store_block<FMT, true>(a, row, b, o);
 }
 
+// SiLU(gate) * up in front of the down projection: x = bf16 of g / (1 +
+// exp(-g)) * u evaluated in binary64 and rounded once.  The lane evaluates
+// it in fp32 first (expf within 1 ulp, IEEE division: v within a few ulp of
+// the exact value, no overflow for |g| <= 64); when v's bits are more than 64
+// ulp away from a bf16 rounding midpoint (low half 0x8000) rounding v gives
+// the same bf16 as the exact value, and otherwise (about 1 in 500, and for
+// |g| outside [2^-60, 64]) the lane evaluates in binary64 and rounds that:
+// directly to 8 significant bits, ties to even, for |v| >= 2^-126, through
+// float below.  A double exp differs from another correctly implemented one
+// by at most an ulp, so only a value within 2^-51 of a midpoint could round
+// differently.
+__device__ __forceinline__ uint32_t bf16_of_double(double v) {
+  const uint64_t bits = __double_as_longlong(v);
+  const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
+  const uint32_t sign = (uint32_t)(bits >> 48) & 0x8000u;
+  if (mag < (897ull << 52)) {                       // |v| < 2^-126
+    const uint32_t f = __float_as_uint((float)v);
+    return (f + 0x7FFFu + ((f >> 16) & 1u)) >> 16;
+  }
+  const uint64_t r = (mag + 0xFFFFFFFFFFFull + ((mag >> 45) & 1ull)) >> 45;   // exponent | 7 bits
+  return sign | (uint32_t)(r - ((uint64_t)(1023 - 127) << 7));
+}
+
+__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+  const float ag = __builtin_fabsf(g);
+  if (ag >= 0x1p-60f && ag <= 64.0f) {
+    const float e = expf(-g);
+    const float d = 1.0f + e;
+    const float sg = g / d;
+    const float v = sg * u;
+    const uint32_t b = __float_as_uint(v);
+    const int off = (int)(b & 0xFFFFu) - 0x8000;
+    if (off > 64 || off < -64) return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  }
+  const double gd = (double)g, ud = (double)u;
+  const double sd = gd / (1.0 + exp(-gd));
+  return bf16_of_double(sd * ud);
+}
+
+// One lane per 32-k block, laid out as prep_flat_kernel's lanes: the block of
+// gate and up (fp32, 128 bytes each), x = SiLU(g) * u, then the preparation
+// of x without a norm.
+template <int R>
+__global__ __launch_bounds__(256) void prep_silu_kernel(PrepArgs a, uint32_t chunks) {
+  constexpr int L = 64 / R;
+  const uint32_t w = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t rg = w / chunks;
+  const int64_t row = (int64_t)rg * R + lane / L;
+  const int64_t b = (int64_t)(w - rg * chunks) * L + lane % L;
+  if (row >= a.m || b >= a.k / 32) return;
+  const u32x4 *gp = reinterpret_cast<const u32x4 *>(a.gate + row * a.ld_gate + 32 * b);
+  const u32x4 *upp = reinterpret_cast<const u32x4 *>(a.up + row * a.ld_up + 32 * b);
+  u32x4 gq[8], uq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    gq[i] = gp[i];
+    uq[i] = upp[i];
+  }
+  uint32_t xw[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t lo = silu_mul_bf16(__uint_as_float(gq[i][2 * j]), __uint_as_float(uq[i][2 * j]));
+      const uint32_t hi = silu_mul_bf16(__uint_as_float(gq[i][2 * j + 1]), __uint_as_float(uq[i][2 * j + 1]));
+      xw[2 * i + j] = lo | (hi << 16);
+    }
+  }
+  float xf[32];
+  unpack32(xw, xf);
+  BlockOut o;
+  quantize_block_mx(xw, xf, o);
+  store_block<0, true>(a, row, b, o);
+}
+
 // NVFP4 tensor amax of x_n.  fp32 bit patterns of non-negative values order
 // like unsigned integers; each workgroup reduces its share (grid-stride) and
 // issues at most one atomic max, so that few atomics meet at the one address.
@@ -813,6 +889,20 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prepare_mx(const PrepArgs &a, hipStream_t s) { return launch_prepare<0>(a, s); }
+
+hipError_t launch_prepare_silu_mx(const PrepArgs &a, hipStream_t s) {
+  const int64_t nblk = a.k / 32;
+  if (a.s_ksm) {
+    const uint32_t chunks = (uint32_t)((nblk + 3) / 4);
+    const uint64_t waves = (uint64_t)((a.m + 15) / 16) * chunks;
+    prep_silu_kernel<16><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a, chunks);
+  } else {
+    const uint32_t chunks = (uint32_t)((nblk + 63) / 64);
+    const uint64_t waves = (uint64_t)a.m * chunks;
+    prep_silu_kernel<1><<<dim3((unsigned)((waves + 3) / 4)), 256, 0, s>>>(a, chunks);
+  }
+  return hipGetLastError();
+}
 hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s) { return launch_prepare<1>(a, s); }
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s) { return launch_quant<0>(a, s); }
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s) { return launch_quant<1>(a, s); }

@@ -181,6 +181,36 @@ sharq_status sharq_prepare_residual(sharq_format fmt, const uint16_t *h_bf16, in
                         ld_out, stream);
 }
 
+sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t ld_gate,
+                                    const float *up, int64_t ld_up, int64_t m, int64_t k,
+                                    const sharq_fp4_view *sp, const sharq_fp4_view *rs,
+                                    void *stream) {
+  if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
+  if (fmt != SHARQ_MXFP4) return SHARQ_ERR_UNSUPPORTED;
+  if (!gate || !up || !sp || !rs) return SHARQ_ERR_NULL;
+  if (m < 1 || k < 32 || k % 32 || ld_gate < k || ld_up < k) return SHARQ_ERR_SHAPE;
+  if (ld_gate % 4 || ld_up % 4 || !aligned(gate, 16) || !aligned(up, 16)) return SHARQ_ERR_ALIGN;
+  CHECK(check_layout(sp, k));
+  CHECK(check_layout(rs, k));
+  if (sp->layout != rs->layout) return SHARQ_ERR_SHAPE;
+  const int L = sp->layout;
+  CHECK(check_array(sp->codes, sp->ld_codes, L, m, k, k / 4, 8, 32, 16));
+  CHECK(check_array(sp->meta, sp->ld_meta, L, m, k, k / 8, 4, 16, 16));
+  CHECK(check_array(rs->codes, rs->ld_codes, L, m, k, k / 2, 16, 64, 16));
+  if (sp->dense_codes) CHECK(check_array(sp->dense_codes, sp->ld_dense, L, m, k, k / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp, m, k, false));
+  CHECK(check_scales(fmt, rs, m, k, false));
+  PrepArgs a{nullptr, 0, m, k, nullptr, 0.0f,
+             sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->scales, sp->ld_scales,
+             rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
+             sp->dense_codes, sp->ld_dense, nullptr, ksm(sp), ksm(rs)};
+  a.gate = gate;
+  a.ld_gate = ld_gate;
+  a.up = up;
+  a.ld_up = ld_up;
+  return from_hip(sharq::launch_prepare_silu_mx(a, static_cast<hipStream_t>(stream)));
+}
+
 sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,
                              const sharq_fp4_view *wsv, const sharq_fp4_view *wdv, int64_t m,
                              int64_t n, int64_t k, float *y, int64_t ld_y,

@@ -136,6 +136,19 @@ def gamma(k: int, seed: Optional[int]) -> np.ndarray:
     return f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32))
 
 
+def gate_up_output(m: int, f: int, seed: int, n_outlier: int = 72, outlier_scale: float = 30.0):
+    """fp32 gate and up [m, f] standing in for the gate+up projection's output
+    in front of the down projection: gate ~ N(0, 2^2), up ~ N(0, 1) with
+    n_outlier up channels scaled by outlier_scale (drawn in that order from
+    ``default_rng(seed)``, cast to float32)."""
+    rng = np.random.default_rng(seed)
+    g = 2.0 * rng.standard_normal((m, f))
+    u = rng.standard_normal((m, f))
+    if n_outlier > 0:
+        u[:, rng.choice(f, n_outlier, replace=False)] *= outlier_scale
+    return g.astype(np.float32), u.astype(np.float32)
+
+
 def workload_x(w: Workload, m: Optional[int] = None) -> np.ndarray:
     return activations(w.dist, w.m if m is None else m, w.k, w.n_outlier, w.outlier_scale, w.seed_x)
 

@@ -136,6 +136,32 @@ def test_prepare_residual_validation(kwargs, status):
     assert prep_res(**kwargs) == status
 
 
+def prep_silu(fmt=0, gate=FAKE, ld_gate=256, up=FAKE, ld_up=256, m=16, k=256, sp=None, rs=None):
+    sp = sp or view(ld_codes=64)
+    rs = rs or view(meta=None)
+    return sq.lib().sharq_prepare_silu_mul(fmt, gate, ld_gate, up, ld_up, m, k, ctypes.byref(sp),
+                                           ctypes.byref(rs), None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(fmt=1), sq.ERR_UNSUPPORTED),
+    (dict(fmt=7), sq.ERR_UNSUPPORTED),
+    (dict(gate=None), sq.ERR_NULL),
+    (dict(up=None), sq.ERR_NULL),
+    (dict(m=0), sq.ERR_SHAPE),
+    (dict(k=100, ld_gate=100, ld_up=100), sq.ERR_SHAPE),
+    (dict(ld_gate=128), sq.ERR_SHAPE),
+    (dict(ld_up=128), sq.ERR_SHAPE),
+    (dict(ld_gate=258), sq.ERR_ALIGN),
+    (dict(up=FAKE + 4), sq.ERR_ALIGN),
+    (dict(sp=view(ld_codes=63)), sq.ERR_SHAPE),
+    (dict(sp=ksm(), rs=view(meta=None)), sq.ERR_SHAPE),
+    (dict(rs=view(meta=None, scales=None)), sq.ERR_NULL),
+])
+def test_prepare_silu_mul_validation(kwargs, status):
+    assert prep_silu(**kwargs) == status
+
+
 def gemm(fmt=0, m=16, n=256, k=256, y=FAKE, ld_y=256, variant=0, sp=None, rs=None, ws=None,
          wd=None):
     sp = sp or view(ld_codes=64)

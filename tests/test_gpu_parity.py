@@ -269,6 +269,24 @@ def test_bound_prepare_residual_repeats():
         _compare_prep(f"step {step}", sp, rs, ref)
 
 
+
+@pytest.mark.parametrize("m,k,layout", [(2048, 14336, sq.LAYOUT_KSTEP_MAJOR), (16, 14336, sq.LAYOUT_KSTEP_MAJOR),
+                                        (37, 4096, sq.LAYOUT_KSTEP_MAJOR), (37, 4096, sq.LAYOUT_ROW_MAJOR),
+                                        (3, 96, sq.LAYOUT_ROW_MAJOR)])
+def test_prepare_silu_mul(m, k, layout):
+    """SiLU(gate) * up fused into the preparation, gate and up being the two
+    column halves of one fp32 [m, 2k] gate+up output: every prepared array
+    byte for byte against the oracle.  The inputs include gates outside the
+    fp32 fast path (|g| > 64, zero, tiny) and zero ups."""
+    g, u = si.gate_up_output(m, k, seed=41)
+    g[0, :8] = [0.0, -0.0, 1e-30, -70.0, 90.0, -100.0, 65.0, -64.0]
+    u[0, 8:12] = [0.0, -0.0, 0.0, 0.0]
+    _, ref = oracle.prepare_silu_mul(sq.MXFP4, g, u, dense_backbone=True)
+    gu = torch.from_numpy(np.concatenate([g, u], axis=1)).to(DEV)
+    sp, rs = sq.prepare_silu_mul(gu[:, :k], gu[:, k:], dense_backbone=True, layout=layout)
+    _compare_prep(f"silu m{m} k{k}", sp, rs, ref)
+
+
 # ------------------------------------------------------------ weights
 @pytest.mark.parametrize("fmt,n,k", [(0, 256, 256), (0, 6144, 4096), (0, 33, 96), (1, 256, 256),
                                      (1, 1000, 4096)])
