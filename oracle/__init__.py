@@ -266,6 +266,38 @@ def dual_gemm(fmt: int, prep: dict, wq: dict, want_f64: bool = False):
     return (y, y64) if want_f64 else y
 
 
+def gather_rows(prep: dict, rows) -> dict:
+    """The prepared operands of the listed activation rows (numpy gather)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = {key: np.ascontiguousarray(val[rows]) for key, val in prep.items() if key != "tensor_scale"}
+    out["tensor_scale"] = prep["tensor_scale"]
+    return out
+
+
+def expert_rows(wq: dict, e: int, n: int) -> dict:
+    """Rows e n .. e n + n - 1 of a stacked weight payload (expert e's W)."""
+    out = {key: np.ascontiguousarray(val[e * n:(e + 1) * n]) for key, val in wq.items() if key != "tensor_scale"}
+    out["tensor_scale"] = wq.get("tensor_scale", np.ones(1, np.float32))
+    return out
+
+
+def grouped_dual_gemm(fmt: int, prep: dict, row_index, offsets, wq: dict, n: int) -> np.ndarray:
+    """Grouped dual GEMM (a mixture-of-experts layer's expert GEMMs): grouped
+    row i of group e (offsets[e] <= i < offsets[e + 1]) is activation row
+    row_index[i] (row i itself when row_index is None), multiplied by group e's
+    weight, rows e n .. e n + n - 1 of the stacked payload: per group, the
+    dual GEMM of the gathered rows.  Returns Y [offsets[-1], n]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    total = int(offsets[-1])
+    idx = np.arange(total) if row_index is None else np.asarray(row_index, dtype=np.int64)
+    y = np.zeros((total, n), np.float32)
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y[lo:hi] = dual_gemm(fmt, gather_rows(prep, idx[lo:hi]), expert_rows(wq, e, n))
+    return y
+
+
 def dual_gemm_pairs(fmt: int, prep: dict, wq: dict, rows, cols, want_f64: bool = False):
     """Y at the listed (row, col) pairs only (sorted by row is fastest)."""
     rows = np.ascontiguousarray(rows, dtype=np.int64)

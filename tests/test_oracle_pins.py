@@ -650,3 +650,37 @@ def test_special_case_exact_sparse_fp4_input():
     q = oracle.quantize_weight(oracle.MXFP4, wb)
     y = oracle.dual_gemm(oracle.MXFP4, p, q)
     assert (y == (x @ wv.T).astype(np.float32)).all()
+
+
+# ------------------------------------------------------------ grouped dual GEMM
+def test_grouped_dual_gemm_one_group_is_dual_gemm():
+    """One group with the identity gather is the plain dual GEMM, bit for bit."""
+    w = si.WORKLOADS["tiny"]
+    p = oracle.prepare(oracle.MXFP4, si.workload_x(w), si.workload_gamma(w))
+    q = oracle.quantize_weight(oracle.MXFP4, si.workload_w(w))
+    y = oracle.grouped_dual_gemm(oracle.MXFP4, p, None, [0, w.m], q, w.n)
+    assert np.array_equal(y, oracle.dual_gemm(oracle.MXFP4, p, q))
+
+
+def test_grouped_dual_gemm_rows_match_exact_products():
+    """Each grouped row equals the exact dot products (rationals) of its
+    gathered activation row with its group's weight rows; empty groups and a
+    row used by two groups included."""
+    rng = np.random.default_rng(5)
+    t, k, n, groups = 9, 128, 6, 4
+    x = si.activations("normal", t, k, 2, 8.0, 51)
+    p = oracle.prepare(oracle.MXFP4, x, None, dense_backbone=True)
+    q = oracle.quantize_weight(oracle.MXFP4, si.weights(groups * n, k, 52))
+    offsets = [0, 3, 3, 8, 11]
+    row_index = rng.integers(0, t, 11)
+    row_index[4] = row_index[9] = 2
+    y = oracle.grouped_dual_gemm(oracle.MXFP4, p, row_index, offsets, q, n)
+    ds = _decode_blocks(_unpack_dense(p["s_dense"]), p["s_scales"], 32, oracle.MXFP4)
+    dr = _decode_blocks(_unpack_dense(p["r_codes"]), p["r_scales"], 32, oracle.MXFP4)
+    dw = _decode_blocks(_unpack_dense(q["codes"]), q["scales"], 32, oracle.MXFP4)
+    for e in range(groups):
+        for i in range(offsets[e], offsets[e + 1]):
+            r = int(row_index[i])
+            for j in range(n):
+                exact = fraction_dot(ds[r], dw[e * n + j]) + fraction_dot(dr[r], dw[e * n + j])
+                assert y[i, j] == np.float32(float(exact)), (e, i, j)
