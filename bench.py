@@ -439,6 +439,87 @@ def chain_main(args):
     print(json.dumps(result), flush=True)
 
 
+def moe_main(args):
+    """One Qwen3-30B-A3B mixture-of-experts layer at prefill (4096 tokens, 128
+    experts, 8 a token, hidden 2048, expert intermediate 768): the tokens'
+    preparation (RMSNorm, once per token), the grouped gate+up dual GEMM over
+    the gathered rows (n 1536, k 2048), SiLU(gate) * up fused into the down
+    projection's preparation, and the grouped down dual GEMM (n 2048, k 768).
+    Seeded routing with uneven expert loads.  Against torch's bf16 grouped GEMM
+    (torch._grouped_mm) on the same groups where this torch build has one.
+    Prints one JSON line."""
+    import torch
+    import sparsity_fp4_quantized_amd as sq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    cfg = si.MOE_QWEN3_30B_A3B
+    T, H, I, E, K8 = 4096, cfg["hidden"], cfg["intermediate"], cfg["experts"], cfg["top_k"]
+    reps, warm = max(args.steps // 4, 10), max(args.warmup // 4, 5)
+
+    def batch_us(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    x = torch.from_numpy(si.activations("student_t4", T, H, 20, 50.0, 101).view(np.int16)).to(dev)
+    g = torch.from_numpy(si.gamma(H, None).view(np.int16)).to(dev)
+    row_index, offsets = si.moe_routing(T, E, K8, 102)
+    rows = int(offsets[-1])
+    idx_d = torch.from_numpy(row_index).to(dev)
+    off_d = torch.from_numpy(offsets).to(dev)
+    w13 = torch.from_numpy(si.weights(E * 2 * I, H, 103).view(np.int16)).to(dev)
+    w2 = torch.from_numpy(si.weights(E * H, I, 104).view(np.int16)).to(dev)
+    q13, q2 = sq.quantize_weight(w13), sq.quantize_weight(w2)
+    sp, rs = sq.alloc_prepared(sq.MXFP4, T, H, dev, dense_backbone=True)
+    y13 = torch.empty((rows, 2 * I), dtype=torch.float32, device=dev)
+    sp2, rs2 = sq.alloc_prepared(sq.MXFP4, rows, I, dev, dense_backbone=True)
+    y2 = torch.empty((rows, H), dtype=torch.float32, device=dev)
+    prep = sq.bind_prepare(x, g, 1e-5, sp, rs)
+    gemm13 = sq.bind_grouped_dual_gemm(sp, rs, q13, off_d, rows, y13, row_index=idx_d)
+    prep2 = sq.bind_prepare_silu_mul(y13[:, :I], y13[:, I:], sp2, rs2)
+    gemm2 = sq.bind_grouped_dual_gemm(sp2, rs2, q2, off_d, rows, y2)
+
+    def layer():
+        prep()
+        gemm13()
+        prep2()
+        gemm2()
+
+    t = {"prepare": batch_us(prep), "grouped_gate_up": batch_us(gemm13),
+         "silu_mul_prepare": batch_us(prep2), "grouped_down": batch_us(gemm2), "layer": batch_us(layer)}
+    f13, f2 = 3.0 * rows * 2 * I * H, 3.0 * rows * H * I
+    res = {"metric": "Qwen3-30B-A3B MoE layer (prefill, 4096 tokens): grouped dual-path FP4 GEMMs",
+           "unit": "us", "higher_is_better": False, "steps": reps, "warmup": warm,
+           "data": "synthetic (seeded activations and routing, N(0,0.02) weights)",
+           "config": {"workload": "qwen3_30b_a3b_moe_prefill", "tokens": T, "experts": E, "top_k": K8,
+                      "hidden": H, "intermediate": I, "rows": rows,
+                      "group_rows_min_max": [int(np.diff(offsets).min()), int(np.diff(offsets).max())]},
+           "times_us": {k: round(v, 2) for k, v in t.items()},
+           "grouped_gate_up_TFLOP/s": round(f13 / (t["grouped_gate_up"] * 1e-6) / 1e12, 1),
+           "grouped_gate_up_frac_of_fp4_peak": round(f13 / (t["grouped_gate_up"] * 1e-6) / 1e12 / PEAK_FP4_TFLOPS, 4),
+           "grouped_down_TFLOP/s": round(f2 / (t["grouped_down"] * 1e-6) / 1e12, 1),
+           "grouped_down_frac_of_fp4_peak": round(f2 / (t["grouped_down"] * 1e-6) / 1e12 / PEAK_FP4_TFLOPS, 4)}
+    # vendor bf16 grouped GEMM on the same groups (gate+up), where available
+    try:
+        xb = x.view(torch.bfloat16)[idx_d.long()]
+        wb = w13.view(torch.bfloat16).view(E, 2 * I, H).transpose(1, 2).contiguous()   # [E, k, n], dense
+        ends = off_d[1:].to(torch.int32)
+        us = batch_us(lambda: torch._grouped_mm(xb, wb, offs=ends, out_dtype=torch.bfloat16))
+        res["bf16_grouped_mm_gate_up_us"] = round(us, 2)
+    except (RuntimeError, AttributeError, TypeError) as e:
+        res["bf16_grouped_mm_gate_up_us"] = {"error": str(e)[:200]}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,6 +536,8 @@ def main():
                     help=f"run one {COPY_BYTES >> 20} MiB device copy first (counter calibration)")
     ap.add_argument("--no-yardsticks", action="store_true",
                     help="skip the plain-copy and vendor FP4 GEMM reference timings")
+    ap.add_argument("--moe", action="store_true",
+                    help="time one Qwen3-30B-A3B mixture-of-experts layer (grouped dual GEMMs) instead")
     ap.add_argument("--chain", action="store_true",
                     help="time the decoder-layer linear chain (SharQ vs bf16 / FP8 vendor GEMMs) instead")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -464,6 +547,9 @@ def main():
         traffic_convert(args, si.WORKLOADS[args.workload])
         return
 
+    if args.moe and args.gpus == 1:
+        moe_main(args)
+        return
     if args.chain and args.gpus == 1:
         chain_main(args)
         return

@@ -270,6 +270,36 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sparse,
                              const sharq_fp4_view *w_dense_view, int64_t m, int64_t n, int64_t k,
                              float *y, int64_t ld_y, sharq_gemm_variant variant, void *stream);
 
+/*
+ * Grouped dual GEMM: the expert GEMMs of a mixture-of-experts layer in one
+ * launch (each expert's product is sharq_dual_gemm's, abstract, sentences 4
+ * and 5).  The activations are prepared once per token (sparse, resid:
+ * `tokens` rows, sparse->dense_codes required); grouped row i of group e,
+ * group_offsets[e] <= i < group_offsets[e + 1], is activation row
+ * row_index[i] (row i itself when row_index is NULL) and meets group e's
+ * weight, rows e n .. e n + n - 1 of the stacked payload w_*_view (groups n
+ * rows; the two views as in sharq_dual_gemm).  Y [rows, n] (fp32, ld_y):
+ * grouped row i of Y is that row's dual GEMM.
+ * group_offsets (int64, groups + 1 entries) and row_index (int32, rows
+ * entries) are DEVICE arrays and are not read on the host: the group sizes
+ * may come from routing on the device.  The offsets must be nondecreasing
+ * from 0 to rows and the indices in [0, tokens); the kernel clamps offsets to
+ * [0, rows], so no value in them makes it write outside Y (an out-of-range
+ * index reads zeros or another row's data).
+ * MXFP4 only.  Requirements: 1 <= groups <= 256; tokens >= 1; rows >= 0 (0:
+ * nothing to do); rows <= tokens without row_index; n >= 1; k >= 128,
+ * k % 128 == 0; ld_y >= n; y 4-byte, group_offsets 8-byte, row_index 4-byte
+ * aligned; the views as sharq_dual_gemm requires for `tokens` activation
+ * rows and groups n weight rows.
+ */
+sharq_status sharq_grouped_dual_gemm(sharq_format fmt, const sharq_fp4_view *sparse,
+                                     const sharq_fp4_view *resid, int64_t tokens,
+                                     const int32_t *row_index, const int64_t *group_offsets,
+                                     int64_t groups, int64_t rows,
+                                     const sharq_fp4_view *w_sparse_view,
+                                     const sharq_fp4_view *w_dense_view, int64_t n, int64_t k,
+                                     float *y, int64_t ld_y, void *stream);
+
 /* Bytes of one packed array (`which` = SHARQ_BYTES_*) for `rows` rows of length k; 0 if invalid. */
 size_t sharq_bytes(sharq_format fmt, int which, int64_t rows, int64_t k);
 
@@ -279,7 +309,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 5
+#define SHARQ_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

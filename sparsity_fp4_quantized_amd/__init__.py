@@ -40,8 +40,9 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 # every symbol include/sharq.h declares
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_prepare_silu_mul",
-           "sharq_dual_gemm", "sharq_bytes", "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 5
+           "sharq_dual_gemm", "sharq_grouped_dual_gemm", "sharq_bytes", "sharq_status_str",
+           "sharq_abi_version")
+ABI_VERSION = 6
 
 
 class SharqError(RuntimeError):
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare_residual.restype = ctypes.c_int
         L.sharq_prepare_silu_mul.argtypes = [ctypes.c_int, P, I64, P, I64, I64, I64, V, V, P]
         L.sharq_prepare_silu_mul.restype = ctypes.c_int
+        L.sharq_grouped_dual_gemm.argtypes = [ctypes.c_int, V, V, I64, P, P, I64, I64, V, V, I64, I64,
+                                              P, I64, P]
+        L.sharq_grouped_dual_gemm.restype = ctypes.c_int
         L.sharq_dual_gemm.argtypes = [ctypes.c_int, V, V, V, V, I64, I64, I64, P, I64,
                                       ctypes.c_int, P]
         L.sharq_dual_gemm.restype = ctypes.c_int
@@ -409,4 +413,41 @@ def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AU
     if out is None:
         out = torch.empty((sp.rows, w.rows), dtype=torch.float32, device=w.codes.device)
     bind_dual_gemm(sp, rs, w, out, variant, w_dense_scales, stream)()
+    return out
+
+
+def bind_grouped_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, group_offsets, rows: int, out,
+                           row_index=None, stream=None) -> BoundCall:
+    """sharq_grouped_dual_gemm into `out` (fp32 [rows, n]): group e's rows
+    (group_offsets[e] .. group_offsets[e + 1], an int64 device tensor of
+    groups + 1 entries) gather activation rows row_index[i] (int32 device
+    tensor; None: row i) and meet W rows e n .. e n + n - 1, bound for repeated
+    calls.  `w` stacks the groups' weights: groups * n rows."""
+    torch = _torch()
+    if group_offsets.dtype != torch.int64 or (row_index is not None and row_index.dtype != torch.int32):
+        raise TypeError("group_offsets must be int64 and row_index int32")
+    groups = group_offsets.numel() - 1
+    n, k = out.shape[1], sp.k
+    if w.rows % groups:
+        raise ValueError("the stacked weight must hold the same number of rows for every group")
+    if w.rows // groups != n:
+        raise ValueError("out has n columns, the stacked weight groups * n rows")
+    ws, vs, vr = w.view(), sp.view(), rs.view()
+    args = (ctypes.c_int(sp.fmt), ctypes.byref(vs), ctypes.byref(vr), ctypes.c_int64(sp.rows),
+            ctypes.c_void_p(_ptr(row_index)), ctypes.c_void_p(group_offsets.data_ptr()),
+            ctypes.c_int64(groups), ctypes.c_int64(rows), ctypes.byref(ws), ctypes.byref(ws),
+            ctypes.c_int64(n), ctypes.c_int64(k), ctypes.c_void_p(out.data_ptr()), ctypes.c_int64(_ld(out)),
+            _stream_ptr(stream))
+    return BoundCall(lib().sharq_grouped_dual_gemm, args, "sharq_grouped_dual_gemm",
+                     (sp, rs, w, group_offsets, row_index, out, ws, vs, vr))
+
+
+def grouped_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, group_offsets, rows: int,
+                      row_index=None, out=None, stream=None):
+    """Grouped dual GEMM (mixture-of-experts expert GEMMs): returns Y [rows, n]."""
+    torch = _torch()
+    groups = group_offsets.numel() - 1
+    if out is None:
+        out = torch.empty((rows, w.rows // groups), dtype=torch.float32, device=w.codes.device)
+    bind_grouped_dual_gemm(sp, rs, w, group_offsets, rows, out, row_index, stream)()
     return out

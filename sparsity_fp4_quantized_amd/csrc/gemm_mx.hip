@@ -85,39 +85,61 @@ struct DOffs {
   uint32_t scale[DPlan<TBM, TBN, NW>::kScalePer];
 };
 
+// Tile rows of the A operands: plain tiles stream rows m0 .. of A (offsets
+// relative to row m0); a grouped tile gathers activation row row_index[i] for
+// its grouped rows i = m0 .. (offsets relative to row 0), rows past the
+// group's end repeating its last row (their outputs are not stored).
+struct ARows {
+  const int32_t *idx;   // grouped: the gather (null: grouped row i is activation row i)
+  int64_t m0, m_end;
+  bool grouped;
+  __device__ __forceinline__ uint32_t operator()(int r) const {
+    if (!grouped) return (uint32_t)r;
+    const int64_t i = min(m0 + r, m_end - 1);
+    return (uint32_t)(idx ? (int64_t)idx[i] : i);
+  }
+};
+
 template <int TBM, int TBN, int NW>
 __device__ __forceinline__ void plan_loads(const GemmArgs &a, int64_t m0, int64_t n0, int wave,
-                                           int lane, DRsrc &R, DOffs<TBM, TBN, NW> &O) {
+                                           int lane, DRsrc &R, DOffs<TBM, TBN, NW> &O,
+                                           const ARows &arow, int64_t w_row0, int64_t w_rows) {
   using P = DPlan<TBM, TBN, NW>;
   const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const int64_t steps = a.k / BK;
-  R.as = op_stream(a.s_dense, a.ld_sd, a.s_ksm, a.m, m0, steps, 64);
-  R.ar = op_stream(a.r_codes, a.ld_rc, a.r_ksm, a.m, m0, steps, 64);
-  R.w = op_stream(a.w_codes, a.ld_wc, a.w_ksm, a.n, n0, steps, 64);
-  R.sas = op_stream(a.s_scales, a.ld_ss, a.s_ksm, a.m, m0, steps, 4);
-  R.sar = op_stream(a.r_scales, a.ld_rs, a.r_ksm, a.m, m0, steps, 4);
-  R.sws = op_stream(a.ws_scales, a.ld_wss, a.w_ksm, a.n, n0, steps, 4);
-  R.swd = op_stream(a.wd_scales, a.ld_wds, a.w_ksm, a.n, n0, steps, 4);
+  const int64_t a_rows = arow.grouped ? a.tokens : a.m, a_r0 = arow.grouped ? 0 : m0;
+  R.as = op_stream(a.s_dense, a.ld_sd, a.s_ksm, a_rows, a_r0, steps, 64);
+  R.ar = op_stream(a.r_codes, a.ld_rc, a.r_ksm, a_rows, a_r0, steps, 64);
+  R.w = op_stream(a.w_codes, a.ld_wc, a.w_ksm, w_rows, w_row0 + n0, steps, 64);
+  R.sas = op_stream(a.s_scales, a.ld_ss, a.s_ksm, a_rows, a_r0, steps, 4);
+  R.sar = op_stream(a.r_scales, a.ld_rs, a.r_ksm, a_rows, a_r0, steps, 4);
+  R.sws = op_stream(a.ws_scales, a.ld_wss, a.w_ksm, w_rows, w_row0 + n0, steps, 4);
+  R.swd = op_stream(a.wd_scales, a.ld_wds, a.w_ksm, w_rows, w_row0 + n0, steps, 4);
 #pragma unroll
   for (int j = 0; j < P::kChunkPer; ++j) {
     int q = wave + NW * j;
-    uint32_t rs = R.as.row_stride;
-    if (q >= P::kA && q < 2 * P::kA) { q -= P::kA; rs = R.ar.row_stride; }
-    else if (q >= 2 * P::kA) { q -= 2 * P::kA; rs = R.w.row_stride; }
-    O.chunk[j] = (uint32_t)(16 * q + lrow) * rs + lchunk * 16;
+    if (q < 2 * P::kA) {
+      uint32_t rs = R.as.row_stride;
+      if (q >= P::kA) { q -= P::kA; rs = R.ar.row_stride; }
+      O.chunk[j] = arow(16 * q + lrow) * rs + lchunk * 16;
+    } else {
+      q -= 2 * P::kA;
+      O.chunk[j] = (uint32_t)(16 * q + lrow) * R.w.row_stride + lchunk * 16;
+    }
   }
 #pragma unroll
   for (int j = 0; j < P::kScalePer; ++j) {
     int t = wave + NW * j;
-    uint32_t rs = R.sas.row_stride;
-    if (t >= TBM / 64) {
-      t -= TBM / 64; rs = R.sar.row_stride;
-      if (t >= TBM / 64) {
-        t -= TBM / 64; rs = R.sws.row_stride;
-        if (t >= TBN / 64) { t -= TBN / 64; rs = R.swd.row_stride; }
-      }
+    if (t < 2 * (TBM / 64)) {
+      uint32_t rs = R.sas.row_stride;
+      if (t >= TBM / 64) { t -= TBM / 64; rs = R.sar.row_stride; }
+      O.scale[j] = arow(64 * t + lane) * rs;
+    } else {
+      t -= 2 * (TBM / 64);
+      uint32_t rs = R.sws.row_stride;
+      if (t >= TBN / 64) { t -= TBN / 64; rs = R.swd.row_stride; }
+      O.scale[j] = (uint32_t)(64 * t + lane) * rs;
     }
-    O.scale[j] = (uint32_t)(64 * t + lane) * rs;
   }
 }
 
@@ -249,9 +271,50 @@ __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN
   }
 }
 
-template <int TBM, int TBN, int NW, int STAGES>
+// Grouped tiles: the grid covers ceil(m / TBM) + groups tile rows, an upper
+// bound of the sum over groups of ceil(rows_e / TBM), so that the group sizes
+// can stay on the device.  The workgroup counts each group's tile rows (group
+// offsets clamped to [0, m] and made nondecreasing, so that no tile writes
+// outside Y whatever the offsets hold), scans them in LDS and finds the group
+// of its tile row; tile rows past the last group's end have no work.
+template <int TBM>
+__device__ __forceinline__ bool grouped_tile(const GemmArgs &a, uint32_t tm, int64_t &m0, int64_t &m_end,
+                                             int64_t &group) {
+  __shared__ int32_t cnt[256];
+  __shared__ int64_t found[3];
+  const int t = threadIdx.x;
+  int64_t lo = 0, hi = 0;
+  if (t < a.groups) {
+    lo = min(max(a.group_off[t], (int64_t)0), a.m);
+    hi = min(max(a.group_off[t + 1], lo), a.m);
+  }
+  const int32_t c = (int32_t)((hi - lo + TBM - 1) / TBM);
+  cnt[t] = c;
+  if (t == 0) found[0] = -1;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {   // inclusive scan
+    const int32_t v = cnt[t] + (t >= d ? cnt[t - d] : 0);
+    __syncthreads();
+    cnt[t] = v;
+    __syncthreads();
+  }
+  const int32_t end = cnt[t], begin = end - c;
+  if (c > 0 && (int32_t)tm >= begin && (int32_t)tm < end) {
+    found[0] = t;
+    found[1] = lo + (int64_t)((int32_t)tm - begin) * TBM;
+    found[2] = hi;
+  }
+  __syncthreads();
+  group = found[0];
+  m0 = found[1];
+  m_end = found[2];
+  return group >= 0;
+}
+
+template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false>
 __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, uint32_t band) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
+  static_assert(!GROUPED || 64 * NW >= 256, "the group scan takes one thread a group, up to 256");
   constexpr int TN = TBN / 64;
   using P = DPlan<TBM, TBN, NW>;
   __shared__ DStage<TBM, TBN> st[STAGES];
@@ -261,8 +324,13 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, li = lane & 31;
   uint32_t tm, tn;
-  xcd_tile(blockIdx.x, (uint32_t)((a.m + TBM - 1) / TBM), (uint32_t)((a.n + TBN - 1) / TBN), band, tm, tn);
-  const int64_t m0 = (int64_t)tm * TBM, n0 = (int64_t)tn * TBN;
+  const uint32_t gm = GROUPED ? (uint32_t)((a.m + TBM - 1) / TBM + a.groups) : (uint32_t)((a.m + TBM - 1) / TBM);
+  xcd_tile(blockIdx.x, gm, (uint32_t)((a.n + TBN - 1) / TBN), band, tm, tn);
+  int64_t m0 = (int64_t)tm * TBM, m_end = a.m, group = 0;
+  if (GROUPED && !grouped_tile<TBM>(a, tm, m0, m_end, group)) return;   // uniform: no work
+  const int64_t n0 = (int64_t)tn * TBN;
+  const ARows arow{a.row_index, m0, m_end, GROUPED};
+  const int64_t w_row0 = GROUPED ? group * a.n : 0, w_rows = GROUPED ? (group + 1) * a.n : a.n;
 
   v16f acc[2][TN];
 #pragma unroll
@@ -275,7 +343,7 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
   const int ksteps = (int)(a.k / BK);
   DRsrc R;
   DOffs<TBM, TBN, NW> O;
-  plan_loads<TBM, TBN, NW>(a, m0, n0, wave, lane, R, O);
+  plan_loads<TBM, TBN, NW>(a, m0, n0, wave, lane, R, O, arow, w_row0, w_rows);
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < ksteps) issue_stage<TBM, TBN, NW>(R, O, wave, p, st[p]);
@@ -307,9 +375,16 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < a.m) __builtin_nontemporal_store(acc[it][jt][r], &a.y[row * a.ld_y + col]);
+        if (row < m_end) __builtin_nontemporal_store(acc[it][jt][r], &a.y[row * a.ld_y + col]);
       }
     }
+}
+
+template <int TBM, int TBN, int NW, int STAGES>
+void launch_grouped(const GemmArgs &a, hipStream_t s) {
+  const int64_t gm = (a.m + TBM - 1) / TBM + a.groups, gn = (a.n + TBN - 1) / TBN;
+  dual_gemm_dense_kernel<TBM, TBN, NW, STAGES, true>
+      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, TBN <= 128 ? 3 : 2));
 }
 
 template <int TBM, int TBN, int NW, int STAGES>
@@ -785,6 +860,17 @@ __global__ __launch_bounds__(256) void dual_gemm_decode_kernel(GemmArgs a) {
 }
 
 }  // namespace
+
+// Grouped (mixture-of-experts) dual GEMM over the dense backbone view: the
+// prefill kernel's tiles, 128 x 192 when there are enough of them, else 128 x 128.
+hipError_t launch_grouped_dual_gemm_mx(const GemmArgs &a, hipStream_t s) {
+  const int64_t mt = (a.m + 127) / 128 + a.groups;
+  if (mt * ((a.n + 191) / 192) >= 512 && a.k <= 8192)
+    launch_grouped<128, 192, 4, 2>(a, s);
+  else
+    launch_grouped<128, 128, 4, 2>(a, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s) {
   // decode with fewer 128-column tiles than half the CUs (Llama-3.1-8B's QKV,

@@ -54,6 +54,13 @@ struct GemmArgs {
   float *y;                int64_t ld_y;
   int64_t m, n, k;
   int s_ksm, r_ksm, w_ksm;   // per operand (codes, meta, dense view, scales): k-step-major
+  // grouped GEMM (mixture of experts): m = grouped rows in total; grouped row
+  // i of group e (group_off[e] <= i < group_off[e + 1], device array) is
+  // activation row row_index[i] (i when row_index is null) of `tokens`
+  // activation rows, and meets group e's weight, rows e n .. e n + n - 1
+  const int32_t *row_index = nullptr;
+  const int64_t *group_off = nullptr;
+  int64_t groups = 0, tokens = 0;
 };
 
 // Offset of the bytes of row r in 128-k step t of an operand array with `bps`
@@ -69,6 +76,7 @@ hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s);
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s);
+hipError_t launch_grouped_dual_gemm_mx(const GemmArgs &a, hipStream_t s);
 hipError_t launch_dual_gemm_nv(const GemmArgs &a, int variant, hipStream_t s);
 
 }  // namespace sharq

@@ -211,6 +211,48 @@ sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t
   return from_hip(sharq::launch_prepare_silu_mx(a, static_cast<hipStream_t>(stream)));
 }
 
+sharq_status sharq_grouped_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp,
+                                     const sharq_fp4_view *rs, int64_t tokens,
+                                     const int32_t *row_index, const int64_t *group_offsets,
+                                     int64_t groups, int64_t rows, const sharq_fp4_view *wsv,
+                                     const sharq_fp4_view *wdv, int64_t n, int64_t k, float *y,
+                                     int64_t ld_y, void *stream) {
+  if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
+  if (fmt != SHARQ_MXFP4) return SHARQ_ERR_UNSUPPORTED;
+  if (!sp || !rs || !wsv || !wdv || !y || !group_offsets) return SHARQ_ERR_NULL;
+  if (groups < 1 || groups > 256) return SHARQ_ERR_UNSUPPORTED;
+  if (tokens < 1 || rows < 0 || n < 1 || k < 128 || k % 128 || ld_y < n) return SHARQ_ERR_SHAPE;
+  if (!row_index && rows > tokens) return SHARQ_ERR_SHAPE;
+  if (!aligned(group_offsets, 8) || (row_index && !aligned(row_index, 4)) || !aligned(y, 4))
+    return SHARQ_ERR_ALIGN;
+  CHECK(check_layout(sp, k));
+  CHECK(check_layout(rs, k));
+  CHECK(check_layout(wsv, k));
+  CHECK(check_layout(wdv, k));
+  if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
+  if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
+    return SHARQ_ERR_SHAPE;
+  if (!sp->dense_codes) return SHARQ_ERR_UNSUPPORTED;   // reads the dense backbone view
+  const int64_t wrows = groups * n;
+  CHECK(check_array(sp->dense_codes, sp->ld_dense, sp->layout, tokens, k, k / 2, 16, 64, 16));
+  CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, tokens, k, k / 2, 16, 64, 16));
+  CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, wrows, k, k / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp, tokens, k, true));
+  CHECK(check_scales(fmt, rs, tokens, k, true));
+  CHECK(check_scales(fmt, wsv, wrows, k, true));
+  CHECK(check_scales(fmt, wdv, wrows, k, true));
+  if (rows == 0) return SHARQ_OK;
+  GemmArgs a{sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->dense_codes, sp->ld_dense,
+             sp->scales, sp->ld_scales, rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
+             wsv->codes, wsv->ld_codes, wsv->scales, wsv->ld_scales, wdv->scales, wdv->ld_scales,
+             nullptr, nullptr, y, ld_y, rows, n, k, ksm(sp), ksm(rs), ksm(wsv)};
+  a.row_index = row_index;
+  a.group_off = group_offsets;
+  a.groups = groups;
+  a.tokens = tokens;
+  return from_hip(sharq::launch_grouped_dual_gemm_mx(a, static_cast<hipStream_t>(stream)));
+}
+
 sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,
                              const sharq_fp4_view *wsv, const sharq_fp4_view *wdv, int64_t m,
                              int64_t n, int64_t k, float *y, int64_t ld_y,

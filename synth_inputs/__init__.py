@@ -149,6 +149,28 @@ def gate_up_output(m: int, f: int, seed: int, n_outlier: int = 72, outlier_scale
     return g.astype(np.float32), u.astype(np.float32)
 
 
+# One mixture-of-experts layer of Qwen3-30B-A3B (hidden 2048, 128 experts of
+# intermediate size 768, 8 experts a token): the grouped dual GEMM workload.
+MOE_QWEN3_30B_A3B = {"hidden": 2048, "intermediate": 768, "experts": 128, "top_k": 8}
+
+
+def moe_routing(tokens: int, experts: int, top_k: int, seed: int):
+    """Seeded top-k routing: logits N(0, 1) [tokens, experts] plus a per-expert
+    bias N(0, 0.5^2) (uneven expert loads), each token's top_k experts.
+    Returns (row_index int32 [tokens * top_k]: the token of each (token,
+    expert) pair, pairs sorted by expert then token; offsets int64
+    [experts + 1]: expert e's pairs are rows offsets[e] .. offsets[e + 1])."""
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((tokens, experts)) + 0.5 * rng.standard_normal(experts)
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]
+    tok = np.repeat(np.arange(tokens), top_k)
+    exp = top.reshape(-1)
+    order = np.lexsort((tok, exp))
+    counts = np.bincount(exp, minlength=experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return tok[order].astype(np.int32), offsets
+
+
 def workload_x(w: Workload, m: Optional[int] = None) -> np.ndarray:
     return activations(w.dist, w.m if m is None else m, w.k, w.n_outlier, w.outlier_scale, w.seed_x)
 

@@ -162,6 +162,39 @@ def test_prepare_silu_mul_validation(kwargs, status):
     assert prep_silu(**kwargs) == status
 
 
+def grouped(fmt=0, tokens=16, idx=FAKE, offs=FAKE, groups=2, rows=32, n=256, k=256, y=FAKE,
+            ld_y=256, sp=None, rs=None, ws=None, wd=None):
+    sp = sp or view(ld_codes=64, dense=FAKE, ld_dense=128)
+    rs = rs or view(meta=None)
+    ws = ws or view(meta=None)
+    wd = wd or ws
+    return sq.lib().sharq_grouped_dual_gemm(fmt, ctypes.byref(sp), ctypes.byref(rs), tokens, idx, offs,
+                                            groups, rows, ctypes.byref(ws), ctypes.byref(wd), n, k, y,
+                                            ld_y, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(fmt=1), sq.ERR_UNSUPPORTED),
+    (dict(groups=0), sq.ERR_UNSUPPORTED),
+    (dict(groups=257), sq.ERR_UNSUPPORTED),
+    (dict(offs=None), sq.ERR_NULL),
+    (dict(y=None), sq.ERR_NULL),
+    (dict(tokens=0), sq.ERR_SHAPE),
+    (dict(rows=-1), sq.ERR_SHAPE),
+    (dict(k=192), sq.ERR_SHAPE),
+    (dict(ld_y=100), sq.ERR_SHAPE),
+    (dict(idx=None, rows=17), sq.ERR_SHAPE),            # identity gather past the last token
+    (dict(offs=FAKE + 4), sq.ERR_ALIGN),
+    (dict(idx=FAKE + 2), sq.ERR_ALIGN),
+    (dict(y=FAKE + 2), sq.ERR_ALIGN),
+    (dict(sp=view(ld_codes=64)), sq.ERR_UNSUPPORTED),   # no dense backbone view
+    (dict(wd=view(meta=None, codes=FAKE + 4096)), sq.ERR_SHAPE),   # two payloads
+    (dict(ws=view(meta=None, ld_codes=100)), sq.ERR_SHAPE),
+])
+def test_grouped_dual_gemm_validation(kwargs, status):
+    assert grouped(**kwargs) == status
+
+
 def gemm(fmt=0, m=16, n=256, k=256, y=FAKE, ld_y=256, variant=0, sp=None, rs=None, ws=None,
          wd=None):
     sp = sp or view(ld_codes=64)

@@ -287,6 +287,111 @@ def test_prepare_silu_mul(m, k, layout):
     _compare_prep(f"silu m{m} k{k}", sp, rs, ref)
 
 
+
+def _grouped_case(tokens, k, n, experts, top_k, seed, layout=sq.LAYOUT_KSTEP_MAJOR):
+    x = si.activations("student_t4", tokens, k, 41 if k >= 4096 else 20, 50.0, seed)
+    g = si.gamma(k, seed + 1)
+    W = si.weights(experts * n, k, seed + 2)
+    row_index, offsets = si.moe_routing(tokens, experts, top_k, seed + 3)
+    p = oracle.prepare(sq.MXFP4, x, g, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, W)
+    sp, rs = sq.prepare(dev16(x), dev16(g), dense_backbone=True, layout=layout)
+    wq = sq.quantize_weight(dev16(W), layout=layout)
+    return p, q, sp, rs, wq, row_index, offsets
+
+
+@pytest.mark.parametrize("tokens,k,n,experts,top_k,layout", [
+    (300, 2048, 320, 8, 2, sq.LAYOUT_KSTEP_MAJOR),
+    (200, 768, 256, 16, 4, sq.LAYOUT_KSTEP_MAJOR),
+    (150, 256, 200, 5, 3, sq.LAYOUT_ROW_MAJOR),
+])
+def test_grouped_dual_gemm(tokens, k, n, experts, top_k, layout):
+    """Grouped (mixture-of-experts) dual GEMM over gathered activation rows
+    against the oracle, every output: uneven groups (some over one 128-row
+    tile, some of a few rows), both layouts."""
+    p, q, sp, rs, wq, row_index, offsets = _grouped_case(tokens, k, n, experts, top_k, 61, layout)
+    rows = int(offsets[-1])
+    ref = oracle.grouped_dual_gemm(sq.MXFP4, p, row_index, offsets, q, n)
+    y = host(sq.grouped_dual_gemm(sp, rs, wq, torch.from_numpy(offsets).to(DEV), rows,
+                                  row_index=torch.from_numpy(row_index).to(DEV)))
+    assert normwise(y, ref) <= GEMM_TOL
+    # each group's rows also equal the plain dual GEMM of the gathered rows
+    e = int(np.argmax(np.diff(offsets)))
+    lo, hi = int(offsets[e]), int(offsets[e + 1])
+    sub = oracle.dual_gemm(sq.MXFP4, oracle.gather_rows(p, row_index[lo:hi]), oracle.expert_rows(q, e, n))
+    assert normwise(y[lo:hi], sub) <= GEMM_TOL
+
+
+def test_grouped_dual_gemm_identity_gather_and_empty_groups():
+    """row_index None (the rows already grouped), empty groups, one group
+    holding everything: equal to the plain dual GEMM of each group's rows."""
+    tokens, k, n = 260, 512, 192
+    x = si.activations("student_t4", tokens, k, 20, 50.0, 71)
+    W = si.weights(3 * n, k, 72)
+    p = oracle.prepare(sq.MXFP4, x, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, W)
+    sp, rs = sq.prepare(dev16(x), None, dense_backbone=True)
+    wq = sq.quantize_weight(dev16(W))
+    for offsets in ([0, 0, 260, 260], [0, 1, 129, 250]):
+        offsets = np.array(offsets, np.int64)
+        rows = int(offsets[-1])
+        y = host(sq.grouped_dual_gemm(sp, rs, wq, torch.from_numpy(offsets).to(DEV), rows))
+        ref = oracle.grouped_dual_gemm(sq.MXFP4, p, None, offsets, q, n)
+        assert normwise(y, ref) <= GEMM_TOL, offsets
+
+
+def test_grouped_dual_gemm_bad_offsets_stay_inside_y():
+    """Offsets that decrease or run past the row count (possible when routing
+    on the device goes wrong) are clamped to [0, rows]: Y's neighbours are
+    never written, and rows that only a well-formed group covers are right
+    (here group 0 alone owns rows 0-9; group 2's clamped range 10-39 overlaps
+    it, so rows 10-29 may hold either group's product)."""
+    tokens, k, n = 64, 256, 128
+    x = si.activations("normal", tokens, k, 4, 20.0, 81)
+    W = si.weights(4 * n, k, 82)
+    sp, rs = sq.prepare(dev16(x), None, dense_backbone=True)
+    wq = sq.quantize_weight(dev16(W))
+    rows = 40
+    offsets = torch.tensor([0, 30, 10, 500, 7], dtype=torch.int64, device=DEV)
+    buf = torch.full((rows + 64, n), 7.5, dtype=torch.float32, device=DEV)
+    out = buf[32:32 + rows]
+    sq.grouped_dual_gemm(sp, rs, wq, offsets, rows, out=out)
+    got = host(buf)
+    assert (got[:32] == 7.5).all() and (got[32 + rows:] == 7.5).all()
+    p = oracle.prepare(sq.MXFP4, x, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, W)
+    ref = oracle.grouped_dual_gemm(sq.MXFP4, p, None, [0, 10], q, n)
+    assert normwise(got[32:42], ref) <= GEMM_TOL
+    # rows 30-39 belong to group 2 alone: activation rows 30-39 with W rows 2n .. 3n - 1
+    assert normwise(got[62:72], oracle.dual_gemm(sq.MXFP4, oracle.gather_rows(p, np.arange(30, 40)),
+                                                 oracle.expert_rows(q, 2, n))) <= GEMM_TOL
+
+
+def test_grouped_dual_gemm_qwen3_layer_sampled():
+    """The bench shape: one Qwen3-30B-A3B MoE layer's gate+up expert GEMMs
+    (4096 tokens, 128 experts, 8 a token, n 1536, k 2048), sampled outputs."""
+    cfg = si.MOE_QWEN3_30B_A3B
+    tokens, k, n, experts = 4096, cfg["hidden"], 2 * cfg["intermediate"], cfg["experts"]
+    p, q, sp, rs, wq, row_index, offsets = _grouped_case(tokens, k, n, experts, cfg["top_k"], 91)
+    rows = int(offsets[-1])
+    y = host(sq.grouped_dual_gemm(sp, rs, wq, torch.from_numpy(offsets).to(DEV), rows,
+                                  row_index=torch.from_numpy(row_index).to(DEV)))
+    rng = np.random.default_rng(3)
+    pick = np.sort(rng.integers(0, rows, 512))
+    pick[:2] = [0, rows - 1]
+    group_of = np.searchsorted(offsets, pick, side="right") - 1
+    got, want = [], []
+    for e in np.unique(group_of):
+        sel = pick[group_of == e]
+        cols = rng.integers(0, n, len(sel))
+        pe = oracle.gather_rows(p, row_index[sel])
+        ref = oracle.dual_gemm_pairs(sq.MXFP4, pe, oracle.expert_rows(q, int(e), n),
+                                     np.arange(len(sel)), cols)
+        got.append(y[sel, cols])
+        want.append(ref)
+    assert normwise(np.concatenate(got), np.concatenate(want)) <= GEMM_TOL
+
+
 # ------------------------------------------------------------ weights
 @pytest.mark.parametrize("fmt,n,k", [(0, 256, 256), (0, 6144, 4096), (0, 33, 96), (1, 256, 256),
                                      (1, 1000, 4096)])
