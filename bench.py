@@ -25,6 +25,12 @@ device copy of known size), read from profiles/traffic.json when it was
 taken on the current kernel source, else null.  `cpu_baseline` times the
 CPU oracle on a bounded sample of the same workload.
 
+Other modes, each printing one JSON line of its own: --chain times one
+Llama-3.1-8B decoder layer's four linears with SharQ against the vendor bf16
+and FP8 GEMMs (and the residual-add and SiLU fusions against their unfused
+forms); --moe times one Qwen3-30B-A3B mixture-of-experts layer on the
+grouped dual GEMM.
+
 Traffic measurement (two counter runs, then the conversion on any host):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o pmc -- \
       python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --calibrate-copy [--workload W]

@@ -17,9 +17,10 @@
 // which accumulate into the same registers.
 //
 // Kernels: dual_gemm_dense_kernel (prefill, backbone in the dense layout the
-// preparation wrote), dual_gemm_decomp_kernel (prefill, the 2:4 backbone
-// expanded in LDS), dual_gemm_decode_kernel and dual_gemm_skinny_kernel (m <=
-// 32, bound by streaming W).  The prefill kernels stage 128-k steps of every
+// preparation wrote; its GROUPED form runs a mixture-of-experts layer's
+// expert GEMMs over gathered activation rows), dual_gemm_decomp_kernel
+// (prefill, the 2:4 backbone expanded in LDS), dual_gemm_decode_kernel and
+// dual_gemm_skinny_kernel (m <= 32, bound by streaming W).  The prefill kernels stage 128-k steps of every
 // operand in LDS with direct global -> LDS loads; LDS rows are 64 bytes (four
 // 16-byte chunks) and chunk c of row r sits at c ^ ((r >> 2) & 3), so sixteen
 // lanes reading one chunk of sixteen consecutive rows hit sixteen different

@@ -8,12 +8,17 @@
 // Work split: one lane owns one 32-element block of a row (one MXFP4 scale
 // block, eight 2:4 groups, or two NVFP4 blocks), so each lane reads 64
 // contiguous bytes and writes whole words of every output.  With RMSNorm a
-// row is spread over ceil(K / 2048) wavefronts of one workgroup; the sum of
-// squares follows a fixed binary tree: a tree over the 32 squares inside the
-// lane, a xor butterfly across the 64 lanes (2048-element chunks), and an
-// 8-leaf tree over the chunk sums in LDS (missing chunks are +0).  That is
-// the pairwise tree over 2^ceil(log2 K) leaves, whatever the wave count.
+// workgroup holds R whole rows (R = 1, 2 or 4 rows per wavefront, a row over
+// W wavefronts); the sum of squares follows a fixed binary tree: a tree over
+// the 32 squares inside the lane, a xor butterfly across the lanes of the
+// row, and a tree over the W wavefronts' sums in LDS (missing leaves +0).
+// That is the pairwise tree over 2^ceil(log2 K) leaves, whatever R and W.
 // Without normalization the blocks are independent and the grid is flat.
+//
+// Fused neighbours (the steps next to the preparation in a decoder layer):
+// the norm kernel's ADD variant adds the residual stream and the sublayer
+// output first (sharq_prepare_residual), and prep_silu_kernel forms SiLU(gate)
+// * up from the gate+up projection's fp32 output (sharq_prepare_silu_mul).
 //
 // MXFP4 element and scale conversions use the gfx950 instructions
 // v_cvt_scalef32_pk_fp4_{bf16,f32} (round to nearest even, saturating, sign
