@@ -272,15 +272,19 @@ __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN
   }
 }
 
-// Grouped tiles: the grid covers ceil(m / TBM) + groups tile rows, an upper
-// bound of the sum over groups of ceil(rows_e / TBM), so that the group sizes
-// can stay on the device.  The workgroup counts each group's tile rows (group
-// offsets clamped to [0, m] and made nondecreasing, so that no tile writes
-// outside Y whatever the offsets hold), scans them in LDS and finds the group
-// of its tile row; tile rows past the last group's end have no work.
+// Grouped tiles: the grid holds ceil(m / TBM) + groups tile rows times the
+// tile columns, an upper bound of the tiles the groups need, so that the group
+// sizes can stay on the device.  The workgroup counts each group's tile rows
+// (group offsets clamped to [0, m], so that no tile writes outside Y whatever
+// the offsets hold), scans them in LDS, and numbers the real tiles group by
+// group (tile row, then tile column).  Workgroups go to the 8 XCDs round
+// robin (XCD = id % 8); XCD x takes the x-th eighth of the real tiles, so that
+// every XCD gets the same share of the work and a group's tiles, which share
+// its weight and its gathered rows, stay in one L2.  Workgroups past their
+// XCD's share have no work.
 template <int TBM>
-__device__ __forceinline__ bool grouped_tile(const GemmArgs &a, uint32_t tm, int64_t &m0, int64_t &m_end,
-                                             int64_t &group) {
+__device__ __forceinline__ bool grouped_tile(const GemmArgs &a, uint32_t id, uint32_t gn, int64_t &m0,
+                                             int64_t &m_end, int64_t &group, uint32_t &tn) {
   __shared__ int32_t cnt[256];
   __shared__ int64_t found[3];
   const int t = threadIdx.x;
@@ -299,16 +303,20 @@ __device__ __forceinline__ bool grouped_tile(const GemmArgs &a, uint32_t tm, int
     cnt[t] = v;
     __syncthreads();
   }
+  const uint32_t real = (uint32_t)cnt[255] * gn, per = (real + 7) / 8;
+  const uint32_t local = id / 8, tile = (id % 8) * per + local;
   const int32_t end = cnt[t], begin = end - c;
-  if (c > 0 && (int32_t)tm >= begin && (int32_t)tm < end) {
+  const int32_t tm = (int32_t)(tile / gn);
+  if (local < per && tile < real && c > 0 && tm >= begin && tm < end) {
     found[0] = t;
-    found[1] = lo + (int64_t)((int32_t)tm - begin) * TBM;
+    found[1] = lo + (int64_t)(tm - begin) * TBM;
     found[2] = hi;
   }
   __syncthreads();
   group = found[0];
   m0 = found[1];
   m_end = found[2];
+  tn = tile % gn;
   return group >= 0;
 }
 
@@ -324,11 +332,11 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, li = lane & 31;
-  uint32_t tm, tn;
-  const uint32_t gm = GROUPED ? (uint32_t)((a.m + TBM - 1) / TBM + a.groups) : (uint32_t)((a.m + TBM - 1) / TBM);
-  xcd_tile(blockIdx.x, gm, (uint32_t)((a.n + TBN - 1) / TBN), band, tm, tn);
+  uint32_t tm = 0, tn = 0;
+  const uint32_t gn = (uint32_t)((a.n + TBN - 1) / TBN);
+  if (!GROUPED) xcd_tile(blockIdx.x, (uint32_t)((a.m + TBM - 1) / TBM), gn, band, tm, tn);
   int64_t m0 = (int64_t)tm * TBM, m_end = a.m, group = 0;
-  if (GROUPED && !grouped_tile<TBM>(a, tm, m0, m_end, group)) return;   // uniform: no work
+  if (GROUPED && !grouped_tile<TBM>(a, blockIdx.x, gn, m0, m_end, group, tn)) return;   // uniform: no work
   const int64_t n0 = (int64_t)tn * TBN;
   const ARows arow{a.row_index, m0, m_end, GROUPED};
   const int64_t w_row0 = GROUPED ? group * a.n : 0, w_rows = GROUPED ? (group + 1) * a.n : a.n;
@@ -383,9 +391,10 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
 
 template <int TBM, int TBN, int NW, int STAGES>
 void launch_grouped(const GemmArgs &a, hipStream_t s) {
+  // an upper bound of the real tiles, rounded up to whole rounds of the 8 XCDs
   const int64_t gm = (a.m + TBM - 1) / TBM + a.groups, gn = (a.n + TBN - 1) / TBN;
-  dual_gemm_dense_kernel<TBM, TBN, NW, STAGES, true>
-      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, TBN <= 128 ? 3 : 2));
+  const int64_t tiles = (gm * gn + 7) / 8 * 8;
+  dual_gemm_dense_kernel<TBM, TBN, NW, STAGES, true><<<dim3((unsigned)tiles), dim3(64 * NW), 0, s>>>(a, 0);
 }
 
 template <int TBM, int TBN, int NW, int STAGES>
