@@ -323,7 +323,7 @@ __device__ __forceinline__ bool grouped_tile(const GemmArgs &a, uint32_t id, uin
 template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false>
 __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, uint32_t band) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
-  static_assert(!GROUPED || 64 * NW >= 256, "the group scan takes one thread a group, up to 256");
+  static_assert(!GROUPED || 64 * NW == 256, "the group scan takes one thread a group: 256 threads, 256 groups");
   constexpr int TN = TBN / 64;
   using P = DPlan<TBM, TBN, NW>;
   __shared__ DStage<TBM, TBN> st[STAGES];
