@@ -13,7 +13,10 @@
  *     normalization, mask generation and residual construction;
  *   - sentence 7: MXFP4 and NVFP4 formats.
  * Concrete readings (2:4 along K, RMSNorm, block sizes, rounding) are stated
- * at each entry point.
+ * at each entry point.  Beyond the path itself, sharq_prepare_residual and
+ * sharq_prepare_silu_mul fuse the decoder layer's neighbouring steps (the
+ * residual add, SiLU(gate) * up) into the preparation, and
+ * sharq_grouped_dual_gemm runs a mixture-of-experts layer's expert GEMMs.
  *
  * Conventions for every entry point:
  *   - All matrices are row-major, K contiguous.  X is [m, k] bf16, W is
