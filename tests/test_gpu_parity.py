@@ -304,6 +304,9 @@ def _grouped_case(tokens, k, n, experts, top_k, seed, layout=sq.LAYOUT_KSTEP_MAJ
     (300, 2048, 320, 8, 2, sq.LAYOUT_KSTEP_MAJOR),
     (200, 768, 256, 16, 4, sq.LAYOUT_KSTEP_MAJOR),
     (150, 256, 200, 5, 3, sq.LAYOUT_ROW_MAJOR),
+    (4096, 256, 512, 32, 8, sq.LAYOUT_KSTEP_MAJOR),    # enough tiles for the 128 x 256 tiles
+    (4096, 256, 384, 32, 8, sq.LAYOUT_KSTEP_MAJOR),    # 128 x 256, n ragged
+    (4096, 256, 256, 32, 8, sq.LAYOUT_KSTEP_MAJOR),    # 128 x 192, n ragged
 ])
 def test_grouped_dual_gemm(tokens, k, n, experts, top_k, layout):
     """Grouped (mixture-of-experts) dual GEMM over gathered activation rows
