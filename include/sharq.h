@@ -15,7 +15,9 @@
  * Concrete readings (2:4 along K, RMSNorm, block sizes, rounding) are stated
  * at each entry point.  Beyond the path itself, sharq_prepare_residual and
  * sharq_prepare_silu_mul fuse the decoder layer's neighbouring steps (the
- * residual add, SiLU(gate) * up) into the preparation, and
+ * residual add, SiLU(gate) * up) into the preparation,
+ * sharq_dual_gemm_silu_prepare runs the gate+up GEMM with SiLU(gate) * up and
+ * the down projection's preparation in its epilogue, and
  * sharq_grouped_dual_gemm runs a mixture-of-experts layer's expert GEMMs.
  *
  * Conventions for every entry point:
@@ -241,6 +243,37 @@ sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t
                                     const sharq_fp4_view *resid_out, void *stream);
 
 /*
+ * The gate+up projection of a gated MLP with the down projection's
+ * preparation fused into its epilogue (the steps on either side of the path in
+ * a decoder layer; abstract, sentences 3-5 for the GEMM and the preparation):
+ *   Y = sharq_dual_gemm's product of (sparse, resid) [m, k] and the weight
+ *       views [2 inter, k]: rows 0 .. inter - 1 of W are the gate projection,
+ *       rows inter .. 2 inter - 1 the up projection;
+ *   x = bf16(g / (1 + exp(-g)) * u) with g = Y[:, j], u = Y[:, inter + j]
+ *       (the fp32 values sharq_dual_gemm would store), exactly as
+ *       sharq_prepare_silu_mul forms it;
+ *   then sharq_prepare's steps 2-4 on x [m, inter] (no normalization) into
+ *   sparse_out and resid_out (dense_codes written when non-NULL).
+ * Neither Y nor x is written: each workgroup forms x for 128 rows and 128
+ * columns in LDS and prepares it there.  The outputs equal, byte for byte,
+ * sharq_dual_gemm (MXFP4, DENSE_EXPANDED) followed by sharq_prepare_silu_mul
+ * on the two halves of Y.
+ * MXFP4 only; reads the dense backbone view (sparse->dense_codes required,
+ * SHARQ_ERR_UNSUPPORTED otherwise).  The outputs must not overlap the inputs.
+ * Requirements: m >= 1; inter >= 128, inter % 128 == 0; k >= 128,
+ * k % 128 == 0; the input views as sharq_dual_gemm requires (m activation
+ * rows, 2 inter weight rows, one payload); the output views as
+ * sharq_prepare requires for m rows of length inter, with one layout.
+ */
+sharq_status sharq_dual_gemm_silu_prepare(sharq_format fmt, const sharq_fp4_view *sparse,
+                                          const sharq_fp4_view *resid,
+                                          const sharq_fp4_view *w_sparse_view,
+                                          const sharq_fp4_view *w_dense_view, int64_t m,
+                                          int64_t inter, int64_t k,
+                                          const sharq_fp4_view *sparse_out,
+                                          const sharq_fp4_view *resid_out, void *stream);
+
+/*
  * Dual-path GEMM (abstract, sentences 4 and 5):
  *   Y = deq(backbone) * deq(W)^T + deq(residual) * deq(W)^T
  * accumulated in fp32 and stored as fp32 [m, n] (row stride ld_y).  NVFP4:
@@ -312,7 +345,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 6
+#define SHARQ_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

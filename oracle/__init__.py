@@ -298,6 +298,18 @@ def grouped_dual_gemm(fmt: int, prep: dict, row_index, offsets, wq: dict, n: int
     return y
 
 
+def dual_gemm_silu_prepare(fmt: int, prep: dict, wq: dict, dense_backbone: bool = False):
+    """The gate+up projection of a gated MLP followed by the down projection's
+    preparation: Y = the dual GEMM of the prepared activations with W
+    [2 inter, k], whose first inter rows are the gate and last inter rows the
+    up projection (abstract, sentences 4-5); x = bf16(silu(gate) * up) with
+    gate = Y[:, :inter] and up = Y[:, inter:] as fp32; then the preparation of
+    x without a norm (sentences 3 and 5).  Returns x and prepare(fmt, x)."""
+    y = dual_gemm(fmt, prep, wq)
+    inter = y.shape[1] // 2
+    return prepare_silu_mul(fmt, y[:, :inter], y[:, inter:], dense_backbone)
+
+
 def dual_gemm_pairs(fmt: int, prep: dict, wq: dict, rows, cols, want_f64: bool = False):
     """Y at the listed (row, col) pairs only (sorted by row is fastest)."""
     rows = np.ascontiguousarray(rows, dtype=np.int64)

@@ -40,9 +40,9 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 # every symbol include/sharq.h declares
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_prepare_silu_mul",
-           "sharq_dual_gemm", "sharq_grouped_dual_gemm", "sharq_bytes", "sharq_status_str",
-           "sharq_abi_version")
-ABI_VERSION = 6
+           "sharq_dual_gemm", "sharq_dual_gemm_silu_prepare", "sharq_grouped_dual_gemm", "sharq_bytes",
+           "sharq_status_str", "sharq_abi_version")
+ABI_VERSION = 7
 
 
 class SharqError(RuntimeError):
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare_residual.restype = ctypes.c_int
         L.sharq_prepare_silu_mul.argtypes = [ctypes.c_int, P, I64, P, I64, I64, I64, V, V, P]
         L.sharq_prepare_silu_mul.restype = ctypes.c_int
+        L.sharq_dual_gemm_silu_prepare.argtypes = [ctypes.c_int, V, V, V, V, I64, I64, I64, V, V, P]
+        L.sharq_dual_gemm_silu_prepare.restype = ctypes.c_int
         L.sharq_grouped_dual_gemm.argtypes = [ctypes.c_int, V, V, I64, P, P, I64, I64, V, V, I64, I64,
                                               P, I64, P]
         L.sharq_grouped_dual_gemm.restype = ctypes.c_int
@@ -414,6 +416,34 @@ def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AU
         out = torch.empty((sp.rows, w.rows), dtype=torch.float32, device=w.codes.device)
     bind_dual_gemm(sp, rs, w, out, variant, w_dense_scales, stream)()
     return out
+
+
+def bind_dual_gemm_silu_prepare(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, out_sp: FP4Tensor,
+                                out_rs: FP4Tensor, stream=None) -> BoundCall:
+    """sharq_dual_gemm_silu_prepare: the gate+up dual GEMM (W: inter gate rows,
+    then inter up rows) with x = bf16(silu(gate) * up) prepared into (out_sp,
+    out_rs) [m, inter] in its epilogue, bound for repeated calls."""
+    m, k = sp.rows, sp.k
+    if w.rows % 2:
+        raise ValueError("the gate+up weight must have 2 * inter rows")
+    inter = w.rows // 2
+    ws, vs, vr, vos, vor = w.view(), sp.view(), rs.view(), out_sp.view(), out_rs.view()
+    args = (ctypes.c_int(sp.fmt), ctypes.byref(vs), ctypes.byref(vr), ctypes.byref(ws), ctypes.byref(ws),
+            ctypes.c_int64(m), ctypes.c_int64(inter), ctypes.c_int64(k), ctypes.byref(vos), ctypes.byref(vor),
+            _stream_ptr(stream))
+    return BoundCall(lib().sharq_dual_gemm_silu_prepare, args, "sharq_dual_gemm_silu_prepare",
+                     (sp, rs, w, out_sp, out_rs, ws, vs, vr, vos, vor))
+
+
+def dual_gemm_silu_prepare(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, dense_backbone: bool = False,
+                           layout: Optional[int] = None, stream=None):
+    """The gate+up projection with SiLU(gate) * up and the preparation fused
+    into its epilogue (MXFP4): returns the down projection's (backbone,
+    residual) operands [m, inter] without writing the fp32 product."""
+    inter = w.rows // 2
+    out_sp, out_rs = alloc_prepared(MXFP4, sp.rows, inter, w.codes.device, dense_backbone, layout)
+    bind_dual_gemm_silu_prepare(sp, rs, w, out_sp, out_rs, stream)()
+    return out_sp, out_rs
 
 
 def bind_grouped_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, group_offsets, rows: int, out,

@@ -6,14 +6,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp4_device.h"
+
 namespace sharq {
 namespace gemm {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-// clang vector types (not HIP's uint4 struct) so that staged data stays in registers
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 128;   // k per pipeline step
 

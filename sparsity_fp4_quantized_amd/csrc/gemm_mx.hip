@@ -38,6 +38,7 @@
 #include "fp4_device.h"
 #include "gemm_common.h"
 #include "kernels.h"
+#include "prep_block.h"
 
 namespace sharq {
 namespace {
@@ -101,10 +102,25 @@ struct ARows {
   }
 };
 
-template <int TBM, int TBN, int NW>
+// Tile rows of W: plain tiles stream rows n0 .. of W (offsets relative to
+// row n0); a gate+up tile (SPLIT) reads the gate rows j0 .. j0 + hb - 1 as its
+// first hb rows and the up rows half + j0 .. as its last hb (offsets relative
+// to row 0), so that one tile holds the gate and up columns of the same j.
+template <bool SPLIT>
+struct WRows {
+  int64_t j0, half;
+  int hb;
+  __device__ __forceinline__ uint32_t operator()(int r) const {
+    if (!SPLIT) return (uint32_t)r;
+    return (uint32_t)(r < hb ? j0 + r : half + j0 + (r - hb));
+  }
+};
+
+template <int TBM, int TBN, int NW, bool SPLIT = false>
 __device__ __forceinline__ void plan_loads(const GemmArgs &a, int64_t m0, int64_t n0, int wave,
                                            int lane, DRsrc &R, DOffs<TBM, TBN, NW> &O,
-                                           const ARows &arow, int64_t w_row0, int64_t w_rows) {
+                                           const ARows &arow, int64_t w_row0, int64_t w_rows,
+                                           const WRows<SPLIT> &wrow = WRows<SPLIT>{0, 0, 0}) {
   using P = DPlan<TBM, TBN, NW>;
   const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const int64_t steps = a.k / BK;
@@ -125,7 +141,7 @@ __device__ __forceinline__ void plan_loads(const GemmArgs &a, int64_t m0, int64_
       O.chunk[j] = arow(16 * q + lrow) * rs + lchunk * 16;
     } else {
       q -= 2 * P::kA;
-      O.chunk[j] = (uint32_t)(16 * q + lrow) * R.w.row_stride + lchunk * 16;
+      O.chunk[j] = wrow(16 * q + lrow) * R.w.row_stride + lchunk * 16;
     }
   }
 #pragma unroll
@@ -139,7 +155,7 @@ __device__ __forceinline__ void plan_loads(const GemmArgs &a, int64_t m0, int64_
       t -= 2 * (TBM / 64);
       uint32_t rs = R.sws.row_stride;
       if (t >= TBN / 64) { t -= TBN / 64; rs = R.swd.row_stride; }
-      O.scale[j] = (uint32_t)(64 * t + lane) * rs;
+      O.scale[j] = wrow(64 * t + lane) * rs;
     }
   }
 }
@@ -320,10 +336,136 @@ __device__ __forceinline__ bool grouped_tile(const GemmArgs &a, uint32_t id, uin
   return group >= 0;
 }
 
-template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false>
-__global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, uint32_t band) {
+// The steps of the epilogue that depend on the wavefront's half, with the
+// half fixed at compile time (a run-time index into the accumulators would
+// put them in scratch memory).  KEEP: the 32-row half (it) this wavefront
+// finishes; 0 for the gate wavefront, 1 for the up wavefront.
+template <int KEEP, int TN>
+__device__ __forceinline__ void silu_hand_over(const v16f (&acc)[2][TN], float *mine, int lane) {
+#pragma unroll
+  for (int jt = 0; jt < TN; ++jt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mine[(jt * 16 + r) * 64 + lane] = acc[1 - KEEP][jt][r];
+}
+
+// 16 values at a time: their LDS reads go out together, the fp32 evaluation
+// runs without branches, and only the lanes and values that need it repeat
+// in binary64 (evaluated one by one with a branch each, every value waited
+// for its own LDS read and took three branches: 43 us of the gate+up GEMM).
+template <int KEEP, int TN>
+__device__ __forceinline__ void silu_finish(v16f (&acc)[2][TN], const float *theirs, int lane) {
+#pragma unroll
+  for (int jt = 0; jt < TN; ++jt) {
+    float other[16];
+    uint32_t x[16], slow = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) other[r] = theirs[(jt * 16 + r) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float g = KEEP == 0 ? acc[KEEP][jt][r] : other[r];
+      const float u = KEEP == 0 ? other[r] : acc[KEEP][jt][r];
+      slow |= silu_mul_fast(g, u, x[r]) ? 0u : 1u << r;
+    }
+    if (slow) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (slow & (1u << r)) {
+          const float g = KEEP == 0 ? acc[KEEP][jt][r] : other[r];
+          const float u = KEEP == 0 ? other[r] : acc[KEEP][jt][r];
+          x[r] = silu_mul_slow(g, u);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[KEEP][jt][r] = __uint_as_float(x[r]);
+  }
+}
+
+template <int KEEP, int TN, int kHs>
+__device__ __forceinline__ void silu_put_x(const v16f (&acc)[2][TN], uint16_t *xs, int wm, int h, int li) {
+#pragma unroll
+  for (int jt = 0; jt < TN; ++jt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + KEEP * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      xs[row * kHs + jt * 32 + li] = (uint16_t)__float_as_uint(acc[KEEP][jt][r]);
+    }
+}
+
+// The exchange and x = bf16(silu(g) u) for this wavefront's half, then the x
+// tile into LDS.  One function per half with its barriers inside (both
+// halves pass the same four): with the halves' steps merged after run-time
+// branches, the accumulators of both halves ended up in scratch memory.
+template <int KEEP, int TN, int kHs, int kVals>
+__device__ __forceinline__ void silu_x_tile(v16f (&acc)[2][TN], float *xch, uint16_t *xs, int wave,
+                                            int wm, int h, int li, int lane) {
+  __syncthreads();                      // every wavefront is done with the stages
+  silu_hand_over<KEEP>(acc, xch + wave * kVals, lane);
+  __syncthreads();
+  silu_finish<KEEP>(acc, xch + (wave ^ 1) * kVals, lane);
+  __syncthreads();                      // the exchange is read before the x tile overwrites it
+  silu_put_x<KEEP, TN, kHs>(acc, xs, wm, h, li);
+  __syncthreads();
+}
+
+// SiLU(gate) * up and the preparation of the result (the down projection's
+// input), from the accumulators of a gate+up tile: its first TBN / 2 columns
+// are the gate columns j0 .. j0 + TBN / 2 - 1 and its last TBN / 2 the up
+// columns of the same j, so wavefront (wm, 0) holds the gate and wavefront
+// (wm, 1) the up accumulators of rows 64 wm .. 64 wm + 63, lane for lane.
+// Each of the two hands the other the half (32 rows) it does not finish
+// itself through LDS (fp32, lane-major: no bank conflicts); each forms x =
+// bf16(silu(g) u) for its own half, exactly as the preparation kernel does
+// from the stored fp32 product; the tile of x (bf16, rows padded by 16 bytes)
+// then goes to LDS, and every lane prepares 32-column blocks of it exactly as
+// the preparation kernel prepares a block.  The stages' LDS is free by then.
+template <int TBM, int TBN, int STAGES>
+__device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES], v16f (&acc)[2][TBN / 64],
+                                                   const PrepArgs &p, int64_t m0, int64_t j0, int wave,
+                                                   int lane) {
+  constexpr int TN = TBN / 64, HB = TBN / 2, NB = HB / 32;
+  constexpr int kVals = TN * 16 * 64;   // floats one wavefront hands over
+  constexpr int kHs = HB + 8;           // LDS row stride of the x tile, in bf16
+  static_assert(TBM == 128 && HB % 32 == 0, "four wavefronts: two row halves x (gate, up)");
+  static_assert(4 * kVals * sizeof(float) <= sizeof(st), "the exchange fits in the stages");
+  static_assert(TBM * kHs * sizeof(uint16_t) <= sizeof(st), "the x tile fits in the stages");
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, li = lane & 31;
+  float *xch = reinterpret_cast<float *>(&st[0]);
+  uint16_t *xs = reinterpret_cast<uint16_t *>(&st[0]);
+  if (wn == 0) silu_x_tile<0, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane);
+  else silu_x_tile<1, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane);
+  // blocks of a row sit in adjacent lanes: k-step-major outputs leave as
+  // contiguous runs (the tile's columns are one 128-k step when HB = 128)
+#pragma unroll
+  for (int i = 0; i < TBM * NB / 256; ++i) {
+    const int q = (int)threadIdx.x + 256 * i, r = q / NB, b = q % NB;
+    const int64_t row = m0 + r;
+    if (row >= p.m) continue;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xs + r * kHs + 32 * b);
+    uint32_t xw[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 t = src[c];
+      xw[4 * c + 0] = t.x;
+      xw[4 * c + 1] = t.y;
+      xw[4 * c + 2] = t.z;
+      xw[4 * c + 3] = t.w;
+    }
+    float xf[32];
+    unpack32(xw, xf);
+    BlockOut o;
+    quantize_block_mx(xw, xf, o);
+    store_block<0, false>(p, row, j0 / 32 + b, o);
+  }
+}
+
+// One tile of the dense-operand GEMM.  SILU: a gate+up tile whose epilogue is
+// silu_prep_epilogue (W's rows: n / 2 gate rows, then n / 2 up rows) instead
+// of the fp32 Y stores.
+template <int TBM, int TBN, int NW, int STAGES, bool GROUPED, bool SILU>
+__device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, const PrepArgs *prep) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
   static_assert(!GROUPED || 64 * NW == 256, "the group scan takes one thread a group: 256 threads, 256 groups");
+  static_assert(!(GROUPED && SILU), "no grouped gate+up epilogue");
   constexpr int TN = TBN / 64;
   using P = DPlan<TBM, TBN, NW>;
   __shared__ DStage<TBM, TBN> st[STAGES];
@@ -352,7 +494,11 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
   const int ksteps = (int)(a.k / BK);
   DRsrc R;
   DOffs<TBM, TBN, NW> O;
-  plan_loads<TBM, TBN, NW>(a, m0, n0, wave, lane, R, O, arow, w_row0, w_rows);
+  if constexpr (SILU)
+    plan_loads<TBM, TBN, NW, true>(a, m0, 0, wave, lane, R, O, arow, 0, a.n,
+                                   WRows<true>{n0 / 2, a.n / 2, TBN / 2});
+  else
+    plan_loads<TBM, TBN, NW>(a, m0, n0, wave, lane, R, O, arow, w_row0, w_rows);
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < ksteps) issue_stage<TBM, TBN, NW>(R, O, wave, p, st[p]);
@@ -372,6 +518,10 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
     cur = cur == STAGES - 1 ? 0 : cur + 1;
   }
 
+  if constexpr (SILU) {
+    silu_prep_epilogue<TBM, TBN, STAGES>(st, acc, *prep, m0, n0 / 2, wave, lane);
+    return;
+  }
   // Y leaves with non-temporal stores: nothing here reads it back, and fp32
   // tiles left dirty in the L2s (qkv shape: 50 MB against 32 MB of L2) slowed
   // the kernel's end and the next kernel's start (qkv GEMM 55.5 -> 52.9 us).
@@ -387,6 +537,20 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
         if (row < m_end) __builtin_nontemporal_store(acc[it][jt][r], &a.y[row * a.ld_y + col]);
       }
     }
+}
+
+template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false>
+__global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, uint32_t band) {
+  dense_tile<TBM, TBN, NW, STAGES, GROUPED, false>(a, band, nullptr);
+}
+
+// The gate+up projection with SiLU(gate) * up and the down projection's
+// preparation in its epilogue (no fp32 Y).  Two wavefronts per SIMD (two
+// workgroups per CU, as the plain kernel): left alone the epilogue's
+// registers took the kernel to 276 VGPRs, one wavefront per SIMD.
+template <int TBM, int TBN, int NW, int STAGES>
+__global__ __launch_bounds__(64 * NW, 2) void dual_gemm_silu_prep_kernel(GemmArgs a, uint32_t band, PrepArgs p) {
+  dense_tile<TBM, TBN, NW, STAGES, false, true>(a, band, &p);
 }
 
 template <int TBM, int TBN, int NW, int STAGES>
@@ -876,6 +1040,16 @@ __global__ __launch_bounds__(256) void dual_gemm_decode_kernel(GemmArgs a) {
 // short K makes each tile's prologue and epilogue weigh more, and wider tiles
 // have fewer: Qwen3-30B-A3B's gate+up 189 -> 176 us against 128 x 192), else
 // 128 x 192 or 128 x 128.
+hipError_t launch_dual_gemm_silu_prep_mx(const GemmArgs &a, const PrepArgs &p, hipStream_t s) {
+  // 128 x 256 tiles: 128 columns of x (one 128-k step of the down
+  // projection's operands) from 128 gate and 128 up columns
+  constexpr int TBM = 128, TBN = 256;
+  const int64_t gm = (a.m + TBM - 1) / TBM, gn = a.n / TBN;
+  dual_gemm_silu_prep_kernel<TBM, TBN, 4, 2>
+      <<<dim3((unsigned)(gm * gn)), dim3(256), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, 2), p);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_dual_gemm_mx(const GemmArgs &a, hipStream_t s) {
   const int64_t mt = (a.m + 127) / 128 + a.groups;
   if (mt * ((a.n + 255) / 256) >= 512 && a.k <= 8192)

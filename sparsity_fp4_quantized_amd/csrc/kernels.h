@@ -77,6 +77,9 @@ hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s);
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s);
 hipError_t launch_grouped_dual_gemm_mx(const GemmArgs &a, hipStream_t s);
+// gate+up dual GEMM (a.n = 2 i: i gate rows, then i up rows of W; i % 128 == 0)
+// with x = bf16(silu(gate) * up) prepared into p's outputs ([a.m, i], no norm)
+hipError_t launch_dual_gemm_silu_prep_mx(const GemmArgs &a, const PrepArgs &p, hipStream_t s);
 hipError_t launch_dual_gemm_nv(const GemmArgs &a, int variant, hipStream_t s);
 
 }  // namespace sharq

@@ -211,6 +211,54 @@ sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t
   return from_hip(sharq::launch_prepare_silu_mx(a, static_cast<hipStream_t>(stream)));
 }
 
+sharq_status sharq_dual_gemm_silu_prepare(sharq_format fmt, const sharq_fp4_view *sp,
+                                          const sharq_fp4_view *rs, const sharq_fp4_view *wsv,
+                                          const sharq_fp4_view *wdv, int64_t m, int64_t inter,
+                                          int64_t k, const sharq_fp4_view *sp_out,
+                                          const sharq_fp4_view *rs_out, void *stream) {
+  if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
+  if (fmt != SHARQ_MXFP4) return SHARQ_ERR_UNSUPPORTED;
+  if (!sp || !rs || !wsv || !wdv || !sp_out || !rs_out) return SHARQ_ERR_NULL;
+  if (m < 1 || inter < 128 || inter % 128 || k < 128 || k % 128) return SHARQ_ERR_SHAPE;
+  CHECK(check_layout(sp, k));
+  CHECK(check_layout(rs, k));
+  CHECK(check_layout(wsv, k));
+  CHECK(check_layout(wdv, k));
+  if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
+  if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
+    return SHARQ_ERR_SHAPE;
+  if (!sp->dense_codes) return SHARQ_ERR_UNSUPPORTED;   // reads the dense backbone view
+  const int64_t n = 2 * inter;
+  CHECK(check_array(sp->dense_codes, sp->ld_dense, sp->layout, m, k, k / 2, 16, 64, 16));
+  CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, m, k, k / 2, 16, 64, 16));
+  CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, n, k, k / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp, m, k, true));
+  CHECK(check_scales(fmt, rs, m, k, true));
+  CHECK(check_scales(fmt, wsv, n, k, true));
+  CHECK(check_scales(fmt, wdv, n, k, true));
+  // the outputs: the preparation's views of x [m, inter]
+  CHECK(check_layout(sp_out, inter));
+  CHECK(check_layout(rs_out, inter));
+  if (sp_out->layout != rs_out->layout) return SHARQ_ERR_SHAPE;
+  const int L = sp_out->layout;
+  CHECK(check_array(sp_out->codes, sp_out->ld_codes, L, m, inter, inter / 4, 8, 32, 16));
+  CHECK(check_array(sp_out->meta, sp_out->ld_meta, L, m, inter, inter / 8, 4, 16, 16));
+  CHECK(check_array(rs_out->codes, rs_out->ld_codes, L, m, inter, inter / 2, 16, 64, 16));
+  if (sp_out->dense_codes)
+    CHECK(check_array(sp_out->dense_codes, sp_out->ld_dense, L, m, inter, inter / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp_out, m, inter, false));
+  CHECK(check_scales(fmt, rs_out, m, inter, false));
+  GemmArgs a{sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->dense_codes, sp->ld_dense,
+             sp->scales, sp->ld_scales, rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
+             wsv->codes, wsv->ld_codes, wsv->scales, wsv->ld_scales, wdv->scales, wdv->ld_scales,
+             nullptr, nullptr, nullptr, 0, m, n, k, ksm(sp), ksm(rs), ksm(wsv)};
+  PrepArgs o{nullptr, 0, m, inter, nullptr, 0.0f,
+             sp_out->codes, sp_out->ld_codes, sp_out->meta, sp_out->ld_meta, sp_out->scales,
+             sp_out->ld_scales, rs_out->codes, rs_out->ld_codes, rs_out->scales, rs_out->ld_scales,
+             sp_out->dense_codes, sp_out->ld_dense, nullptr, ksm(sp_out), ksm(rs_out)};
+  return from_hip(sharq::launch_dual_gemm_silu_prep_mx(a, o, static_cast<hipStream_t>(stream)));
+}
+
 sharq_status sharq_grouped_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp,
                                      const sharq_fp4_view *rs, int64_t tokens,
                                      const int32_t *row_index, const int64_t *group_offsets,

@@ -136,6 +136,22 @@ def gamma(k: int, seed: Optional[int]) -> np.ndarray:
     return f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32))
 
 
+# Magnitudes of the E2M1 element format (OCP Microscaling v1.0).
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def fp4_grid(rows: int, k: int, exp2: int, seed: int) -> np.ndarray:
+    """bf16 bits [rows, k] of values drawn uniformly from the signed E2M1 grid
+    times 2^exp2 (magnitude index, then sign, from ``default_rng(seed)``).
+    Block-scaled FP4 holds every 32-block of such values exactly, and their
+    products and sums stay exact in fp32 for the sizes used here, so these
+    inputs make a GEMM's result independent of its summation order."""
+    rng = np.random.default_rng(seed)
+    mag = np.asarray(E2M1_GRID)[rng.integers(0, 8, (rows, k))]
+    sign = rng.choice(np.array([-1.0, 1.0]), (rows, k))
+    return f32_to_bf16_bits((mag * sign * 2.0 ** exp2).astype(np.float32))
+
+
 def gate_up_output(m: int, f: int, seed: int, n_outlier: int = 72, outlier_scale: float = 30.0):
     """fp32 gate and up [m, f] standing in for the gate+up projection's output
     in front of the down projection: gate ~ N(0, 2^2), up ~ N(0, 1) with

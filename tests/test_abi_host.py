@@ -162,6 +162,44 @@ def test_prepare_silu_mul_validation(kwargs, status):
     assert prep_silu(**kwargs) == status
 
 
+NULLV = object()   # pass a NULL view pointer
+
+
+def silu_gemm(fmt=0, m=16, inter=128, k=256, sp=None, rs=None, ws=None, wd=None, osp=None, ors=None):
+    sp = sp or view(ld_codes=64, dense=FAKE, ld_dense=128)
+    rs = rs or view(meta=None)
+    ws = ws or view(meta=None)
+    wd = wd or ws
+    osp = osp or view(ld_codes=32, ld_meta=16, ld_scales=4)
+    ors = ors or view(meta=None, ld_codes=64, ld_scales=4)
+    ref = [None if v is NULLV else ctypes.byref(v) for v in (sp, rs, ws, wd, osp, ors)]
+    return sq.lib().sharq_dual_gemm_silu_prepare(fmt, ref[0], ref[1], ref[2], ref[3], m, inter, k,
+                                                 ref[4], ref[5], None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(fmt=1), sq.ERR_UNSUPPORTED),
+    (dict(fmt=7), sq.ERR_UNSUPPORTED),
+    (dict(sp=NULLV), sq.ERR_NULL),
+    (dict(osp=NULLV), sq.ERR_NULL),
+    (dict(ors=NULLV), sq.ERR_NULL),
+    (dict(m=0), sq.ERR_SHAPE),
+    (dict(inter=64), sq.ERR_SHAPE),
+    (dict(inter=192), sq.ERR_SHAPE),                    # x's columns come in 128-column tiles
+    (dict(k=192), sq.ERR_SHAPE),
+    (dict(sp=view(ld_codes=64)), sq.ERR_UNSUPPORTED),   # no dense backbone view
+    (dict(wd=view(meta=None, codes=FAKE + 4096)), sq.ERR_SHAPE),   # two payloads
+    (dict(ws=view(meta=None, ld_codes=100)), sq.ERR_SHAPE),
+    (dict(ws=view(meta=None, ld_scales=6)), sq.ERR_SHAPE),
+    (dict(osp=view(ld_codes=31, ld_meta=16, ld_scales=4)), sq.ERR_SHAPE),
+    (dict(ors=view(meta=None, ld_codes=64, scales=None)), sq.ERR_NULL),
+    (dict(osp=ksm(), ors=view(meta=None, ld_codes=64, ld_scales=4)), sq.ERR_SHAPE),   # output layouts differ
+    (dict(osp=ksm(8), ors=ksm(8, meta=None)), sq.ERR_SHAPE),                         # rows per step < m
+])
+def test_dual_gemm_silu_prepare_validation(kwargs, status):
+    assert silu_gemm(**kwargs) == status
+
+
 def grouped(fmt=0, tokens=16, idx=FAKE, offs=FAKE, groups=2, rows=32, n=256, k=256, y=FAKE,
             ld_y=256, sp=None, rs=None, ws=None, wd=None):
     sp = sp or view(ld_codes=64, dense=FAKE, ld_dense=128)

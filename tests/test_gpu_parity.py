@@ -395,6 +395,79 @@ def test_grouped_dual_gemm_qwen3_layer_sampled():
     assert normwise(np.concatenate(got), np.concatenate(want)) <= GEMM_TOL
 
 
+# ------------------------------------------------------------ gate+up GEMM with SiLU(gate) * up and the preparation
+KSM, ROW = sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR
+
+
+def _silu_gemm_grid_case(m, inter, k, seed, layout):
+    """FP4-grid X [m, k] and W [2 inter, k] (see synth_inputs.fp4_grid): the
+    dual GEMM of their FP4 operands is exact in fp32 in any summation order."""
+    xb = si.fp4_grid(m, k, 0, seed)
+    wb = si.fp4_grid(2 * inter, k, -6, seed + 1)
+    sp, rs = sq.prepare(dev16(xb), None, dense_backbone=True, layout=layout)
+    wq = sq.quantize_weight(dev16(wb), layout=layout)
+    return xb, wb, sp, rs, wq
+
+
+@pytest.mark.parametrize("m,inter,k,in_layout,out_layout,dense", [
+    (200, 256, 384, KSM, KSM, True), (1, 128, 128, KSM, KSM, True), (300, 384, 512, ROW, ROW, True),
+    (129, 128, 256, ROW, KSM, False), (256, 512, 1024, KSM, ROW, True), (37, 1024, 256, KSM, KSM, False)])
+def test_dual_gemm_silu_prepare_exact(m, inter, k, in_layout, out_layout, dense):
+    """The gate+up GEMM with SiLU(gate) * up and the preparation in its
+    epilogue, on FP4-grid inputs (the GEMM exact in fp32): every prepared
+    array byte for byte against the oracle's GEMM -> SiLU(gate) * up ->
+    preparation, in full; ragged m, one to eight column tiles, both layouts
+    of the inputs and of the outputs, with and without the dense backbone
+    view."""
+    xb, wb, sp, rs, wq = _silu_gemm_grid_case(m, inter, k, 71, in_layout)
+    p = oracle.prepare(sq.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    _, ref = oracle.dual_gemm_silu_prepare(sq.MXFP4, p, q, dense_backbone=True)
+    osp, ors = sq.dual_gemm_silu_prepare(sp, rs, wq, dense_backbone=dense, layout=out_layout)
+    _compare_prep(f"silu gemm m{m} inter{inter} k{k}", osp, ors, ref, dense=dense)
+
+
+def test_dual_gemm_silu_prepare_llama_gate_up_sampled():
+    """Llama-3.1-8B's gate+up at prefill (m 2048, inter 14336, k 4096, the
+    bench's launch) on FP4-grid inputs: sampled rows of every output array
+    byte for byte against the oracle (the preparation is row-independent)."""
+    m, inter, k = 2048, 14336, 4096
+    xb, wb, sp, rs, wq = _silu_gemm_grid_case(m, inter, k, 81, KSM)
+    osp, ors = sq.dual_gemm_silu_prepare(sp, rs, wq, dense_backbone=True)
+    rows = np.array([0, 1, 127, 128, 1000, 2047])
+    p = oracle.prepare(sq.MXFP4, xb[rows], None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    _, ref = oracle.dual_gemm_silu_prepare(sq.MXFP4, p, q, dense_backbone=True)
+    got = {"meta": osp.row_major("meta"), "s_codes": osp.row_major("codes"),
+           "s_scales": osp.row_major("scales"), "s_dense": osp.row_major("dense_codes"),
+           "r_codes": ors.row_major("codes"), "r_scales": ors.row_major("scales")}
+    for key, val in got.items():
+        val = host(val)[rows]
+        assert np.array_equal(val, ref[key]), (key, int((val != ref[key]).sum()))
+
+
+def test_dual_gemm_silu_prepare_matches_two_step_path():
+    """The layer's own inputs (RMSNorm of heavy-tailed activations with outlier
+    channels, N(0, 0.02) weights; fp32 products not exact): the fused entry
+    point writes what sharq_dual_gemm followed by sharq_prepare_silu_mul on
+    the two halves of Y writes, byte for byte (the same fp32 products, SiLU and
+    preparation).  A consistency check between two library paths, each of
+    which the tests above hold to the oracle."""
+    w = si.layer_workload("gate_up", 2048)
+    x, g, W = si.workload_x(w), si.workload_gamma(w), si.workload_w(w)
+    inter = W.shape[0] // 2
+    sp, rs = sq.prepare(dev16(x), dev16(g), dense_backbone=True)
+    wq = sq.quantize_weight(dev16(W))
+    osp, ors = sq.dual_gemm_silu_prepare(sp, rs, wq, dense_backbone=True)
+    y = sq.dual_gemm(sp, rs, wq)
+    tsp, trs = sq.prepare_silu_mul(y[:, :inter], y[:, inter:], dense_backbone=True)
+    torch.cuda.synchronize()
+    for a, b, name in ((osp.codes, tsp.codes, "s_codes"), (osp.meta, tsp.meta, "meta"),
+                       (osp.scales, tsp.scales, "s_scales"), (osp.dense_codes, tsp.dense_codes, "s_dense"),
+                       (ors.codes, trs.codes, "r_codes"), (ors.scales, trs.scales, "r_scales")):
+        assert torch.equal(a, b), (name, int((a != b).sum()))
+
+
 # ------------------------------------------------------------ weights
 @pytest.mark.parametrize("fmt,n,k", [(0, 256, 256), (0, 6144, 4096), (0, 33, 96), (1, 256, 256),
                                      (1, 1000, 4096)])

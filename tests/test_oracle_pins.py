@@ -684,3 +684,39 @@ def test_grouped_dual_gemm_rows_match_exact_products():
             for j in range(n):
                 exact = fraction_dot(ds[r], dw[e * n + j]) + fraction_dot(dr[r], dw[e * n + j])
                 assert y[i, j] == np.float32(float(exact)), (e, i, j)
+
+
+# ------------------------------------------------------------ gate+up GEMM, SiLU and the preparation
+def test_dual_gemm_silu_prepare_vs_exact_product_and_decimal():
+    """On FP4-grid inputs the preparation and the weight quantization keep
+    every value exactly, so the dual GEMM is the exact product X W^T (numpy
+    float64, exact for these values; fp32 holds it).  Then x[r, j] must be
+    bf16(silu(Y[r, j]) * Y[r, inter + j]) by 60-digit Decimal arithmetic: the
+    first inter rows of W are the gate, the last inter the up projection.  The
+    returned operands dequantize to x within 2 2^e_r per block (e_r the
+    residual's scale exponent: the E2M1 grid's widest gap is 2 at the top,
+    and values up to 8 2^e_r saturate to 6 2^e_r)."""
+    import decimal
+    decimal.getcontext().prec = 60
+    m, inter, k = 5, 128, 256
+    xb = si.fp4_grid(m, k, 0, 61)
+    wb = si.fp4_grid(2 * inter, k, -6, 62)
+    X = si.bf16_bits_to_f32(xb).astype(np.float64)
+    W = si.bf16_bits_to_f32(wb).astype(np.float64)
+    p = oracle.prepare(oracle.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(oracle.MXFP4, wb)
+    x, out = oracle.dual_gemm_silu_prepare(oracle.MXFP4, p, q, dense_backbone=True)
+    Y = X @ W.T
+    assert (Y.astype(np.float32).astype(np.float64) == Y).all()
+    one = decimal.Decimal(1)
+    for r in range(m):
+        for j in range(0, inter, 5):
+            g, u = decimal.Decimal(float(Y[r, j])), decimal.Decimal(float(Y[r, inter + j]))
+            assert x[r, j] == _bf16_of_decimal(g / (one + (-g).exp()) * u), (r, j)
+    # swapping the halves gives other values (the pin above tells them apart)
+    assert (oracle.silu_mul(Y[:, inter:].astype(np.float32), Y[:, :inter].astype(np.float32)) != x).any()
+    xf = si.bf16_bits_to_f32(x).astype(np.float64)
+    ds = _decode_blocks(_unpack_dense(out["s_dense"]), out["s_scales"], 32, oracle.MXFP4)
+    dr = _decode_blocks(_unpack_dense(out["r_codes"]), out["r_scales"], 32, oracle.MXFP4)
+    bound = 2.0 * 2.0 ** (out["r_scales"].astype(np.float64) - 127)
+    assert (np.abs(ds + dr - xf) <= np.repeat(bound, 32, axis=1)).all()
