@@ -317,7 +317,10 @@ def chain_main(args):
     baselines get no RMSNorm, SharQ's preparation includes it where the layer
     has one.  Speed only: accuracy needs the model's weights.  Weights: one
     seeded N(0, 0.02) draw per linear, and CHAIN_LAYERS row-rotated copies that
-    the timed loop cycles through.  Prints one JSON line."""
+    the timed loop cycles through.  ``sharq_with_silu_fused`` is the layer as
+    SharQ runs it: QKV and O as above, then gate+up with SiLU(gate) * up and
+    down's preparation in its epilogue, and down without a preparation of its
+    own (it does the SiLU the other chains leave out).  Prints one JSON line."""
     import torch
     import torch.nn.functional as F
     import sparsity_fp4_quantized_amd as sq
@@ -434,11 +437,44 @@ def chain_main(args):
 
         silu_mul = {"fused_us": round(batch_us(lambda i: fused_s()), 2),
                     "torch_silu_mul_then_prepare_us": round(batch_us(unfused_s), 2)}
+        # the SharQ layer as it runs: gate+up's epilogue forms SiLU(gate) * up
+        # and prepares it for down (sharq_dual_gemm_silu_prepare; at decode,
+        # where 128-row tiles waste the GEMM, the fp32 product goes through
+        # sharq_prepare_silu_mul), so down has no preparation of its own.  It
+        # does the SiLU work that the chains above leave out.
+        wgu = si.layer_workload("gate_up", m)
+        inter = wgu.n // 2
+        xg = torch.from_numpy(si.workload_x(wgu).view(np.int16)).to(dev)
+        gg = torch.from_numpy(si.workload_gamma(wgu).view(np.int16)).to(dev)
+        spg, rsg = sq.alloc_prepared(sq.MXFP4, m, wgu.k, dev, dense_backbone=True)
+        spx, rsx = sq.alloc_prepared(sq.MXFP4, m, inter, dev, dense_backbone=True)
+        yd = torch.empty((m, si.LAYER_LINEARS["down"][1]), dtype=torch.float32, device=dev)
+        prep_g = sq.bind_prepare(xg, gg, 1e-5, spg, rsg)
+        if m > 32:
+            gu_calls = [sq.bind_dual_gemm_silu_prepare(spg, rsg, wts["gate_up"][3][l], spx, rsx)
+                        for l in range(CHAIN_LAYERS)]
+        else:
+            ygu = torch.empty((m, wgu.n), dtype=torch.float32, device=dev)
+            silu_p = sq.bind_prepare_silu_mul(ygu[:, :inter], ygu[:, inter:], spx, rsx)
+            gu_calls = [(lambda q=sq.bind_dual_gemm(spg, rsg, wts["gate_up"][3][l], ygu): (q(), silu_p()))
+                        for l in range(CHAIN_LAYERS)]
+        down_calls = [sq.bind_dual_gemm(spx, rsx, wts["down"][3][l], yd) for l in range(CHAIN_LAYERS)]
+
+        def mlp(i):
+            prep_g()
+            gu_calls[i % CHAIN_LAYERS]()
+            down_calls[i % CHAIN_LAYERS]()
+
+        per["gate_up_silu_down"] = {"sharq_fused": round(batch_us(mlp), 2)}
         chain = {}
         for k, fns in runs.items():
             if fns is not None and len(fns) == len(si.LAYER_LINEARS):
                 chain[k] = round(batch_us(lambda i, fns=fns: [fn(i) for fn in fns]), 2)
-        speed = {f"sharq_speedup_vs_{k}": round(chain[k] / chain["sharq"], 3) for k in chain if k != "sharq"}
+        if runs["sharq"] is not None:
+            layer = runs["sharq"][:2] + [mlp]
+            chain["sharq_with_silu_fused"] = round(batch_us(lambda i: [fn(i) for fn in layer]), 2)
+        speed = {f"sharq_speedup_vs_{k}": round(chain[k] / chain["sharq"], 3)
+                 for k in chain if not k.startswith("sharq")}
         result[phase] = {"m": m, "chain_us": chain, "per_linear_us": per, **speed,
                          "qkv_residual_add_and_prepare": residual_add,
                          "down_silu_mul_and_prepare": silu_mul}
