@@ -486,7 +486,9 @@ def moe_main(args):
     experts, 8 a token, hidden 2048, expert intermediate 768): the tokens'
     preparation (RMSNorm, once per token), the grouped gate+up dual GEMM over
     the gathered rows (n 1536, k 2048), SiLU(gate) * up fused into the down
-    projection's preparation, and the grouped down dual GEMM (n 2048, k 768).
+    projection's preparation, and the grouped down dual GEMM (n 2048, k 768);
+    ``layer_silu_fused`` runs SiLU(gate) * up and that preparation in the
+    grouped gate+up GEMM's epilogue instead.
     Seeded routing with uneven expert loads.  Against torch's bf16 grouped GEMM
     (torch._grouped_mm) on the same groups where this torch build has one.
     Prints one JSON line."""
@@ -530,14 +532,26 @@ def moe_main(args):
     prep2 = sq.bind_prepare_silu_mul(y13[:, :I], y13[:, I:], sp2, rs2)
     gemm2 = sq.bind_grouped_dual_gemm(sp2, rs2, q2, off_d, rows, y2)
 
+    # the same with SiLU(gate) * up and down's preparation in the grouped
+    # gate+up GEMM's epilogue (no fp32 gate+up output)
+    sp3, rs3 = sq.alloc_prepared(sq.MXFP4, rows, I, dev, dense_backbone=True)
+    fused13 = sq.bind_grouped_dual_gemm_silu_prepare(sp, rs, q13, off_d, rows, sp3, rs3, row_index=idx_d)
+    gemm2f = sq.bind_grouped_dual_gemm(sp3, rs3, q2, off_d, rows, y2)
+
     def layer():
         prep()
         gemm13()
         prep2()
         gemm2()
 
+    def layer_fused():
+        prep()
+        fused13()
+        gemm2f()
+
     t = {"prepare": batch_us(prep), "grouped_gate_up": batch_us(gemm13),
-         "silu_mul_prepare": batch_us(prep2), "grouped_down": batch_us(gemm2), "layer": batch_us(layer)}
+         "silu_mul_prepare": batch_us(prep2), "grouped_down": batch_us(gemm2), "layer": batch_us(layer),
+         "grouped_gate_up_silu_prepare": batch_us(fused13), "layer_silu_fused": batch_us(layer_fused)}
     f13, f2 = 3.0 * rows * 2 * I * H, 3.0 * rows * H * I
     res = {"metric": "Qwen3-30B-A3B MoE layer (prefill, 4096 tokens): grouped dual-path FP4 GEMMs",
            "unit": "us", "higher_is_better": False, "steps": reps, "warmup": warm,

@@ -18,7 +18,8 @@
  * residual add, SiLU(gate) * up) into the preparation,
  * sharq_dual_gemm_silu_prepare runs the gate+up GEMM with SiLU(gate) * up and
  * the down projection's preparation in its epilogue, and
- * sharq_grouped_dual_gemm runs a mixture-of-experts layer's expert GEMMs.
+ * sharq_grouped_dual_gemm (and its _silu_prepare form) runs a
+ * mixture-of-experts layer's expert GEMMs.
  *
  * Conventions for every entry point:
  *   - All matrices are row-major, K contiguous.  X is [m, k] bf16, W is
@@ -336,6 +337,27 @@ sharq_status sharq_grouped_dual_gemm(sharq_format fmt, const sharq_fp4_view *spa
                                      const sharq_fp4_view *w_dense_view, int64_t n, int64_t k,
                                      float *y, int64_t ld_y, void *stream);
 
+/*
+ * The grouped form of sharq_dual_gemm_silu_prepare: a mixture-of-experts
+ * layer's gate+up expert GEMMs (as sharq_grouped_dual_gemm: grouped row i of
+ * group e is activation row row_index[i], or i, and meets group e's weight)
+ * with SiLU(gate) * up and the down projections' preparation in the
+ * epilogue.  Group e's weight is rows e 2 inter .. (e + 1) 2 inter - 1 of the
+ * stacked payload: inter gate rows, then inter up rows.  Writes the
+ * preparation of x [rows, inter] (grouped rows; x as in
+ * sharq_dual_gemm_silu_prepare) to sparse_out and resid_out; byte for byte
+ * what sharq_grouped_dual_gemm followed by sharq_prepare_silu_mul on the two
+ * halves of its Y writes.
+ * MXFP4 only.  Requirements: as sharq_grouped_dual_gemm with n = 2 inter,
+ * inter >= 128 and inter % 128 == 0, and for the outputs as
+ * sharq_dual_gemm_silu_prepare with rows rows (rows == 0: nothing to do).
+ */
+sharq_status sharq_grouped_dual_gemm_silu_prepare(
+    sharq_format fmt, const sharq_fp4_view *sparse, const sharq_fp4_view *resid, int64_t tokens,
+    const int32_t *row_index, const int64_t *group_offsets, int64_t groups, int64_t rows,
+    const sharq_fp4_view *w_sparse_view, const sharq_fp4_view *w_dense_view, int64_t inter,
+    int64_t k, const sharq_fp4_view *sparse_out, const sharq_fp4_view *resid_out, void *stream);
+
 /* Bytes of one packed array (`which` = SHARQ_BYTES_*) for `rows` rows of length k; 0 if invalid. */
 size_t sharq_bytes(sharq_format fmt, int which, int64_t rows, int64_t k);
 
@@ -345,7 +367,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 7
+#define SHARQ_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

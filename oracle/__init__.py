@@ -310,6 +310,17 @@ def dual_gemm_silu_prepare(fmt: int, prep: dict, wq: dict, dense_backbone: bool 
     return prepare_silu_mul(fmt, y[:, :inter], y[:, inter:], dense_backbone)
 
 
+def grouped_dual_gemm_silu_prepare(fmt: int, prep: dict, row_index, offsets, wq: dict, inter: int,
+                                   dense_backbone: bool = False):
+    """The grouped gate+up GEMMs of a mixture-of-experts layer followed by the
+    down projections' preparation: Y = grouped_dual_gemm with 2 inter rows a
+    group (inter gate rows, then inter up rows), then SiLU(gate) * up and the
+    preparation of x [rows, inter] without a norm.  Returns x and
+    prepare(fmt, x)."""
+    y = grouped_dual_gemm(fmt, prep, row_index, offsets, wq, 2 * inter)
+    return prepare_silu_mul(fmt, y[:, :inter], y[:, inter:], dense_backbone)
+
+
 def dual_gemm_pairs(fmt: int, prep: dict, wq: dict, rows, cols, want_f64: bool = False):
     """Y at the listed (row, col) pairs only (sorted by row is fastest)."""
     rows = np.ascontiguousarray(rows, dtype=np.int64)

@@ -40,9 +40,9 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 
 # every symbol include/sharq.h declares
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_prepare_silu_mul",
-           "sharq_dual_gemm", "sharq_dual_gemm_silu_prepare", "sharq_grouped_dual_gemm", "sharq_bytes",
-           "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 7
+           "sharq_dual_gemm", "sharq_dual_gemm_silu_prepare", "sharq_grouped_dual_gemm",
+           "sharq_grouped_dual_gemm_silu_prepare", "sharq_bytes", "sharq_status_str", "sharq_abi_version")
+ABI_VERSION = 8
 
 
 class SharqError(RuntimeError):
@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare_silu_mul.restype = ctypes.c_int
         L.sharq_dual_gemm_silu_prepare.argtypes = [ctypes.c_int, V, V, V, V, I64, I64, I64, V, V, P]
         L.sharq_dual_gemm_silu_prepare.restype = ctypes.c_int
+        L.sharq_grouped_dual_gemm_silu_prepare.argtypes = [ctypes.c_int, V, V, I64, P, P, I64, I64, V, V,
+                                                           I64, I64, V, V, P]
+        L.sharq_grouped_dual_gemm_silu_prepare.restype = ctypes.c_int
         L.sharq_grouped_dual_gemm.argtypes = [ctypes.c_int, V, V, I64, P, P, I64, I64, V, V, I64, I64,
                                               P, I64, P]
         L.sharq_grouped_dual_gemm.restype = ctypes.c_int
@@ -481,3 +484,39 @@ def grouped_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, group_offsets,
         out = torch.empty((rows, w.rows // groups), dtype=torch.float32, device=w.codes.device)
     bind_grouped_dual_gemm(sp, rs, w, group_offsets, rows, out, row_index, stream)()
     return out
+
+
+def bind_grouped_dual_gemm_silu_prepare(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, group_offsets, rows: int,
+                                        out_sp: FP4Tensor, out_rs: FP4Tensor, row_index=None,
+                                        stream=None) -> BoundCall:
+    """sharq_grouped_dual_gemm_silu_prepare: every group's gate+up dual GEMM
+    (group e's weight: rows e 2 inter .. of the stacked payload, inter gate
+    rows then inter up rows) over its gathered rows, with x = bf16(silu(gate) *
+    up) prepared into (out_sp, out_rs) [rows, inter], bound for repeated calls."""
+    torch = _torch()
+    if group_offsets.dtype != torch.int64 or (row_index is not None and row_index.dtype != torch.int32):
+        raise TypeError("group_offsets must be int64 and row_index int32")
+    groups = group_offsets.numel() - 1
+    if w.rows % (2 * groups):
+        raise ValueError("the stacked weight must hold 2 * inter rows for every group")
+    inter, k = w.rows // (2 * groups), sp.k
+    ws, vs, vr, vos, vor = w.view(), sp.view(), rs.view(), out_sp.view(), out_rs.view()
+    args = (ctypes.c_int(sp.fmt), ctypes.byref(vs), ctypes.byref(vr), ctypes.c_int64(sp.rows),
+            ctypes.c_void_p(_ptr(row_index)), ctypes.c_void_p(group_offsets.data_ptr()),
+            ctypes.c_int64(groups), ctypes.c_int64(rows), ctypes.byref(ws), ctypes.byref(ws),
+            ctypes.c_int64(inter), ctypes.c_int64(k), ctypes.byref(vos), ctypes.byref(vor), _stream_ptr(stream))
+    return BoundCall(lib().sharq_grouped_dual_gemm_silu_prepare, args, "sharq_grouped_dual_gemm_silu_prepare",
+                     (sp, rs, w, group_offsets, row_index, out_sp, out_rs, ws, vs, vr, vos, vor))
+
+
+def grouped_dual_gemm_silu_prepare(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, group_offsets, rows: int,
+                                   row_index=None, dense_backbone: bool = False, layout: Optional[int] = None,
+                                   stream=None):
+    """A mixture-of-experts layer's gate+up expert GEMMs with SiLU(gate) * up
+    and the down projections' preparation fused in (MXFP4): returns the
+    (backbone, residual) operands [rows, inter] of the grouped rows."""
+    groups = group_offsets.numel() - 1
+    inter = w.rows // (2 * groups)
+    out_sp, out_rs = alloc_prepared(MXFP4, max(rows, 1), inter, w.codes.device, dense_backbone, layout)
+    bind_grouped_dual_gemm_silu_prepare(sp, rs, w, group_offsets, rows, out_sp, out_rs, row_index, stream)()
+    return out_sp, out_rs

@@ -420,8 +420,8 @@ __device__ __forceinline__ void silu_x_tile(v16f (&acc)[2][TN], float *xch, uint
 // the preparation kernel prepares a block.  The stages' LDS is free by then.
 template <int TBM, int TBN, int STAGES>
 __device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES], v16f (&acc)[2][TBN / 64],
-                                                   const PrepArgs &p, int64_t m0, int64_t j0, int wave,
-                                                   int lane) {
+                                                   const PrepArgs &p, int64_t m0, int64_t m_end, int64_t j0,
+                                                   int wave, int lane) {
   constexpr int TN = TBN / 64, HB = TBN / 2, NB = HB / 32;
   constexpr int kVals = TN * 16 * 64;   // floats one wavefront hands over
   constexpr int kHs = HB + 8;           // LDS row stride of the x tile, in bf16
@@ -439,7 +439,7 @@ __device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES
   for (int i = 0; i < TBM * NB / 256; ++i) {
     const int q = (int)threadIdx.x + 256 * i, r = q / NB, b = q % NB;
     const int64_t row = m0 + r;
-    if (row >= p.m) continue;
+    if (row >= m_end) continue;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(xs + r * kHs + 32 * b);
     uint32_t xw[16];
 #pragma unroll
@@ -465,7 +465,6 @@ template <int TBM, int TBN, int NW, int STAGES, bool GROUPED, bool SILU>
 __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, const PrepArgs *prep) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
   static_assert(!GROUPED || 64 * NW == 256, "the group scan takes one thread a group: 256 threads, 256 groups");
-  static_assert(!(GROUPED && SILU), "no grouped gate+up epilogue");
   constexpr int TN = TBN / 64;
   using P = DPlan<TBM, TBN, NW>;
   __shared__ DStage<TBM, TBN> st[STAGES];
@@ -495,7 +494,7 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
   DRsrc R;
   DOffs<TBM, TBN, NW> O;
   if constexpr (SILU)
-    plan_loads<TBM, TBN, NW, true>(a, m0, 0, wave, lane, R, O, arow, 0, a.n,
+    plan_loads<TBM, TBN, NW, true>(a, m0, 0, wave, lane, R, O, arow, w_row0, w_rows,
                                    WRows<true>{n0 / 2, a.n / 2, TBN / 2});
   else
     plan_loads<TBM, TBN, NW>(a, m0, n0, wave, lane, R, O, arow, w_row0, w_rows);
@@ -519,7 +518,7 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
   }
 
   if constexpr (SILU) {
-    silu_prep_epilogue<TBM, TBN, STAGES>(st, acc, *prep, m0, n0 / 2, wave, lane);
+    silu_prep_epilogue<TBM, TBN, STAGES>(st, acc, *prep, m0, m_end, n0 / 2, wave, lane);
     return;
   }
   // Y leaves with non-temporal stores: nothing here reads it back, and fp32
@@ -545,12 +544,13 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, ui
 }
 
 // The gate+up projection with SiLU(gate) * up and the down projection's
-// preparation in its epilogue (no fp32 Y).  Two wavefronts per SIMD (two
+// preparation in its epilogue (no fp32 Y); GROUPED: every expert's, over the
+// gathered rows of each group (the output rows are the grouped rows).  Two wavefronts per SIMD (two
 // workgroups per CU, as the plain kernel): left alone the epilogue's
 // registers took the kernel to 276 VGPRs, one wavefront per SIMD.
-template <int TBM, int TBN, int NW, int STAGES>
+template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false>
 __global__ __launch_bounds__(64 * NW, 2) void dual_gemm_silu_prep_kernel(GemmArgs a, uint32_t band, PrepArgs p) {
-  dense_tile<TBM, TBN, NW, STAGES, false, true>(a, band, &p);
+  dense_tile<TBM, TBN, NW, STAGES, GROUPED, true>(a, band, &p);
 }
 
 template <int TBM, int TBN, int NW, int STAGES>
@@ -1047,6 +1047,15 @@ hipError_t launch_dual_gemm_silu_prep_mx(const GemmArgs &a, const PrepArgs &p, h
   const int64_t gm = (a.m + TBM - 1) / TBM, gn = a.n / TBN;
   dual_gemm_silu_prep_kernel<TBM, TBN, 4, 2>
       <<<dim3((unsigned)(gm * gn)), dim3(256), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, 2), p);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_dual_gemm_silu_prep_mx(const GemmArgs &a, const PrepArgs &p, hipStream_t s) {
+  // the grouped kernel's upper bound of the tiles, whole rounds of the 8 XCDs
+  constexpr int TBM = 128, TBN = 256;
+  const int64_t gm = (a.m + TBM - 1) / TBM + a.groups, gn = a.n / TBN;
+  const int64_t tiles = (gm * gn + 7) / 8 * 8;
+  dual_gemm_silu_prep_kernel<TBM, TBN, 4, 2, true><<<dim3((unsigned)tiles), dim3(256), 0, s>>>(a, 0, p);
   return hipGetLastError();
 }
 

@@ -80,6 +80,9 @@ hipError_t launch_grouped_dual_gemm_mx(const GemmArgs &a, hipStream_t s);
 // gate+up dual GEMM (a.n = 2 i: i gate rows, then i up rows of W; i % 128 == 0)
 // with x = bf16(silu(gate) * up) prepared into p's outputs ([a.m, i], no norm)
 hipError_t launch_dual_gemm_silu_prep_mx(const GemmArgs &a, const PrepArgs &p, hipStream_t s);
+// the same over the groups of a grouped GEMM (each group's W: a.n rows, gate
+// then up); p's outputs have a.m (grouped) rows
+hipError_t launch_grouped_dual_gemm_silu_prep_mx(const GemmArgs &a, const PrepArgs &p, hipStream_t s);
 hipError_t launch_dual_gemm_nv(const GemmArgs &a, int variant, hipStream_t s);
 
 }  // namespace sharq

@@ -259,6 +259,63 @@ sharq_status sharq_dual_gemm_silu_prepare(sharq_format fmt, const sharq_fp4_view
   return from_hip(sharq::launch_dual_gemm_silu_prep_mx(a, o, static_cast<hipStream_t>(stream)));
 }
 
+sharq_status sharq_grouped_dual_gemm_silu_prepare(
+    sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs, int64_t tokens,
+    const int32_t *row_index, const int64_t *group_offsets, int64_t groups, int64_t rows,
+    const sharq_fp4_view *wsv, const sharq_fp4_view *wdv, int64_t inter, int64_t k,
+    const sharq_fp4_view *sp_out, const sharq_fp4_view *rs_out, void *stream) {
+  if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
+  if (fmt != SHARQ_MXFP4) return SHARQ_ERR_UNSUPPORTED;
+  if (!sp || !rs || !wsv || !wdv || !group_offsets || !sp_out || !rs_out) return SHARQ_ERR_NULL;
+  if (groups < 1 || groups > 256) return SHARQ_ERR_UNSUPPORTED;
+  if (tokens < 1 || rows < 0 || inter < 128 || inter % 128 || k < 128 || k % 128) return SHARQ_ERR_SHAPE;
+  if (!row_index && rows > tokens) return SHARQ_ERR_SHAPE;
+  if (!aligned(group_offsets, 8) || (row_index && !aligned(row_index, 4))) return SHARQ_ERR_ALIGN;
+  CHECK(check_layout(sp, k));
+  CHECK(check_layout(rs, k));
+  CHECK(check_layout(wsv, k));
+  CHECK(check_layout(wdv, k));
+  if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
+  if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
+    return SHARQ_ERR_SHAPE;
+  if (!sp->dense_codes) return SHARQ_ERR_UNSUPPORTED;   // reads the dense backbone view
+  const int64_t n = 2 * inter, wrows = groups * n;
+  CHECK(check_array(sp->dense_codes, sp->ld_dense, sp->layout, tokens, k, k / 2, 16, 64, 16));
+  CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, tokens, k, k / 2, 16, 64, 16));
+  CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, wrows, k, k / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp, tokens, k, true));
+  CHECK(check_scales(fmt, rs, tokens, k, true));
+  CHECK(check_scales(fmt, wsv, wrows, k, true));
+  CHECK(check_scales(fmt, wdv, wrows, k, true));
+  // the outputs: the preparation's views of x [max(rows, 1), inter]
+  const int64_t orows = rows > 0 ? rows : 1;
+  CHECK(check_layout(sp_out, inter));
+  CHECK(check_layout(rs_out, inter));
+  if (sp_out->layout != rs_out->layout) return SHARQ_ERR_SHAPE;
+  const int L = sp_out->layout;
+  CHECK(check_array(sp_out->codes, sp_out->ld_codes, L, orows, inter, inter / 4, 8, 32, 16));
+  CHECK(check_array(sp_out->meta, sp_out->ld_meta, L, orows, inter, inter / 8, 4, 16, 16));
+  CHECK(check_array(rs_out->codes, rs_out->ld_codes, L, orows, inter, inter / 2, 16, 64, 16));
+  if (sp_out->dense_codes)
+    CHECK(check_array(sp_out->dense_codes, sp_out->ld_dense, L, orows, inter, inter / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp_out, orows, inter, false));
+  CHECK(check_scales(fmt, rs_out, orows, inter, false));
+  if (rows == 0) return SHARQ_OK;
+  GemmArgs a{sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->dense_codes, sp->ld_dense,
+             sp->scales, sp->ld_scales, rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
+             wsv->codes, wsv->ld_codes, wsv->scales, wsv->ld_scales, wdv->scales, wdv->ld_scales,
+             nullptr, nullptr, nullptr, 0, rows, n, k, ksm(sp), ksm(rs), ksm(wsv)};
+  a.row_index = row_index;
+  a.group_off = group_offsets;
+  a.groups = groups;
+  a.tokens = tokens;
+  PrepArgs o{nullptr, 0, rows, inter, nullptr, 0.0f,
+             sp_out->codes, sp_out->ld_codes, sp_out->meta, sp_out->ld_meta, sp_out->scales,
+             sp_out->ld_scales, rs_out->codes, rs_out->ld_codes, rs_out->scales, rs_out->ld_scales,
+             sp_out->dense_codes, sp_out->ld_dense, nullptr, ksm(sp_out), ksm(rs_out)};
+  return from_hip(sharq::launch_grouped_dual_gemm_silu_prep_mx(a, o, static_cast<hipStream_t>(stream)));
+}
+
 sharq_status sharq_grouped_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp,
                                      const sharq_fp4_view *rs, int64_t tokens,
                                      const int32_t *row_index, const int64_t *group_offsets,

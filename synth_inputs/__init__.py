@@ -142,14 +142,16 @@ E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 def fp4_grid(rows: int, k: int, exp2: int, seed: int) -> np.ndarray:
     """bf16 bits [rows, k] of values drawn uniformly from the signed E2M1 grid
-    times 2^exp2 (magnitude index, then sign, from ``default_rng(seed)``).
-    Block-scaled FP4 holds every 32-block of such values exactly, and their
-    products and sums stay exact in fp32 for the sizes used here, so these
-    inputs make a GEMM's result independent of its summation order."""
+    times 2^exp2: a uniform 4-bit index from ``default_rng(seed)``, bit 3 the
+    sign and bits 0-2 the magnitude's place in E2M1_GRID.  Block-scaled FP4
+    holds every 32-block of such values exactly, and their products and sums
+    stay exact in fp32 for the sizes used here, so these inputs make a GEMM's
+    result independent of its summation order."""
     rng = np.random.default_rng(seed)
-    mag = np.asarray(E2M1_GRID)[rng.integers(0, 8, (rows, k))]
-    sign = rng.choice(np.array([-1.0, 1.0]), (rows, k))
-    return f32_to_bf16_bits((mag * sign * 2.0 ** exp2).astype(np.float32))
+    idx = rng.integers(0, 16, (rows, k), dtype=np.uint8)
+    mags = np.asarray(E2M1_GRID, dtype=np.float64) * 2.0 ** exp2
+    table = f32_to_bf16_bits(np.concatenate([mags, -mags]).astype(np.float32))   # exact in bf16
+    return table[idx]
 
 
 def gate_up_output(m: int, f: int, seed: int, n_outlier: int = 72, outlier_scale: float = 30.0):

@@ -200,6 +200,41 @@ def test_dual_gemm_silu_prepare_validation(kwargs, status):
     assert silu_gemm(**kwargs) == status
 
 
+def grouped_silu(fmt=0, tokens=16, idx=FAKE, offs=FAKE, groups=2, rows=32, inter=128, k=256, sp=None, rs=None,
+                 ws=None, wd=None, osp=None, ors=None):
+    sp = sp or view(ld_codes=64, dense=FAKE, ld_dense=128)
+    rs = rs or view(meta=None)
+    ws = ws or view(meta=None)
+    wd = wd or ws
+    osp = osp or view(ld_codes=32, ld_meta=16, ld_scales=4)
+    ors = ors or view(meta=None, ld_codes=64, ld_scales=4)
+    ref = [None if v is NULLV else ctypes.byref(v) for v in (sp, rs, ws, wd, osp, ors)]
+    return sq.lib().sharq_grouped_dual_gemm_silu_prepare(fmt, ref[0], ref[1], tokens, idx, offs, groups, rows,
+                                                         ref[2], ref[3], inter, k, ref[4], ref[5], None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(fmt=1), sq.ERR_UNSUPPORTED),
+    (dict(groups=0), sq.ERR_UNSUPPORTED),
+    (dict(groups=257), sq.ERR_UNSUPPORTED),
+    (dict(offs=None), sq.ERR_NULL),
+    (dict(osp=NULLV), sq.ERR_NULL),
+    (dict(tokens=0), sq.ERR_SHAPE),
+    (dict(rows=-1), sq.ERR_SHAPE),
+    (dict(inter=192), sq.ERR_SHAPE),
+    (dict(k=192), sq.ERR_SHAPE),
+    (dict(idx=None, rows=17), sq.ERR_SHAPE),
+    (dict(offs=FAKE + 4), sq.ERR_ALIGN),
+    (dict(sp=view(ld_codes=64)), sq.ERR_UNSUPPORTED),   # no dense backbone view
+    (dict(wd=view(meta=None, codes=FAKE + 4096)), sq.ERR_SHAPE),
+    (dict(osp=view(ld_codes=31, ld_meta=16, ld_scales=4)), sq.ERR_SHAPE),
+    (dict(osp=ksm(16), ors=ksm(16, meta=None)), sq.ERR_SHAPE),   # rows per step < rows (32)
+    (dict(rows=0), sq.OK),                                       # nothing to do: no launch
+])
+def test_grouped_dual_gemm_silu_prepare_validation(kwargs, status):
+    assert grouped_silu(**kwargs) == status
+
+
 def grouped(fmt=0, tokens=16, idx=FAKE, offs=FAKE, groups=2, rows=32, n=256, k=256, y=FAKE,
             ld_y=256, sp=None, rs=None, ws=None, wd=None):
     sp = sp or view(ld_codes=64, dense=FAKE, ld_dense=128)

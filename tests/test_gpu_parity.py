@@ -468,6 +468,90 @@ def test_dual_gemm_silu_prepare_matches_two_step_path():
         assert torch.equal(a, b), (name, int((a != b).sum()))
 
 
+def _grouped_silu_grid_case(tokens, k, inter, experts, top_k, seed, layout):
+    xb = si.fp4_grid(tokens, k, 0, seed)
+    wb = si.fp4_grid(experts * 2 * inter, k, -6, seed + 1)
+    row_index, offsets = si.moe_routing(tokens, experts, top_k, seed + 2)
+    sp, rs = sq.prepare(dev16(xb), None, dense_backbone=True, layout=layout)
+    wq = sq.quantize_weight(dev16(wb), layout=layout)
+    return xb, wb, row_index, offsets, sp, rs, wq
+
+
+@pytest.mark.parametrize("tokens,k,inter,experts,top_k,layout", [
+    (300, 256, 128, 8, 2, KSM), (200, 384, 256, 5, 3, ROW), (64, 128, 384, 16, 4, KSM)])
+def test_grouped_dual_gemm_silu_prepare_exact(tokens, k, inter, experts, top_k, layout):
+    """The grouped gate+up GEMMs with SiLU(gate) * up and the preparation in
+    the epilogue, on FP4-grid inputs (every product exact in fp32): every
+    prepared array of every grouped row byte for byte against the oracle's
+    grouped GEMM -> SiLU(gate) * up -> preparation; seeded routing with uneven
+    groups, both layouts."""
+    xb, wb, row_index, offsets, sp, rs, wq = _grouped_silu_grid_case(tokens, k, inter, experts, top_k, 101, layout)
+    rows = int(offsets[-1])
+    p = oracle.prepare(sq.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    _, ref = oracle.grouped_dual_gemm_silu_prepare(sq.MXFP4, p, row_index, offsets, q, inter, dense_backbone=True)
+    osp, ors = sq.grouped_dual_gemm_silu_prepare(sp, rs, wq, torch.from_numpy(offsets).to(DEV), rows,
+                                                 row_index=torch.from_numpy(row_index).to(DEV),
+                                                 dense_backbone=True, layout=layout)
+    _compare_prep(f"grouped silu t{tokens} k{k} inter{inter}", osp, ors, ref)
+
+
+def test_grouped_dual_gemm_silu_prepare_identity_and_empty_groups():
+    """Identity gather (no row index) with empty groups at the start, middle
+    and end: the same bytes as the oracle."""
+    tokens, k, inter = 150, 256, 128
+    xb, wb, _, _, sp, rs, wq = _grouped_silu_grid_case(tokens, k, inter, 5, 1, 111, KSM)
+    offsets = np.array([0, 0, 70, 70, 150, 150], dtype=np.int64)
+    p = oracle.prepare(sq.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    _, ref = oracle.grouped_dual_gemm_silu_prepare(sq.MXFP4, p, None, offsets, q, inter, dense_backbone=True)
+    osp, ors = sq.grouped_dual_gemm_silu_prepare(sp, rs, wq, torch.from_numpy(offsets).to(DEV), tokens,
+                                                 dense_backbone=True)
+    _compare_prep("grouped silu identity", osp, ors, ref)
+
+
+def test_grouped_dual_gemm_silu_prepare_qwen3_layer():
+    """The MoE bench shape (4096 tokens, 128 experts, 8 a token, inter 768, k
+    2048): on FP4-grid inputs, sampled grouped rows byte for byte against the
+    oracle; on the layer's own inputs, every byte equal to the grouped GEMM
+    followed by sharq_prepare_silu_mul (a consistency check between two
+    library paths)."""
+    cfg = si.MOE_QWEN3_30B_A3B
+    tokens, k, inter, experts, top_k = 4096, cfg["hidden"], cfg["intermediate"], cfg["experts"], cfg["top_k"]
+    xb, wb, row_index, offsets, sp, rs, wq = _grouped_silu_grid_case(tokens, k, inter, experts, top_k, 121, KSM)
+    rows = int(offsets[-1])
+    doff, didx = torch.from_numpy(offsets).to(DEV), torch.from_numpy(row_index).to(DEV)
+    osp, ors = sq.grouped_dual_gemm_silu_prepare(sp, rs, wq, doff, rows, row_index=didx, dense_backbone=True)
+    got = {"meta": host(osp.row_major("meta")), "s_codes": host(osp.row_major("codes")),
+           "s_scales": host(osp.row_major("scales")), "s_dense": host(osp.row_major("dense_codes")),
+           "r_codes": host(ors.row_major("codes")), "r_scales": host(ors.row_major("scales"))}
+    rng = np.random.default_rng(7)
+    pick = np.concatenate([[0, rows - 1], rng.integers(0, rows, 22)])
+    for i in pick:
+        e = int(np.searchsorted(offsets, i, side="right") - 1)
+        # the preparation and the weight quantization are row-independent:
+        # the oracle prepares the one token and quantizes the one expert
+        p = oracle.prepare(sq.MXFP4, xb[row_index[i]:row_index[i] + 1], None, dense_backbone=True)
+        q = oracle.quantize_weight(sq.MXFP4, wb[e * 2 * inter:(e + 1) * 2 * inter])
+        _, ref = oracle.dual_gemm_silu_prepare(sq.MXFP4, p, q, dense_backbone=True)
+        for key, val in got.items():
+            assert np.array_equal(val[i], ref[key][0]), (int(i), e, key)
+    # the layer's own inputs: fused against the two library steps
+    x = si.activations("student_t4", tokens, k, 41, 50.0, 131)
+    g = si.gamma(k, 132)
+    W = si.weights(experts * 2 * inter, k, 133)
+    sp, rs = sq.prepare(dev16(x), dev16(g), dense_backbone=True)
+    wq = sq.quantize_weight(dev16(W))
+    osp, ors = sq.grouped_dual_gemm_silu_prepare(sp, rs, wq, doff, rows, row_index=didx, dense_backbone=True)
+    y = sq.grouped_dual_gemm(sp, rs, wq, doff, rows, row_index=didx)
+    tsp, trs = sq.prepare_silu_mul(y[:, :inter], y[:, inter:], dense_backbone=True)
+    torch.cuda.synchronize()
+    for a, b, name in ((osp.codes, tsp.codes, "s_codes"), (osp.meta, tsp.meta, "meta"),
+                       (osp.scales, tsp.scales, "s_scales"), (osp.dense_codes, tsp.dense_codes, "s_dense"),
+                       (ors.codes, trs.codes, "r_codes"), (ors.scales, trs.scales, "r_scales")):
+        assert torch.equal(a, b), (name, int((a != b).sum()))
+
+
 # ------------------------------------------------------------ weights
 @pytest.mark.parametrize("fmt,n,k", [(0, 256, 256), (0, 6144, 4096), (0, 33, 96), (1, 256, 256),
                                      (1, 1000, 4096)])

@@ -720,3 +720,26 @@ def test_dual_gemm_silu_prepare_vs_exact_product_and_decimal():
     dr = _decode_blocks(_unpack_dense(out["r_codes"]), out["r_scales"], 32, oracle.MXFP4)
     bound = 2.0 * 2.0 ** (out["r_scales"].astype(np.float64) - 127)
     assert (np.abs(ds + dr - xf) <= np.repeat(bound, 32, axis=1)).all()
+
+
+def test_grouped_dual_gemm_silu_prepare_rows_are_per_group_products():
+    """Each grouped row of the grouped gate+up with SiLU is the single-row
+    dual GEMM of its gathered activation row with its group's 2 inter weight
+    rows (gate, then up), then SiLU(gate) * up and the preparation: checked
+    against the plain (ungrouped) composition, which the pin above ties to the
+    exact product and Decimal arithmetic; an empty group included."""
+    inter, k, groups, t = 128, 256, 3, 7
+    xb = si.fp4_grid(t, k, 0, 141)
+    wb = si.fp4_grid(groups * 2 * inter, k, -6, 142)
+    p = oracle.prepare(oracle.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(oracle.MXFP4, wb)
+    offsets = [0, 4, 4, 9]
+    row_index = np.array([6, 0, 3, 3, 1, 2, 5, 6, 0])
+    x, out = oracle.grouped_dual_gemm_silu_prepare(oracle.MXFP4, p, row_index, offsets, q, inter, True)
+    for e in range(groups):
+        for i in range(offsets[e], offsets[e + 1]):
+            xr, ref = oracle.dual_gemm_silu_prepare(oracle.MXFP4, oracle.gather_rows(p, [row_index[i]]),
+                                                    oracle.expert_rows(q, e, 2 * inter), True)
+            assert np.array_equal(x[i], xr[0]), (e, i)
+            for key in ("s_codes", "meta", "s_scales", "s_dense", "r_codes", "r_scales"):
+                assert np.array_equal(out[key][i], ref[key][0]), (e, i, key)
