@@ -86,9 +86,9 @@ def source_hash(*names) -> str:
 
 
 def kernel_sources(fmt: int):
-    gemm = "gemm_mx.hip" if fmt == si.MXFP4 else "gemm_nv.hip"
-    return ((gemm, "gemm_common.h", "fp4_device.h", "kernels.h"),
-            ("prep.hip", "fp4_device.h", "kernels.h"))
+    gemm = ("gemm_mx.hip", "prep_block.h") if fmt == si.MXFP4 else ("gemm_nv.hip",)
+    return ((*gemm, "gemm_common.h", "fp4_device.h", "kernels.h"),
+            ("prep.hip", "prep_block.h", "fp4_device.h", "kernels.h"))
 
 
 def traffic_key(kind: str, w: si.Workload, variant: int, dense_view: bool) -> str:
