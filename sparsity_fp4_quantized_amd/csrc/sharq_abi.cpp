@@ -62,6 +62,48 @@ int ksm(const sharq_fp4_view *v) { return v->layout == SHARQ_LAYOUT_KSTEP_MAJOR 
     if (st_ != SHARQ_OK) return st_;         \
   } while (0)
 
+// The two views a preparation writes, for `rows` rows of length k: one layout,
+// 2:4 codes, meta, residual codes, the optional dense backbone view and the
+// scales as the writers store them.
+sharq_status check_prep_views(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,
+                              int64_t rows, int64_t k) {
+  CHECK(check_layout(sp, k));
+  CHECK(check_layout(rs, k));
+  if (sp->layout != rs->layout) return SHARQ_ERR_SHAPE;
+  const int L = sp->layout;
+  CHECK(check_array(sp->codes, sp->ld_codes, L, rows, k, k / 4, 8, 32, 16));
+  CHECK(check_array(sp->meta, sp->ld_meta, L, rows, k, k / 8, 4, 16, 16));
+  CHECK(check_array(rs->codes, rs->ld_codes, L, rows, k, k / 2, 16, 64, 16));
+  if (sp->dense_codes) CHECK(check_array(sp->dense_codes, sp->ld_dense, L, rows, k, k / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp, rows, k, false));
+  CHECK(check_scales(fmt, rs, rows, k, false));
+  return SHARQ_OK;
+}
+
+// The operands of the dense-view GEMM kernels (grouped and gate+up forms):
+// `a_rows` activation rows with the dense backbone view, `w_rows` weight rows
+// given as two views of one payload.
+sharq_status check_dense_gemm_views(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,
+                                    const sharq_fp4_view *wsv, const sharq_fp4_view *wdv, int64_t a_rows,
+                                    int64_t w_rows, int64_t k) {
+  CHECK(check_layout(sp, k));
+  CHECK(check_layout(rs, k));
+  CHECK(check_layout(wsv, k));
+  CHECK(check_layout(wdv, k));
+  if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
+  if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
+    return SHARQ_ERR_SHAPE;
+  if (!sp->dense_codes) return SHARQ_ERR_UNSUPPORTED;   // reads the dense backbone view
+  CHECK(check_array(sp->dense_codes, sp->ld_dense, sp->layout, a_rows, k, k / 2, 16, 64, 16));
+  CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, a_rows, k, k / 2, 16, 64, 16));
+  CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, w_rows, k, k / 2, 16, 64, 16));
+  CHECK(check_scales(fmt, sp, a_rows, k, true));
+  CHECK(check_scales(fmt, rs, a_rows, k, true));
+  CHECK(check_scales(fmt, wsv, w_rows, k, true));
+  CHECK(check_scales(fmt, wdv, w_rows, k, true));
+  return SHARQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,16 +168,7 @@ sharq_status prepare_common(sharq_format fmt, const uint16_t *x_bf16, int64_t m,
   if (gamma_bf16 && k > 16384) return SHARQ_ERR_UNSUPPORTED;
   if (ld_x % 8 || !aligned(x_bf16, 16)) return SHARQ_ERR_ALIGN;
   if (gamma_bf16 && !aligned(gamma_bf16, 16)) return SHARQ_ERR_ALIGN;
-  CHECK(check_layout(sp, k));
-  CHECK(check_layout(rs, k));
-  if (sp->layout != rs->layout) return SHARQ_ERR_SHAPE;
-  const int L = sp->layout;
-  CHECK(check_array(sp->codes, sp->ld_codes, L, m, k, k / 4, 8, 32, 16));
-  CHECK(check_array(sp->meta, sp->ld_meta, L, m, k, k / 8, 4, 16, 16));
-  CHECK(check_array(rs->codes, rs->ld_codes, L, m, k, k / 2, 16, 64, 16));
-  if (sp->dense_codes) CHECK(check_array(sp->dense_codes, sp->ld_dense, L, m, k, k / 2, 16, 64, 16));
-  CHECK(check_scales(fmt, sp, m, k, false));
-  CHECK(check_scales(fmt, rs, m, k, false));
+  CHECK(check_prep_views(fmt, sp, rs, m, k));
   if (fmt == SHARQ_NVFP4) {
     if (!sp->tensor_scale) return SHARQ_ERR_NULL;
     if (rs->tensor_scale && rs->tensor_scale != sp->tensor_scale) return SHARQ_ERR_SHAPE;
@@ -190,16 +223,7 @@ sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t
   if (!gate || !up || !sp || !rs) return SHARQ_ERR_NULL;
   if (m < 1 || k < 32 || k % 32 || ld_gate < k || ld_up < k) return SHARQ_ERR_SHAPE;
   if (ld_gate % 4 || ld_up % 4 || !aligned(gate, 16) || !aligned(up, 16)) return SHARQ_ERR_ALIGN;
-  CHECK(check_layout(sp, k));
-  CHECK(check_layout(rs, k));
-  if (sp->layout != rs->layout) return SHARQ_ERR_SHAPE;
-  const int L = sp->layout;
-  CHECK(check_array(sp->codes, sp->ld_codes, L, m, k, k / 4, 8, 32, 16));
-  CHECK(check_array(sp->meta, sp->ld_meta, L, m, k, k / 8, 4, 16, 16));
-  CHECK(check_array(rs->codes, rs->ld_codes, L, m, k, k / 2, 16, 64, 16));
-  if (sp->dense_codes) CHECK(check_array(sp->dense_codes, sp->ld_dense, L, m, k, k / 2, 16, 64, 16));
-  CHECK(check_scales(fmt, sp, m, k, false));
-  CHECK(check_scales(fmt, rs, m, k, false));
+  CHECK(check_prep_views(fmt, sp, rs, m, k));
   PrepArgs a{nullptr, 0, m, k, nullptr, 0.0f,
              sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->scales, sp->ld_scales,
              rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
@@ -220,34 +244,9 @@ sharq_status sharq_dual_gemm_silu_prepare(sharq_format fmt, const sharq_fp4_view
   if (fmt != SHARQ_MXFP4) return SHARQ_ERR_UNSUPPORTED;
   if (!sp || !rs || !wsv || !wdv || !sp_out || !rs_out) return SHARQ_ERR_NULL;
   if (m < 1 || inter < 128 || inter % 128 || k < 128 || k % 128) return SHARQ_ERR_SHAPE;
-  CHECK(check_layout(sp, k));
-  CHECK(check_layout(rs, k));
-  CHECK(check_layout(wsv, k));
-  CHECK(check_layout(wdv, k));
-  if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
-  if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
-    return SHARQ_ERR_SHAPE;
-  if (!sp->dense_codes) return SHARQ_ERR_UNSUPPORTED;   // reads the dense backbone view
   const int64_t n = 2 * inter;
-  CHECK(check_array(sp->dense_codes, sp->ld_dense, sp->layout, m, k, k / 2, 16, 64, 16));
-  CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, m, k, k / 2, 16, 64, 16));
-  CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, n, k, k / 2, 16, 64, 16));
-  CHECK(check_scales(fmt, sp, m, k, true));
-  CHECK(check_scales(fmt, rs, m, k, true));
-  CHECK(check_scales(fmt, wsv, n, k, true));
-  CHECK(check_scales(fmt, wdv, n, k, true));
-  // the outputs: the preparation's views of x [m, inter]
-  CHECK(check_layout(sp_out, inter));
-  CHECK(check_layout(rs_out, inter));
-  if (sp_out->layout != rs_out->layout) return SHARQ_ERR_SHAPE;
-  const int L = sp_out->layout;
-  CHECK(check_array(sp_out->codes, sp_out->ld_codes, L, m, inter, inter / 4, 8, 32, 16));
-  CHECK(check_array(sp_out->meta, sp_out->ld_meta, L, m, inter, inter / 8, 4, 16, 16));
-  CHECK(check_array(rs_out->codes, rs_out->ld_codes, L, m, inter, inter / 2, 16, 64, 16));
-  if (sp_out->dense_codes)
-    CHECK(check_array(sp_out->dense_codes, sp_out->ld_dense, L, m, inter, inter / 2, 16, 64, 16));
-  CHECK(check_scales(fmt, sp_out, m, inter, false));
-  CHECK(check_scales(fmt, rs_out, m, inter, false));
+  CHECK(check_dense_gemm_views(fmt, sp, rs, wsv, wdv, m, n, k));
+  CHECK(check_prep_views(fmt, sp_out, rs_out, m, inter));   // the preparation of x [m, inter]
   GemmArgs a{sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->dense_codes, sp->ld_dense,
              sp->scales, sp->ld_scales, rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
              wsv->codes, wsv->ld_codes, wsv->scales, wsv->ld_scales, wdv->scales, wdv->ld_scales,
@@ -271,35 +270,9 @@ sharq_status sharq_grouped_dual_gemm_silu_prepare(
   if (tokens < 1 || rows < 0 || inter < 128 || inter % 128 || k < 128 || k % 128) return SHARQ_ERR_SHAPE;
   if (!row_index && rows > tokens) return SHARQ_ERR_SHAPE;
   if (!aligned(group_offsets, 8) || (row_index && !aligned(row_index, 4))) return SHARQ_ERR_ALIGN;
-  CHECK(check_layout(sp, k));
-  CHECK(check_layout(rs, k));
-  CHECK(check_layout(wsv, k));
-  CHECK(check_layout(wdv, k));
-  if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
-  if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
-    return SHARQ_ERR_SHAPE;
-  if (!sp->dense_codes) return SHARQ_ERR_UNSUPPORTED;   // reads the dense backbone view
-  const int64_t n = 2 * inter, wrows = groups * n;
-  CHECK(check_array(sp->dense_codes, sp->ld_dense, sp->layout, tokens, k, k / 2, 16, 64, 16));
-  CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, tokens, k, k / 2, 16, 64, 16));
-  CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, wrows, k, k / 2, 16, 64, 16));
-  CHECK(check_scales(fmt, sp, tokens, k, true));
-  CHECK(check_scales(fmt, rs, tokens, k, true));
-  CHECK(check_scales(fmt, wsv, wrows, k, true));
-  CHECK(check_scales(fmt, wdv, wrows, k, true));
-  // the outputs: the preparation's views of x [max(rows, 1), inter]
-  const int64_t orows = rows > 0 ? rows : 1;
-  CHECK(check_layout(sp_out, inter));
-  CHECK(check_layout(rs_out, inter));
-  if (sp_out->layout != rs_out->layout) return SHARQ_ERR_SHAPE;
-  const int L = sp_out->layout;
-  CHECK(check_array(sp_out->codes, sp_out->ld_codes, L, orows, inter, inter / 4, 8, 32, 16));
-  CHECK(check_array(sp_out->meta, sp_out->ld_meta, L, orows, inter, inter / 8, 4, 16, 16));
-  CHECK(check_array(rs_out->codes, rs_out->ld_codes, L, orows, inter, inter / 2, 16, 64, 16));
-  if (sp_out->dense_codes)
-    CHECK(check_array(sp_out->dense_codes, sp_out->ld_dense, L, orows, inter, inter / 2, 16, 64, 16));
-  CHECK(check_scales(fmt, sp_out, orows, inter, false));
-  CHECK(check_scales(fmt, rs_out, orows, inter, false));
+  const int64_t n = 2 * inter;
+  CHECK(check_dense_gemm_views(fmt, sp, rs, wsv, wdv, tokens, groups * n, k));
+  CHECK(check_prep_views(fmt, sp_out, rs_out, rows > 0 ? rows : 1, inter));   // x [rows, inter]
   if (rows == 0) return SHARQ_OK;
   GemmArgs a{sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->dense_codes, sp->ld_dense,
              sp->scales, sp->ld_scales, rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
@@ -330,22 +303,7 @@ sharq_status sharq_grouped_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp,
   if (!row_index && rows > tokens) return SHARQ_ERR_SHAPE;
   if (!aligned(group_offsets, 8) || (row_index && !aligned(row_index, 4)) || !aligned(y, 4))
     return SHARQ_ERR_ALIGN;
-  CHECK(check_layout(sp, k));
-  CHECK(check_layout(rs, k));
-  CHECK(check_layout(wsv, k));
-  CHECK(check_layout(wdv, k));
-  if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
-  if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
-    return SHARQ_ERR_SHAPE;
-  if (!sp->dense_codes) return SHARQ_ERR_UNSUPPORTED;   // reads the dense backbone view
-  const int64_t wrows = groups * n;
-  CHECK(check_array(sp->dense_codes, sp->ld_dense, sp->layout, tokens, k, k / 2, 16, 64, 16));
-  CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, tokens, k, k / 2, 16, 64, 16));
-  CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, wrows, k, k / 2, 16, 64, 16));
-  CHECK(check_scales(fmt, sp, tokens, k, true));
-  CHECK(check_scales(fmt, rs, tokens, k, true));
-  CHECK(check_scales(fmt, wsv, wrows, k, true));
-  CHECK(check_scales(fmt, wdv, wrows, k, true));
+  CHECK(check_dense_gemm_views(fmt, sp, rs, wsv, wdv, tokens, groups * n, k));
   if (rows == 0) return SHARQ_OK;
   GemmArgs a{sp->codes, sp->ld_codes, sp->meta, sp->ld_meta, sp->dense_codes, sp->ld_dense,
              sp->scales, sp->ld_scales, rs->codes, rs->ld_codes, rs->scales, rs->ld_scales,
