@@ -261,6 +261,8 @@ sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t
  * on the two halves of Y.
  * MXFP4 only; reads the dense backbone view (sparse->dense_codes required,
  * SHARQ_ERR_UNSUPPORTED otherwise).  The outputs must not overlap the inputs.
+ * Built for prefill: it runs 128-row tiles, so for m <= 32 (decode) the
+ * two-step path (sharq_dual_gemm, then sharq_prepare_silu_mul) is faster.
  * Requirements: m >= 1; inter >= 128, inter % 128 == 0; k >= 128,
  * k % 128 == 0; the input views as sharq_dual_gemm requires (m activation
  * rows, 2 inter weight rows, one payload); the output views as
