@@ -392,9 +392,11 @@ __device__ __forceinline__ void silu_put_x(const v16f (&acc)[2][TN], uint16_t *x
 }
 
 // The exchange and x = bf16(silu(g) u) for this wavefront's half, then the x
-// tile into LDS.  One function per half with its barriers inside (both
-// halves pass the same four): with the halves' steps merged after run-time
-// branches, the accumulators of both halves ended up in scratch memory.
+// tile into LDS.  One function per half with its barriers inside: the half
+// is wave-uniform (from the readfirstlane'd wavefront index, a scalar
+// branch) and both halves pass the same four barriers.  With the halves'
+// steps merged after run-time branches instead, the accumulators of both
+// halves ended up in scratch memory.
 template <int KEEP, int TN, int kHs, int kVals>
 __device__ __forceinline__ void silu_x_tile(v16f (&acc)[2][TN], float *xch, uint16_t *xs, int wave,
                                             int wm, int h, int li, int lane) {
