@@ -740,6 +740,37 @@ def test_dual_gemm_padded_leading_dims(fmt, m, n, k):
         assert np.isnan(host(out)[:, n:]).all()        # nothing written past n
 
 
+@pytest.mark.parametrize("layout", [sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR])
+def test_dual_gemm_silu_prepare_padded_leading_dims(layout):
+    """The fused gate+up entry point with every input and output array inside
+    a larger buffer (padding 0xA5): outputs byte for byte equal to the
+    oracle's on FP4-grid inputs, and the padding untouched."""
+    m, inter, k = 140, 256, 384
+    xb, wb, sp, rs, wq = _silu_gemm_grid_case(m, inter, k, 151, layout)
+    p = oracle.prepare(sq.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    _, ref = oracle.dual_gemm_silu_prepare(sq.MXFP4, p, q, dense_backbone=True)
+    pad = dict(extra_rows=24, extra_bytes=48)
+    for t in (sp, rs, wq):
+        t.codes = _padded(t.codes, layout, **pad)
+        t.scales = _padded(t.scales, layout, **pad)
+    sp.meta = _padded(sp.meta, layout, **pad)
+    sp.dense_codes = _padded(sp.dense_codes, layout, **pad)
+    osp, ors = sq.alloc_prepared(sq.MXFP4, m, inter, DEV, dense_backbone=True, layout=layout)
+    for t in (osp, ors):
+        t.codes = _padded(t.codes, layout, **pad)
+        t.scales = _padded(t.scales, layout, **pad)
+    osp.meta = _padded(osp.meta, layout, **pad)
+    osp.dense_codes = _padded(osp.dense_codes, layout, **pad)
+    sq.bind_dual_gemm_silu_prepare(sp, rs, wq, osp, ors)()
+    _compare_prep(f"silu gemm padded {layout}", osp, ors, ref)
+    for t in (osp.codes, osp.meta, osp.scales, osp.dense_codes, ors.codes, ors.scales):
+        base = t._base                     # the padded buffer: dim 1 is rows (k-step-major) or bytes
+        pad_mask = torch.ones_like(base, dtype=torch.bool)
+        pad_mask[:, :t.shape[1]] = False
+        assert bool((base[pad_mask] == 0xA5).all()), layout
+
+
 NV_VARIANTS = (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED, sq.GEMM_SPARSE_MFMA)
 
 
