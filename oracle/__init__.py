@@ -25,10 +25,16 @@ BLOCK = {MXFP4: 32, NVFP4: 16}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sharq_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_OMP_LIB_PATH = os.path.join(_HERE, "liboracle_omp.so")
 
 # IEEE binary32 semantics: no contraction into FMA, no fast-math, single thread.
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-          "-Wall", "-Wextra", "-Wno-unused-parameter"]
+          "-Wall", "-Wextra", "-Wno-unused-parameter", "-Wno-unknown-pragmas"]
+# The same source for the timed CPU baseline: optimized for the host and with
+# the row loops on OpenMP threads; the arithmetic is unchanged (no contraction,
+# no fast-math, so every value is the one the plain build computes).
+OMP_CFLAGS = ["-O3", "-march=native", "-fopenmp", "-std=c11", "-fPIC", "-shared",
+              "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
 
 def build(force: bool = True) -> str:
@@ -40,7 +46,41 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_omp(force: bool = True) -> str:
+    """Compile the OpenMP build used by the benchmark's CPU baseline into
+    ``oracle/liboracle_omp.so``."""
+    if force or not os.path.exists(_OMP_LIB_PATH):
+        tmp = _OMP_LIB_PATH + ".tmp"
+        subprocess.run(["gcc", *OMP_CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _OMP_LIB_PATH)
+    return _OMP_LIB_PATH
+
+
 _lib = None
+
+
+def _declare(L):
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    L.oracle_prepare.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_float,
+                                 P, P, P, P, P, P, P]
+    L.oracle_prepare.restype = ctypes.c_int
+    L.oracle_dual_gemm_pairs.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, I64,
+                                         P, P, I64, P, P, P]
+    L.oracle_dual_gemm_pairs.restype = ctypes.c_int
+    L.oracle_dual_gemm.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, I64,
+                                   P, P, P]
+    L.oracle_dual_gemm.restype = ctypes.c_int
+    L.oracle_threads.argtypes = [ctypes.c_int]
+    L.oracle_threads.restype = ctypes.c_int
+    return L
+
+
+def omp_lib():
+    """The OpenMP build (CPU baseline only): the same C entry points."""
+    if not os.path.exists(_OMP_LIB_PATH):
+        build_omp(force=False)
+    return _declare(ctypes.CDLL(_OMP_LIB_PATH))
 
 
 def lib():
@@ -48,7 +88,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        L = ctypes.CDLL(_LIB_PATH)
+        L = _declare(ctypes.CDLL(_LIB_PATH))
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         L.oracle_e2m1_encode.argtypes = [ctypes.c_double]
@@ -71,6 +111,14 @@ def lib():
         L.oracle_nv_tensor_scale.restype = ctypes.c_float
         L.oracle_rmsnorm_row.argtypes = [P, P, I64, ctypes.c_float, P]
         L.oracle_rmsnorm_row.restype = None
+        L.oracle_rms_reciprocal.argtypes = [P, I64, ctypes.c_float]
+        L.oracle_rms_reciprocal.restype = ctypes.c_float
+        L.oracle_rmsnorm_scale.argtypes = [P, P, I64, ctypes.c_float, P]
+        L.oracle_rmsnorm_scale.restype = None
+        L.oracle_mx_block.argtypes = [P, ctypes.c_int, P, P, P]
+        L.oracle_mx_block.restype = None
+        L.oracle_nv_block.argtypes = [P, ctypes.c_int, ctypes.c_float, P, P, P]
+        L.oracle_nv_block.restype = None
         L.oracle_residual_add.argtypes = [P, P, I64, P]
         L.oracle_residual_add.restype = None
         L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
@@ -83,17 +131,8 @@ def lib():
         L.oracle_normalize.restype = ctypes.c_int
         L.oracle_residual_f32.argtypes = [ctypes.c_int, P, I64, I64, ctypes.c_float, P]
         L.oracle_residual_f32.restype = ctypes.c_int
-        L.oracle_prepare.argtypes = [ctypes.c_int, P, I64, I64, P, ctypes.c_float,
-                                     P, P, P, P, P, P, P]
-        L.oracle_prepare.restype = ctypes.c_int
         L.oracle_quantize_weight.argtypes = [ctypes.c_int, P, I64, I64, P, P, P]
         L.oracle_quantize_weight.restype = ctypes.c_int
-        L.oracle_dual_gemm_pairs.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, I64,
-                                             P, P, I64, P, P]
-        L.oracle_dual_gemm_pairs.restype = ctypes.c_int
-        L.oracle_dual_gemm.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, I64,
-                                       P, P]
-        L.oracle_dual_gemm.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -161,6 +200,43 @@ def normalize(x: np.ndarray, gamma: Optional[np.ndarray], eps: float = 1e-5) -> 
     g = None if gamma is None else _u16(gamma)
     lib().oracle_normalize(_p(x), m, k, _p(g), eps, _p(out))
     return out
+
+
+def rms_reciprocal(x_row: np.ndarray, eps: float = 1e-5) -> np.float32:
+    """r = 1 / sqrt(mean(x^2) + eps) of one bf16 row, as the RMSNorm computes it."""
+    x = _u16(x_row).ravel()
+    return np.float32(lib().oracle_rms_reciprocal(_p(x), x.size, eps))
+
+
+def rmsnorm_scale(x_row: np.ndarray, gamma: np.ndarray, r: float) -> np.ndarray:
+    """The normalized row in fp32, before its rounding to bf16."""
+    x = _u16(x_row).ravel()
+    g = _u16(gamma).ravel()
+    assert g.size == x.size
+    y = np.empty(x.size, np.float32)
+    lib().oracle_rmsnorm_scale(_p(x), _p(g), x.size, float(r), _p(y))
+    return y
+
+
+def mx_block(v: np.ndarray):
+    """One MXFP4 block of fp32 values: (codes, scale byte, fp32 dequantized values)."""
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    codes = np.zeros(v.size, np.uint8)
+    sb = np.zeros(1, np.uint8)
+    deq = np.zeros(v.size, np.float32)
+    lib().oracle_mx_block(_p(v), v.size, _p(codes), _p(sb), _p(deq))
+    return codes, int(sb[0]), deq
+
+
+def nv_block(v: np.ndarray, s_t: float):
+    """One NVFP4-style block of fp32 values under tensor scale s_t:
+    (codes, E4M3 scale byte, fp32 dequantized values)."""
+    v = np.ascontiguousarray(v, dtype=np.float32).ravel()
+    codes = np.zeros(v.size, np.uint8)
+    sb = np.zeros(1, np.uint8)
+    deq = np.zeros(v.size, np.float32)
+    lib().oracle_nv_block(_p(v), v.size, float(s_t), _p(codes), _p(sb), _p(deq))
+    return codes, int(sb[0]), deq
 
 
 def residual_f32(fmt: int, xn: np.ndarray, s_t: float = 1.0) -> np.ndarray:
@@ -253,17 +329,30 @@ def quantize_weight(fmt: int, w: np.ndarray) -> dict:
     return out
 
 
-def dual_gemm(fmt: int, prep: dict, wq: dict, want_f64: bool = False):
+def _dual_gemm(fmt, prep, wq, want_f64, want_abs, L=None):
     m = prep["r_codes"].shape[0]
     k = prep["r_codes"].shape[1] * 2
     n = wq["codes"].shape[0]
     y = np.zeros((m, n), np.float32)
     y64 = np.zeros((m, n), np.float64) if want_f64 else None
-    lib().oracle_dual_gemm(fmt, _p(prep["s_codes"]), _p(prep["meta"]), _p(prep["s_scales"]),
-                           _p(prep["r_codes"]), _p(prep["r_scales"]), _p(prep["tensor_scale"]),
-                           _p(wq["codes"]), _p(wq["scales"]), _p(wq["tensor_scale"]),
-                           m, n, k, _p(y), _p(y64))
+    yabs = np.zeros((m, n), np.float64) if want_abs else None
+    (L or lib()).oracle_dual_gemm(fmt, _p(prep["s_codes"]), _p(prep["meta"]), _p(prep["s_scales"]),
+                                  _p(prep["r_codes"]), _p(prep["r_scales"]), _p(prep["tensor_scale"]),
+                                  _p(wq["codes"]), _p(wq["scales"]), _p(wq["tensor_scale"]),
+                                  m, n, k, _p(y), _p(y64), _p(yabs))
+    return y, y64, yabs
+
+
+def dual_gemm(fmt: int, prep: dict, wq: dict, want_f64: bool = False):
+    y, y64, _ = _dual_gemm(fmt, prep, wq, want_f64, False)
     return (y, y64) if want_f64 else y
+
+
+def dual_gemm_bound(fmt: int, prep: dict, wq: dict):
+    """Y and, per output, the sum of the magnitudes of its 2k products
+    (sum_k |ds w| + |dr w|, with the tensor scales): (y, y_abs)."""
+    y, _, yabs = _dual_gemm(fmt, prep, wq, False, True)
+    return y, yabs
 
 
 def gather_rows(prep: dict, rows) -> dict:
@@ -282,20 +371,26 @@ def expert_rows(wq: dict, e: int, n: int) -> dict:
 
 
 def grouped_dual_gemm(fmt: int, prep: dict, row_index, offsets, wq: dict, n: int) -> np.ndarray:
+    return grouped_dual_gemm_bound(fmt, prep, row_index, offsets, wq, n)[0]
+
+
+def grouped_dual_gemm_bound(fmt: int, prep: dict, row_index, offsets, wq: dict, n: int):
     """Grouped dual GEMM (a mixture-of-experts layer's expert GEMMs): grouped
     row i of group e (offsets[e] <= i < offsets[e + 1]) is activation row
     row_index[i] (row i itself when row_index is None), multiplied by group e's
     weight, rows e n .. e n + n - 1 of the stacked payload: per group, the
-    dual GEMM of the gathered rows.  Returns Y [offsets[-1], n]."""
+    dual GEMM of the gathered rows.  Returns Y [offsets[-1], n] and the sums
+    of the magnitudes of each output's products."""
     offsets = np.asarray(offsets, dtype=np.int64)
     total = int(offsets[-1])
     idx = np.arange(total) if row_index is None else np.asarray(row_index, dtype=np.int64)
     y = np.zeros((total, n), np.float32)
+    yabs = np.zeros((total, n), np.float64)
     for e in range(len(offsets) - 1):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
-            y[lo:hi] = dual_gemm(fmt, gather_rows(prep, idx[lo:hi]), expert_rows(wq, e, n))
-    return y
+            y[lo:hi], yabs[lo:hi] = dual_gemm_bound(fmt, gather_rows(prep, idx[lo:hi]), expert_rows(wq, e, n))
+    return y, yabs
 
 
 def dual_gemm_silu_prepare(fmt: int, prep: dict, wq: dict, dense_backbone: bool = False):
@@ -321,16 +416,28 @@ def grouped_dual_gemm_silu_prepare(fmt: int, prep: dict, row_index, offsets, wq:
     return prepare_silu_mul(fmt, y[:, :inter], y[:, inter:], dense_backbone)
 
 
-def dual_gemm_pairs(fmt: int, prep: dict, wq: dict, rows, cols, want_f64: bool = False):
-    """Y at the listed (row, col) pairs only (sorted by row is fastest)."""
+def _dual_gemm_pairs(fmt, prep, wq, rows, cols, want_f64, want_abs):
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     cols = np.ascontiguousarray(cols, dtype=np.int64)
     k = prep["r_codes"].shape[1] * 2
     y = np.zeros(rows.size, np.float32)
     y64 = np.zeros(rows.size, np.float64) if want_f64 else None
+    yabs = np.zeros(rows.size, np.float64) if want_abs else None
     lib().oracle_dual_gemm_pairs(fmt, _p(prep["s_codes"]), _p(prep["meta"]), _p(prep["s_scales"]),
                                  _p(prep["r_codes"]), _p(prep["r_scales"]),
                                  _p(prep["tensor_scale"]), _p(wq["codes"]), _p(wq["scales"]),
                                  _p(wq["tensor_scale"]), k, _p(rows), _p(cols), rows.size,
-                                 _p(y), _p(y64))
+                                 _p(y), _p(y64), _p(yabs))
+    return y, y64, yabs
+
+
+def dual_gemm_pairs(fmt: int, prep: dict, wq: dict, rows, cols, want_f64: bool = False):
+    """Y at the listed (row, col) pairs only (sorted by row is fastest)."""
+    y, y64, _ = _dual_gemm_pairs(fmt, prep, wq, rows, cols, want_f64, False)
     return (y, y64) if want_f64 else y
+
+
+def dual_gemm_pairs_bound(fmt: int, prep: dict, wq: dict, rows, cols):
+    """Y at the listed pairs and the sums of the magnitudes of their products."""
+    y, _, yabs = _dual_gemm_pairs(fmt, prep, wq, rows, cols, False, True)
+    return y, yabs

@@ -2,8 +2,10 @@
  * SharQ CPU oracle.  TEST INFRASTRUCTURE ONLY: tests, the smoke check and the
  * benchmark's CPU-baseline leg call it; the product path never does.
  *
- * A plain, slow, single-threaded statement of what the SharQ linear-layer
- * path computes, following "SharQ: Bridging Activation Sparsity and FP4
+ * A plain, slow statement of what the SharQ linear-layer path computes
+ * (single-threaded as the tests build it; the benchmark's CPU baseline also
+ * builds it with OpenMP, which runs independent rows on threads and changes
+ * no value), following "SharQ: Bridging Activation Sparsity and FP4
  * Quantization for LLM Inference" (arXiv:2606.26587), abstract:
  *   sentence 3: an input-adaptive N:M mask extracts an outlier-dominated
  *               sparse backbone, which is quantized to FP4; the dense
@@ -31,6 +33,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_MXFP4 0
 #define ORACLE_NVFP4 1
@@ -175,17 +180,12 @@ float oracle_tree_sum(const float *q, int64_t n)
 }
 
 /*
- * RMSNorm of one row: ss = tree sum of fl32(x*x); mean = fl32(ss/K);
- * r = fl32(1 / fl32(sqrt(fl32(mean + eps)))); out = bf16(fl32(fl32(x*r)*g)).
- * gamma == NULL: no normalization, out = x.
+ * The reciprocal RMS of one row: ss = tree sum of fl32(x*x);
+ * r = fl32(1 / fl32(sqrt(fl32(fl32(ss / K) + eps)))), with an IEEE square
+ * root and division (no reciprocal square root).
  */
-void oracle_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t k, float eps,
-                        uint16_t *out)
+float oracle_rms_reciprocal(const uint16_t *x, int64_t k, float eps)
 {
-    if (!gamma) {
-        memcpy(out, x, (size_t)k * sizeof(uint16_t));
-        return;
-    }
     float *q = (float *)malloc((size_t)k * sizeof(float));
     if (!q)
         abort();
@@ -198,14 +198,39 @@ void oracle_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t k, flo
     float mean = ss / (float)k;
     float var = mean + eps;
     float s = sqrtf(var);
-    float r = 1.0f / s;
+    return 1.0f / s;
+}
+
+/* The normalized row before its rounding to bf16: y = fl32(fl32(x*r)*g). */
+void oracle_rmsnorm_scale(const uint16_t *x, const uint16_t *gamma, int64_t k, float r, float *y)
+{
     for (int64_t i = 0; i < k; i++) {
         float v = oracle_bf16_to_f32(x[i]);
         float g = oracle_bf16_to_f32(gamma[i]);
-        float y = v * r;
-        y = y * g;
-        out[i] = oracle_f32_to_bf16(y);
+        float t = v * r;
+        y[i] = t * g;
     }
+}
+
+/*
+ * RMSNorm of one row: out = bf16(y) with y and r as above.
+ * gamma == NULL: no normalization, out = x.
+ */
+void oracle_rmsnorm_row(const uint16_t *x, const uint16_t *gamma, int64_t k, float eps,
+                        uint16_t *out)
+{
+    if (!gamma) {
+        memcpy(out, x, (size_t)k * sizeof(uint16_t));
+        return;
+    }
+    float r = oracle_rms_reciprocal(x, k, eps);
+    float *y = (float *)malloc((size_t)k * sizeof(float));
+    if (!y)
+        abort();
+    oracle_rmsnorm_scale(x, gamma, k, r, y);
+    for (int64_t i = 0; i < k; i++)
+        out[i] = oracle_f32_to_bf16(y[i]);
+    free(y);
 }
 
 /*
@@ -298,7 +323,7 @@ void oracle_mask_group(const float v[4], int *i0, int *i1)
 /* ------------------------------------------------------------------ */
 
 /* MXFP4: one E8M0 scale per block of n values; codes and exact dequant. */
-static void mx_block(const float *v, int n, uint8_t *codes, uint8_t *scale_byte, float *deq)
+void oracle_mx_block(const float *v, int n, uint8_t *codes, uint8_t *scale_byte, float *deq)
 {
     double amax = 0.0;
     for (int i = 0; i < n; i++)
@@ -319,7 +344,7 @@ static void mx_block(const float *v, int n, uint8_t *codes, uint8_t *scale_byte,
  * effective scale S = fl32(e4m3value(sb) * s_t), t = fl32(v / S),
  * dequant fl32(e2m1value * S).  S == 0 gives signed zero codes.
  */
-static void nv_block(const float *v, int n, float s_t, uint8_t *codes, uint8_t *scale_byte,
+void oracle_nv_block(const float *v, int n, float s_t, uint8_t *codes, uint8_t *scale_byte,
                      float *deq)
 {
     float amax = 0.0f;
@@ -352,9 +377,9 @@ static void quant_row(int fmt, const float *v, int64_t k, float s_t, uint8_t *co
     int blk = (fmt == ORACLE_MXFP4) ? 32 : 16;
     for (int64_t b = 0; b < k / blk; b++) {
         if (fmt == ORACLE_MXFP4)
-            mx_block(v + b * blk, blk, codes + b * blk, scales + b, deq + b * blk);
+            oracle_mx_block(v + b * blk, blk, codes + b * blk, scales + b, deq + b * blk);
         else
-            nv_block(v + b * blk, blk, s_t, codes + b * blk, scales + b, deq + b * blk);
+            oracle_nv_block(v + b * blk, blk, s_t, codes + b * blk, scales + b, deq + b * blk);
     }
 }
 
@@ -371,6 +396,65 @@ float oracle_nv_tensor_scale(float amax)
 /* ------------------------------------------------------------------ */
 
 /*
+ * Mask, backbone and residual of one normalized row xn_row (k values), with
+ * its own work buffers; writes row i of each output array.
+ */
+static void prepare_row(int fmt, const uint16_t *xn_row, int64_t i, int64_t k, float s_t,
+                        uint8_t *meta, uint8_t *s_codes, uint8_t *s_scales, uint8_t *r_codes,
+                        uint8_t *r_scales, uint8_t *s_dense)
+{
+    int blk = (fmt == ORACLE_MXFP4) ? 32 : 16;
+    float *xf = (float *)malloc((size_t)k * sizeof(float));
+    float *v = (float *)malloc((size_t)k * sizeof(float));
+    float *d = (float *)malloc((size_t)k * sizeof(float));
+    float *rr = (float *)malloc((size_t)k * sizeof(float));
+    uint8_t *cs = (uint8_t *)malloc((size_t)k);
+    uint8_t *cr = (uint8_t *)malloc((size_t)k);
+    int *keep = (int *)malloc((size_t)k * sizeof(int));
+    if (!xf || !v || !d || !rr || !cs || !cr || !keep)
+        abort();
+    for (int64_t j = 0; j < k; j++)
+        xf[j] = oracle_bf16_to_f32(xn_row[j]);
+    /* mask */
+    for (int64_t g = 0; g < k / 4; g++) {
+        int i0, i1;
+        oracle_mask_group(xf + 4 * g, &i0, &i1);
+        for (int t = 0; t < 4; t++)
+            keep[4 * g + t] = (t == i0 || t == i1);
+        uint8_t nib = (uint8_t)(i0 | (i1 << 2));
+        uint8_t *mb = meta + i * (k / 8) + g / 2;
+        if (g % 2 == 0)
+            *mb = nib;
+        else
+            *mb = (uint8_t)(*mb | (nib << 4));
+    }
+    /* backbone */
+    for (int64_t j = 0; j < k; j++)
+        v[j] = keep[j] ? xf[j] : 0.0f;
+    quant_row(fmt, v, k, s_t, cs, s_scales + i * (k / blk), d);
+    for (int64_t g = 0; g < k / 4; g++) {
+        int i0 = -1, i1 = -1;
+        for (int t = 0; t < 4; t++) {
+            if (keep[4 * g + t]) {
+                if (i0 < 0) i0 = t; else i1 = t;
+            }
+        }
+        s_codes[i * (k / 4) + g] = (uint8_t)(cs[4 * g + i0] | (cs[4 * g + i1] << 4));
+    }
+    if (s_dense) {
+        for (int64_t j = 0; j < k; j += 2)
+            s_dense[i * (k / 2) + j / 2] = (uint8_t)(cs[j] | (cs[j + 1] << 4));
+    }
+    /* residual against the quantized backbone */
+    for (int64_t j = 0; j < k; j++)
+        rr[j] = xf[j] - d[j];
+    quant_row(fmt, rr, k, s_t, cr, r_scales + i * (k / blk), d);
+    for (int64_t j = 0; j < k; j += 2)
+        r_codes[i * (k / 2) + j / 2] = (uint8_t)(cr[j] | (cr[j + 1] << 4));
+    free(xf); free(v); free(d); free(rr); free(cs); free(cr); free(keep);
+}
+
+/*
  * For each row of X [m, k] (bf16, row stride k):
  *   x_n = RMSNorm(x) (or x when gamma == NULL);
  *   2:4 mask on |x_n| per aligned group of four along k;
@@ -384,7 +468,8 @@ float oracle_nv_tensor_scale(float amax)
  *   r_scales one scale byte per block of the residual
  *   s_dense  (optional, may be NULL) backbone codes in the dense layout of r_codes
  *   tensor_scale (NVFP4 only) fl32(amax(x_n)/2688), shared by both paths
- * Returns 0, or -1 on a bad argument.
+ * Rows are independent; the row loops may run on several threads (built with
+ * OpenMP) without changing any value.  Returns 0, or -1 on a bad argument.
  */
 int oracle_prepare(int fmt, const uint16_t *x, int64_t m, int64_t k, const uint16_t *gamma,
                    float eps, uint8_t *meta, uint8_t *s_codes, uint8_t *s_scales,
@@ -394,16 +479,10 @@ int oracle_prepare(int fmt, const uint16_t *x, int64_t m, int64_t k, const uint1
     if ((fmt != ORACLE_MXFP4 && fmt != ORACLE_NVFP4) || m < 0 || k <= 0 || k % blk)
         return -1;
     uint16_t *xn = (uint16_t *)malloc((size_t)(m * k + 1) * sizeof(uint16_t));
-    float *xf = (float *)malloc((size_t)k * sizeof(float));
-    float *v = (float *)malloc((size_t)k * sizeof(float));
-    float *d = (float *)malloc((size_t)k * sizeof(float));
-    float *rr = (float *)malloc((size_t)k * sizeof(float));
-    uint8_t *cs = (uint8_t *)malloc((size_t)k);
-    uint8_t *cr = (uint8_t *)malloc((size_t)k);
-    int *keep = (int *)malloc((size_t)k * sizeof(int));
-    if (!xn || !xf || !v || !d || !rr || !cs || !cr || !keep)
+    if (!xn)
         abort();
 
+    #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < m; i++)
         oracle_rmsnorm_row(x + i * k, gamma, k, eps, xn + i * k);
 
@@ -420,47 +499,11 @@ int oracle_prepare(int fmt, const uint16_t *x, int64_t m, int64_t k, const uint1
             *tensor_scale = s_t;
     }
 
-    for (int64_t i = 0; i < m; i++) {
-        for (int64_t j = 0; j < k; j++)
-            xf[j] = oracle_bf16_to_f32(xn[i * k + j]);
-        /* mask */
-        for (int64_t g = 0; g < k / 4; g++) {
-            int i0, i1;
-            oracle_mask_group(xf + 4 * g, &i0, &i1);
-            for (int t = 0; t < 4; t++)
-                keep[4 * g + t] = (t == i0 || t == i1);
-            uint8_t nib = (uint8_t)(i0 | (i1 << 2));
-            uint8_t *mb = meta + i * (k / 8) + g / 2;
-            if (g % 2 == 0)
-                *mb = nib;
-            else
-                *mb = (uint8_t)(*mb | (nib << 4));
-        }
-        /* backbone */
-        for (int64_t j = 0; j < k; j++)
-            v[j] = keep[j] ? xf[j] : 0.0f;
-        quant_row(fmt, v, k, s_t, cs, s_scales + i * (k / blk), d);
-        for (int64_t g = 0; g < k / 4; g++) {
-            int i0 = -1, i1 = -1;
-            for (int t = 0; t < 4; t++) {
-                if (keep[4 * g + t]) {
-                    if (i0 < 0) i0 = t; else i1 = t;
-                }
-            }
-            s_codes[i * (k / 4) + g] = (uint8_t)(cs[4 * g + i0] | (cs[4 * g + i1] << 4));
-        }
-        if (s_dense) {
-            for (int64_t j = 0; j < k; j += 2)
-                s_dense[i * (k / 2) + j / 2] = (uint8_t)(cs[j] | (cs[j + 1] << 4));
-        }
-        /* residual against the quantized backbone */
-        for (int64_t j = 0; j < k; j++)
-            rr[j] = xf[j] - d[j];
-        quant_row(fmt, rr, k, s_t, cr, r_scales + i * (k / blk), d);
-        for (int64_t j = 0; j < k; j += 2)
-            r_codes[i * (k / 2) + j / 2] = (uint8_t)(cr[j] | (cr[j + 1] << 4));
-    }
-    free(xn); free(xf); free(v); free(d); free(rr); free(cs); free(cr); free(keep);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; i++)
+        prepare_row(fmt, xn + i * k, i, k, s_t, meta, s_codes, s_scales, r_codes, r_scales,
+                    s_dense);
+    free(xn);
     return 0;
 }
 
@@ -593,14 +636,17 @@ static void decode_dense_row(int fmt, const uint8_t *codes, const uint8_t *scale
  * Y[i, j] = sum_k ds[i,k] w[j,k] + sum_k dr[i,k] w[j,k] (both sums in k
  * order, one fp64 accumulator, backbone first), NVFP4: times the two tensor
  * scales in fp64; then rounded once to fp32.  Each pair (rows[p], cols[p])
- * gives y[p]; y64 (optional) receives the fp64 value before rounding.
+ * gives y[p]; y64 (optional) receives the fp64 value before rounding, and
+ * y_abs (optional) the sum of the magnitudes of the same 2k products (with
+ * the tensor scales), which bounds the error of any fp32 summation order.
  */
 int oracle_dual_gemm_pairs(int fmt, const uint8_t *s_codes, const uint8_t *meta,
                            const uint8_t *s_scales, const uint8_t *r_codes,
                            const uint8_t *r_scales, const float *a_tensor_scale,
                            const uint8_t *w_codes, const uint8_t *w_scales,
                            const float *w_tensor_scale, int64_t k, const int64_t *rows,
-                           const int64_t *cols, int64_t count, float *y, double *y64)
+                           const int64_t *cols, int64_t count, float *y, double *y64,
+                           double *y_abs)
 {
     double *ds = (double *)malloc((size_t)k * sizeof(double));
     double *dr = (double *)malloc((size_t)k * sizeof(double));
@@ -621,36 +667,60 @@ int oracle_dual_gemm_pairs(int fmt, const uint8_t *s_codes, const uint8_t *meta,
             acc += ds[t] * dw[t];
         for (int64_t t = 0; t < k; t++)
             acc += dr[t] * dw[t];
-        if (fmt == ORACLE_NVFP4)
+        double mag = 0.0;
+        if (y_abs) {
+            for (int64_t t = 0; t < k; t++)
+                mag += fabs(ds[t] * dw[t]) + fabs(dr[t] * dw[t]);
+        }
+        if (fmt == ORACLE_NVFP4) {
             acc = acc * (double)*a_tensor_scale * (double)*w_tensor_scale;
+            mag = mag * (double)*a_tensor_scale * (double)*w_tensor_scale;
+        }
         if (y64)
             y64[p] = acc;
+        if (y_abs)
+            y_abs[p] = mag;
         y[p] = (float)acc;
     }
     free(ds); free(dr); free(dw);
     return 0;
 }
 
-/* Full Y [m, n] (row stride n); same arithmetic as oracle_dual_gemm_pairs. */
+/* Full Y [m, n] (row stride n); same arithmetic as oracle_dual_gemm_pairs,
+ * one output row at a time (rows may run on several threads). */
 int oracle_dual_gemm(int fmt, const uint8_t *s_codes, const uint8_t *meta,
                      const uint8_t *s_scales, const uint8_t *r_codes, const uint8_t *r_scales,
                      const float *a_tensor_scale, const uint8_t *w_codes,
                      const uint8_t *w_scales, const float *w_tensor_scale, int64_t m, int64_t n,
-                     int64_t k, float *y, double *y64)
+                     int64_t k, float *y, double *y64, double *y_abs)
 {
-    int64_t *rows = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
-    int64_t *cols = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
-    if (!rows || !cols)
-        abort();
+    #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < m; i++) {
+        int64_t *rows = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+        int64_t *cols = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+        if (!rows || !cols)
+            abort();
         for (int64_t j = 0; j < n; j++) {
             rows[j] = i;
             cols[j] = j;
         }
         oracle_dual_gemm_pairs(fmt, s_codes, meta, s_scales, r_codes, r_scales, a_tensor_scale,
                                w_codes, w_scales, w_tensor_scale, k, rows, cols, n, y + i * n,
-                               y64 ? y64 + i * n : NULL);
+                               y64 ? y64 + i * n : NULL, y_abs ? y_abs + i * n : NULL);
+        free(rows); free(cols);
     }
-    free(rows); free(cols);
     return 0;
+}
+
+/* Number of threads the row loops use (1 unless built with OpenMP). */
+int oracle_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
 }

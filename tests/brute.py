@@ -94,3 +94,87 @@ def mx_quantize_brute(v: np.ndarray):
 
 def fraction_dot(a, b) -> Fraction:
     return sum((Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a, b)), Fraction(0))
+
+
+# ---------------------------------------------------------------- fp32 steps
+# numpy float32 scalars and arrays round every +, -, *, / and sqrt to nearest
+# even (IEEE binary32) and never contract a product into an FMA, so these
+# restate the fp32 step sequences of the RMSNorm and of the NVFP4-style block
+# quantizer with an arithmetic of their own.
+
+def bf16_rne_bits(v) -> np.ndarray:
+    """bf16 bit patterns of finite float32 values: the value rounded to its
+    8 leading significant bits (or to a multiple of 2^-133 below 2^-126),
+    nearest, ties to even, computed on the exact value in float64."""
+    v64 = np.asarray(v, dtype=np.float32).astype(np.float64)
+    _, e = np.frexp(np.abs(v64))                 # |v| = f 2^e, f in [0.5, 1)
+    q = np.maximum(e - 8, -133)                  # weight of the last kept bit
+    r = np.ldexp(np.rint(np.ldexp(np.abs(v64), -q)), q)
+    out = np.copysign(r, v64).astype(np.float32)   # exact: at most 8 significant bits
+    return (out.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_bits_value(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def pairwise_halves_f32(q: np.ndarray) -> np.float32:
+    """fl32 sum as a perfect binary tree over the next power of two of
+    leaves (missing leaves +0): the sum of a run is the fl32 sum of the sums
+    of its two halves."""
+    q = np.asarray(q, dtype=np.float32)
+    n = 1
+    while n < q.size:
+        n *= 2
+    leaves = np.zeros(n, np.float32)
+    leaves[:q.size] = q
+
+    def rec(lo: int, hi: int) -> np.float32:
+        if hi - lo == 1:
+            return leaves[lo]
+        if hi - lo <= 64:                        # small runs: level by level
+            a = leaves[lo:hi].copy()
+            while a.size > 1:
+                a = (a[: a.size // 2 * 2].reshape(-1, 2)[:, 0]
+                     + a[: a.size // 2 * 2].reshape(-1, 2)[:, 1]).astype(np.float32)
+            return np.float32(a[0])
+        mid = (lo + hi) // 2
+        return np.float32(rec(lo, mid) + rec(mid, hi))
+
+    return rec(0, n)
+
+
+def rms_reciprocal_f32(x_bits, eps: float) -> np.float32:
+    """r of the RMSNorm of one bf16 row: 1 / sqrt(sum(x^2) / K + eps), each
+    step one binary32 operation, the sum a perfect binary tree."""
+    x = bf16_bits_value(x_bits).ravel()
+    ss = pairwise_halves_f32((x * x).astype(np.float32))
+    mean = np.float32(ss / np.float32(x.size))
+    s = np.sqrt(np.float32(mean + np.float32(eps)), dtype=np.float32)
+    return np.float32(np.float32(1.0) / s)
+
+
+def rmsnorm_f32(x_bits, g_bits, r) -> np.ndarray:
+    """(x * r) * gamma in binary32, before the rounding to bf16."""
+    x = bf16_bits_value(x_bits)
+    g = bf16_bits_value(g_bits)
+    return ((x * np.float32(r)).astype(np.float32) * g).astype(np.float32)
+
+
+def nv_block_brute(v, s_t):
+    """NVFP4-style block of float32 values under tensor scale s_t: E4M3 scale
+    code = nearest to amax / (6 s_t) (one binary32 division by the binary32
+    product 6 s_t), S = e4m3 value * s_t (binary32), element codes = nearest
+    E2M1 to the binary32 quotient v / S; S == 0 gives signed zeros."""
+    v = np.asarray(v, dtype=np.float32)
+    s_t = np.float32(s_t)
+    amax = np.float32(np.abs(v).max())
+    ratio = np.float32(amax / np.float32(np.float32(6.0) * s_t))
+    sb = int(e4m3_argmin(np.float64(ratio)))
+    S = np.float32(np.float32(E4M3_VALUES[sb]) * s_t)
+    if S == 0:
+        c = (np.signbit(v) * 8).astype(np.uint8)
+        return c, sb, np.where(np.signbit(v), -0.0, 0.0).astype(np.float32)
+    t = (v / S).astype(np.float32)
+    c = e2m1_argmin(t.astype(np.float64))
+    return c, sb, (e2m1_value(c).astype(np.float32) * S).astype(np.float32)
