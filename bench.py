@@ -271,37 +271,76 @@ def mfma_yardstick(torch, dev) -> dict:
     return res
 
 
-def cpu_baseline(w: si.Workload, x, W, g, seconds: float = 12.0) -> dict:
-    """The CPU oracle (single thread, as committed) on a bounded sample of the
-    workload; reported in the same unit as `value` by projecting the sample's
-    per-row and per-output rates to the full step."""
+def _host_cpu():
+    """(CPU model name, CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    return model, nproc
+
+
+def cpu_baseline(w: si.Workload, x, W, g, reps: int = 3) -> dict:
+    """The CPU oracle as committed, built for this host (gcc -O3 -march=native
+    -fopenmp -ffp-contract=off, no fast-math: the same values as the test
+    build), timed on one thread and on all the threads this process may use:
+    the preparation on the whole X, the dual GEMM on a sample of whole rows of
+    Y (every column), each the median of `reps` runs.  The full step's time is
+    the preparation's plus the GEMM sample's scaled to all rows; `value` is
+    the all-threads figure in the unit of the GPU line."""
+    import statistics
+
     import oracle
-    fmt = w.fmt
-    rows = 128
-    t0 = time.perf_counter()
-    p = oracle.prepare(fmt, x[:rows], g)
-    t_prep = (time.perf_counter() - t0) / rows                 # s per row
-    q = oracle.quantize_weight(fmt, W[:256])
-    rng = np.random.default_rng(0)
-    # budget ~`seconds` of GEMM work; calibrate on a small batch first
-    probe = 256
-    pr = np.sort(rng.integers(0, rows, probe))
-    pc = rng.integers(0, 256, probe)
-    t0 = time.perf_counter()
-    oracle.dual_gemm_pairs(fmt, p, q, pr, pc)
-    per = (time.perf_counter() - t0) / probe
-    count = int(max(probe, min(2_000_000, seconds / max(per, 1e-9))))
-    pr = np.sort(rng.integers(0, rows, count))
-    pc = rng.integers(0, 256, count)
-    t0 = time.perf_counter()
-    oracle.dual_gemm_pairs(fmt, p, q, pr, pc)
-    t_out = (time.perf_counter() - t0) / count                # s per output element
-    step_s = t_prep * w.m + t_out * w.m * w.n
+    try:
+        L = oracle.omp_lib_built()
+        build = "gcc " + " ".join(oracle.OMP_CFLAGS)
+    except Exception as e:                      # no compiler: the plain build, one thread
+        L, build = None, f"plain build ({type(e).__name__} building the OpenMP one)"
+    model, nproc = _host_cpu()
+    env = os.environ.get("OMP_NUM_THREADS")
+    all_threads = int(env) if env and env.isdigit() else nproc
+    q = oracle.quantize_weight(w.fmt, W)      # the weight is quantized offline: untimed
     flops = 3.0 * w.m * w.n * w.k
-    return {"value": flops / step_s / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": (f"oracle prepare on {rows} rows of X and dual GEMM on {count} sampled "
-                       f"outputs (K={w.k}), single thread; full-step time projected from the "
-                       f"per-row and per-output rates: {step_s:.1f} s")}
+
+    def run(threads):
+        used = L.oracle_threads(threads) if L is not None else 1
+        rows = min(w.m, -(-max(8, used) // used) * used)
+        tp, tg = [], []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            p = oracle.prepare(w.fmt, x, g, L=L)
+            tp.append(time.perf_counter() - t0)
+            ps = oracle.gather_rows(p, np.arange(rows))
+            t0 = time.perf_counter()
+            oracle.dual_gemm(w.fmt, ps, q, L=L)
+            tg.append(time.perf_counter() - t0)
+        prep_s, gemm_rows_s = statistics.median(tp), statistics.median(tg)
+        gemm_s = gemm_rows_s * w.m / rows
+        step_s = prep_s + gemm_s
+        pbytes = w.m * w.k * prep_bytes_per_elem(w.fmt)
+        return {"threads": used, "prep_s": round(prep_s, 4), "prep_GB/s": round(pbytes / prep_s / 1e9, 3),
+                "gemm_rows_sampled": rows, "gemm_sample_s": round(gemm_rows_s, 4),
+                "gemm_s_projected": round(gemm_s, 2), "gemm_TFLOP/s": flops / gemm_s / 1e12,
+                "step_s_projected": round(step_s, 2), "TFLOP/s": flops / step_s / 1e12}
+
+    one = run(1)
+    many = run(all_threads) if L is not None and all_threads > 1 else one
+    return {"value": many["TFLOP/s"], "unit": "TFLOP/s", "cores": many["threads"], "kind": "oracle",
+            "sample": (f"oracle preparation of the whole X ({w.m}x{w.k}) and dual GEMM of the first "
+                       f"{many['gemm_rows_sampled']} (all threads) / {one['gemm_rows_sampled']} (one thread) "
+                       f"rows of Y against all {w.n} columns (K={w.k}); median of {reps} runs each; the "
+                       f"full step's time is the preparation's plus the GEMM sample's scaled to {w.m} rows"),
+            "single_thread": one, "all_threads": many, "nproc": nproc, "OMP_NUM_THREADS": env,
+            "cpu_model": model, "build": build}
 
 
 CHAIN_LAYERS = 3     # weight copies cycled, so that no linear's W stays in the 256 MB cache

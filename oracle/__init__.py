@@ -83,6 +83,22 @@ def omp_lib():
     return _declare(ctypes.CDLL(_OMP_LIB_PATH))
 
 
+_omp_fresh = None
+
+
+def omp_lib_built():
+    """The OpenMP build compiled in this process (-march=native is this host's
+    instruction set, so a library built on another machine is not reused)."""
+    global _omp_fresh
+    if _omp_fresh is None:
+        import tempfile
+        d = tempfile.mkdtemp(prefix="oracle_omp_")
+        path = os.path.join(d, "liboracle_omp.so")
+        subprocess.run(["gcc", *OMP_CFLAGS, "-o", path, _SRC, "-lm"], check=True)
+        _omp_fresh = _declare(ctypes.CDLL(path))
+    return _omp_fresh
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -249,8 +265,9 @@ def residual_f32(fmt: int, xn: np.ndarray, s_t: float = 1.0) -> np.ndarray:
 
 
 def prepare(fmt: int, x: np.ndarray, gamma: Optional[np.ndarray] = None, eps: float = 1e-5,
-            dense_backbone: bool = False) -> dict:
-    """Preparation operator on X [m, k]; returns the exported arrays."""
+            dense_backbone: bool = False, L=None) -> dict:
+    """Preparation operator on X [m, k]; returns the exported arrays.  L: the
+    library to run (the OpenMP build for the CPU baseline; default the plain one)."""
     x = _u16(x)
     m, k = x.shape
     blk = BLOCK[fmt]
@@ -265,7 +282,7 @@ def prepare(fmt: int, x: np.ndarray, gamma: Optional[np.ndarray] = None, eps: fl
     if dense_backbone:
         out["s_dense"] = np.zeros((m, k // 2), np.uint8)
     g = None if gamma is None else _u16(gamma)
-    rc = lib().oracle_prepare(fmt, _p(x), m, k, _p(g), eps, _p(out["meta"]), _p(out["s_codes"]),
+    rc = (L or lib()).oracle_prepare(fmt, _p(x), m, k, _p(g), eps, _p(out["meta"]), _p(out["s_codes"]),
                               _p(out["s_scales"]), _p(out["r_codes"]), _p(out["r_scales"]),
                               _p(out.get("s_dense")), _p(out["tensor_scale"]))
     if rc != 0:
@@ -343,8 +360,8 @@ def _dual_gemm(fmt, prep, wq, want_f64, want_abs, L=None):
     return y, y64, yabs
 
 
-def dual_gemm(fmt: int, prep: dict, wq: dict, want_f64: bool = False):
-    y, y64, _ = _dual_gemm(fmt, prep, wq, want_f64, False)
+def dual_gemm(fmt: int, prep: dict, wq: dict, want_f64: bool = False, L=None):
+    y, y64, _ = _dual_gemm(fmt, prep, wq, want_f64, False, L)
     return (y, y64) if want_f64 else y
 
 

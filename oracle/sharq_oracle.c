@@ -254,11 +254,14 @@ void oracle_residual_add(const uint16_t *h, const uint16_t *o, int64_t n, uint16
 
 /*
  * bf16 nearest-even of a double: directly from the double for |v| >= 2^-126
- * (8 significant bits, ties to even); below 2^-126, the bf16 subnormal range,
- * through float (the double rounded to float, then to bf16).
+ * (8 significant bits, ties to even; a result of 2^128 or more, and an
+ * infinite v, is infinite); below 2^-126, the bf16 subnormal range, through
+ * float (the double rounded to float, then to bf16).
  */
 uint16_t oracle_f64_to_bf16(double v)
 {
+    if (isnan(v))                             /* a NaN rounds to a (quiet) NaN */
+        return signbit(v) ? 0xFFC0u : 0x7FC0u;
     if (v == 0.0)
         return signbit(v) ? 0x8000u : 0u;
     int e;

@@ -141,8 +141,23 @@ def _ptr(t) -> Optional[int]:
 
 def _ld(t) -> int:
     """Row stride of a row-major 2-D tensor, in elements (the stride of a
-    single-row tensor is arbitrary; its row length is used instead)."""
+    single-row tensor is arbitrary; its row length is used instead).  The
+    library reads and writes each row as contiguous elements, so a view whose
+    last dimension is strided is refused."""
+    if t.dim() != 2:
+        raise ValueError(f"expected a 2-D tensor, got {t.dim()} dimensions")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("the last dimension must have unit stride (rows are read as contiguous elements)")
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _vec(t, n: int, what: str):
+    """A 1-D device tensor of n contiguous elements."""
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on the GPU")
+    if t.dim() != 1 or t.shape[0] != n or (n > 1 and t.stride(0) != 1):
+        raise ValueError(f"{what} must be a contiguous 1-D tensor of {n} elements")
+    return t
 
 
 def _bits16(t):
@@ -314,8 +329,8 @@ class BoundCall:
 def bind_prepare(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None) -> BoundCall:
     """sharq_prepare into caller-provided buffers, bound for repeated calls."""
     x = _bits16(x)
-    g = None if gamma is None else _bits16(gamma)
     m, k = x.shape
+    g = None if gamma is None else _vec(_bits16(gamma), k, "gamma")
     vs, vr = sp.view(), rs.view()
     args = (ctypes.c_int(sp.fmt), ctypes.c_void_p(x.data_ptr()), ctypes.c_int64(m), ctypes.c_int64(k),
             ctypes.c_int64(_ld(x)), ctypes.c_void_p(_ptr(g)), ctypes.c_float(float(eps)),
@@ -331,8 +346,9 @@ def prepare_into(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None):
 def bind_prepare_residual(h, o, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, out, stream=None) -> BoundCall:
     """sharq_prepare_residual: out = bf16(h + o) (the new residual stream; may
     be h or o itself), then the preparation of out, bound for repeated calls."""
-    h, o, out, g = _bits16(h), _bits16(o), _bits16(out), _bits16(gamma)
+    h, o, out = _bits16(h), _bits16(o), _bits16(out)
     m, k = h.shape
+    g = _vec(_bits16(gamma), k, "gamma")
     if tuple(o.shape) != (m, k) or tuple(out.shape) != (m, k):
         raise ValueError("h, o and out must have the same shape")
     vs, vr = sp.view(), rs.view()
@@ -396,6 +412,9 @@ def bind_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, out, variant: int
                    w_dense_scales=None, stream=None) -> BoundCall:
     """sharq_dual_gemm into `out` (fp32 [m, n]), bound for repeated calls."""
     m, k, n = sp.rows, sp.k, w.rows
+    out = _f32(out)
+    if out.dim() != 2 or tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
     wv_s = w.view()
     if w_dense_scales is not None:
         wv_d = FP4ViewC.from_buffer_copy(wv_s)
@@ -460,6 +479,14 @@ def bind_grouped_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, group_off
     if group_offsets.dtype != torch.int64 or (row_index is not None and row_index.dtype != torch.int32):
         raise TypeError("group_offsets must be int64 and row_index int32")
     groups = group_offsets.numel() - 1
+    _vec(group_offsets, groups + 1, "group_offsets")
+    if row_index is not None:
+        _vec(row_index, row_index.numel(), "row_index")
+        if row_index.numel() < rows:
+            raise ValueError("row_index must hold an entry for every grouped row")
+    out = _f32(out)
+    if out.dim() != 2 or out.shape[0] < rows:
+        raise ValueError(f"out must be 2-D with at least {rows} rows")
     n, k = out.shape[1], sp.k
     if w.rows % groups:
         raise ValueError("the stacked weight must hold the same number of rows for every group")
@@ -497,6 +524,11 @@ def bind_grouped_dual_gemm_silu_prepare(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tens
     if group_offsets.dtype != torch.int64 or (row_index is not None and row_index.dtype != torch.int32):
         raise TypeError("group_offsets must be int64 and row_index int32")
     groups = group_offsets.numel() - 1
+    _vec(group_offsets, groups + 1, "group_offsets")
+    if row_index is not None:
+        _vec(row_index, row_index.numel(), "row_index")
+        if row_index.numel() < rows:
+            raise ValueError("row_index must hold an entry for every grouped row")
     if w.rows % (2 * groups):
         raise ValueError("the stacked weight must hold 2 * inter rows for every group")
     inter, k = w.rows // (2 * groups), sp.k

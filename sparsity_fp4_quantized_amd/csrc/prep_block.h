@@ -219,15 +219,23 @@ __device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int6
 // float below.  A double exp differs from another correctly implemented one
 // by at most an ulp, so only a value within 2^-51 of a midpoint could round
 // differently.
-__device__ __forceinline__ uint32_t bf16_of_double(double v) {
-  const uint64_t bits = __double_as_longlong(v);
+// The rounding itself is IEEE nearest-even with overflow: |v| >= 2^128 (or a
+// carry out of the largest binade) gives Inf, a NaN gives a quiet NaN of the
+// same sign.  Host and device: a host build of this header checks it against
+// the CPU reference on every branch.
+__host__ __device__ __forceinline__ uint32_t bf16_of_double(double v) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, v);
   const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
   const uint32_t sign = (uint32_t)(bits >> 48) & 0x8000u;
-  if (mag < (897ull << 52)) {                       // |v| < 2^-126
-    const uint32_t f = __float_as_uint((float)v);
+  if (mag > 0x7FF0000000000000ull) return sign | 0x7FC0u;   // NaN
+  if (mag >= (1151ull << 52)) return sign | 0x7F80u;        // |v| >= 2^128, Inf
+  if (mag < (897ull << 52)) {                               // |v| < 2^-126
+    const uint32_t f = __builtin_bit_cast(uint32_t, (float)v);
     return (f + 0x7FFFu + ((f >> 16) & 1u)) >> 16;
   }
-  const uint64_t r = (mag + 0xFFFFFFFFFFFull + ((mag >> 45) & 1ull)) >> 45;   // exponent | 7 bits
+  // exponent | 7 bits, nearest even; a carry out of the 2^127 binade lands
+  // on exactly 0x7F80 (Inf)
+  const uint64_t r = (mag + 0xFFFFFFFFFFFull + ((mag >> 45) & 1ull)) >> 45;
   return sign | (uint32_t)(r - ((uint64_t)(1023 - 127) << 7));
 }
 

@@ -322,3 +322,17 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sq, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         sq.lib()
+
+
+def test_binding_refuses_strided_rows():
+    """The library reads and writes each row as contiguous elements: a view
+    whose last dimension is strided (x[:, ::2]) must be refused by the
+    binding, not passed on with a row stride that the ABI would accept."""
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    assert sq._ld(x) == 64
+    assert sq._ld(x[:, :32]) == 64          # padded rows are fine
+    assert sq._ld(x[:1]) == 64
+    for bad in (x[:, ::2], x.t(), x.view(4, 8, 8)):
+        with pytest.raises(ValueError):
+            sq._ld(bad)

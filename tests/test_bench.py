@@ -46,6 +46,27 @@ def test_gemm_bytes(name, mb):
     assert round(bench.gemm_bytes(w) / 1e6, 1) == mb
 
 
+def test_openmp_oracle_build_gives_the_same_values():
+    """The CPU baseline's build (-O3 -march=native -fopenmp, rows on threads)
+    computes exactly what the test build computes."""
+    import numpy as np
+
+    import oracle
+    L = oracle.omp_lib_built()
+    assert L.oracle_threads(4) == 4
+    for fmt, name in ((oracle.MXFP4, "tiny"), (oracle.NVFP4, "tiny")):
+        w = si.WORKLOADS[name]
+        x, W = si.workload_x(w, m=37), si.workload_w(w, n=70)
+        g = si.gamma(w.k, 3)
+        a = oracle.prepare(fmt, x, g, dense_backbone=True)
+        b = oracle.prepare(fmt, x, g, dense_backbone=True, L=L)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), key
+        q = oracle.quantize_weight(fmt, W)
+        assert np.array_equal(oracle.dual_gemm(fmt, a, q).view(np.uint32),
+                              oracle.dual_gemm(fmt, a, q, L=L).view(np.uint32))
+
+
 @pytest.mark.gpu
 def test_bench_line_contract():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "20", "--warmup", "5"],
@@ -66,3 +87,5 @@ def test_bench_line_contract():
     assert r["bound"] == "mfma" and r["peak"] == 10100.0 and 0 < r["frac"] < 1
     c = b["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] >= 1 and c["value"] > 0 and c["sample"]
+    assert c["single_thread"]["threads"] == 1 and c["all_threads"]["threads"] == c["cores"]
+    assert c["nproc"] >= 1 and c["cpu_model"]
