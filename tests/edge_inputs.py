@@ -115,7 +115,7 @@ MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 
 def nv_tie_weight(j: int, seed: int = 0) -> np.ndarray:
-    """W [rows, 64] (bf16 bits) whose tensor maximum is 2688 2^j, so the
+    """W [rows, 128] (bf16 bits) whose tensor maximum is 2688 2^j, so the
     tensor scale is exactly 2^j; each 16-block has maximum e4m3(sb) 6 2^j for
     one sb and holds midpoint * S (S = e4m3(sb) 2^j, exact in bf16: the
     quotient lands on the E2M1 tie itself), their bf16 neighbours and signs."""
@@ -137,11 +137,11 @@ def nv_tie_weight(j: int, seed: int = 0) -> np.ndarray:
             blk[1:1 + chunk.size] = chunk
             blocks.append(np.roll(blk, int(rng.integers(0, 16))))
     blocks.append(np.r_[np.uint16(_bf16s(2688.0 * 2.0 ** j)), np.zeros(15, np.uint16)])
-    return _rows_of(np.array(blocks, np.uint16), 64)
+    return _rows_of(np.array(blocks, np.uint16), 128)
 
 
 def nv_near_midpoint_weights(count: int, seed: int = 0):
-    """`count` weight tensors [rows, 64] (bf16 bits), each with its own
+    """`count` weight tensors [rows, 128] (bf16 bits), each with its own
     tensor maximum A (tensor scale s_t = fl32(A / 2688)), holding elements v
     whose quotient fl32(v / S) lies within two ulps of an E2M1 midpoint or
     whose code differs from that of fl32(v * fl32(1 / S)): the cases where the
@@ -185,7 +185,7 @@ def nv_near_midpoint_weights(count: int, seed: int = 0):
         if not blocks:
             continue
         blocks.append(np.r_[np.uint16(A_bits), np.zeros(15, np.uint16)])
-        tensors.append(_rows_of(np.array(blocks, np.uint16), 64))
+        tensors.append(_rows_of(np.array(blocks, np.uint16), 128))
     return tensors
 
 
