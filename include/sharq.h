@@ -68,7 +68,7 @@ typedef enum {
     SHARQ_GEMM_AUTO = 0,           /* the format's default (see sharq_dual_gemm) */
     SHARQ_GEMM_DECOMPRESS = 1,     /* backbone expanded from its 2:4 form to dense FP4 while staged in LDS */
     SHARQ_GEMM_DENSE_EXPANDED = 2, /* backbone read from the dense view written by sharq_prepare */
-    SHARQ_GEMM_SPARSE_MFMA = 3     /* backbone on the structured-sparse MFMA (see sharq_dual_gemm) */
+    SHARQ_GEMM_SPARSE_MFMA = 3     /* backbone on a structured-sparse MFMA (see sharq_dual_gemm) */
 } sharq_gemm_variant;
 
 /*
@@ -291,12 +291,17 @@ sharq_status sharq_dual_gemm_silu_prepare(sharq_format fmt, const sharq_fp4_view
  * Variants: DECOMPRESS reads the 2:4 backbone (codes + meta) and expands it
  * to dense codes inside the GEMM; DENSE_EXPANDED reads sparse->dense_codes
  * instead; AUTO is, for MXFP4, DENSE_EXPANDED when sparse->dense_codes is
- * non-NULL, else DECOMPRESS, and for NVFP4 SPARSE_MFMA.  SPARSE_MFMA (NVFP4
- * only) feeds the 2:4 backbone codes and
- * indices to the structured-sparse fp16 MFMA; gfx950 has no
- * structured-sparse MFMA for FP4 operands, so it returns
- * SHARQ_ERR_UNSUPPORTED for MXFP4.  The 2:4 indices must be as
- * sharq_prepare writes them (the two kept positions of a group distinct).
+ * non-NULL, else DECOMPRESS, and for NVFP4 SPARSE_MFMA.  SPARSE_MFMA feeds
+ * the 2:4 backbone codes and indices to a structured-sparse MFMA: for NVFP4
+ * the fp16 one; for MXFP4, since gfx950 has no structured-sparse MFMA for FP4
+ * operands, the FP8 one, after rebasing each backbone row and each weight
+ * row (its w_sparse_view scales) to one power of two per row, which is exact
+ * in E4M3 when the row's block scales span at most 12 binades; a 128 x 128
+ * output tile with a row spanning more runs its backbone expanded to dense
+ * FP4 instead.  The backbone product is then summed in its own fp32
+ * accumulator and scaled by the two rows' powers of two.  The 2:4 indices
+ * must be as sharq_prepare writes them (the two kept positions of a group
+ * distinct).
  * NVFP4 runs on fp16 MFMAs (2:4 and dense): each operand element
  * q * e4m3 scale is exact in fp16.
  * Requirements: m, n >= 1; k >= 128, k % 128 == 0; ld_y >= n; y 4-byte
@@ -369,7 +374,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 8
+#define SHARQ_ABI_VERSION 9
 
 #ifdef __cplusplus
 }

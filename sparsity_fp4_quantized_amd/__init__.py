@@ -42,7 +42,7 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_prepare_silu_mul",
            "sharq_dual_gemm", "sharq_dual_gemm_silu_prepare", "sharq_grouped_dual_gemm",
            "sharq_grouped_dual_gemm_silu_prepare", "sharq_bytes", "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class SharqError(RuntimeError):

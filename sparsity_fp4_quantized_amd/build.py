@@ -30,15 +30,18 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
-# source -> extra flags.  The NVFP4 GEMM keeps its MFMA accumulators in VGPRs:
-# its 2:4 MFMA (v_smfmac) accumulates in VGPRs only, so accumulators in AGPRs
-# were copied between the two register files around every sparse MFMA, and
-# the dense kernels fit two wavefronts per SIMD only without AGPRs.
+# source -> extra flags.  The NVFP4 GEMM and the MXFP4 GEMM on the FP8 sparse
+# MFMA keep their MFMA accumulators in VGPRs: the 2:4 MFMA (v_smfmac)
+# accumulates in VGPRs only, so accumulators in AGPRs were copied between the
+# two register files around every sparse MFMA, and the NVFP4 dense kernels fit
+# two wavefronts per SIMD only without AGPRs.
 SOURCES = {
     "sharq_abi.cpp": [],
     "prep.hip": [],
     "gemm_mx.hip": [],
     "gemm_nv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the MXFP4 backbone on the 2:4 FP8 MFMA (v_smfmac, VGPR accumulators)
+    "gemm_mx_fp8sp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 YARDSTICK_SOURCES = {"yardstick.hip": []}
 

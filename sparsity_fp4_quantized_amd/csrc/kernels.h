@@ -76,6 +76,9 @@ hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s);
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s);
+// the 2:4 backbone (codes + meta) on the structured-sparse FP8 MFMA, rebased
+// per tile; tiles that cannot be rebased exactly expand it to dense FP4
+hipError_t launch_dual_gemm_mx_fp8sp(const GemmArgs &a, hipStream_t s);
 hipError_t launch_grouped_dual_gemm_mx(const GemmArgs &a, hipStream_t s);
 // gate+up dual GEMM (a.n = 2 i: i gate rows, then i up rows of W; i % 128 == 0)
 // with x = bf16(silu(gate) * up) prepared into p's outputs ([a.m, i], no norm)

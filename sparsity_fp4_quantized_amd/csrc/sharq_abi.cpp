@@ -332,7 +332,6 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
   if (!wsv->codes || !wdv->codes) return SHARQ_ERR_NULL;
   if (wsv->codes != wdv->codes || wsv->ld_codes != wdv->ld_codes || wsv->layout != wdv->layout)
     return SHARQ_ERR_SHAPE;
-  if (fmt == SHARQ_MXFP4 && variant == SHARQ_GEMM_SPARSE_MFMA) return SHARQ_ERR_UNSUPPORTED;
   // AUTO: NVFP4 runs the 2:4 backbone on the structured-sparse MFMA (its
   // fastest variant); MXFP4 reads the dense backbone view when the caller has
   // one (no expansion work in the GEMM), else the 2:4 form
@@ -362,6 +361,7 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
              sp->tensor_scale, wsv->tensor_scale, y, ld_y, m, n, k,
              ksm(sp), ksm(rs), ksm(wsv)};
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fmt == SHARQ_MXFP4 && variant == SHARQ_GEMM_SPARSE_MFMA) return from_hip(sharq::launch_dual_gemm_mx_fp8sp(a, s));
   if (fmt == SHARQ_MXFP4) return from_hip(sharq::launch_dual_gemm_mx(a, dense_expanded, s));
   const int v = variant == SHARQ_GEMM_SPARSE_MFMA ? 3 : dense_expanded ? 2 : 1;
   return from_hip(sharq::launch_dual_gemm_nv(a, v, s));

@@ -26,6 +26,7 @@ hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t) { return count(a.x 
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t) { return count(a.w && a.codes && a.scales); }
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t) { return count(a.w && a.tensor_scale); }
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool, hipStream_t) { return count(a.y && a.k % 128 == 0); }
+hipError_t launch_dual_gemm_mx_fp8sp(const GemmArgs &a, hipStream_t) { return count(a.y && a.s_codes && a.meta); }
 hipError_t launch_grouped_dual_gemm_mx(const GemmArgs &a, hipStream_t) { return count(a.group_off && a.groups > 0); }
 hipError_t launch_dual_gemm_silu_prep_mx(const GemmArgs &a, const PrepArgs &p, hipStream_t) {
   return count(a.n % 2 == 0 && p.s_codes);

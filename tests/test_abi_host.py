@@ -284,7 +284,7 @@ def gemm(fmt=0, m=16, n=256, k=256, y=FAKE, ld_y=256, variant=0, sp=None, rs=Non
     (dict(n=0), sq.ERR_SHAPE),
     (dict(ld_y=100), sq.ERR_SHAPE),
     (dict(wd=view(meta=None, codes=FAKE + 4096)), sq.ERR_SHAPE),   # two payloads
-    (dict(variant=sq.GEMM_SPARSE_MFMA), sq.ERR_UNSUPPORTED),
+    (dict(variant=sq.GEMM_SPARSE_MFMA, sp=view(ld_codes=64, meta=None)), sq.ERR_NULL),   # reads the 2:4 form
     (dict(variant=9), sq.ERR_UNSUPPORTED),
     (dict(variant=sq.GEMM_DENSE_EXPANDED), sq.ERR_NULL),
     (dict(rs=view(meta=None, scales=FAKE + 2)), sq.ERR_ALIGN),

@@ -585,6 +585,11 @@ def test_quantize_weight(fmt, n, k):
 
 
 # ------------------------------------------------------------ GEMM
+# MXFP4: the backbone's dense view, the 2:4 form expanded in LDS, and the 2:4
+# form rebased to FP8 on the structured-sparse FP8 MFMA
+MX_VARIANTS = (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED, sq.GEMM_SPARSE_MFMA)
+
+
 def _gemm_case(m, n, k, seed, fmt=sq.MXFP4, norm=True):
     x = si.activations("student_t4", m, k, max(1, k // 100), 50.0, seed=seed)
     w = si.weights(n, k, seed=seed + 1)
@@ -604,7 +609,7 @@ def test_dual_gemm_mx_vs_oracle(m, n, k):
     for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
         sp, rs = to_dev_prep(sq.MXFP4, p, layout)
         wq = to_dev_weight(sq.MXFP4, q, layout)
-        for variant in (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED):
+        for variant in MX_VARIANTS:
             y = host(sq.dual_gemm(sp, rs, wq, variant=variant))
             check_gemm(y, ref, yabs, k, f"test_dual_gemm_mx_vs_oracle {layout} {variant}")
 
@@ -627,8 +632,8 @@ def test_dual_gemm_mx_large_tile_configs(m, n, k):
     for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
         sp, rs = to_dev_prep(sq.MXFP4, p, layout)
         wq = to_dev_weight(sq.MXFP4, q, layout)
-        ys = [host(sq.dual_gemm(sp, rs, wq, variant=v)) for v in (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)]
-        for v, y in zip(("decompress", "dense"), ys):
+        ys = [host(sq.dual_gemm(sp, rs, wq, variant=v)) for v in MX_VARIANTS]
+        for v, y in zip(("decompress", "dense", "sparse_fp8"), ys):
             assert np.isfinite(y).all(), (layout, v)
             check_gemm(y[rows, cols], ref, yabs, k, f"test_dual_gemm_mx_large_tile_configs {layout} {v}")
 
@@ -667,11 +672,12 @@ def test_dual_gemm_exact_special_case():
     q = oracle.quantize_weight(sq.MXFP4, wb)
     ref, yabs = oracle.dual_gemm_bound(sq.MXFP4, p, q)
     assert (ref == (xv @ wv.T).astype(np.float32)).all()
-    sp, rs = sq.prepare(dev16(xb), None)
+    sp, rs = sq.prepare(dev16(xb), None, dense_backbone=True)
     wq = sq.quantize_weight(dev16(wb))
-    y = host(sq.dual_gemm(sp, rs, wq))
-    assert np.array_equal(y, ref)
-    check_gemm(y, ref, yabs, k, "test_dual_gemm_exact_special_case")
+    for variant in (sq.GEMM_AUTO, *MX_VARIANTS):
+        y = host(sq.dual_gemm(sp, rs, wq, variant=variant))
+        assert np.array_equal(y, ref), variant
+        check_gemm(y, ref, yabs, k, "test_dual_gemm_exact_special_case")
 
 
 def _check_end_to_end(w, samples):
@@ -684,10 +690,12 @@ def _check_end_to_end(w, samples):
     wq = sq.quantize_weight(dev16(W))
     y = host(sq.dual_gemm(sp, rs, wq))
     y2 = host(sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DECOMPRESS))
+    y3 = host(sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA))
     if samples is None:
         ref, yabs = oracle.dual_gemm_bound(sq.MXFP4, p, q)
         check_gemm(y2, ref, yabs, w.k, "end_to_end decompress")
         check_gemm(y, ref, yabs, w.k, "end_to_end dense")
+        check_gemm(y3, ref, yabs, w.k, "end_to_end sparse_fp8")
         return
     rng = np.random.default_rng(0)
     rows = np.sort(rng.integers(0, w.m, samples))
@@ -700,6 +708,7 @@ def _check_end_to_end(w, samples):
     # normwise: normalized by the largest |Y| over the sample (the full max is at least this)
     check_gemm(y[rows, cols], ref, yabs, w.k, "end_to_end dense")
     check_gemm(y2[rows, cols], ref, yabs, w.k, "end_to_end decompress")
+    check_gemm(y3[rows, cols], ref, yabs, w.k, "end_to_end sparse_fp8")
 
 
 @pytest.mark.parametrize("name,samples", [("tiny", None), ("qkv_prefill", 4096),
@@ -738,7 +747,7 @@ def test_dual_gemm_padded_leading_dims(fmt, m, n, k):
     operand; the GEMM must read only the described bytes."""
     x, w, g, p, q = _gemm_case(m, n, k, seed=m + n, fmt=fmt)
     ref, yabs = oracle.dual_gemm_bound(fmt, p, q)
-    variants = NV_VARIANTS if fmt == sq.NVFP4 else (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)
+    variants = NV_VARIANTS if fmt == sq.NVFP4 else MX_VARIANTS
     for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR):
         sp, rs = to_dev_prep(fmt, p, layout)
         wq = to_dev_weight(fmt, q, layout)
@@ -815,7 +824,7 @@ def test_dual_gemm_random_shapes(fmt):
     """Seeded random shapes (m 1-299, n 1-399, k 128-512, both layouts, every
     variant): ragged tiles in every position, the decode / prefill switch at
     m = 32 and single-step K."""
-    variants = NV_VARIANTS if fmt == sq.NVFP4 else (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)
+    variants = NV_VARIANTS if fmt == sq.NVFP4 else MX_VARIANTS
     for i, (m, n, k) in enumerate(_random_shapes(11 + fmt, 10)):
         x, w, g, p, q = _gemm_case(m, n, k, seed=1000 + i, fmt=fmt, norm=bool(i % 2))
         ref, yabs = oracle.dual_gemm_bound(fmt, p, q)
@@ -867,7 +876,7 @@ def test_dual_gemm_path_specific_weight_views(fmt):
     ya, abs_a = oracle.dual_gemm_bound(fmt, _zeroed(p, "residual"), q)
     yb, abs_b = oracle.dual_gemm_bound(fmt, _zeroed(p, "backbone"), q2)
     ref, yabs = ya.astype(np.float64) + yb, abs_a + abs_b
-    variants = NV_VARIANTS if fmt == sq.NVFP4 else (sq.GEMM_DECOMPRESS, sq.GEMM_DENSE_EXPANDED)
+    variants = NV_VARIANTS if fmt == sq.NVFP4 else MX_VARIANTS
     for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
         sp, rs = to_dev_prep(fmt, p, layout)
         wq = to_dev_weight(fmt, q, layout)
@@ -905,10 +914,44 @@ def test_end_to_end_nv_workloads(name, samples):
         check_gemm(y[rows, cols], ref, yabs, w.k, f"test_end_to_end_nv_workloads {v}")
 
 
-def test_sparse_mfma_unsupported_for_mxfp4():
-    x, w, g, p, q = _gemm_case(16, 128, 128, seed=9)
-    sp, rs = to_dev_prep(sq.MXFP4, p)
-    wq = to_dev_weight(sq.MXFP4, q)
-    with pytest.raises(sq.SharqError) as e:
-        sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA)
-    assert e.value.status == sq.ERR_UNSUPPORTED
+def _blocks_at(v, exps):
+    """v [rows, k] with each 32-block rescaled so that its largest magnitude is
+    5 * 2^e (e from exps [rows, k / 32]): its MX scale exponent is then e."""
+    rows, k = v.shape
+    b = v.reshape(rows, k // 32, 32).astype(np.float64)
+    b = b / np.abs(b).max(axis=2, keepdims=True) * 5.0 * 2.0 ** exps[..., None]
+    return b.reshape(rows, k).astype(np.float32)
+
+
+@pytest.mark.parametrize("layout", [sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR])
+def test_dual_gemm_mx_sparse_fp8_rebasing_and_fallback(layout):
+    """SPARSE_MFMA for MXFP4: tiles whose A rows and W rows each span at most
+    12 block exponents run the backbone rebased to FP8 on the 2:4 FP8 MFMA
+    (here spans of exactly 12, so the lowest blocks sit 7 below the reference
+    and their FP8 values are subnormal); a tile with an A row or a W row
+    spanning more falls back to the expanded FP4 backbone.  Tiles of 128:
+    A row 5 spans 16 (tile row 0 falls back), rows 128-299 span 12; W row 200
+    spans 22 (tile column 1 falls back), the other rows 12."""
+    m, n, k = 300, 400, 512
+    rng = np.random.default_rng(12)
+    ex = np.zeros((m, k // 32), np.int64)
+    ex[128:, 3], ex[128:, 9] = 6, -6
+    ex[5, 2] = 16
+    x = _blocks_at(rng.standard_normal((m, k)), ex)
+    ew = np.full((n, k // 32), -6, np.int64)
+    ew[:, 1], ew[:, 14] = 0, -12
+    ew[200, 7] = 10
+    w = _blocks_at(rng.standard_normal((n, k)), ew)
+    xb, wb = si.f32_to_bf16_bits(x), si.f32_to_bf16_bits(w)
+    p = oracle.prepare(sq.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    span = lambda sc: sc.max(axis=1).astype(int) - sc.min(axis=1).astype(int)
+    assert span(p["s_scales"])[5] == 16 and (span(p["s_scales"])[128:] == 12).all()
+    assert span(q["scales"])[200] == 22 and (span(q["scales"])[np.arange(n) != 200] == 12).all()
+    ref, yabs = oracle.dual_gemm_bound(sq.MXFP4, p, q)
+    sp, rs = to_dev_prep(sq.MXFP4, p, layout)
+    wq = to_dev_weight(sq.MXFP4, q, layout)
+    y = host(sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA))
+    check_gemm(y, ref, yabs, k, f"test_dual_gemm_mx_sparse_fp8 {layout}")
+    # repeatable bit for bit
+    assert np.array_equal(host(sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_SPARSE_MFMA)), y)

@@ -1,12 +1,13 @@
 """The structured-sparse gate (row a8): which sparse MFMA forms gfx950 has.
 
-The MXFP4 backbone could use a 2:4 sparse MFMA only if gfx950 had one for FP4
-operands.  The ROCm assembler and compiler for gfx950 decide it: the block-
-scaled FP4 MFMA and the fp16 2:4 SMFMAC exist (the kernels use both); no
-SMFMAC form takes FP4 / f8f6f4 operands, and clang has no builtin for one.  So
-the MXFP4 GEMM runs its backbone on the dense FP4 MFMA, and SPARSE_MFMA is
-refused for MXFP4 (checked host-side in test_abi_host.py and on the GPU in
-test_gpu_parity.py).  Host-only: nothing here runs on a GPU."""
+The MXFP4 backbone could use a 2:4 sparse MFMA on its own operand type only
+if gfx950 had one for FP4 operands.  The ROCm assembler and compiler for
+gfx950 decide it: the block-scaled FP4 MFMA and the fp16 and FP8 2:4 SMFMACs
+exist (the kernels use all three); no SMFMAC form takes FP4 / f8f6f4
+operands, and clang has no builtin for one.  So the MXFP4 GEMM runs its
+backbone on the dense FP4 MFMA by default, and its SPARSE_MFMA variant
+converts the backbone to FP8 (exact after a per-row power-of-two rebasing)
+for the FP8 SMFMAC.  Host-only: nothing here runs on a GPU."""
 import os
 import subprocess
 
@@ -21,6 +22,9 @@ ACCEPTED = [
     "v_mfma_scale_f32_16x16x128_f8f6f4 a[0:3], v[0:3], v[4:7], a[0:3], v8, v9 op_sel_hi:[0,0,0] cbsz:4 blgp:4",
     # the NV GEMM's 2:4 sparse MFMA on fp16 operands
     "v_smfmac_f32_32x32x32_f16 v[0:15], v[16:19], v[20:27], v28",
+    # the MX GEMM's SPARSE_MFMA variant: the backbone rebased to FP8 on the FP8 2:4 MFMA
+    "v_smfmac_f32_32x32x64_fp8_fp8 v[0:15], v[16:19], v[20:27], v28",
+    "v_smfmac_f32_16x16x128_fp8_fp8 v[0:3], v[4:7], v[8:15], v16",
     "v_smfmac_f32_16x16x64_f16 v[0:3], v[4:7], v[8:15], v16",
 ]
 
