@@ -627,6 +627,8 @@ def main():
     ap.add_argument("--no-dense-view", action="store_true",
                     help="prepare writes only the 2:4 backbone; the GEMM expands it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="time only the CPU oracle on the workload (no GPU work) and print its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help=f"run one {COPY_BYTES >> 20} MiB device copy first (counter calibration)")
     ap.add_argument("--no-yardsticks", action="store_true",
@@ -640,6 +642,12 @@ def main():
     args = ap.parse_args()
     if args.traffic_from:
         traffic_convert(args, si.WORKLOADS[args.workload])
+        return
+    if args.cpu_baseline_only:
+        w = si.WORKLOADS[args.workload]
+        out = {"workload": w.name, "cpu_baseline": cpu_baseline(w, si.workload_x(w), si.workload_w(w),
+                                                               si.workload_gamma(w))}
+        print(json.dumps(out), flush=True)
         return
 
     if args.moe and args.gpus == 1:
