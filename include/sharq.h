@@ -26,7 +26,8 @@
  *     [n, k] bf16, Y = X * W^T is [m, n] fp32.  bf16 values are passed as
  *     their uint16 bit patterns.
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library
- *     allocates nothing, keeps no state between calls and never synchronizes.
+ *     allocates nothing, keeps no state between calls and never synchronizes
+ *     (sharq_prepare_noalloc alone keeps a 256-byte static workspace per GPU).
  *     Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and is complete when the stream is.
  *   - Leading dimensions (`ld_*`) are in elements of the array they describe
@@ -197,6 +198,28 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
                            int64_t ld_x, const uint16_t *gamma_bf16, float eps,
                            const sharq_fp4_view *sparse_out, const sharq_fp4_view *resid_out,
                            void *stream);
+
+/*
+ * sharq_prepare for callers that cannot allocate, or whose calls must not
+ * write beyond their outputs: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same operation, arguments, outputs
+ * and requirements as sharq_prepare, with one difference: for NVFP4 the
+ * tensor amax is reduced in a workspace the library holds in a file-scope
+ * static device array (256 bytes on each GPU the library runs on, held until
+ * the process ends) instead of in sparse_out->tensor_scale[1], so the caller's
+ * tensor_scale needs one float ([0] receives s_t; [1] is not touched).  The
+ * workspace holds one value whatever the shapes, so no size is refused for
+ * it.  Nothing is allocated: no hipMalloc, hipFree or allocating library
+ * call; the first call on a device takes the workspace's address there
+ * (hipGetSymbolAddress) and keeps it.  Each call clears the workspace with a
+ * kernel before using it.  Every call on one GPU shares the workspace, so
+ * calls that overlap on one GPU (on different streams) race.  MXFP4 uses no
+ * workspace: the call is exactly sharq_prepare's.
+ */
+sharq_status sharq_prepare_noalloc(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
+                                   int64_t ld_x, const uint16_t *gamma_bf16, float eps,
+                                   const sharq_fp4_view *sparse_out,
+                                   const sharq_fp4_view *resid_out, void *stream);
 
 /*
  * The preparation operator with the residual add in front of its norm fused
@@ -374,7 +397,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 9
+#define SHARQ_ABI_VERSION 10
 
 #ifdef __cplusplus
 }

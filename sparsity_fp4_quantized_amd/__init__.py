@@ -41,8 +41,9 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 # every symbol include/sharq.h declares
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_prepare_silu_mul",
            "sharq_dual_gemm", "sharq_dual_gemm_silu_prepare", "sharq_grouped_dual_gemm",
-           "sharq_grouped_dual_gemm_silu_prepare", "sharq_bytes", "sharq_status_str", "sharq_abi_version")
-ABI_VERSION = 9
+           "sharq_grouped_dual_gemm_silu_prepare", "sharq_bytes", "sharq_status_str", "sharq_abi_version",
+           "sharq_prepare_noalloc")
+ABI_VERSION = 10
 
 
 class SharqError(RuntimeError):
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.sharq_quantize_weight.restype = ctypes.c_int
         L.sharq_prepare.argtypes = [ctypes.c_int, P, I64, I64, I64, P, ctypes.c_float, V, V, P]
         L.sharq_prepare.restype = ctypes.c_int
+        L.sharq_prepare_noalloc.argtypes = [ctypes.c_int, P, I64, I64, I64, P, ctypes.c_float, V, V, P]
+        L.sharq_prepare_noalloc.restype = ctypes.c_int
         L.sharq_prepare_residual.argtypes = [ctypes.c_int, P, I64, P, I64, P, I64, I64, I64, P,
                                              ctypes.c_float, V, V, P]
         L.sharq_prepare_residual.restype = ctypes.c_int
@@ -326,8 +329,9 @@ class BoundCall:
             raise SharqError(status, self._where)
 
 
-def bind_prepare(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None) -> BoundCall:
-    """sharq_prepare into caller-provided buffers, bound for repeated calls."""
+def bind_prepare(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None, noalloc: bool = False) -> BoundCall:
+    """sharq_prepare (or, noalloc, sharq_prepare_noalloc) into caller-provided
+    buffers, bound for repeated calls."""
     x = _bits16(x)
     m, k = x.shape
     g = None if gamma is None else _vec(_bits16(gamma), k, "gamma")
@@ -335,7 +339,8 @@ def bind_prepare(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None) -> Bo
     args = (ctypes.c_int(sp.fmt), ctypes.c_void_p(x.data_ptr()), ctypes.c_int64(m), ctypes.c_int64(k),
             ctypes.c_int64(_ld(x)), ctypes.c_void_p(_ptr(g)), ctypes.c_float(float(eps)),
             ctypes.byref(vs), ctypes.byref(vr), _stream_ptr(stream))
-    return BoundCall(lib().sharq_prepare, args, "sharq_prepare", (x, g, sp, rs, vs, vr))
+    fn, where = (lib().sharq_prepare_noalloc, "sharq_prepare_noalloc") if noalloc else (lib().sharq_prepare, "sharq_prepare")
+    return BoundCall(fn, args, where, (x, g, sp, rs, vs, vr))
 
 
 def prepare_into(x, gamma, eps, sp: FP4Tensor, rs: FP4Tensor, stream=None):

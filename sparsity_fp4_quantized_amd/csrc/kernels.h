@@ -18,7 +18,7 @@ struct PrepArgs {
   uint8_t *r_codes;  int64_t ld_rc;
   uint8_t *r_scales; int64_t ld_rs;
   uint8_t *s_dense;  int64_t ld_sd;   // optional
-  float *tensor_scale;                // NVFP4: [0] scale, [1] amax
+  float *tensor_scale;                // NVFP4: [0] receives the tensor scale
   int s_ksm, r_ksm;                   // backbone / residual view k-step-major (every array)
   // residual add in front of the norm (MXFP4 with normalization only):
   // x = bf16(x + add), written to x_out, then prepared; add == nullptr: none
@@ -28,6 +28,9 @@ struct PrepArgs {
   // and up [m, k] replace x
   const float *gate = nullptr;    int64_t ld_gate = 0;
   const float *up = nullptr;      int64_t ld_up = 0;
+  // NVFP4: where the tensor amax passes reduce (tensor_scale + 1, or the
+  // allocation-free entry point's static workspace)
+  float *amax = nullptr;
 };
 
 struct QuantArgs {
@@ -73,6 +76,9 @@ __host__ __device__ inline int64_t arr_off(int64_t r, int64_t t, int64_t ld, int
 hipError_t launch_prepare_mx(const PrepArgs &a, hipStream_t s);
 hipError_t launch_prepare_silu_mx(const PrepArgs &a, hipStream_t s);
 hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s);
+// sharq_prepare_noalloc's launches: a.amax is set to this device's static
+// workspace (its address taken once per device); MXFP4 uses no workspace
+hipError_t launch_prepare_noalloc(PrepArgs a, int fmt, hipStream_t s);
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s);
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s);
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool dense_expanded, hipStream_t s);

@@ -26,6 +26,8 @@
 // and v_cvt_scalef32_pk_f32_fp4 (exact dequantization).  The NVFP4-style path
 // divides by its non-power-of-two scale in IEEE fp32 first and converts at
 // scale 1.
+#include <mutex>
+
 #include "fp4_device.h"
 #include "kernels.h"
 #include "prep_block.h"
@@ -235,8 +237,9 @@ __device__ __forceinline__ void quantize_block_nv(const float xf[32], float s_t,
 
 // ---------------------------------------------------------------- stores
 
-__device__ __forceinline__ float nv_tensor_scale(const float *ts) {
-  float amax = ts[1];
+// s_t = fl32(amax / 2688) (1 when amax = 0), from the reduced tensor amax
+__device__ __forceinline__ float nv_tensor_scale(const float *amax_slot) {
+  float amax = *amax_slot;
   return amax == 0.0f ? 1.0f : amax / 2688.0f;
 }
 
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
   if (FMT == 0) {
     quantize_block_mx(xw, xf, o);
   } else {
-    const float s_t = nv_tensor_scale(a.tensor_scale);
+    const float s_t = nv_tensor_scale(a.amax);
     if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
     quantize_block_nv(xf, s_t, o);
   }
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chu
   if (FMT == 0) {
     quantize_block_mx(xw, xf, o);
   } else {
-    float s_t = nv_tensor_scale(a.tensor_scale);
+    float s_t = nv_tensor_scale(a.amax);
     if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
     quantize_block_nv(xf, s_t, o);
   }
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(256) void prep_silu_kernel(PrepArgs a, uint32_t chu
 // NVFP4 tensor amax of x_n.  fp32 bit patterns of non-negative values order
 // like unsigned integers; each workgroup reduces its share (grid-stride) and
 // issues at most one atomic max, so that few atomics meet at the one address.
-__device__ __forceinline__ void block_amax_atomic(uint32_t am, float *ts) {
+__device__ __forceinline__ void block_amax_atomic(uint32_t am, float *slot) {
   __shared__ uint32_t wmax[8];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off, 64));
@@ -449,7 +452,7 @@ __device__ __forceinline__ void block_amax_atomic(uint32_t am, float *ts) {
     uint32_t m = 0;
     for (int i = 0; i < nw; ++i) m = max(m, wmax[i]);
     // the value only grows: skip the atomic when memory already holds >= m
-    unsigned int *p = reinterpret_cast<unsigned int *>(ts + 1);
+    unsigned int *p = reinterpret_cast<unsigned int *>(slot);
     if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
   }
 }
@@ -483,11 +486,11 @@ __global__ __launch_bounds__(512) void amax_norm_kernel(PrepArgs a) {
     }
     __syncthreads();   // the row reduction's LDS is reused by the next row group
   }
-  block_amax_atomic(am, a.tensor_scale);
+  block_amax_atomic(am, a.amax);
 }
 
 __global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *x, int64_t ld, int64_t m,
-                                                        int64_t k, float *ts) {
+                                                        int64_t k, float *slot) {
   const int64_t nblk = k / 32, total = m * nblk;
   uint32_t am = 0;
   for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total;
@@ -498,10 +501,10 @@ __global__ __launch_bounds__(256) void amax_flat_kernel(const uint16_t *x, int64
 #pragma unroll
     for (int i = 0; i < 16; ++i) am = max(am, max(xw[i] & 0x7FFFu, (xw[i] >> 16) & 0x7FFFu));
   }
-  block_amax_atomic(am << 16, ts);
+  block_amax_atomic(am << 16, slot);
 }
 
-__global__ void zero_amax_kernel(float *ts) { ts[1] = 0.0f; }
+__global__ void zero_amax_kernel(float *slot) { *slot = 0.0f; }
 
 template <int FMT, int R, int W, bool ADD>
 void launch_norm(const PrepArgs &a, hipStream_t s) {
@@ -541,7 +544,7 @@ template <int FMT>
 hipError_t launch_prepare(const PrepArgs &a, hipStream_t s) {
   const int64_t nblk = a.k / 32;
   const bool ksm = a.s_ksm != 0;
-  if (FMT == 1) zero_amax_kernel<<<1, 1, 0, s>>>(a.tensor_scale);
+  if (FMT == 1) zero_amax_kernel<<<1, 1, 0, s>>>(a.amax);
   if (a.gamma) {
     if (FMT == 1) {
       switch ((nblk + 63) / 64) {   // wavefronts per row of the pre-pass
@@ -570,7 +573,7 @@ hipError_t launch_prepare(const PrepArgs &a, hipStream_t s) {
     if (FMT == 1) {
       const int64_t total = a.m * nblk;
       const dim3 flat_grid((unsigned)((total + 255) / 256));
-      amax_flat_kernel<<<dim3(min(flat_grid.x, kAmaxGrid)), 256, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.tensor_scale);
+      amax_flat_kernel<<<dim3(min(flat_grid.x, kAmaxGrid)), 256, 0, s>>>(a.x, a.ld_x, a.m, a.k, a.amax);
     }
     if (ksm) {
       const uint32_t chunks = (uint32_t)((nblk + 3) / 4);
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(QuantArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) q[j] = w4[j];
   } else {
-    float s_t = nv_tensor_scale(a.tensor_scale);
+    float s_t = nv_tensor_scale(a.tensor_scale + 1);
     if (gid == 0) a.tensor_scale[0] = s_t;
     uint32_t a0 = 0, a1 = 0;
 #pragma unroll
@@ -646,8 +649,8 @@ hipError_t launch_quant(const QuantArgs &a, hipStream_t s) {
   const int64_t total = a.n * (a.k / 32);
   dim3 grid((unsigned)((total + 255) / 256)), block(256);
   if (FMT == 1) {
-    zero_amax_kernel<<<1, 1, 0, s>>>(a.tensor_scale);
-    amax_flat_kernel<<<dim3(min(grid.x, kAmaxGrid)), block, 0, s>>>(a.w, a.ld_w, a.n, a.k, a.tensor_scale);
+    zero_amax_kernel<<<1, 1, 0, s>>>(a.tensor_scale + 1);
+    amax_flat_kernel<<<dim3(min(grid.x, kAmaxGrid)), block, 0, s>>>(a.w, a.ld_w, a.n, a.k, a.tensor_scale + 1);
   }
   quant_weight_kernel<FMT><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
@@ -671,6 +674,45 @@ hipError_t launch_prepare_silu_mx(const PrepArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t s) { return launch_prepare<1>(a, s); }
+
+// ---------------------------------------------------------------- allocation-free entry point
+
+// The workspace of sharq_prepare_noalloc: the NVFP4 tensor amax is reduced
+// here instead of in the caller's tensor_scale[1].  Each GPU holds its own
+// copy until the process ends; the host takes its address once per device
+// (hipGetSymbolAddress with the device current) and passes that address to
+// the kernels.  Every call on a GPU shares it (calls that overlap on one GPU
+// race); each call clears it with a kernel before the amax passes.
+constexpr int kNoallocScratchFloats = 64;   // 256 bytes; one float is used
+static __device__ __align__(256) float scratch[kNoallocScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t launch_prepare_noalloc(PrepArgs a, int fmt, hipStream_t s) {
+  if (fmt == 0) return launch_prepare<0>(a, s);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float *ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      e = hipGetSymbolAddress(reinterpret_cast<void **>(&g_scratch_ptr[dev]), HIP_SYMBOL(scratch));
+      if (e != hipSuccess) {
+        g_scratch_ptr[dev] = nullptr;
+        return e;
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  a.amax = ptr;
+  return launch_prepare<1>(a, s);
+}
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t s) { return launch_quant<0>(a, s); }
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t s) { return launch_quant<1>(a, s); }
 

@@ -161,7 +161,7 @@ sharq_status prepare_common(sharq_format fmt, const uint16_t *x_bf16, int64_t m,
                             int64_t ld_x, const uint16_t *gamma_bf16, float eps,
                             const sharq_fp4_view *sp, const sharq_fp4_view *rs,
                             const uint16_t *add, int64_t ld_add, uint16_t *x_out, int64_t ld_out,
-                            void *stream) {
+                            void *stream, bool noalloc = false) {
   if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
   if (!x_bf16 || !sp || !rs) return SHARQ_ERR_NULL;
   if (m < 1 || k < 32 || k % 32 || ld_x < k) return SHARQ_ERR_SHAPE;
@@ -183,6 +183,8 @@ sharq_status prepare_common(sharq_format fmt, const uint16_t *x_bf16, int64_t m,
   a.x_out = x_out;
   a.ld_xout = ld_out;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (noalloc) return from_hip(sharq::launch_prepare_noalloc(a, fmt == SHARQ_MXFP4 ? 0 : 1, s));
+  a.amax = fmt == SHARQ_NVFP4 ? sp->tensor_scale + 1 : nullptr;
   return from_hip(fmt == SHARQ_MXFP4 ? sharq::launch_prepare_mx(a, s)
                                      : sharq::launch_prepare_nv(a, s));
 }
@@ -194,6 +196,13 @@ sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, 
                            const sharq_fp4_view *sp, const sharq_fp4_view *rs, void *stream) {
   return prepare_common(fmt, x_bf16, m, k, ld_x, gamma_bf16, eps, sp, rs, nullptr, 0, nullptr, 0,
                         stream);
+}
+
+sharq_status sharq_prepare_noalloc(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
+                                   int64_t ld_x, const uint16_t *gamma_bf16, float eps,
+                                   const sharq_fp4_view *sp, const sharq_fp4_view *rs, void *stream) {
+  return prepare_common(fmt, x_bf16, m, k, ld_x, gamma_bf16, eps, sp, rs, nullptr, 0, nullptr, 0,
+                        stream, true);
 }
 
 sharq_status sharq_prepare_residual(sharq_format fmt, const uint16_t *h_bf16, int64_t ld_h,

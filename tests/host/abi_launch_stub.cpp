@@ -22,7 +22,10 @@ static hipError_t count(bool ok) {
 
 hipError_t launch_prepare_mx(const PrepArgs &a, hipStream_t) { return count(a.x && a.m > 0 && a.k % 32 == 0); }
 hipError_t launch_prepare_silu_mx(const PrepArgs &a, hipStream_t) { return count(a.gate && a.up && a.m > 0); }
-hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t) { return count(a.x && a.tensor_scale && a.k % 16 == 0); }
+hipError_t launch_prepare_nv(const PrepArgs &a, hipStream_t) {
+  return count(a.x && a.tensor_scale && a.amax == a.tensor_scale + 1 && a.k % 16 == 0);
+}
+hipError_t launch_prepare_noalloc(PrepArgs a, int fmt, hipStream_t) { return count(a.x && (fmt == 0 || a.tensor_scale)); }
 hipError_t launch_quantize_weight_mx(const QuantArgs &a, hipStream_t) { return count(a.w && a.codes && a.scales); }
 hipError_t launch_quantize_weight_nv(const QuantArgs &a, hipStream_t) { return count(a.w && a.tensor_scale); }
 hipError_t launch_dual_gemm_mx(const GemmArgs &a, bool, hipStream_t) { return count(a.y && a.k % 128 == 0); }
