@@ -31,6 +31,8 @@ struct PrepArgs {
   // NVFP4: where the tensor amax passes reduce (tensor_scale + 1, or the
   // allocation-free entry point's static workspace)
   float *amax = nullptr;
+  // fl32(1 / k), set by the preparation's launcher for the row mean
+  float inv_k = 0.0f;
 };
 
 struct QuantArgs {

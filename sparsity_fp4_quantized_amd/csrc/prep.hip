@@ -27,6 +27,7 @@
 // divides by its non-power-of-two scale in IEEE fp32 first and converts at
 // scale 1.
 #include <mutex>
+#include <type_traits>
 
 #include "fp4_device.h"
 #include "kernels.h"
@@ -292,6 +293,23 @@ __device__ __forceinline__ void normalize32(float xf[32], uint32_t xw[16], const
   normalize32(xf, xw, gf, r);
 }
 
+// base + uniform + lane bytes: the uniform part stays in scalar registers and
+// the access takes a 32-bit vector offset
+template <class T>
+__device__ __forceinline__ T *at_bytes(T *base, int64_t uniform_bytes, uint32_t lane_bytes) {
+  using B = typename std::conditional<std::is_const<T>::value, const uint8_t, uint8_t>::type;
+  return reinterpret_cast<T *>(reinterpret_cast<B *>(base) + uniform_bytes + lane_bytes);
+}
+
+// fl32(ss / k): Markstein's correction with the host's fl32(1 / k) where no
+// step can leave the normal range (ss = 0 or ss in [2^-100, 2^100]), an IEEE
+// division otherwise (zero rows aside, practically never)
+__device__ __forceinline__ float row_mean(float ss, const PrepArgs &a) {
+  const float kf = (float)a.k;
+  if (ss == 0.0f || (ss >= 0x1p-100f && ss <= 0x1p100f)) return div_rn(ss, kf, a.inv_k);
+  return ss / kf;
+}
+
 // ---------------------------------------------------------------- kernels
 
 // A lane's 32 bf16 values as four 16-byte stores.  Plain stores: each one
@@ -304,58 +322,73 @@ __device__ __forceinline__ void store32(uint16_t *p, const uint32_t w[16]) {
   for (int i = 0; i < 4; ++i) q[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
 }
 
-// Workgroup = R rows x W wavefronts: lane l of wavefront w takes row q = l / L
-// (L = 64 / R lanes per row) and block w * L + l % L, so a wavefront stores R
-// consecutive rows of each 128-k step next to each other in the k-step-major
-// layout (R = 1 keeps a row's blocks contiguous for the row-major layout).
+// Workgroup = R rows x W wavefronts: lane l of wavefront w takes row rl =
+// l / L (L = 64 / R lanes per row) and block b = w L + l % L, so a wavefront
+// stores R consecutive rows of each 128-k step next to each other in the
+// k-step-major layout (R = 1 keeps a row's blocks contiguous for the
+// row-major layout).
 // The row's sum of squares is the oracle's perfect binary tree: the lane's 32
 // values, then adjacent lanes of the row (butterfly over L lanes), then the W
 // wavefronts in LDS (padded to a power of two with zeros).  Lanes past the row
 // end (or past the last row) load a valid block of X and contribute +0; they
 // store nothing.  ADD: the residual add in front of the norm, x = bf16(x +
 // add) (the binary32 sum rounded to nearest even), stored to x_out as the new
-// residual stream and prepared in place of X; x_out may be X itself or
-// `add`, since every lane reads its block before it writes it.
-template <int FMT, int R, int W, bool ADD = false>
+// residual stream and prepared in place of X; x_out may be X itself or `add`,
+// since every lane reads its block before it writes it.
+// Addresses: wavefront-uniform 64-bit bases plus 32-bit lane offsets (the
+// host bounds the row strides of the bf16 arrays below 2^28 elements and every
+// output array below 4 GiB); on the qkv shape this, the median-of-three in the
+// mask and the row mean without an IEEE division took the VALU instructions
+// per wavefront from 723 to 666 (SQ_INSTS_VALU) and the kernel time down by
+// about 5%.  (Two row groups per workgroup, the second group's loads issued
+// during the first group's quantization, ran at two wavefronts per SIMD and
+// was 4% slower than this; two blocks of one row per lane, 13% slower.)
+template <int FMT, int R, int W, bool ADD>
 __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
   constexpr int L = 64 / R;
   __shared__ float part[R][W];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int q = lane / L;
-  const int64_t row = (int64_t)blockIdx.x * R + q;
+  const uint32_t rl = (uint32_t)lane / L, lb = (uint32_t)lane % L;
+  const int64_t rs = (int64_t)blockIdx.x * R;    // the group's first row (< m)
+  const bool row_ok = rs + rl < a.m;
   const int64_t nblk = a.k / 32;
-  const int64_t b = (int64_t)wave * L + lane % L;
-  const bool has = row < a.m && b < nblk;
-  const int64_t lrow = row < a.m ? row : 0, lb = b < nblk ? b : 0;
-  // gamma's loads go out with X's, so that they land during the row
-  // reduction rather than after it (-4% on the qkv shape)
-  uint32_t xw[16], gw[16], ow[16];
+  const int64_t b0 = (int64_t)wave * L;          // the wavefront's first block (uniform)
+  const int64_t b = b0 + lb;
+  const bool has = row_ok && b < nblk;
+  // bf16 arrays: byte offset 2 ld row + 64 b; lanes past the row end read
+  // block 0, rows past the last one the group's first row
+  const uint32_t vb = b < nblk ? 64u * (uint32_t)b : 0u;
+  const uint32_t rlx = row_ok ? rl : 0u;
+  uint32_t xw[16], gw[16];
   float xf[32];
-  load32(a.x + lrow * a.ld_x + 32 * lb, xw);
-  if (ADD) load32(a.add + lrow * a.ld_add + 32 * lb, ow);
-  load32(a.gamma + 32 * lb, gw);
+  load32(at_bytes(a.x, 2 * rs * a.ld_x, rlx * (2u * (uint32_t)a.ld_x) + vb), xw);
+  // gamma's loads go out with X's, so that they land during the row
+  // reduction rather than after it
+  load32(at_bytes(a.gamma, 0, vb), gw);
   if (ADD) {
+    uint32_t ow[16];
+    load32(at_bytes(a.add, 2 * rs * a.ld_add, rlx * (2u * (uint32_t)a.ld_add) + vb), ow);
     float of[32];
     unpack32(xw, xf);
     unpack32(ow, of);
 #pragma unroll
     for (int i = 0; i < 16; ++i) xw[i] = pack_bf16x2(xf[2 * i] + of[2 * i], xf[2 * i + 1] + of[2 * i + 1]);
-    if (has) store32(a.x_out + row * a.ld_xout + 32 * b, xw);
+    if (has) store32(at_bytes(a.x_out, 2 * rs * a.ld_xout, rl * (2u * (uint32_t)a.ld_xout) + vb), xw);
   }
   unpack32(xw, xf);
-  float s = lane_tree_sum<L>(has ? block_sumsq(xf) : 0.0f);
-  if (lane % L == 0) part[q][wave] = s;
+  const float s = lane_tree_sum<L>(has ? block_sumsq(xf) : 0.0f);
+  if (lb == 0) part[rl][wave] = s;
   __syncthreads();
   float c[W];
 #pragma unroll
-  for (int i = 0; i < W; ++i) c[i] = part[q][i];
+  for (int i = 0; i < W; ++i) c[i] = part[rl][i];
 #pragma unroll
   for (int w = W / 2; w >= 1; w >>= 1) {
 #pragma unroll
     for (int i = 0; i < w; ++i) c[i] = c[2 * i] + c[2 * i + 1];
   }
-  const float r = 1.0f / __builtin_sqrtf(c[0] / (float)a.k + a.eps);
+  const float r = 1.0f / __builtin_sqrtf(row_mean(c[0], a) + a.eps);
   if (!has) return;
   {
     float gf[32];
@@ -367,10 +400,10 @@ __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
     quantize_block_mx(xw, xf, o);
   } else {
     const float s_t = nv_tensor_scale(a.amax);
-    if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
+    if (rs + rl == 0 && b == 0) a.tensor_scale[0] = s_t;
     quantize_block_nv(xf, s_t, o);
   }
-  store_block<FMT, (R >= 4)>(a, row, b, o);
+  store_block_at<FMT, (R >= 4)>(a, rs, b0 / 4, lane_offsets<FMT>(a, rl, lb >> 2, lb & 3), o);
 }
 
 // No normalization: blocks are independent.  A wavefront takes R rows x
@@ -541,7 +574,9 @@ void launch_norm_rows(const PrepArgs &a, int64_t nblk, hipStream_t s) {
 }
 
 template <int FMT>
-hipError_t launch_prepare(const PrepArgs &a, hipStream_t s) {
+hipError_t launch_prepare(const PrepArgs &args, hipStream_t s) {
+  PrepArgs a = args;
+  a.inv_k = 1.0f / (float)a.k;   // IEEE binary32 division on the host
   const int64_t nblk = a.k / 32;
   const bool ksm = a.s_ksm != 0;
   if (FMT == 1) zero_amax_kernel<<<1, 1, 0, s>>>(a.amax);

@@ -26,6 +26,14 @@ __device__ __forceinline__ float e8m0_operand(uint32_t byte) { return __uint_as_
 
 // ---------------------------------------------------------------- 2:4 mask
 
+// Median of three unsigned values: one v_med3_u32 (the compiler does not form
+// it from min/max on its own)
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // Per group of four: keys order by magnitude, then by lower index.  u values
 // are 3 - index of the two kept entries (umax for the lower index).
 struct MaskOut {
@@ -42,9 +50,12 @@ __device__ __forceinline__ void mask_block(const float xf[32], MaskOut &o) {
     uint32_t k1 = (__float_as_uint(xf[4 * g + 1]) & 0x7FFF0000u) | 2u;
     uint32_t k2 = (__float_as_uint(xf[4 * g + 2]) & 0x7FFF0000u) | 1u;
     uint32_t k3 = (__float_as_uint(xf[4 * g + 3]) & 0x7FFF0000u);
-    uint32_t a = max(k0, k1), b = min(k0, k1), c = max(k2, k3), d = min(k2, k3);
-    uint32_t top = max(a, c);
-    uint32_t second = max(max(min(a, c), b), d);
+    // the largest and the median of k0..k2 (v_max3, v_med3), then k3 against
+    // them: top = max(t3, k3), second = max(med, min(t3, k3))
+    uint32_t t3 = max(max(k0, k1), k2);
+    uint32_t md = med3_u32(k0, k1, k2);
+    uint32_t top = max(t3, k3);
+    uint32_t second = max(md, min(t3, k3));
     uint32_t ut = top & 3u, us = second & 3u;
     uint32_t umax = max(ut, us), umin = min(ut, us);
     o.top[g] = top;
@@ -206,6 +217,61 @@ __device__ __forceinline__ void store_block(const PrepArgs &a, int64_t row, int6
             reinterpret_cast<u32x4 *>(a.s_dense + arr_off(row, t, a.ld_sd, a.s_ksm, 64) + 16 * q));
   store_scale<FMT, NT>(a.s_scales, a.ld_ss, a.s_ksm, row, b, o.s_scale);
   store_scale<FMT, NT>(a.r_scales, a.ld_rs, a.r_ksm, row, b, o.r_scale);
+}
+
+// arr_off is linear in the row and the k-step, so the offset of (rs + rl,
+// ts + tl) splits into arr_off(rs, ts), wavefront-uniform (64-bit, scalar
+// registers), plus this lane part.  Every array of a view spans less than
+// 4 GiB, so the lane part fits 32 bits and the store takes a scalar base and a
+// 32-bit vector offset.
+template <int BPS>
+__device__ __forceinline__ uint32_t lane_off(int64_t ld, int ksm, uint32_t rl, uint32_t tl) {
+  return ksm ? tl * ((uint32_t)ld * BPS) + rl * BPS : rl * (uint32_t)ld + tl * BPS;
+}
+
+// The lane parts of one lane's block in every array of a view pair: row rl of
+// the row group, k-step tl of the pass, block q of the k-step.
+struct LaneOffsets {
+  uint32_t sc, meta, rc, sd, ss, rs;
+};
+
+template <int FMT>
+__device__ __forceinline__ LaneOffsets lane_offsets(const PrepArgs &a, uint32_t rl, uint32_t tl,
+                                                    uint32_t q) {
+  constexpr int SB = FMT == 0 ? 4 : 8;   // scale bytes per row and k-step
+  LaneOffsets o;
+  o.sc = lane_off<32>(a.ld_sc, a.s_ksm, rl, tl) + 8 * q;
+  o.meta = lane_off<16>(a.ld_meta, a.s_ksm, rl, tl) + 4 * q;
+  o.rc = lane_off<64>(a.ld_rc, a.r_ksm, rl, tl) + 16 * q;
+  o.sd = a.s_dense ? lane_off<64>(a.ld_sd, a.s_ksm, rl, tl) + 16 * q : 0u;
+  o.ss = lane_off<SB>(a.ld_ss, a.s_ksm, rl, tl) + (SB / 4) * q;
+  o.rs = lane_off<SB>(a.ld_rs, a.r_ksm, rl, tl) + (SB / 4) * q;
+  return o;
+}
+
+// store_block for the block at row rs + rl, k-step ts + tl, given the uniform
+// (rs, ts) and the lane parts.
+template <int FMT, bool NT>
+__device__ __forceinline__ void store_block_at(const PrepArgs &a, int64_t rs, int64_t ts,
+                                               const LaneOffsets &lo, const BlockOut &o) {
+  constexpr int SB = FMT == 0 ? 4 : 8;
+  put<NT>(u32x2{o.s_comp[0], o.s_comp[1]},
+          reinterpret_cast<u32x2 *>(a.s_codes + arr_off(rs, ts, a.ld_sc, a.s_ksm, 32) + lo.sc));
+  put<NT>(o.meta, reinterpret_cast<uint32_t *>(a.meta + arr_off(rs, ts, a.ld_meta, a.s_ksm, 16) + lo.meta));
+  put<NT>(u32x4{o.r_codes[0], o.r_codes[1], o.r_codes[2], o.r_codes[3]},
+          reinterpret_cast<u32x4 *>(a.r_codes + arr_off(rs, ts, a.ld_rc, a.r_ksm, 64) + lo.rc));
+  if (a.s_dense)
+    put<NT>(u32x4{o.s_dense[0], o.s_dense[1], o.s_dense[2], o.s_dense[3]},
+            reinterpret_cast<u32x4 *>(a.s_dense + arr_off(rs, ts, a.ld_sd, a.s_ksm, 64) + lo.sd));
+  uint8_t *ps = a.s_scales + arr_off(rs, ts, a.ld_ss, a.s_ksm, SB) + lo.ss;
+  uint8_t *pr = a.r_scales + arr_off(rs, ts, a.ld_rs, a.r_ksm, SB) + lo.rs;
+  if (FMT == 0) {
+    put<NT>((uint8_t)o.s_scale, ps);
+    put<NT>((uint8_t)o.r_scale, pr);
+  } else {
+    put<NT>((uint16_t)o.s_scale, reinterpret_cast<uint16_t *>(ps));
+    put<NT>((uint16_t)o.r_scale, reinterpret_cast<uint16_t *>(pr));
+  }
 }
 
 // SiLU(gate) * up in front of the down projection: x = bf16 of g / (1 +

@@ -155,6 +155,10 @@ sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int
 
 namespace {
 
+// Row strides of the bf16 inputs and x_out: the preparation addresses a row
+// group with 32-bit offsets from a per-group base.
+constexpr int64_t kMaxRowStride = (int64_t)1 << 28;
+
 // Validation and launch shared by sharq_prepare and sharq_prepare_residual
 // (add == nullptr: no residual add).
 sharq_status prepare_common(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
@@ -166,6 +170,8 @@ sharq_status prepare_common(sharq_format fmt, const uint16_t *x_bf16, int64_t m,
   if (!x_bf16 || !sp || !rs) return SHARQ_ERR_NULL;
   if (m < 1 || k < 32 || k % 32 || ld_x < k) return SHARQ_ERR_SHAPE;
   if (gamma_bf16 && k > 16384) return SHARQ_ERR_UNSUPPORTED;
+  if (ld_x >= kMaxRowStride || (add && (ld_add >= kMaxRowStride || ld_out >= kMaxRowStride)))
+    return SHARQ_ERR_UNSUPPORTED;
   if (ld_x % 8 || !aligned(x_bf16, 16)) return SHARQ_ERR_ALIGN;
   if (gamma_bf16 && !aligned(gamma_bf16, 16)) return SHARQ_ERR_ALIGN;
   CHECK(check_prep_views(fmt, sp, rs, m, k));
