@@ -113,17 +113,6 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
 
 // ---------------------------------------------------------------- NVFP4 block
 
-// fl32(v / S) from y = fl32(1 / S): q0 = fl32(v y) is within an ulp of v / S,
-// r = fma(-q0, S, v) is then exact, and fma(r, y, q0) is the correctly rounded
-// quotient (Markstein's correction of a faithful quotient with a correctly
-// rounded reciprocal).  Valid while neither y nor the quotient leaves the
-// normal range: S in [2^-100, 2^100] and |v / S| < 8 here.
-__device__ __forceinline__ float div_rn(float v, float S, float y) {
-  const float q0 = v * y;
-  const float r = __builtin_fmaf(-q0, S, v);
-  return __builtin_fmaf(r, y, q0);
-}
-
 // E2M1 codes of fl32(v / S) for 32 values (two 16-blocks with scales S[0], S[1]),
 // signed zeros when S == 0; packed two per byte.
 __device__ __forceinline__ void nv_codes(const float v[32], const float S[2], uint32_t out[4]) {
@@ -301,13 +290,8 @@ __device__ __forceinline__ T *at_bytes(T *base, int64_t uniform_bytes, uint32_t 
   return reinterpret_cast<T *>(reinterpret_cast<B *>(base) + uniform_bytes + lane_bytes);
 }
 
-// fl32(ss / k): Markstein's correction with the host's fl32(1 / k) where no
-// step can leave the normal range (ss = 0 or ss in [2^-100, 2^100]), an IEEE
-// division otherwise (zero rows aside, practically never)
 __device__ __forceinline__ float row_mean(float ss, const PrepArgs &a) {
-  const float kf = (float)a.k;
-  if (ss == 0.0f || (ss >= 0x1p-100f && ss <= 0x1p100f)) return div_rn(ss, kf, a.inv_k);
-  return ss / kf;
+  return row_mean_of(ss, (float)a.k, a.inv_k);
 }
 
 // ---------------------------------------------------------------- kernels

@@ -274,6 +274,28 @@ __device__ __forceinline__ void store_block_at(const PrepArgs &a, int64_t rs, in
   }
 }
 
+// fl32(v / S) from y = fl32(1 / S): q0 = fl32(v y) is within an ulp of v / S,
+// r = fma(-q0, S, v) is then exact, and fma(r, y, q0) is the correctly rounded
+// quotient (Markstein's correction of a faithful quotient with a correctly
+// rounded reciprocal).  Valid while neither y nor the quotient nor the
+// remainder leaves the normal range: the NVFP4 scales S in [2^-100, 2^100]
+// with |v / S| < 8, and the row mean below.  Host and device: a host build
+// checks it against IEEE division over the row mean's whole domain.
+__host__ __device__ __forceinline__ float div_rn(float v, float S, float y) {
+  const float q0 = v * y;
+  const float r = __builtin_fmaf(-q0, S, v);
+  return __builtin_fmaf(r, y, q0);
+}
+
+// The row mean fl32(ss / k) for k = 32 .. 16384 from inv_k = fl32(1 / k):
+// Markstein's correction where no step can leave the normal range (ss = 0 or
+// ss in [2^-100, 2^100]), an IEEE division otherwise (zero rows aside,
+// practically never: ss is a sum of squares of bf16 values).
+__host__ __device__ __forceinline__ float row_mean_of(float ss, float kf, float inv_k) {
+  if (ss == 0.0f || (ss >= 0x1p-100f && ss <= 0x1p100f)) return div_rn(ss, kf, inv_k);
+  return ss / kf;
+}
+
 // SiLU(gate) * up in front of the down projection: x = bf16 of g / (1 +
 // exp(-g)) * u evaluated in binary64 and rounded once.  The lane evaluates
 // it in fp32 first and keeps that when rounding it must give the same bf16

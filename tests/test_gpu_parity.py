@@ -141,6 +141,22 @@ def test_prepare_mx_degenerate_rows():
     check_prep(sq.MXFP4, xb, si.gamma(k, None), label="degenerate norm")
 
 
+@pytest.mark.parametrize("k", [224, 4000])
+def test_prepare_mx_row_mean_ranges(k):
+    """Finite rows whose sums of squares span 2^-130 .. Inf: the row mean's
+    Markstein path (ss in [2^-100, 2^100] or 0), its IEEE-division path on
+    both sides and a sum that overflows to Inf (r = 0, x_n = 0).  Inf and NaN
+    elements are outside the supported inputs."""
+    rows = []
+    for e in range(-70, 71, 4):
+        x = si.bf16_bits_to_f32(si.activations("student_t4", 1, k, 2, 50.0, seed=e + 100))[0]
+        rows.append(x * np.float32(2.0 ** e))
+    rows.append(np.zeros(k, np.float32))
+    xb = si.f32_to_bf16_bits(np.stack(rows))
+    for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR) if k % 128 == 0 else (None,):
+        check_prep(sq.MXFP4, xb, si.gamma(k, seed=3), label=f"row mean ranges k{k}", layout=layout)
+
+
 def test_prepare_padded_row_stride():
     m, k, ld = 10, 512, 640
     x = si.activations("normal", m, ld, 3, 40.0, seed=77)

@@ -87,3 +87,30 @@ def test_oracle_f64_to_bf16_non_finite_and_overflow():
     x = oracle.silu_mul(np.array([[20.0, -20.0, 3e38]], np.float32), np.array([[3e38, 3e38, 3e38]], np.float32))
     assert x[0][0] == 0x7F80 and x[0][2] == 0x7F80
     assert x[0][1] & 0x8000 and (x[0][1] & 0x7F80) != 0x7F80        # -20 sigmoid(-20) 3e38 is finite
+
+
+@pytest.fixture(scope="module")
+def host_row_mean(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc is not installed")
+    out = str(tmp_path_factory.mktemp("rowmean") / "librowmean.so")
+    subprocess.run([HIPCC, "-x", "hip", "--offload-arch=gfx950", "--cuda-host-only", "-O2", "-std=c++17",
+                    "-ffp-contract=off", "-fPIC", "-shared", "-I", CSRC, "-o", out,
+                    os.path.join(HERE, "host", "row_mean_host.cpp")], check=True, capture_output=True)
+    lib = ctypes.CDLL(out)
+    lib.host_row_mean_mismatches.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64,
+                                             ctypes.POINTER(ctypes.c_int64)]
+    lib.host_row_mean_mismatches.restype = ctypes.c_int64
+    return lib.host_row_mean_mismatches
+
+
+def test_row_mean_is_the_ieee_quotient(host_row_mean):
+    """The normalized preparation's row mean fl32(ss / k) (the RMSNorm step of
+    the preparation operator, abstract sentence 5) takes Markstein's
+    correction from fl32(1 / k) inside [2^-100, 2^100] and IEEE division
+    outside: identical to ss / k for every k = 32 .. 16384 the kernels take,
+    over 2^-110 .. 2^110 and the special values."""
+    cases = ctypes.c_int64(0)
+    bad = host_row_mean(16384, 4000, 12345, ctypes.byref(cases))
+    assert cases.value > 2_000_000
+    assert bad == 0, f"{bad} of {cases.value} row means differ from ss / k"
