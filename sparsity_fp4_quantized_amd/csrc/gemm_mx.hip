@@ -526,18 +526,7 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
   // Y leaves with non-temporal stores: nothing here reads it back, and fp32
   // tiles left dirty in the L2s (qkv shape: 50 MB against 32 MB of L2) slowed
   // the kernel's end and the next kernel's start (qkv GEMM 55.5 -> 52.9 us).
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int jt = 0; jt < TN; ++jt) {
-      const int64_t col = n0 + wn * (TBN / 2) + jt * 32 + li;
-      if (col >= a.n) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < m_end) __builtin_nontemporal_store(acc[it][jt][r], &a.y[row * a.ld_y + col]);
-      }
-    }
+  store_tile<TBM, TBN>(a.y, a.ld_y, m0, n0, m_end, a.n, wm, wn, h, li, acc, 1.0f);
 }
 
 template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false>

@@ -442,18 +442,7 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a, uint3
   }
 
   const float ts = a.a_tensor_scale[0] * a.w_tensor_scale[0];
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int jt = 0; jt < TN; ++jt) {
-      const int64_t col = n0 + wn * (TBN / 2) + jt * 32 + li;
-      if (col >= a.n) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < a.m) __builtin_nontemporal_store(acc[it][jt][r] * ts, &a.y[row * a.ld_y + col]);
-      }
-    }
+  store_tile<TBM, TBN>(a.y, a.ld_y, m0, n0, a.m, a.n, wm, wn, h, li, acc, ts);
 }
 
 template <int TBN, int STAGES, int BB>
