@@ -771,8 +771,10 @@ def main():
                     "peak": peak, "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
                     "traffic": gemm_traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
                     "algorithmic_flops_per_launch": flops,
-                    "executed_TFLOP/s": round((1.0 if (w.fmt == sq.NVFP4 and args.variant == 3) else 4.0 / 3.0)
-                                              * gemm_tflops, 2),
+                    # the structured-sparse MFMA skips the backbone's zero half
+                    # (SPARSE_MFMA, and AUTO for NVFP4, which resolves to it)
+                    "executed_TFLOP/s": round((1.0 if (args.variant == 3 or (w.fmt == sq.NVFP4 and args.variant == 0))
+                                               else 4.0 / 3.0) * gemm_tflops, 2),
                     "dense_equivalent_TFLOP/s": round(2.0 / 3.0 * gemm_tflops, 2)}
 
     out = {
