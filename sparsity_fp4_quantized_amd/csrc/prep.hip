@@ -361,18 +361,28 @@ __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
     if (has) store32(at_bytes(a.x_out, 2 * rs * a.ld_xout, rl * (2u * (uint32_t)a.ld_xout) + vb), xw);
   }
   unpack32(xw, xf);
-  const float s = lane_tree_sum<L>(has ? block_sumsq(xf) : 0.0f);
-  if (lb == 0) part[rl][wave] = s;
-  __syncthreads();
-  float c[W];
+  float r;
+  if constexpr (FMT == 1) {
+    // NVFP4: the tensor-amax pre-pass computed the row's r (the same tree and
+    // steps) and left it in the first 4 bytes of the row's residual codes;
+    // every lane has read it before the barrier, and only then does the
+    // row's first block overwrite it
+    r = *reinterpret_cast<const float *>(a.r_codes + arr_off(rs + rlx, 0, a.ld_rc, a.r_ksm, 64));
+    __syncthreads();
+  } else {
+    const float s = lane_tree_sum<L>(has ? block_sumsq(xf) : 0.0f);
+    if (lb == 0) part[rl][wave] = s;
+    __syncthreads();
+    float c[W];
 #pragma unroll
-  for (int i = 0; i < W; ++i) c[i] = part[rl][i];
+    for (int i = 0; i < W; ++i) c[i] = part[rl][i];
 #pragma unroll
-  for (int w = W / 2; w >= 1; w >>= 1) {
+    for (int w = W / 2; w >= 1; w >>= 1) {
 #pragma unroll
-    for (int i = 0; i < w; ++i) c[i] = c[2 * i] + c[2 * i + 1];
+      for (int i = 0; i < w; ++i) c[i] = c[2 * i] + c[2 * i + 1];
+    }
+    r = 1.0f / __builtin_sqrtf(row_mean(c[0], a) + a.eps);
   }
-  const float r = 1.0f / __builtin_sqrtf(row_mean(c[0], a) + a.eps);
   if (!has) return;
   {
     float gf[32];
@@ -496,6 +506,10 @@ __global__ __launch_bounds__(512) void amax_norm_kernel(PrepArgs a) {
     unpack32(xw, xf);
     float s = block_sumsq(xf);
     float r = row_rms<WPR>(has ? s : 0.0f, riw, wir, a.k, a.eps);
+    // the row's r for the preparation pass, in the first 4 bytes of the row's
+    // residual codes (that pass reads it before it stores the codes there)
+    if (row < a.m && wir == 0 && lane == 0)
+      *reinterpret_cast<float *>(a.r_codes + arr_off(row, 0, a.ld_rc, a.r_ksm, 64)) = r;
     if (has) {
       normalize32(xf, xw, a.gamma + 32 * b, r);
 #pragma unroll
