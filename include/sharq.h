@@ -192,8 +192,8 @@ sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int
  * same pointer: one tensor scale serves both paths).
  * Requirements: m >= 1; k >= 32, k % 32 == 0; k <= 16384 when gamma is given;
  * ld_x >= k, ld_x % 8 == 0; x 16-byte aligned; both views as the view
- * requirements above state (m rows), with the same layout.  ld_x < 2^28
- * (SHARQ_ERR_UNSUPPORTED otherwise: the kernels address a row group of X
+ * requirements above state (m rows), with the same layout.  ld_x < 2^26
+ * (SHARQ_ERR_UNSUPPORTED otherwise: the kernels address a group of rows of X
  * with 32-bit offsets from a per-group base).
  */
 sharq_status sharq_prepare(sharq_format fmt, const uint16_t *x_bf16, int64_t m, int64_t k,
@@ -237,7 +237,7 @@ sharq_status sharq_prepare_noalloc(sharq_format fmt, const uint16_t *x_bf16, int
  * MXFP4 only (SHARQ_ERR_UNSUPPORTED for NVFP4, whose tensor-scale pre-pass
  * would need the sum first).
  * Requirements: as sharq_prepare with gamma given, and for h, o and x_out:
- * ld >= k, ld % 8 == 0, ld < 2^28, 16-byte aligned.
+ * ld >= k, ld % 8 == 0, ld < 2^26, 16-byte aligned.
  */
 sharq_status sharq_prepare_residual(sharq_format fmt, const uint16_t *h_bf16, int64_t ld_h,
                                     const uint16_t *o_bf16, int64_t ld_o, uint16_t *x_out_bf16,
@@ -259,9 +259,10 @@ sharq_status sharq_prepare_residual(sharq_format fmt, const uint16_t *h_bf16, in
  *                                     round differently);
  * then sharq_prepare's steps 2-4 on x (no normalization).  x itself is not
  * written.  One HBM pass over g and u.  MXFP4 only.
- * Requirements: m >= 1; k >= 32, k % 32 == 0; ld_gate, ld_up >= k and
- * multiples of 4; gate and up 16-byte aligned; both views as sharq_prepare
- * requires.  Inputs are finite with |x| below the bf16 maximum.
+ * Requirements: m >= 1; k >= 32, k % 32 == 0; ld_gate, ld_up >= k,
+ * multiples of 4 and below 2^26 (SHARQ_ERR_UNSUPPORTED otherwise); gate and
+ * up 16-byte aligned; both views as sharq_prepare requires.  Inputs are
+ * finite with |x| below the bf16 maximum.
  */
 sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t ld_gate,
                                     const float *up, int64_t ld_up, int64_t m, int64_t k,

@@ -404,18 +404,21 @@ __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
 // 64 / R consecutive blocks: R = 16 (one 128-k step of 16 consecutive rows)
 // makes every store of the k-step-major layout 16 rows contiguous; R = 1 (64
 // blocks of one row) does the same for the row-major layout.
+// Addresses as in the norm kernel: wavefront-uniform bases (the wavefront's
+// first row and block) plus 32-bit lane offsets.
 template <int FMT, int R>
 __global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chunks) {
   constexpr int L = 64 / R;
   const uint32_t w = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const uint32_t rg = w / chunks;
-  const int64_t row = (int64_t)rg * R + lane / L;
-  const int64_t b = (int64_t)(w - rg * chunks) * L + lane % L;
+  const uint32_t rl = (uint32_t)lane / L, lb = (uint32_t)lane % L;
+  const int64_t rs = (int64_t)rg * R, b0 = (int64_t)(w - rg * chunks) * L;   // uniform
+  const int64_t row = rs + rl, b = b0 + lb;
   if (row >= a.m || b >= a.k / 32) return;
   uint32_t xw[16];
   float xf[32];
-  load32(a.x + row * a.ld_x + 32 * b, xw);
+  load32(at_bytes(a.x, 2 * rs * a.ld_x + 64 * b0, rl * (2u * (uint32_t)a.ld_x) + 64u * lb), xw);
   unpack32(xw, xf);
   BlockOut o;
   if (FMT == 0) {
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(256) void prep_flat_kernel(PrepArgs a, uint32_t chu
     if (row == 0 && b == 0) a.tensor_scale[0] = s_t;
     quantize_block_nv(xf, s_t, o);
   }
-  store_block<FMT, true>(a, row, b, o);
+  store_block_at<FMT, true>(a, rs, b0 / 4, lane_offsets<FMT>(a, rl, lb >> 2, lb & 3), o);
 }
 
 // One lane per 32-k block, laid out as prep_flat_kernel's lanes: the block of
@@ -437,11 +440,14 @@ __global__ __launch_bounds__(256) void prep_silu_kernel(PrepArgs a, uint32_t chu
   const uint32_t w = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const uint32_t rg = w / chunks;
-  const int64_t row = (int64_t)rg * R + lane / L;
-  const int64_t b = (int64_t)(w - rg * chunks) * L + lane % L;
+  const uint32_t rl = (uint32_t)lane / L, lb = (uint32_t)lane % L;
+  const int64_t rs = (int64_t)rg * R, b0 = (int64_t)(w - rg * chunks) * L;   // uniform
+  const int64_t row = rs + rl, b = b0 + lb;
   if (row >= a.m || b >= a.k / 32) return;
-  const u32x4 *gp = reinterpret_cast<const u32x4 *>(a.gate + row * a.ld_gate + 32 * b);
-  const u32x4 *upp = reinterpret_cast<const u32x4 *>(a.up + row * a.ld_up + 32 * b);
+  const u32x4 *gp = reinterpret_cast<const u32x4 *>(
+      at_bytes(a.gate, 4 * rs * a.ld_gate + 128 * b0, rl * (4u * (uint32_t)a.ld_gate) + 128u * lb));
+  const u32x4 *upp = reinterpret_cast<const u32x4 *>(
+      at_bytes(a.up, 4 * rs * a.ld_up + 128 * b0, rl * (4u * (uint32_t)a.ld_up) + 128u * lb));
   u32x4 gq[8], uq[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -462,7 +468,7 @@ __global__ __launch_bounds__(256) void prep_silu_kernel(PrepArgs a, uint32_t chu
   unpack32(xw, xf);
   BlockOut o;
   quantize_block_mx(xw, xf, o);
-  store_block<0, true>(a, row, b, o);
+  store_block_at<0, true>(a, rs, b0 / 4, lane_offsets<0>(a, rl, lb >> 2, lb & 3), o);
 }
 
 // NVFP4 tensor amax of x_n.  fp32 bit patterns of non-negative values order

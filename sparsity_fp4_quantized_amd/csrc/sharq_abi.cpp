@@ -155,9 +155,10 @@ sharq_status sharq_quantize_weight(sharq_format fmt, const uint16_t *w_bf16, int
 
 namespace {
 
-// Row strides of the bf16 inputs and x_out: the preparation addresses a row
-// group with 32-bit offsets from a per-group base.
-constexpr int64_t kMaxRowStride = (int64_t)1 << 28;
+// Row strides of the preparation's row inputs (bf16 X, h, o, x_out; fp32
+// gate, up): the kernels address a group of up to 16 rows with 32-bit offsets
+// from a per-group base (15 x 4 B x 2^26 < 2^32).
+constexpr int64_t kMaxRowStride = (int64_t)1 << 26;
 
 // Validation and launch shared by sharq_prepare and sharq_prepare_residual
 // (add == nullptr: no residual add).
@@ -237,6 +238,7 @@ sharq_status sharq_prepare_silu_mul(sharq_format fmt, const float *gate, int64_t
   if (fmt != SHARQ_MXFP4) return SHARQ_ERR_UNSUPPORTED;
   if (!gate || !up || !sp || !rs) return SHARQ_ERR_NULL;
   if (m < 1 || k < 32 || k % 32 || ld_gate < k || ld_up < k) return SHARQ_ERR_SHAPE;
+  if (ld_gate >= kMaxRowStride || ld_up >= kMaxRowStride) return SHARQ_ERR_UNSUPPORTED;
   if (ld_gate % 4 || ld_up % 4 || !aligned(gate, 16) || !aligned(up, 16)) return SHARQ_ERR_ALIGN;
   CHECK(check_prep_views(fmt, sp, rs, m, k));
   PrepArgs a{nullptr, 0, m, k, nullptr, 0.0f,

@@ -85,7 +85,7 @@ def prep(fmt=0, x=FAKE, m=16, k=256, ld_x=256, gamma=None, sp=None, rs=None):
     (dict(ld_x=260), sq.ERR_ALIGN),
     (dict(x=FAKE + 2), sq.ERR_ALIGN),
     (dict(k=32768, ld_x=32768, gamma=FAKE), sq.ERR_UNSUPPORTED),
-    (dict(ld_x=1 << 28), sq.ERR_UNSUPPORTED),   # row strides below 2^28 (32-bit lane offsets)
+    (dict(ld_x=1 << 26), sq.ERR_UNSUPPORTED),   # row strides below 2^26 (32-bit lane offsets)
     (dict(fmt=7), sq.ERR_UNSUPPORTED),
     (dict(sp=view(ld_codes=63)), sq.ERR_SHAPE),
     (dict(sp=view(ld_codes=64, meta=None)), sq.ERR_NULL),
@@ -132,9 +132,9 @@ def prep_res(fmt=0, h=FAKE, ld_h=256, o=FAKE, ld_o=256, out=FAKE, ld_out=256, m=
     (dict(h=FAKE + 2), sq.ERR_ALIGN),      # then every sharq_prepare check on h and the views
     (dict(m=0), sq.ERR_SHAPE),
     (dict(sp=view(ld_codes=63)), sq.ERR_SHAPE),
-    (dict(h=FAKE + 8192, ld_h=1 << 28), sq.ERR_UNSUPPORTED),   # row strides below 2^28
-    (dict(o=FAKE + 8192, ld_o=1 << 28), sq.ERR_UNSUPPORTED),
-    (dict(out=FAKE + 4096, ld_out=1 << 28), sq.ERR_UNSUPPORTED),
+    (dict(h=FAKE + 8192, ld_h=1 << 26), sq.ERR_UNSUPPORTED),   # row strides below 2^26
+    (dict(o=FAKE + 8192, ld_o=1 << 26), sq.ERR_UNSUPPORTED),
+    (dict(out=FAKE + 4096, ld_out=1 << 26), sq.ERR_UNSUPPORTED),
 ])
 def test_prepare_residual_validation(kwargs, status):
     assert prep_res(**kwargs) == status
@@ -158,6 +158,8 @@ def prep_silu(fmt=0, gate=FAKE, ld_gate=256, up=FAKE, ld_up=256, m=16, k=256, sp
     (dict(ld_up=128), sq.ERR_SHAPE),
     (dict(ld_gate=258), sq.ERR_ALIGN),
     (dict(up=FAKE + 4), sq.ERR_ALIGN),
+    (dict(ld_gate=1 << 26), sq.ERR_UNSUPPORTED),   # row strides below 2^26
+    (dict(ld_up=1 << 26), sq.ERR_UNSUPPORTED),
     (dict(sp=view(ld_codes=63)), sq.ERR_SHAPE),
     (dict(sp=ksm(), rs=view(meta=None)), sq.ERR_SHAPE),
     (dict(rs=view(meta=None, scales=None)), sq.ERR_NULL),
