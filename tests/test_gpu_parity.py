@@ -171,6 +171,42 @@ def test_prepare_padded_row_stride():
         assert np.array_equal(host(sp.row_major("meta")), ref["meta"])
 
 
+@pytest.mark.parametrize("norm", [True, False])
+def test_prepare_padded_row_stride_row_groups(norm):
+    """Row strides above k with several rows per wavefront (four with the
+    norm, sixteen in the k-step-major flat kernel), where each lane's offset
+    in X carries its row within the group times the stride; both layouts."""
+    m, k, ld = 1100, 1024, 1024 + 192
+    x = si.activations("student_t4", m, ld, 12, 50.0, seed=78)
+    g = si.gamma(k, seed=79) if norm else None
+    xt = dev16(x)[:, :k]
+    assert xt.stride(0) == ld
+    ref = oracle.prepare(sq.MXFP4, np.ascontiguousarray(x[:, :k]), g, dense_backbone=True)
+    for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR):
+        sp, rs = sq.prepare(xt, None if g is None else dev16(g), 1e-5, dense_backbone=True, layout=layout)
+        _compare_prep(f"padded rows norm{norm} layout {layout}", sp, rs, ref)
+
+
+def test_prepare_residual_padded_row_groups():
+    """The residual add with padded h, o and x_out at four rows per
+    wavefront: each input's own stride in every lane offset."""
+    m, k = 1100, 2048
+    h = si.activations("student_t4", m, k, 20, 50.0, seed=80)
+    o = si.activations("normal", m, k, 0, 1.0, seed=81)
+    g = si.gamma(k, 82)
+    x_ref, ref = oracle.prepare_residual(sq.MXFP4, h, o, g, dense_backbone=True)
+    hb = torch.zeros((m, k + 64), dtype=torch.int16, device=DEV)
+    ob = torch.zeros((m, k + 128), dtype=torch.int16, device=DEV)
+    xb = torch.full((m, k + 256), 0x7A5A, dtype=torch.int16, device=DEV)
+    hb[:, :k] = dev16(h)
+    ob[:, :k] = dev16(o)
+    x, sp, rs = sq.prepare_residual(hb[:, :k], ob[:, :k], dev16(g), dense_backbone=True, out=xb[:, :k])
+    got = host(xb).view(np.uint16)
+    assert np.array_equal(got[:, :k], x_ref)
+    assert (got[:, k:] == 0x7A5A).all()
+    _compare_prep("residual padded row groups", sp, rs, ref)
+
+
 def test_prepare_nv_small():
     for m, k, norm in [(3, 64, True), (17, 512, False), (8, 4096, True)]:
         x = si.activations("student_t4", m, k, 2, 50.0, seed=31 + k)
