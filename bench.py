@@ -615,6 +615,115 @@ def moe_main(args):
     print(json.dumps(res), flush=True)
 
 
+def power_main(w: si.Workload, torch, dev, preps, gemms, nsets: int) -> None:
+    """Socket power and engine clocks while one kernel runs back to back.
+
+    A sampler thread reads `amd-smi metric -p -c --csv` (socket power, the
+    eight XCDs' gfx clocks; the reading refreshes about once a second; the
+    board's limit from `rocm-smi -M`) while
+    the dual GEMM, the preparation and the FP4 MFMA yardstick (random and
+    constant operands) each run for a few seconds, with an idle gap between
+    them.  Per phase: the launch time and the median of the samples taken
+    after its first second (the settled state).  This tells whether a kernel
+    runs at the board's power limit, where the engine clock, not the
+    schedule, sets its speed."""
+    import ctypes
+    import statistics
+    import subprocess
+    import threading
+
+    samples, phase, stop = [], ["start"], threading.Event()
+
+    def read():
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--csv"], capture_output=True, text=True)
+        ls = r.stdout.strip().splitlines()
+        hdr = next((l.split(",") for l in ls if l.startswith("gpu,")), None)
+        row = next((l.split(",") for l in ls if l[:1].isdigit()), None)
+        if not hdr or not row or len(hdr) != len(row):
+            return None
+        d = dict(zip(hdr, row))
+        try:
+            clk = [float(d[f"gfx_{i}_clk"]) for i in range(8) if f"gfx_{i}_clk" in d]
+            return float(d["socket_power"]), sum(clk) / len(clk)
+        except (KeyError, ValueError, ZeroDivisionError):
+            return None
+
+    def sampler():
+        while not stop.is_set():
+            v = read()
+            if v is not None:
+                samples.append((time.time(), phase[0], v[0], v[1]))
+            time.sleep(0.1)
+
+    cap = subprocess.run(["rocm-smi", "-M", "--csv"], capture_output=True, text=True)
+    if read() is None:
+        raise SystemExit("amd-smi gave no socket power reading on this machine")
+    path = os.path.join(ROOT, "sparsity_fp4_quantized_amd", "libsharq_yardstick.so")
+    L = ctypes.CDLL(path)
+    L.sharq_yardstick_mfma_fp4.restype = ctypes.c_int
+    L.sharq_yardstick_mfma_fp4.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    out = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    ticks = torch.empty(1024, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def yard(rnd):
+        def f(i):
+            if L.sharq_yardstick_mfma_fp4(512, 4000, rnd, out.data_ptr(), ticks.data_ptr(), stream) != 0:
+                raise RuntimeError("yardstick launch failed")
+        return f
+
+    for p in preps:   # every set's GEMM operands prepared from its X
+        p()
+    torch.cuda.synchronize()
+    phases = [("dual_gemm", lambda i: gemms[i % nsets](), 4.0, 200),
+              ("prepare", lambda i: preps[i % nsets](), 3.0, 1000),
+              ("mfma_fp4_random_operands", yard(1), 4.0, 20),
+              ("mfma_fp4_constant_operands", yard(0), 3.0, 20)]
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    res, spans = {}, {}
+    time.sleep(1.5)
+    for name, fn, secs, per in phases:
+        phase[0] = name
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, n = time.time(), 0
+        e0.record()
+        while time.time() - t0 < secs:
+            for _ in range(per):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        spans[name] = (t0 + 1.0, time.time())
+        res[name] = {"launches": n, "us_per_launch": round(e0.elapsed_time(e1) * 1e3 / n, 2)}
+        phase[0] = "idle"
+        time.sleep(1.5)
+    stop.set()
+    th.join()
+    for name, (a, b) in spans.items():
+        ps = [p for t, ph, p, c in samples if ph == name and a <= t <= b]
+        cs = [c for t, ph, p, c in samples if ph == name and a <= t <= b]
+        if ps:
+            res[name]["socket_power_W"] = round(statistics.median(ps), 1)
+            res[name]["gfx_clock_MHz"] = round(statistics.median(cs), 1)
+            res[name]["samples"] = len(ps)
+    idle = [p for t, ph, p, c in samples if ph == "start"]
+    cap_w = None
+    for l in cap.stdout.splitlines():
+        f = l.split(",")
+        if len(f) == 2 and f[0].startswith("card"):
+            try:
+                cap_w = float(f[1])
+            except ValueError:
+                pass
+    print(json.dumps({"metric": "socket power and engine clock per kernel, back to back", "workload": w.name,
+                      "power_cap_W": cap_w,
+                      "idle_socket_power_W": round(statistics.median(idle), 1) if idle else None,
+                      "phases": res, "sampler": "amd-smi metric -p -c --csv, every ~0.1 s"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -637,6 +746,9 @@ def main():
                     help="time one Qwen3-30B-A3B mixture-of-experts layer (grouped dual GEMMs) instead")
     ap.add_argument("--chain", action="store_true",
                     help="time the decoder-layer linear chain (SharQ vs bf16 / FP8 vendor GEMMs) instead")
+    ap.add_argument("--power", action="store_true",
+                    help="sample socket power and engine clocks (amd-smi) while the workload's dual GEMM, "
+                         "its preparation and the FP4 MFMA yardstick each run back to back, and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="convert two rocprofv3 --pmc runs into profiles/traffic.json and exit")
     args = ap.parse_args()
@@ -702,6 +814,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.power:
+        power_main(w, torch, dev, preps, gemms, nsets)
+        return
 
     for i in range(args.warmup):
         step(i)
