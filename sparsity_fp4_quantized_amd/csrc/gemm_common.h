@@ -45,17 +45,20 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
 struct OpStream {
   i32x4 rsrc;
   uint32_t row_stride, step;
+  uint32_t size;   // the descriptor's byte range: offsets at or past it read 0
 };
 
 __device__ __forceinline__ OpStream op_stream(const uint8_t *p, int64_t ld, int ksm, int64_t rows,
                                               int64_t r0, int64_t steps, int64_t bps) {
   OpStream s;
   if (ksm) {
-    s.rsrc = make_rsrc(p + r0 * bps, (uint32_t)(((steps - 1) * ld + rows - r0) * bps));
+    s.size = (uint32_t)(((steps - 1) * ld + rows - r0) * bps);
+    s.rsrc = make_rsrc(p + r0 * bps, s.size);
     s.row_stride = (uint32_t)bps;
     s.step = (uint32_t)(ld * bps);
   } else {
-    s.rsrc = make_rsrc(p + r0 * ld, (uint32_t)((rows - r0) * ld));
+    s.size = (uint32_t)((rows - r0) * ld);
+    s.rsrc = make_rsrc(p + r0 * ld, s.size);
     s.row_stride = (uint32_t)ld;
     s.step = (uint32_t)bps;
   }

@@ -326,10 +326,14 @@ def test_prepare_silu_mul(m, k, layout):
     """SiLU(gate) * up fused into the preparation, gate and up being the two
     column halves of one fp32 [m, 2k] gate+up output: every prepared array
     byte for byte against the oracle.  The inputs include gates outside the
-    fp32 fast path (|g| > 64, zero, tiny) and zero ups."""
+    fp32 fast path (|g| > 64, tiny), signed zero gates against ups of both
+    signs and signed zero ups (exact on the fast path), and zero ups."""
     g, u = si.gate_up_output(m, k, seed=41)
     g[0, :8] = [0.0, -0.0, 1e-30, -70.0, 90.0, -100.0, 65.0, -64.0]
     u[0, 8:12] = [0.0, -0.0, 0.0, 0.0]
+    if m > 1:
+        g[1, :8] = [0.0, -0.0, 0.0, -0.0, 0.0, -0.0, 0.0, -0.0]
+        u[1, :8] = [1.5, 1.5, -2.5, -2.5, 0.0, 0.0, -0.0, -0.0]
     _, ref = oracle.prepare_silu_mul(sq.MXFP4, g, u, dense_backbone=True)
     gu = torch.from_numpy(np.concatenate([g, u], axis=1)).to(DEV)
     sp, rs = sq.prepare_silu_mul(gu[:, :k], gu[:, k:], dense_backbone=True, layout=layout)
