@@ -35,6 +35,8 @@
 // Accumulator: lane l holds column l % 32, rows 8 (r / 4) + 4 h + r % 4.
 #include <stddef.h>
 
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -371,7 +373,7 @@ __device__ __forceinline__ void silu_hand_over(const v16f (&acc)[2][TN], float *
 // in binary64 (evaluated one by one with a branch each, every value waited
 // for its own LDS read and took three branches: 43 us of the gate+up GEMM).
 template <int KEEP, int TN>
-__device__ __forceinline__ void silu_finish(v16f (&acc)[2][TN], const float *theirs, int lane) {
+__device__ __forceinline__ void silu_finish(v16f (&acc)[2][TN], const float *theirs, int lane, bool active) {
 #pragma unroll
   for (int jt = 0; jt < TN; ++jt) {
     float other[16];
@@ -384,7 +386,9 @@ __device__ __forceinline__ void silu_finish(v16f (&acc)[2][TN], const float *the
       const float u = KEEP == 0 ? other[r] : acc[KEEP][jt][r];
       slow |= silu_mul_fast(g, u, x[r]) ? 0u : 1u << r;
     }
-    if (slow) {
+    // rows of a wavefront that skipped its MFMAs (all past the group's end:
+    // zero gates, outputs not stored) leave their fast values unrepaired
+    if (slow && active) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (slow & (1u << r)) {
@@ -417,11 +421,11 @@ __device__ __forceinline__ void silu_put_x(const v16f (&acc)[2][TN], uint16_t *x
 // halves ended up in scratch memory.
 template <int KEEP, int TN, int kHs, int kVals>
 __device__ __forceinline__ void silu_x_tile(v16f (&acc)[2][TN], float *xch, uint16_t *xs, int wave,
-                                            int wm, int h, int li, int lane) {
+                                            int wm, int h, int li, int lane, bool active) {
   __syncthreads();                      // every wavefront is done with the stages
   silu_hand_over<KEEP>(acc, xch + wave * kVals, lane);
   __syncthreads();
-  silu_finish<KEEP>(acc, xch + (wave ^ 1) * kVals, lane);
+  silu_finish<KEEP>(acc, xch + (wave ^ 1) * kVals, lane, active);
   __syncthreads();                      // the exchange is read before the x tile overwrites it
   silu_put_x<KEEP, TN, kHs>(acc, xs, wm, h, li);
   __syncthreads();
@@ -441,7 +445,7 @@ __device__ __forceinline__ void silu_x_tile(v16f (&acc)[2][TN], float *xch, uint
 template <int TBM, int TBN, int STAGES>
 __device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES], v16f (&acc)[2][TBN / 64],
                                                    const PrepArgs &p, int64_t m0, int64_t m_end, int64_t j0,
-                                                   int wave, int lane) {
+                                                   int wave, int lane, bool active) {
   constexpr int TN = TBN / 64, HB = TBN / 2, NB = HB / 32;
   constexpr int kVals = TN * 16 * 64;   // floats one wavefront hands over
   constexpr int kHs = HB + 8;           // LDS row stride of the x tile, in bf16
@@ -451,8 +455,8 @@ __device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, li = lane & 31;
   float *xch = reinterpret_cast<float *>(&st[0]);
   uint16_t *xs = reinterpret_cast<uint16_t *>(&st[0]);
-  if (wn == 0) silu_x_tile<0, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane);
-  else silu_x_tile<1, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane);
+  if (wn == 0) silu_x_tile<0, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane, active);
+  else silu_x_tile<1, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane, active);
   // blocks of a row sit in adjacent lanes: k-step-major outputs leave as
   // contiguous runs (the tile's columns are one 128-k step when HB = 128)
 #pragma unroll
@@ -500,6 +504,11 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
   if (GROUPED && !grouped_tile<TBM>(a, blockIdx.x, gn, m0, m_end, group, tn)) return;   // uniform: no work
   const int64_t n0 = (int64_t)tn * TBN;
   const ARows arow{a.row_index, m0, m_end, GROUPED, !SILU};
+  // a grouped tile's wavefronts whose 64 rows all lie past the group's end
+  // skip their LDS reads and MFMAs (they still issue their share of the
+  // stage loads and meet every barrier); their outputs are not stored, and
+  // the SiLU epilogue does not repair their (zero-gate) values in binary64.
+  const bool active = !GROUPED || m0 + wm * 64 < m_end;
   const int64_t w_row0 = GROUPED ? group * a.n : 0, w_rows = GROUPED ? (group + 1) * a.n : a.n;
 
   v16f acc[2][TN];
@@ -522,8 +531,10 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
   for (int p = 0; p < STAGES - 1; ++p)
     if (p < ksteps) issue_stage<TBM, TBN, NW>(R, O, wave, p, st[p]);
 
+  // one step: wait for its stage, the barrier, the next stage's loads, and
+  // (COMPUTE) the step's LDS reads and MFMAs
   int cur = 0;
-  for (int kt = 0; kt < ksteps; ++kt) {
+  auto step = [&](int kt, auto compute) {
     // stages kt + 1 .. kt + STAGES - 2 may stay in flight
     const int ahead = min(ksteps - 1 - kt, STAGES - 2);
     if (STAGES == 3 && ahead >= 1) wait_vmcnt<P::kMinPerWave>();
@@ -533,12 +544,19 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
       const int nxt = cur == 0 ? STAGES - 1 : cur - 1;
       issue_stage<TBM, TBN, NW>(R, O, wave, kt + STAGES - 1, st[nxt]);
     }
-    compute_stage<TBM, TBN>(st[cur], acc, wm, wn, h, li);
+    if constexpr (decltype(compute)::value) compute_stage<TBM, TBN>(st[cur], acc, wm, wn, h, li);
     cur = cur == STAGES - 1 ? 0 : cur + 1;
+  };
+  // the branch stays outside the loops, so that the accumulators keep their
+  // registers through the loop
+  if (active) {
+    for (int kt = 0; kt < ksteps; ++kt) step(kt, std::true_type{});
+  } else {
+    for (int kt = 0; kt < ksteps; ++kt) step(kt, std::false_type{});
   }
 
   if constexpr (SILU) {
-    silu_prep_epilogue<TBM, TBN, STAGES>(st, acc, *prep, m0, m_end, n0 / 2, wave, lane);
+    silu_prep_epilogue<TBM, TBN, STAGES>(st, acc, *prep, m0, m_end, n0 / 2, wave, lane, active);
     return;
   }
   // Y leaves with non-temporal stores: nothing here reads it back, and fp32
