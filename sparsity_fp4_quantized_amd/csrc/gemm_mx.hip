@@ -227,16 +227,19 @@ struct NoSide {
   __device__ __forceinline__ void post() {}
 };
 
-template <int TBM, int TBN, class Stage, class Side = NoSide>
+template <int TBM, int TBN, int NIT = 2, class Stage, class Side = NoSide>
 __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN / 64],
                                               int wm, int wn, int h, int li, Side side = Side()) {
+  // NIT: the wavefront's 32-row tiles that take part (1: rows 64 wm + 32 ..
+  // lie past a grouped tile's group; the other tile keeps its zeros)
   constexpr int TN = TBN / 64;
+  static_assert(NIT == 1 || NIT == 2, "one or both 32-row tiles");
   // the step's LDS reads are issued at raised wavefront priority, so that they
   // go out ahead of the MFMAs another wavefront of the SIMD is issuing
   __builtin_amdgcn_s_setprio(1);
   int sas[2], sar[2], sws[TN], swd[TN];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
+  for (int it = 0; it < NIT; ++it) {
     const int r = wm * 64 + it * 32 + li;
     sas[it] = (int)(S.sas[r] >> (16 * h));
     sar[it] = (int)(S.sar[r] >> (16 * h));
@@ -252,7 +255,7 @@ __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN
   for (int s = 0; s < 2; ++s) {
     const int c = 2 * h + s;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < NIT; ++it) {
       const int r = wm * 64 + it * 32 + li;
       ras[s][it] = S.as[lds_slot(r, c)];
       rar[s][it] = S.ar[lds_slot(r, c)];
@@ -274,7 +277,7 @@ __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN
   for (int s = 0; s < 2; ++s) {
     v8i fas[2], far[2], fb[TN];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < NIT; ++it) {
       fas[it] = as_operand(ras[s][it]);
       far[it] = as_operand(rar[s][it]);
     }
@@ -285,7 +288,7 @@ __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN
 #pragma unroll
     for (int path = 0; path < 2; ++path)
 #pragma unroll
-      for (int it = 0; it < 2; ++it)
+      for (int it = 0; it < NIT; ++it)
 #pragma unroll
         for (int jt = 0; jt < TN; ++jt) {
           const v8i fa = path == 0 ? fas[it] : far[it];
@@ -298,6 +301,7 @@ __device__ __forceinline__ void compute_stage(const Stage &S, v16f (&acc)[2][TBN
         }
   }
   if (Side::kValuPerMfma > 0) {
+    static_assert(Side::kValuPerMfma == 0 || NIT == 2, "the side work's schedule assumes both tiles");
     side.post();
     // one MFMA, then kValuPerMfma VALU instructions of the side work, ...
 #pragma unroll
@@ -445,7 +449,7 @@ __device__ __forceinline__ void silu_x_tile(v16f (&acc)[2][TN], float *xch, uint
 template <int TBM, int TBN, int STAGES>
 __device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES], v16f (&acc)[2][TBN / 64],
                                                    const PrepArgs &p, int64_t m0, int64_t m_end, int64_t j0,
-                                                   int wave, int lane, bool active) {
+                                                   int wave, int lane, int nit) {
   constexpr int TN = TBN / 64, HB = TBN / 2, NB = HB / 32;
   constexpr int kVals = TN * 16 * 64;   // floats one wavefront hands over
   constexpr int kHs = HB + 8;           // LDS row stride of the x tile, in bf16
@@ -455,8 +459,9 @@ __device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, li = lane & 31;
   float *xch = reinterpret_cast<float *>(&st[0]);
   uint16_t *xs = reinterpret_cast<uint16_t *>(&st[0]);
-  if (wn == 0) silu_x_tile<0, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane, active);
-  else silu_x_tile<1, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane, active);
+  // the wavefront finishing 32-row tile KEEP = wn of its rows
+  if (wn == 0) silu_x_tile<0, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane, nit > 0);
+  else silu_x_tile<1, TN, kHs, kVals>(acc, xch, xs, wave, wm, h, li, lane, nit > 1);
   // blocks of a row sit in adjacent lanes: k-step-major outputs leave as
   // contiguous runs (the tile's columns are one 128-k step when HB = 128)
 #pragma unroll
@@ -504,11 +509,13 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
   if (GROUPED && !grouped_tile<TBM>(a, blockIdx.x, gn, m0, m_end, group, tn)) return;   // uniform: no work
   const int64_t n0 = (int64_t)tn * TBN;
   const ARows arow{a.row_index, m0, m_end, GROUPED, !SILU};
-  // a grouped tile's wavefronts whose 64 rows all lie past the group's end
-  // skip their LDS reads and MFMAs (they still issue their share of the
-  // stage loads and meet every barrier); their outputs are not stored, and
-  // the SiLU epilogue does not repair their (zero-gate) values in binary64.
-  const bool active = !GROUPED || m0 + wm * 64 < m_end;
+  // a grouped tile's wavefronts skip the LDS reads and MFMAs of their 32-row
+  // tiles that lie wholly past the group's end (nit of their two take part;
+  // they still issue their share of the stage loads and meet every
+  // barrier); those outputs are not stored, and the SiLU epilogue does not
+  // repair their (zero-gate) values in binary64.
+  const int64_t wr0 = m0 + wm * 64;
+  const int nit = !GROUPED ? 2 : (wr0 >= m_end ? 0 : (wr0 + 32 >= m_end ? 1 : 2));
   const int64_t w_row0 = GROUPED ? group * a.n : 0, w_rows = GROUPED ? (group + 1) * a.n : a.n;
 
   v16f acc[2][TN];
@@ -544,19 +551,22 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
       const int nxt = cur == 0 ? STAGES - 1 : cur - 1;
       issue_stage<TBM, TBN, NW>(R, O, wave, kt + STAGES - 1, st[nxt]);
     }
-    if constexpr (decltype(compute)::value) compute_stage<TBM, TBN>(st[cur], acc, wm, wn, h, li);
+    if constexpr (decltype(compute)::value > 0)
+      compute_stage<TBM, TBN, decltype(compute)::value>(st[cur], acc, wm, wn, h, li);
     cur = cur == STAGES - 1 ? 0 : cur + 1;
   };
   // the branch stays outside the loops, so that the accumulators keep their
   // registers through the loop
-  if (active) {
-    for (int kt = 0; kt < ksteps; ++kt) step(kt, std::true_type{});
-  } else {
-    for (int kt = 0; kt < ksteps; ++kt) step(kt, std::false_type{});
+  if (nit == 2) {
+    for (int kt = 0; kt < ksteps; ++kt) step(kt, std::integral_constant<int, 2>{});
+  } else if (GROUPED && nit == 1) {
+    for (int kt = 0; kt < ksteps; ++kt) step(kt, std::integral_constant<int, 1>{});
+  } else if (GROUPED) {
+    for (int kt = 0; kt < ksteps; ++kt) step(kt, std::integral_constant<int, 0>{});
   }
 
   if constexpr (SILU) {
-    silu_prep_epilogue<TBM, TBN, STAGES>(st, acc, *prep, m0, m_end, n0 / 2, wave, lane, active);
+    silu_prep_epilogue<TBM, TBN, STAGES>(st, acc, *prep, m0, m_end, n0 / 2, wave, lane, nit);
     return;
   }
   // Y leaves with non-temporal stores: nothing here reads it back, and fp32
