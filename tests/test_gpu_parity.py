@@ -414,6 +414,50 @@ def test_grouped_dual_gemm_identity_gather_and_empty_groups():
         check_gemm(y, ref, yabs, k, f"test_grouped_dual_gemm_identity_gather_and_empty_groups {offsets}")
 
 
+# group sizes whose last 128-row tile ends in every 32-row quarter and on its
+# edges: wavefronts with both, one or none of their 32-row tiles in the group
+_RESIDUE_GROUPS = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 161, 192, 255]
+
+
+def test_grouped_dual_gemm_tile_residues():
+    """Groups whose sizes end their last tile in every 32-row quarter (the
+    tiles past a group's end skip their MFMAs and read zeros): every output
+    against the oracle, through a random gather."""
+    k, n = 256, 192
+    sizes = np.array(_RESIDUE_GROUPS, np.int64)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    rows, tokens = int(offsets[-1]), 700
+    x = si.activations("student_t4", tokens, k, 20, 50.0, 91)
+    W = si.weights(len(sizes) * n, k, 92)
+    row_index = np.random.default_rng(93).integers(0, tokens, rows).astype(np.int32)
+    p = oracle.prepare(sq.MXFP4, x, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, W)
+    sp, rs = sq.prepare(dev16(x), None, dense_backbone=True)
+    wq = sq.quantize_weight(dev16(W))
+    ref, yabs = oracle.grouped_dual_gemm_bound(sq.MXFP4, p, row_index, offsets, q, n)
+    y = host(sq.grouped_dual_gemm(sp, rs, wq, torch.from_numpy(offsets).to(DEV), rows,
+                                  row_index=torch.from_numpy(row_index).to(DEV)))
+    check_gemm(y, ref, yabs, k, "test_grouped_dual_gemm_tile_residues")
+
+
+def test_grouped_dual_gemm_silu_prepare_tile_residues():
+    """The fused gate+up form on the same group sizes, FP4-grid inputs: every
+    prepared byte of every grouped row against the oracle."""
+    k, inter = 256, 128
+    sizes = np.array(_RESIDUE_GROUPS, np.int64)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    rows, tokens = int(offsets[-1]), 700
+    xb, wb, _, _, sp, rs, wq = _grouped_silu_grid_case(tokens, k, inter, len(sizes), 1, 131, KSM)
+    row_index = np.random.default_rng(133).integers(0, tokens, rows).astype(np.int32)
+    p = oracle.prepare(sq.MXFP4, xb, None, dense_backbone=True)
+    q = oracle.quantize_weight(sq.MXFP4, wb)
+    _, ref = oracle.grouped_dual_gemm_silu_prepare(sq.MXFP4, p, row_index, offsets, q, inter, dense_backbone=True)
+    osp, ors = sq.grouped_dual_gemm_silu_prepare(sp, rs, wq, torch.from_numpy(offsets).to(DEV), rows,
+                                                 row_index=torch.from_numpy(row_index).to(DEV),
+                                                 dense_backbone=True)
+    _compare_prep("grouped silu residues", osp, ors, ref)
+
+
 def test_grouped_dual_gemm_bad_offsets_stay_inside_y():
     """Offsets that decrease or run past the row count (possible when routing
     on the device goes wrong) are clamped to [0, rows]: Y's neighbours are
