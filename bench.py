@@ -577,6 +577,14 @@ def moe_main(args):
     fused13 = sq.bind_grouped_dual_gemm_silu_prepare(sp, rs, q13, off_d, rows, sp3, rs3, row_index=idx_d)
     gemm2f = sq.bind_grouped_dual_gemm(sp3, rs3, q2, off_d, rows, y2)
 
+    if args.power:
+        # the grouped gate+up GEMM back to back (its operands prepared first),
+        # then the tokens' preparation, beside the FP4 MFMA yardstick
+        import types
+        power_main(types.SimpleNamespace(name="qwen3_30b_a3b_moe_grouped_gate_up"), torch, dev,
+                   [prep], [gemm13], 1)
+        return
+
     def layer():
         prep()
         gemm13()
@@ -748,7 +756,8 @@ def main():
                     help="time the decoder-layer linear chain (SharQ vs bf16 / FP8 vendor GEMMs) instead")
     ap.add_argument("--power", action="store_true",
                     help="sample socket power and engine clocks (amd-smi) while the workload's dual GEMM, "
-                         "its preparation and the FP4 MFMA yardstick each run back to back, and exit")
+                         "its preparation and the FP4 MFMA yardstick each run back to back, and exit "
+                         "(with --moe: the grouped gate+up GEMM and the tokens' preparation)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="convert two rocprofv3 --pmc runs into profiles/traffic.json and exit")
     args = ap.parse_args()
