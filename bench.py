@@ -623,6 +623,23 @@ def moe_main(args):
     print(json.dumps(res), flush=True)
 
 
+def parse_amd_smi_power(text: str):
+    """(socket power W, mean gfx clock MHz over the XCDs) from the CSV that
+    `amd-smi metric -p -c --csv` prints for one GPU (a header line starting
+    `gpu,` and one data line), or None when either is missing."""
+    ls = text.strip().splitlines()
+    hdr = next((l.split(",") for l in ls if l.startswith("gpu,")), None)
+    row = next((l.split(",") for l in ls if l[:1].isdigit()), None)
+    if not hdr or not row or len(hdr) != len(row):
+        return None
+    d = dict(zip(hdr, row))
+    try:
+        clk = [float(d[f"gfx_{i}_clk"]) for i in range(8) if f"gfx_{i}_clk" in d]
+        return float(d["socket_power"]), sum(clk) / len(clk)
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
 def power_main(w: si.Workload, torch, dev, preps, gemms, nsets: int) -> None:
     """Socket power and engine clocks while one kernel runs back to back.
 
@@ -644,17 +661,7 @@ def power_main(w: si.Workload, torch, dev, preps, gemms, nsets: int) -> None:
 
     def read():
         r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--csv"], capture_output=True, text=True)
-        ls = r.stdout.strip().splitlines()
-        hdr = next((l.split(",") for l in ls if l.startswith("gpu,")), None)
-        row = next((l.split(",") for l in ls if l[:1].isdigit()), None)
-        if not hdr or not row or len(hdr) != len(row):
-            return None
-        d = dict(zip(hdr, row))
-        try:
-            clk = [float(d[f"gfx_{i}_clk"]) for i in range(8) if f"gfx_{i}_clk" in d]
-            return float(d["socket_power"]), sum(clk) / len(clk)
-        except (KeyError, ValueError, ZeroDivisionError):
-            return None
+        return parse_amd_smi_power(r.stdout)
 
     def sampler():
         while not stop.is_set():

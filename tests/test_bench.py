@@ -27,6 +27,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""
 
 
+def test_amd_smi_power_parser():
+    """The power sampler's reading of `amd-smi metric -p -c --csv`: socket power
+    and the mean of the XCD clocks; None when the tool printed no data line."""
+    hdr = "gpu,socket_power,gfx_voltage," + ",".join(f"gfx_{i}_clk,gfx_{i}_min_clk" for i in range(8)) + ",mem_0_clk"
+    row = "0,1381,N/A," + ",".join(f"{1700 + 10 * i},500" for i in range(8)) + ",2000"
+    p, c = bench.parse_amd_smi_power(hdr + "\n" + row + "\n")
+    assert p == 1381.0 and c == 1735.0
+    assert bench.parse_amd_smi_power("WARNING: no data\n") is None
+    assert bench.parse_amd_smi_power(hdr + "\n") is None
+    assert bench.parse_amd_smi_power(hdr + "\n0,N/A,N/A," + ",".join("1700,500" for _ in range(8)) + ",2000") is None
+
+
 def test_preparation_bytes_per_element():
     assert bench.prep_bytes_per_elem(si.MXFP4) == 2.9375
     assert bench.prep_bytes_per_elem(si.NVFP4) == 3.0
