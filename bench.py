@@ -69,12 +69,12 @@ def prep_bytes_per_elem(fmt: int) -> float:
     return 2.0 + 0.25 + 0.125 + 0.5 + (2.0 / 32 if fmt == si.MXFP4 else 2.0 / 16)
 
 
-def gemm_bytes(w: si.Workload) -> float:
+def gemm_bytes(w: si.Workload, y_bytes: float = 4.0) -> float:
     m, n, k = w.m, w.n, w.k
     blk = 32 if w.fmt == si.MXFP4 else 16
     a = m * k * (0.25 + 0.125 + 0.5) + 2 * m * k / blk
     wb = n * k * 0.5 + n * k / blk
-    return a + wb + 4.0 * m * n
+    return a + wb + y_bytes * m * n
 
 
 def source_hash(*names) -> str:
@@ -91,9 +91,9 @@ def kernel_sources(fmt: int):
             ("prep.hip", "prep_block.h", "fp4_device.h", "kernels.h"))
 
 
-def traffic_key(kind: str, w: si.Workload, variant: int, dense_view: bool) -> str:
+def traffic_key(kind: str, w: si.Workload, variant: int, dense_view: bool, bf16_out: bool = False) -> str:
     if kind == "dual_gemm":
-        return f"dual_gemm/{w.name}/v{variant}"
+        return f"dual_gemm/{w.name}/v{variant}" + ("/bf16_out" if bf16_out else "")
     return f"prepare/{w.name}/{'dense' if dense_view else 'nodense'}"
 
 
@@ -156,7 +156,7 @@ def traffic_convert(args, w: si.Workload):
     f, wr = res["FETCH_SIZE"], res["WRITE_SIZE"]
     gemm_src, prep_src = kernel_sources(w.fmt)
     entries = {
-        traffic_key("dual_gemm", w, args.variant, not args.no_dense_view): {
+        traffic_key("dual_gemm", w, args.variant, not args.no_dense_view, args.bf16_out): {
             "source_hash": source_hash(*gemm_src),
             "fetch_kib": round(f["gemm_kib"], 1), "write_kib": round(wr["gemm_kib"], 1),
             "bytes_per_launch": round(f["gemm_kib"] * 1024 * f["factor"] + wr["gemm_kib"] * 1024 * wr["factor"]),
@@ -399,7 +399,7 @@ def chain_main(args):
               "unit": "us", "higher_is_better": False, "layers_cycled": CHAIN_LAYERS,
               "steps": reps, "warmup": warm, "data": "synthetic (seeded activations, N(0,0.02) weights)"}
     for phase, m in (("prefill", 2048), ("decode", 16)):
-        runs = {"sharq": [], "bf16": [], "fp8": [], "fp8_with_act_quant": []}
+        runs = {"sharq": [], "sharq_bf16_out": [], "bf16": [], "fp8": [], "fp8_with_act_quant": []}
         per = {}
         for lin in si.LAYER_LINEARS:
             w = si.layer_workload(lin, m)
@@ -413,8 +413,18 @@ def chain_main(args):
             y = torch.empty((m, w.n), dtype=torch.float32, device=dev)
             calls = [(sq.bind_prepare(x, g, 1e-5, sp, rs), sq.bind_dual_gemm(sp, rs, wq[l], y))
                      for l in range(CHAIN_LAYERS)]
+            # the same with Y stored in bf16 (sharq_dual_gemm_bf16), the
+            # output type the vendor GEMMs below write
+            y16 = torch.empty((m, w.n), dtype=torch.bfloat16, device=dev)
+            calls16 = [(sq.bind_prepare(x, g, 1e-5, sp, rs), sq.bind_dual_gemm(sp, rs, wq[l], y16))
+                       for l in range(CHAIN_LAYERS)]
 
             def sharq(i, calls=calls):
+                p, q = calls[i % CHAIN_LAYERS]
+                p()
+                q()
+
+            def sharq16(i, calls=calls16):
                 p, q = calls[i % CHAIN_LAYERS]
                 p()
                 q()
@@ -430,7 +440,7 @@ def chain_main(args):
                 q8 = (xb / s_).to(fp8)
                 torch._scaled_mm(q8, w8[i % CHAIN_LAYERS].t(), s_, ws[i % CHAIN_LAYERS], out_dtype=torch.bfloat16)
 
-            fns = {"sharq": sharq, "bf16": bf16, "fp8": f8, "fp8_with_act_quant": f8q}
+            fns = {"sharq": sharq, "sharq_bf16_out": sharq16, "bf16": bf16, "fp8": f8, "fp8_with_act_quant": f8q}
             per[lin] = {}
             for k, fn in fns.items():
                 try:
@@ -498,13 +508,21 @@ def chain_main(args):
             gu_calls = [(lambda q=sq.bind_dual_gemm(spg, rsg, wts["gate_up"][3][l], ygu): (q(), silu_p()))
                         for l in range(CHAIN_LAYERS)]
         down_calls = [sq.bind_dual_gemm(spx, rsx, wts["down"][3][l], yd) for l in range(CHAIN_LAYERS)]
+        yd16 = torch.empty((m, si.LAYER_LINEARS["down"][1]), dtype=torch.bfloat16, device=dev)
+        down_calls16 = [sq.bind_dual_gemm(spx, rsx, wts["down"][3][l], yd16) for l in range(CHAIN_LAYERS)]
 
         def mlp(i):
             prep_g()
             gu_calls[i % CHAIN_LAYERS]()
             down_calls[i % CHAIN_LAYERS]()
 
-        per["gate_up_silu_down"] = {"sharq_fused": round(batch_us(mlp), 2)}
+        def mlp16(i):
+            prep_g()
+            gu_calls[i % CHAIN_LAYERS]()
+            down_calls16[i % CHAIN_LAYERS]()
+
+        per["gate_up_silu_down"] = {"sharq_fused": round(batch_us(mlp), 2),
+                                    "sharq_fused_bf16_out": round(batch_us(mlp16), 2)}
         chain = {}
         for k, fns in runs.items():
             if fns is not None and len(fns) == len(si.LAYER_LINEARS):
@@ -512,8 +530,14 @@ def chain_main(args):
         if runs["sharq"] is not None:
             layer = runs["sharq"][:2] + [mlp]
             chain["sharq_with_silu_fused"] = round(batch_us(lambda i: [fn(i) for fn in layer]), 2)
+        if runs["sharq_bf16_out"] is not None:
+            layer16 = runs["sharq_bf16_out"][:2] + [mlp16]
+            chain["sharq_with_silu_fused_bf16_out"] = round(batch_us(lambda i: [fn(i) for fn in layer16]), 2)
         speed = {f"sharq_speedup_vs_{k}": round(chain[k] / chain["sharq"], 3)
                  for k in chain if not k.startswith("sharq")}
+        if "sharq_bf16_out" in chain:
+            speed.update({f"sharq_bf16_out_speedup_vs_{k}": round(chain[k] / chain["sharq_bf16_out"], 3)
+                          for k in chain if not k.startswith("sharq")})
         result[phase] = {"m": m, "chain_us": chain, "per_linear_us": per, **speed,
                          "qkv_residual_add_and_prepare": residual_add,
                          "down_silu_mul_and_prepare": silu_mul}
@@ -750,6 +774,8 @@ def main():
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--no-dense-view", action="store_true",
                     help="prepare writes only the 2:4 backbone; the GEMM expands it")
+    ap.add_argument("--bf16-out", action="store_true",
+                    help="the dual GEMM writes Y in bf16 (sharq_dual_gemm_bf16) instead of fp32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="time only the CPU oracle on the workload (no GPU work) and print its JSON")
@@ -798,7 +824,8 @@ def main():
 
     x_np, W_np, g_np = si.workload_x(w), si.workload_w(w), si.workload_gamma(w)
     blk = sq.BLOCK[w.fmt]
-    per_set = w.m * w.k * (2 + 0.9375) + w.n * w.k * 0.53 + 4.0 * w.m * w.n
+    y_bytes = 2.0 if args.bf16_out else 4.0
+    per_set = w.m * w.k * (2 + 0.9375) + w.n * w.k * 0.53 + y_bytes * w.m * w.n
     nsets = int(min(16, max(2, np.ceil(2 * LLC_BYTES / per_set))))
 
     x0 = torch.from_numpy(x_np.view(np.int16)).to(dev)
@@ -809,7 +836,7 @@ def main():
         xi = x0.clone()
         wq = sq.quantize_weight(W0.clone() if i else W0, w.fmt)
         sp, rs = sq.alloc_prepared(w.fmt, w.m, w.k, dev, dense_backbone=not args.no_dense_view)
-        y = torch.empty((w.m, w.n), dtype=torch.float32, device=dev)
+        y = torch.empty((w.m, w.n), dtype=torch.bfloat16 if args.bf16_out else torch.float32, device=dev)
         sets.append((xi, wq, sp, rs, y))
     torch.cuda.synchronize()
 
@@ -886,11 +913,11 @@ def main():
 
     gemm_src, prep_src = kernel_sources(w.fmt)
     dense_view = not args.no_dense_view
-    gemm_traffic = traffic_from_profiles(traffic_key("dual_gemm", w, args.variant, dense_view),
+    gemm_traffic = traffic_from_profiles(traffic_key("dual_gemm", w, args.variant, dense_view, args.bf16_out),
                                          source_hash(*gemm_src))
     prep_traffic = traffic_from_profiles(traffic_key("prepare", w, args.variant, dense_view),
                                          source_hash(*prep_src))
-    gbytes = gemm_bytes(w)
+    gbytes = gemm_bytes(w, y_bytes)
     if w.m <= 64:
         # decode: the GEMM streams W once; HBM bandwidth bounds it
         gemm_gbps = gbytes / (gemm_ms * 1e-3) / 1e9
@@ -928,6 +955,7 @@ def main():
                                f"{'MXFP4' if w.fmt == sq.MXFP4 else 'NVFP4-style'}",
                    "m": w.m, "n": w.n, "k": w.k, "gemm_variant": args.variant,
                    "backbone_dense_view": not args.no_dense_view,
+                   "y_dtype": "bf16" if args.bf16_out else "fp32",
                    "buffer_sets": nsets},
         "roofline": roofline,
         "roofline_prep": {"bound": "hbm", "kernel": "prepare", "achieved": round(prep_gbps, 1),

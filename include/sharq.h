@@ -341,6 +341,27 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sparse,
                              float *y, int64_t ld_y, sharq_gemm_variant variant, void *stream);
 
 /*
+ * sharq_dual_gemm with a bf16 output (abstract, sentences 4 and 5: the same
+ * dual-path product; the bf16 store is the epilogue a decoder layer's next
+ * step reads, e.g. attention after QKV or the residual add after O and
+ * down).  Y is accumulated in fp32 exactly as sharq_dual_gemm accumulates it
+ * (same kernels, same summation order, same variants and AUTO choice) and
+ * each value is rounded once to bf16, to nearest with ties to even, and
+ * stored as its bit pattern into y_bf16 [m, n] (row stride ld_y elements).
+ * So y_bf16 equals, bit for bit, the bf16 rounding of what sharq_dual_gemm
+ * writes for the same inputs.  The rounding adds up to 2^-8 of |Y| per
+ * value, more than the 1e-3 normwise budget of the fp32 output: use
+ * sharq_dual_gemm where that budget matters.
+ * Requirements: those of sharq_dual_gemm, with y_bf16 2-byte aligned.
+ * Errors as sharq_dual_gemm (y_bf16 NULL: SHARQ_ERR_NULL).
+ */
+sharq_status sharq_dual_gemm_bf16(sharq_format fmt, const sharq_fp4_view *sparse,
+                                  const sharq_fp4_view *resid, const sharq_fp4_view *w_sparse_view,
+                                  const sharq_fp4_view *w_dense_view, int64_t m, int64_t n,
+                                  int64_t k, uint16_t *y_bf16, int64_t ld_y,
+                                  sharq_gemm_variant variant, void *stream);
+
+/*
  * Grouped dual GEMM: the expert GEMMs of a mixture-of-experts layer in one
  * launch (each expert's product is sharq_dual_gemm's, abstract, sentences 4
  * and 5).  The activations are prepared once per token (sparse, resid:
@@ -400,7 +421,7 @@ const char *sharq_status_str(sharq_status status);
 /* ABI version of this header (increments on any incompatible change). */
 int sharq_abi_version(void);
 
-#define SHARQ_ABI_VERSION 10
+#define SHARQ_ABI_VERSION 11
 
 #ifdef __cplusplus
 }

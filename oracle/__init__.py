@@ -71,6 +71,8 @@ def _declare(L):
     L.oracle_dual_gemm.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, P, P, I64, I64, I64,
                                    P, P, P]
     L.oracle_dual_gemm.restype = ctypes.c_int
+    L.oracle_round_bf16.argtypes = [P, I64, P]
+    L.oracle_round_bf16.restype = None
     L.oracle_threads.argtypes = [ctypes.c_int]
     L.oracle_threads.restype = ctypes.c_int
     return L
@@ -363,6 +365,21 @@ def _dual_gemm(fmt, prep, wq, want_f64, want_abs, L=None):
 def dual_gemm(fmt: int, prep: dict, wq: dict, want_f64: bool = False, L=None):
     y, y64, _ = _dual_gemm(fmt, prep, wq, want_f64, False, L)
     return (y, y64) if want_f64 else y
+
+
+def round_bf16(y) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp32 values, each rounded once to nearest
+    even (oracle_round_bf16)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, np.uint16)
+    lib().oracle_round_bf16(_p(y), y.size, _p(out))
+    return out
+
+
+def dual_gemm_bf16(fmt: int, prep: dict, wq: dict) -> np.ndarray:
+    """The dual GEMM's bf16 output: the fp32 Y of ``dual_gemm`` rounded once to
+    bf16 (bit patterns, uint16 [m, n])."""
+    return round_bf16(dual_gemm(fmt, prep, wq))
 
 
 def dual_gemm_bound(fmt: int, prep: dict, wq: dict):

@@ -62,6 +62,19 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+/*
+ * A bf16 output of the dual GEMM: each fp32 value of Y rounded to bf16 once,
+ * to nearest with ties to even (oracle_f32_to_bf16).  Reading: the abstract
+ * (sentence 4) sums both paths into one fp32-accumulated output; a bf16
+ * output is that fp32 sum rounded once, which is what storing the fp32
+ * result in bf16 gives.  Y is finite here, so no NaN or overflow case arises.
+ */
+void oracle_round_bf16(const float *y, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_bf16(y[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* Element and scale codecs (OCP MX v1.0 E2M1 / E8M0, OCP FP8 E4M3)     */
 /* ------------------------------------------------------------------ */

@@ -42,8 +42,8 @@ LIB_PATH = os.path.join(_HERE, "libsharq.so")
 EXPORTS = ("sharq_quantize_weight", "sharq_prepare", "sharq_prepare_residual", "sharq_prepare_silu_mul",
            "sharq_dual_gemm", "sharq_dual_gemm_silu_prepare", "sharq_grouped_dual_gemm",
            "sharq_grouped_dual_gemm_silu_prepare", "sharq_bytes", "sharq_status_str", "sharq_abi_version",
-           "sharq_prepare_noalloc")
-ABI_VERSION = 10
+           "sharq_prepare_noalloc", "sharq_dual_gemm_bf16")
+ABI_VERSION = 11
 
 
 class SharqError(RuntimeError):
@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.sharq_dual_gemm.argtypes = [ctypes.c_int, V, V, V, V, I64, I64, I64, P, I64,
                                       ctypes.c_int, P]
         L.sharq_dual_gemm.restype = ctypes.c_int
+        L.sharq_dual_gemm_bf16.argtypes = [ctypes.c_int, V, V, V, V, I64, I64, I64, P, I64,
+                                           ctypes.c_int, P]
+        L.sharq_dual_gemm_bf16.restype = ctypes.c_int
         L.sharq_bytes.argtypes = [ctypes.c_int, ctypes.c_int, I64, I64]
         L.sharq_bytes.restype = ctypes.c_size_t
         L.sharq_status_str.argtypes = [ctypes.c_int]
@@ -415,9 +418,12 @@ def prepare_silu_mul(gate, up, dense_backbone: bool = False, layout: Optional[in
 
 def bind_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, out, variant: int = GEMM_AUTO,
                    w_dense_scales=None, stream=None) -> BoundCall:
-    """sharq_dual_gemm into `out` (fp32 [m, n]), bound for repeated calls."""
+    """sharq_dual_gemm into `out` (fp32 [m, n]), or sharq_dual_gemm_bf16 when
+    `out` is bfloat16, bound for repeated calls."""
     m, k, n = sp.rows, sp.k, w.rows
-    out = _f32(out)
+    torch = _torch()
+    bf16_out = out.dtype == torch.bfloat16
+    out = _bits16(out) if bf16_out else _f32(out)
     if out.dim() != 2 or tuple(out.shape) != (m, n):
         raise ValueError(f"out must be [{m}, {n}]")
     wv_s = w.view()
@@ -431,16 +437,21 @@ def bind_dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, out, variant: int
     args = (ctypes.c_int(sp.fmt), ctypes.byref(vs), ctypes.byref(vr), ctypes.byref(wv_s), ctypes.byref(wv_d),
             ctypes.c_int64(m), ctypes.c_int64(n), ctypes.c_int64(k), ctypes.c_void_p(out.data_ptr()),
             ctypes.c_int64(_ld(out)), ctypes.c_int(variant), _stream_ptr(stream))
-    return BoundCall(lib().sharq_dual_gemm, args, "sharq_dual_gemm",
-                     (sp, rs, w, out, w_dense_scales, vs, vr, wv_s, wv_d))
+    name = "sharq_dual_gemm_bf16" if bf16_out else "sharq_dual_gemm"
+    return BoundCall(getattr(lib(), name), args, name, (sp, rs, w, out, w_dense_scales, vs, vr, wv_s, wv_d))
 
 
 def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AUTO,
-              w_dense_scales=None, out=None, stream=None):
-    """Y = deq(backbone) deq(W)^T + deq(residual) deq(W)^T, fp32 [m, n]."""
+              w_dense_scales=None, out=None, stream=None, out_dtype=None):
+    """Y = deq(backbone) deq(W)^T + deq(residual) deq(W)^T, [m, n]: fp32, or
+    bf16 (each fp32 value rounded to nearest even) when out_dtype or `out`
+    is torch.bfloat16."""
     torch = _torch()
     if out is None:
-        out = torch.empty((sp.rows, w.rows), dtype=torch.float32, device=w.codes.device)
+        dt = torch.float32 if out_dtype is None else out_dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise TypeError(f"out_dtype must be float32 or bfloat16, got {dt}")
+        out = torch.empty((sp.rows, w.rows), dtype=dt, device=w.codes.device)
     bind_dual_gemm(sp, rs, w, out, variant, w_dense_scales, stream)()
     return out
 

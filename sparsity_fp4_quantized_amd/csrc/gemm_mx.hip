@@ -490,7 +490,7 @@ __device__ __forceinline__ void silu_prep_epilogue(DStage<TBM, TBN> (&st)[STAGES
 // One tile of the dense-operand GEMM.  SILU: a gate+up tile whose epilogue is
 // silu_prep_epilogue (W's rows: n / 2 gate rows, then n / 2 up rows) instead
 // of the fp32 Y stores.
-template <int TBM, int TBN, int NW, int STAGES, bool GROUPED, bool SILU>
+template <int TBM, int TBN, int NW, int STAGES, bool GROUPED, bool SILU, bool BF16 = false>
 __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, const PrepArgs *prep) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
   static_assert(!GROUPED || 64 * NW == 256, "the group scan takes one thread a group: 256 threads, 256 groups");
@@ -572,12 +572,19 @@ __device__ __forceinline__ void dense_tile(const GemmArgs &a, uint32_t band, con
   // Y leaves with non-temporal stores: nothing here reads it back, and fp32
   // tiles left dirty in the L2s (qkv shape: 50 MB against 32 MB of L2) slowed
   // the kernel's end and the next kernel's start (qkv GEMM 55.5 -> 52.9 us).
-  store_tile<TBM, TBN>(a.y, a.ld_y, m0, n0, m_end, a.n, wm, wn, h, li, acc, 1.0f);
+  // BF16 (sharq_dual_gemm_bf16): the same values rounded to bf16, in
+  // instances of their own (the conversion's registers would otherwise count
+  // against every fp32 instance: 128 x 256 grouped tiles went from two
+  // wavefronts per SIMD to one)
+  if constexpr (BF16)
+    store_tile_bf16<TBM, TBN>(a.y16, a.ld_y, m0, n0, m_end, a.n, wm, wn, h, li, acc, 1.0f);
+  else
+    store_tile<TBM, TBN>(a.y, a.ld_y, m0, n0, m_end, a.n, wm, wn, h, li, acc, 1.0f);
 }
 
-template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false>
+template <int TBM, int TBN, int NW, int STAGES, bool GROUPED = false, bool BF16 = false>
 __global__ __launch_bounds__(64 * NW) void dual_gemm_dense_kernel(GemmArgs a, uint32_t band) {
-  dense_tile<TBM, TBN, NW, STAGES, GROUPED, false>(a, band, nullptr);
+  dense_tile<TBM, TBN, NW, STAGES, GROUPED, false, BF16>(a, band, nullptr);
 }
 
 // The gate+up projection with SiLU(gate) * up and the down projection's
@@ -601,8 +608,11 @@ void launch_grouped(const GemmArgs &a, hipStream_t s) {
 template <int TBM, int TBN, int NW, int STAGES>
 void launch_dense(const GemmArgs &a, hipStream_t s) {
   const int64_t gm = (a.m + TBM - 1) / TBM, gn = (a.n + TBN - 1) / TBN;
-  dual_gemm_dense_kernel<TBM, TBN, NW, STAGES>
-      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, TBN <= 128 ? 3 : 2));
+  const uint32_t band = xcd_band_rows(gm, gn, TBM, TBN, TBN <= 128 ? 3 : 2);
+  if (a.y16)
+    dual_gemm_dense_kernel<TBM, TBN, NW, STAGES, false, true><<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, band);
+  else
+    dual_gemm_dense_kernel<TBM, TBN, NW, STAGES><<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, band);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,7 +780,7 @@ struct ExpandSide {
   }
 };
 
-template <int TBM, int TBN, int NW>
+template <int TBM, int TBN, int NW, bool BF16 = false>
 __global__ __launch_bounds__(64 * NW) void dual_gemm_decomp_kernel(GemmArgs a, uint32_t band) {
   static_assert(TBM == 32 * NW, "two 32-row tiles per wavefront, two wavefronts per column");
   constexpr int TN = TBN / 64;
@@ -828,7 +838,7 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_decomp_kernel(GemmArgs a, u
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < a.m) __builtin_nontemporal_store(acc[it][jt][r], &a.y[row * a.ld_y + col]);
+        if (row < a.m) put_y<true>(a.y, BF16 ? a.y16 : nullptr, row * a.ld_y + col, acc[it][jt][r]);
       }
     }
 }
@@ -836,8 +846,11 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_decomp_kernel(GemmArgs a, u
 template <int TBM, int TBN, int NW>
 void launch_decomp(const GemmArgs &a, hipStream_t s) {
   const int64_t gm = (a.m + TBM - 1) / TBM, gn = (a.n + TBN - 1) / TBN;
-  dual_gemm_decomp_kernel<TBM, TBN, NW>
-      <<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, xcd_band_rows(gm, gn, TBM, TBN, TBN >= 256 ? 1 : 2));
+  const uint32_t band = xcd_band_rows(gm, gn, TBM, TBN, TBN >= 256 ? 1 : 2);
+  if (a.y16)
+    dual_gemm_decomp_kernel<TBM, TBN, NW, true><<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, band);
+  else
+    dual_gemm_decomp_kernel<TBM, TBN, NW><<<dim3((unsigned)(gm * gn)), dim3(64 * NW), 0, s>>>(a, band);
 }
 
 
@@ -949,7 +962,7 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_skinny_kernel(GemmArgs a) {
       for (int width = NW / 2; width >= 1; width >>= 1)
 #pragma unroll
         for (int w = 0; w < width; ++w) v[w] = v[2 * w] + v[2 * w + 1];
-      if (row < a.m) a.y[row * a.ld_y + ocol] = v[0];
+      if (row < a.m) put_y<false>(a.y, a.y16, row * a.ld_y + ocol, v[0]);
     }
   }
 }
@@ -1065,7 +1078,7 @@ __global__ __launch_bounds__(256) void dual_gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row < a.m) a.y[row * a.ld_y + col] = acc[r];
+      if (row < a.m) put_y<false>(a.y, a.y16, row * a.ld_y + col, acc[r]);
     }
   }
 }

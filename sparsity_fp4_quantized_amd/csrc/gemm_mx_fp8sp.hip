@@ -401,7 +401,7 @@ __global__ __launch_bounds__(64 * NW, 2) void dual_gemm_fp8sp_kernel(GemmArgs a,
         if (row >= a.m) continue;
         float v = acc_r[it][jt][r];
         if (fp8) v += __builtin_ldexpf(acc_s[it][jt][r], ref_a[rl] + ew);
-        __builtin_nontemporal_store(v, &a.y[row * a.ld_y + col]);
+        put_y<true>(a.y, a.y16, row * a.ld_y + col, v);
       }
     }
 }

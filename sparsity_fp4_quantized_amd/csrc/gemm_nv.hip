@@ -442,7 +442,8 @@ __global__ __launch_bounds__(64 * NW) void dual_gemm_nv_kernel(GemmArgs a, uint3
   }
 
   const float ts = a.a_tensor_scale[0] * a.w_tensor_scale[0];
-  store_tile<TBM, TBN>(a.y, a.ld_y, m0, n0, a.m, a.n, wm, wn, h, li, acc, ts);
+  if (a.y16) store_tile_bf16<TBM, TBN>(a.y16, a.ld_y, m0, n0, a.m, a.n, wm, wn, h, li, acc, ts);
+  else store_tile<TBM, TBN>(a.y, a.ld_y, m0, n0, a.m, a.n, wm, wn, h, li, acc, ts);
 }
 
 template <int TBN, int STAGES, int BB>

@@ -56,7 +56,7 @@ struct GemmArgs {
   const uint8_t *wd_scales; int64_t ld_wds; // dense-path scale view of W
   const float *a_tensor_scale;              // NVFP4
   const float *w_tensor_scale;              // NVFP4
-  float *y;                int64_t ld_y;
+  float *y;                int64_t ld_y;      // fp32 Y [m, n] (null when y16 is set)
   int64_t m, n, k;
   int s_ksm, r_ksm, w_ksm;   // per operand (codes, meta, dense view, scales): k-step-major
   // grouped GEMM (mixture of experts): m = grouped rows in total; grouped row
@@ -66,6 +66,9 @@ struct GemmArgs {
   const int32_t *row_index = nullptr;
   const int64_t *group_off = nullptr;
   int64_t groups = 0, tokens = 0;
+  // bf16 Y [m, n] (row stride ld_y elements) in place of y: each value the
+  // bf16 rounding (nearest even) of the fp32 value y would receive
+  uint16_t *y16 = nullptr;
 };
 
 // Offset of the bytes of row r in 128-k step t of an operand array with `bps`

@@ -333,13 +333,19 @@ sharq_status sharq_grouped_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp,
   return from_hip(sharq::launch_grouped_dual_gemm_mx(a, static_cast<hipStream_t>(stream)));
 }
 
-sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,
-                             const sharq_fp4_view *wsv, const sharq_fp4_view *wdv, int64_t m,
-                             int64_t n, int64_t k, float *y, int64_t ld_y,
-                             sharq_gemm_variant variant, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by sharq_dual_gemm (fp32 Y) and
+// sharq_dual_gemm_bf16 (y16: bf16 Y); exactly one of y and y16 is set.
+sharq_status dual_gemm_common(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,
+                              const sharq_fp4_view *wsv, const sharq_fp4_view *wdv, int64_t m,
+                              int64_t n, int64_t k, float *y, uint16_t *y16, int64_t ld_y,
+                              sharq_gemm_variant variant, void *stream) {
   if (!valid_format(fmt)) return SHARQ_ERR_UNSUPPORTED;
   if (variant < SHARQ_GEMM_AUTO || variant > SHARQ_GEMM_SPARSE_MFMA) return SHARQ_ERR_UNSUPPORTED;
-  if (!sp || !rs || !wsv || !wdv || !y) return SHARQ_ERR_NULL;
+  if (!sp || !rs || !wsv || !wdv || (!y && !y16)) return SHARQ_ERR_NULL;
   if (m < 1 || n < 1 || k < 128 || k % 128 || ld_y < n) return SHARQ_ERR_SHAPE;
   CHECK(check_layout(sp, k));
   CHECK(check_layout(rs, k));
@@ -363,7 +369,7 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
   }
   CHECK(check_array(rs->codes, rs->ld_codes, rs->layout, m, k, k / 2, 16, 64, 16));
   CHECK(check_array(wsv->codes, wsv->ld_codes, wsv->layout, n, k, k / 2, 16, 64, 16));
-  if (!aligned(y, 4)) return SHARQ_ERR_ALIGN;
+  if (y ? !aligned(y, 4) : !aligned(y16, 2)) return SHARQ_ERR_ALIGN;
   CHECK(check_scales(fmt, sp, m, k, true));
   CHECK(check_scales(fmt, rs, m, k, true));
   CHECK(check_scales(fmt, wsv, n, k, true));
@@ -377,11 +383,33 @@ sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const s
              wsv->codes, wsv->ld_codes, wsv->scales, wsv->ld_scales, wdv->scales, wdv->ld_scales,
              sp->tensor_scale, wsv->tensor_scale, y, ld_y, m, n, k,
              ksm(sp), ksm(rs), ksm(wsv)};
+  a.y16 = y16;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fmt == SHARQ_MXFP4 && variant == SHARQ_GEMM_SPARSE_MFMA) return from_hip(sharq::launch_dual_gemm_mx_fp8sp(a, s));
   if (fmt == SHARQ_MXFP4) return from_hip(sharq::launch_dual_gemm_mx(a, dense_expanded, s));
   const int v = variant == SHARQ_GEMM_SPARSE_MFMA ? 3 : dense_expanded ? 2 : 1;
   return from_hip(sharq::launch_dual_gemm_nv(a, v, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+sharq_status sharq_dual_gemm(sharq_format fmt, const sharq_fp4_view *sp, const sharq_fp4_view *rs,
+                             const sharq_fp4_view *wsv, const sharq_fp4_view *wdv, int64_t m,
+                             int64_t n, int64_t k, float *y, int64_t ld_y,
+                             sharq_gemm_variant variant, void *stream) {
+  if (!y) return SHARQ_ERR_NULL;
+  return dual_gemm_common(fmt, sp, rs, wsv, wdv, m, n, k, y, nullptr, ld_y, variant, stream);
+}
+
+sharq_status sharq_dual_gemm_bf16(sharq_format fmt, const sharq_fp4_view *sp,
+                                  const sharq_fp4_view *rs, const sharq_fp4_view *wsv,
+                                  const sharq_fp4_view *wdv, int64_t m, int64_t n, int64_t k,
+                                  uint16_t *y_bf16, int64_t ld_y, sharq_gemm_variant variant,
+                                  void *stream) {
+  if (!y_bf16) return SHARQ_ERR_NULL;
+  return dual_gemm_common(fmt, sp, rs, wsv, wdv, m, n, k, nullptr, y_bf16, ld_y, variant, stream);
 }
 
 }  // extern "C"

@@ -49,3 +49,32 @@ def check_gemm(y, ref, yabs, k: int, label: str = "") -> float:
     key = label.split(" ")[0] if label else "gemm"
     WORST[key] = max(WORST.get(key, 0.0), ratio)
     return ratio
+
+
+def bf16_value(bits) -> np.ndarray:
+    """float64 values of bf16 bit patterns."""
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_gemm_bf16(y16, ref, yabs, k: int, label: str = ""):
+    """bf16 outputs (bit patterns): each must be the bf16 rounding, nearest
+    even, of a value within the element-wise fp32 bound of the oracle's Y
+    (|dY| <= 4 K 2^-24 sum|a w|).  Rounding is monotone, so that holds exactly
+    when the output lies between the roundings of the bound's two ends (each
+    end widened by one fp32 ulp for its own rounding to fp32)."""
+    import oracle
+    y16 = np.asarray(y16)
+    ref = np.asarray(ref, np.float64)
+    b = 4.0 * k * UNIT * np.asarray(yabs, np.float64)
+    assert y16.shape == ref.shape, (label, y16.shape, ref.shape)
+    y = bf16_value(y16)
+    assert np.isfinite(y).all(), (label, "non-finite output")
+    lo = np.nextafter((ref - b).astype(np.float32), np.float32(-np.inf))
+    hi = np.nextafter((ref + b).astype(np.float32), np.float32(np.inf))
+    lo_b, hi_b = bf16_value(oracle.round_bf16(lo)), bf16_value(oracle.round_bf16(hi))
+    ok = (lo_b <= y) & (y <= hi_b)
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{label}: {int((~ok).sum())} bf16 outputs outside the rounded bound; first at {i}: "
+                             f"gpu {y[i]!r} oracle {ref[i]!r} allowed [{lo_b[i]!r}, {hi_b[i]!r}]")
+

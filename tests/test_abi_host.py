@@ -308,6 +308,31 @@ def test_gemm_validation(kwargs, status):
     assert gemm(**kwargs) == status
 
 
+def gemm_bf16(fmt=0, m=16, n=256, k=256, y=FAKE, ld_y=256, variant=0):
+    sp, rs, ws, wd = view(ld_codes=64), view(meta=None), view(meta=None), view(meta=None)
+    return sq.lib().sharq_dual_gemm_bf16(fmt, ctypes.byref(sp), ctypes.byref(rs), ctypes.byref(ws),
+                                         ctypes.byref(wd), m, n, k, y, ld_y, variant, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(y=None), sq.ERR_NULL),
+    (dict(y=FAKE + 1), sq.ERR_ALIGN),        # bf16 output: 2-byte alignment
+    (dict(ld_y=255), sq.ERR_SHAPE),
+    (dict(k=192), sq.ERR_SHAPE),
+    (dict(variant=9), sq.ERR_UNSUPPORTED),
+    (dict(fmt=1), sq.ERR_SHAPE),
+])
+def test_gemm_bf16_validation(kwargs, status):
+    assert gemm_bf16(**kwargs) == status
+
+
+def test_gemm_bf16_output_alignment_is_two_bytes():
+    """A 2-byte aligned bf16 output passes the output checks (the call then
+    fails on the views: m = 0 rows, refused before any launch)."""
+    assert gemm_bf16(y=FAKE + 2, m=0) == sq.ERR_SHAPE
+    assert gemm(y=FAKE + 2) == sq.ERR_ALIGN
+
+
 def test_quantize_weight_validation():
     L = sq.lib()
     v = view(meta=None)

@@ -129,6 +129,46 @@ def test_bf16_rounding_matches_torch():
     assert (si.f32_to_bf16_bits(f) == want).all()
 
 
+def test_round_bf16_array_matches_torch():
+    """oracle.round_bf16 (the dual GEMM's bf16 output) against torch's fp32 ->
+    bf16 conversion on every pattern class: random finite fp32, exact ties
+    with even and odd kept bits, subnormals, values that round up into the
+    next binade, and values past the largest bf16 that round to infinity."""
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 1 << 32, 300000, dtype=np.uint64).astype(np.uint32)
+    hi = rng.integers(0, 1 << 16, 20000, dtype=np.uint32) << 16
+    special = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001, hi | 0xFFFF,
+                              rng.integers(0, 1 << 23, 5000, dtype=np.uint32),
+                              np.array([0x7F7F8000, 0x7F7FFFFF, 0x7F7F7FFF, 0xFF7F8000, 0x00000000,
+                                        0x80000000, 0x00008000, 0x00018000], np.uint32)])
+    allb = np.concatenate([bits, special]).astype(np.uint32)
+    allb = allb[(allb & 0x7F800000) != 0x7F800000]
+    f = allb.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round_bf16(f), want)
+    n2 = f.size // 7 * 7       # a 2-D array keeps its shape
+    assert np.array_equal(oracle.round_bf16(f[:n2].reshape(-1, 7)), want[:n2].reshape(-1, 7))
+
+
+def test_dual_gemm_bf16_exact_product():
+    """FP4-grid X and W: the dual GEMM is exact in fp32, so its bf16 output is
+    the bf16 rounding (torch's) of the exact product X W^T (numpy, fp64)."""
+    m, k, n = 24, 256, 40
+    xb = si.fp4_grid(m, k, 0, 21)
+    wb = si.fp4_grid(n, k, -6, 22)
+    xv = xb.astype(np.uint32) << 16
+    wv = wb.astype(np.uint32) << 16
+    exact = xv.view(np.float32).astype(np.float64) @ wv.view(np.float32).astype(np.float64).T
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    p = oracle.prepare(oracle.MXFP4, xb, None)
+    q = oracle.quantize_weight(oracle.MXFP4, wb)
+    got = oracle.dual_gemm_bf16(oracle.MXFP4, p, q)
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(got, want.view(np.uint16))
+    # many of these products are not bf16 values: the rounding is exercised
+    assert (exact.astype(np.float32).view(np.uint32) & 0xFFFF).any()
+
+
 # ------------------------------------------------------------ residual add
 def _bf16_pairs(rng, n):
     """Random finite bf16 bit patterns with exponents that keep sums finite,
