@@ -400,6 +400,160 @@ __global__ __launch_bounds__(64 * W) void prep_norm_kernel(PrepArgs a) {
   store_block_at<FMT, (R >= 4)>(a, rs, b0 / 4, lane_offsets<FMT>(a, rl, lb >> 2, lb & 3), o);
 }
 
+// Few rows (decode: m <= 32, MXFP4 with RMSNorm, K <= 8192).  With one lane
+// per 32-element block a row is only K / 32 lanes: the GPU runs a few dozen
+// wavefronts, and each lane's chain of about 660 dependent instructions sets
+// the time.  Here four lanes share a block, eight consecutive k each (two 2:4
+// groups): the four lanes of a quad hold one block, and its two block maxima
+// meet through DPP quad permutes.  One workgroup per row, W wavefronts.
+// Every value comes from the same steps as in the one-lane-per-block kernels:
+// the sum of squares by the same tree (the lane's 8 squares, a xor butterfly
+// over the wavefront, the wavefronts' sums in LDS, missing leaves +0), the
+// mask by the same keys, the codes and scales by the same conversions.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t quad_max_all(uint32_t v) {
+  v = quad_max<0xB1>(v);   // quad_perm [1, 0, 3, 2]: the lane's neighbour
+  return quad_max<0x4E>(v);  // quad_perm [2, 3, 0, 1]: the other pair
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W) void prep_norm_quad_kernel(PrepArgs a) {
+  __shared__ float part[W];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t t = threadIdx.x;                 // the lane's 8-element slice of the row
+  const int64_t row = blockIdx.x;
+  const bool has = (int64_t)t < a.k / 8;          // whole quads: k % 32 == 0
+  const uint32_t vb = has ? 16u * t : 0u;         // lanes past the row end read slice 0
+  const u32x4 xv = *reinterpret_cast<const u32x4 *>(at_bytes(a.x, 2 * row * a.ld_x, vb));
+  const u32x4 gv = *reinterpret_cast<const u32x4 *>(at_bytes(a.gamma, 0, vb));
+  uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  float xf[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xf[2 * i] = bf16_lo(xw[i]);
+    xf[2 * i + 1] = bf16_hi(xw[i]);
+  }
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = xf[i] * xf[i];
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) q[i] = q[2 * i] + q[2 * i + 1];
+  }
+  const float s = wave_tree_sum(has ? q[0] : 0.0f);
+  if ((threadIdx.x & 63) == 0) part[wave] = s;
+  __syncthreads();
+  float c[W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) c[i] = part[i];
+#pragma unroll
+  for (int w = W / 2; w >= 1; w >>= 1) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) c[i] = c[2 * i] + c[2 * i + 1];
+  }
+  const float r = 1.0f / __builtin_sqrtf(row_mean(c[0], a) + a.eps);
+  if (!has) return;   // whole quads leave together
+
+  // x_n = bf16((x r) gamma)
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xw[i] = pack_bf16x2((xf[2 * i] * r) * bf16_lo(gw[i]), (xf[2 * i + 1] * r) * bf16_hi(gw[i]));
+    xf[2 * i] = bf16_lo(xw[i]);
+    xf[2 * i + 1] = bf16_hi(xw[i]);
+  }
+
+  // 2:4 mask of the lane's two groups (the keys of mask_block)
+  uint32_t top[2], umax[2], umin[2], meta = 0;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const uint32_t k0 = (__float_as_uint(xf[4 * g + 0]) & 0x7FFF0000u) | 3u;
+    const uint32_t k1 = (__float_as_uint(xf[4 * g + 1]) & 0x7FFF0000u) | 2u;
+    const uint32_t k2 = (__float_as_uint(xf[4 * g + 2]) & 0x7FFF0000u) | 1u;
+    const uint32_t k3 = (__float_as_uint(xf[4 * g + 3]) & 0x7FFF0000u);
+    const uint32_t t3 = max(max(k0, k1), k2);
+    const uint32_t md = med3_u32(k0, k1, k2);
+    top[g] = max(t3, k3);
+    const uint32_t second = max(md, min(t3, k3));
+    const uint32_t ut = top[g] & 3u, us = second & 3u;
+    umax[g] = max(ut, us);
+    umin[g] = min(ut, us);
+    meta |= (15u - (umax[g] + (umin[g] << 2))) << (4 * g);
+  }
+
+  // backbone scale from the block amax (the quad's four lanes)
+  const uint32_t am = quad_max_all(max(top[0], top[1]));
+  const int ex = (int)(am >> 23);
+  const uint32_t sb = ex > 2 ? (uint32_t)(ex - 2) : 0u;
+  const float ss = e8m0_operand(sb);
+
+  // compressed backbone: one byte per group
+  uint32_t comp = 0u;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const uint32_t z = umax[g] | (umin[g] << 16);
+    const uint32_t sel = 0x07060706u - __umul24(z, 0x0202u);
+    const bf16x2 pv = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(xw[2 * g + 1], xw[2 * g], sel));
+    comp = g == 0 ? __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(comp, pv, ss, 0)
+                  : __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(comp, pv, ss, 1);
+  }
+  // dense backbone codes: all eight, then the dropped nibbles cleared
+  uint32_t full = 0u;
+  full = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(full, __builtin_bit_cast(bf16x2, xw[0]), ss, 0);
+  full = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(full, __builtin_bit_cast(bf16x2, xw[1]), ss, 1);
+  full = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(full, __builtin_bit_cast(bf16x2, xw[2]), ss, 2);
+  full = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(full, __builtin_bit_cast(bf16x2, xw[3]), ss, 3);
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+    keep |= ((0xFu << (12u - 4u * umax[g])) | (0xFu << (12u - 4u * umin[g]))) << (16 * g);
+  const uint32_t dense = full & keep;
+
+  // residual against the quantized backbone (exact in fp32), its scale from
+  // the quad's amax
+  float res[8];
+  uint32_t ramax = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x2 d;
+    switch (i) {
+      case 0: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dense, ss, 0); break;
+      case 1: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dense, ss, 1); break;
+      case 2: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dense, ss, 2); break;
+      default: d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(dense, ss, 3); break;
+    }
+    res[2 * i] = xf[2 * i] - d[0];
+    res[2 * i + 1] = xf[2 * i + 1] - d[1];
+    ramax = max(ramax, max(__float_as_uint(res[2 * i]) & 0x7FFFFFFFu, __float_as_uint(res[2 * i + 1]) & 0x7FFFFFFFu));
+  }
+  ramax = quad_max_all(ramax);
+  const int rex = (int)(ramax >> 23);
+  const uint32_t rb = rex > 2 ? (uint32_t)(rex - 2) : 0u;
+  const float rsc = e8m0_operand(rb);
+  uint32_t rc = 0u;
+  rc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rc, res[0], res[1], rsc, 0);
+  rc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rc, res[2], res[3], rsc, 1);
+  rc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rc, res[4], res[5], rsc, 2);
+  rc = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(rc, res[6], res[7], rsc, 3);
+
+  // stores: slice t is k 8t .. 8t + 7, in 128-k step t / 16
+  const int64_t step = t >> 4;
+  const uint32_t j = t & 15u;
+  *reinterpret_cast<uint16_t *>(a.s_codes + arr_off(row, step, a.ld_sc, a.s_ksm, 32) + 2 * j) = (uint16_t)comp;
+  a.meta[arr_off(row, step, a.ld_meta, a.s_ksm, 16) + j] = (uint8_t)meta;
+  *reinterpret_cast<uint32_t *>(a.r_codes + arr_off(row, step, a.ld_rc, a.r_ksm, 64) + 4 * j) = rc;
+  if (a.s_dense) *reinterpret_cast<uint32_t *>(a.s_dense + arr_off(row, step, a.ld_sd, a.s_ksm, 64) + 4 * j) = dense;
+  if ((t & 3u) == 0u) {
+    a.s_scales[arr_off(row, step, a.ld_ss, a.s_ksm, 4) + (j >> 2)] = (uint8_t)sb;
+    a.r_scales[arr_off(row, step, a.ld_rs, a.r_ksm, 4) + (j >> 2)] = (uint8_t)rb;
+  }
+}
+
 // No normalization: blocks are independent.  A wavefront takes R rows x
 // 64 / R consecutive blocks: R = 16 (one 128-k step of 16 consecutive rows)
 // makes every store of the k-step-major layout 16 rows contiguous; R = 1 (64
@@ -605,7 +759,16 @@ hipError_t launch_prepare(const PrepArgs &args, hipStream_t s) {
     // Few rows (decode) keep one row per group, so that there
     // are more workgroups; NVFP4 too: its arithmetic, not its memory traffic,
     // sets its time, and fewer, larger workgroups were slower.
-    if (FMT == 0 && a.m >= 1024 && nblk <= 8 * 16) launch_norm_rows<FMT, 4>(a, nblk, s);
+    if (FMT == 0 && a.m <= 32 && nblk <= 256 && !a.add) {
+      // few rows: four lanes a block, one workgroup a row
+      const int64_t w = (nblk * 4 + 63) / 64;
+      const dim3 g((unsigned)a.m);
+      if (w <= 1) prep_norm_quad_kernel<1><<<g, dim3(64), 0, s>>>(a);
+      else if (w <= 2) prep_norm_quad_kernel<2><<<g, dim3(128), 0, s>>>(a);
+      else if (w <= 4) prep_norm_quad_kernel<4><<<g, dim3(256), 0, s>>>(a);
+      else if (w <= 8) prep_norm_quad_kernel<8><<<g, dim3(512), 0, s>>>(a);
+      else prep_norm_quad_kernel<16><<<g, dim3(1024), 0, s>>>(a);
+    } else if (FMT == 0 && a.m >= 1024 && nblk <= 8 * 16) launch_norm_rows<FMT, 4>(a, nblk, s);
     else if (FMT == 0 && a.m >= 512 && nblk <= 8 * 32) launch_norm_rows<FMT, 2>(a, nblk, s);
     else launch_norm_rows<FMT, 1>(a, nblk, s);
   } else {

@@ -141,6 +141,32 @@ def test_prepare_mx_degenerate_rows():
     check_prep(sq.MXFP4, xb, si.gamma(k, None), label="degenerate norm")
 
 
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (16, 224), (32, 512), (7, 992), (16, 4096),
+                                 (29, 8192), (32, 6144)])
+def test_prepare_mx_few_rows(m, k):
+    """m <= 32 rows with the norm and k <= 8192 (decode): four lanes share a
+    block (prep_norm_quad_kernel), one workgroup a row; random gain, both
+    layouts where k allows, with and without the dense backbone view."""
+    x = si.activations("student_t4", m, k, max(1, k // 100), 50.0, seed=3 * m + k)
+    g = si.gamma(k, seed=k + 5)
+    for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR) if k % 128 == 0 else (None,):
+        check_prep(sq.MXFP4, x, g, label=f"few rows m{m} k{k} layout {layout}", layout=layout)
+    check_prep(sq.MXFP4, x, g, dense=False, label=f"few rows m{m} k{k} no dense view")
+
+
+def test_prepare_mx_few_rows_match_row_groups():
+    """The same rows prepared with 32 rows (four lanes a block) and 33 rows
+    (one lane a block): identical bytes for the common rows."""
+    k = 4096
+    x = si.activations("student_t4", 33, k, 41, 50.0, seed=91)
+    g = si.gamma(k, seed=92)
+    sp33, rs33 = sq.prepare(dev16(x), dev16(g), 1e-5, dense_backbone=True)
+    sp32, rs32 = sq.prepare(dev16(x[:32]), dev16(g), 1e-5, dense_backbone=True)
+    for t33, t32, key in ((sp33, sp32, "codes"), (sp33, sp32, "meta"), (sp33, sp32, "scales"),
+                          (sp33, sp32, "dense_codes"), (rs33, rs32, "codes"), (rs33, rs32, "scales")):
+        assert np.array_equal(host(t33.row_major(key))[:32], host(t32.row_major(key))), key
+
+
 @pytest.mark.parametrize("k", [224, 4000])
 def test_prepare_mx_row_mean_ranges(k):
     """Finite rows whose sums of squares span 2^-130 .. Inf: the row mean's
@@ -155,6 +181,9 @@ def test_prepare_mx_row_mean_ranges(k):
     xb = si.f32_to_bf16_bits(np.stack(rows))
     for layout in (sq.LAYOUT_ROW_MAJOR, sq.LAYOUT_KSTEP_MAJOR) if k % 128 == 0 else (None,):
         check_prep(sq.MXFP4, xb, si.gamma(k, seed=3), label=f"row mean ranges k{k}", layout=layout)
+        # at most 32 rows a call: the few-rows kernel (four lanes a block)
+        for part in (xb[:32], xb[32:]):
+            check_prep(sq.MXFP4, part, si.gamma(k, seed=3), label=f"row mean ranges few rows k{k}", layout=layout)
 
 
 def test_prepare_padded_row_stride():
