@@ -447,6 +447,8 @@ def dual_gemm(sp: FP4Tensor, rs: FP4Tensor, w: FP4Tensor, variant: int = GEMM_AU
     bf16 (each fp32 value rounded to nearest even) when out_dtype or `out`
     is torch.bfloat16."""
     torch = _torch()
+    if out is not None and out_dtype is not None and out.dtype != out_dtype:
+        raise TypeError(f"out is {out.dtype} but out_dtype is {out_dtype}")
     if out is None:
         dt = torch.float32 if out_dtype is None else out_dtype
         if dt not in (torch.float32, torch.bfloat16):

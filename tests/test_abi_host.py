@@ -367,3 +367,13 @@ def test_binding_refuses_strided_rows():
     for bad in (x[:, ::2], x.t(), x.view(4, 8, 8)):
         with pytest.raises(ValueError):
             sq._ld(bad)
+
+
+def test_dual_gemm_output_dtype_checks():
+    """The binding refuses an output type other than fp32 or bf16, and an
+    `out` whose type contradicts out_dtype, before any library call."""
+    import torch
+    with pytest.raises(TypeError, match="out_dtype"):
+        sq.dual_gemm(None, None, None, out_dtype=torch.float16)
+    with pytest.raises(TypeError, match="out is"):
+        sq.dual_gemm(None, None, None, out=torch.empty(2, 2), out_dtype=torch.bfloat16)
