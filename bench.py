@@ -235,7 +235,42 @@ def yardsticks(w: si.Workload, torch, dev) -> dict:
             out["vendor_mxfp4_gemm_folded"] = {"error": str(e)[:200]}
     if w.fmt == si.MXFP4 and w.m > 64:
         out["mfma_fp4_random_operands"] = mfma_yardstick(torch, dev)
+    if w.m <= 64:
+        out["stream_read_gemm_bytes"] = stream_read_yardstick(torch, dev, gemm_bytes(w))
     return out
+
+
+def stream_read_yardstick(torch, dev, nbytes: float) -> dict:
+    """A kernel that only reads (csrc/yardstick.hip), over as many bytes as the
+    decode GEMM's algorithmic traffic: the rate a plain read of that size
+    reaches from HBM.  Five buffers are read in turn (more than the 256 MB
+    Infinity Cache holds), 20 launches between two events."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "sparsity_fp4_quantized_amd", "libsharq_yardstick.so"))
+    L.sharq_yardstick_stream_read.restype = ctypes.c_int
+    L.sharq_yardstick_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    size = int((nbytes + 16383) // 16384 * 16384)
+    bufs = [torch.ones(size, dtype=torch.uint8, device=dev) for _ in range(5)]
+    out = torch.empty(size // 16384, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    reps = 20
+
+    def launch(i):
+        rc = L.sharq_yardstick_stream_read(bufs[i % 5].data_ptr(), size, out.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"stream read yardstick: launch returned {rc}")
+
+    for i in range(5):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"us": round(us, 3), "bytes": size, "GB/s": round(size / (us * 1e-6) / 1e9, 1)}
 
 
 def mfma_yardstick(torch, dev) -> dict:

@@ -1,5 +1,5 @@
-// Measurement kernel behind bench.py's MFMA yardstick; it is not part of the
-// sharq ABI and the hot path never calls it.
+// Measurement kernels behind bench.py's yardsticks; they are not part of the
+// sharq ABI and the hot path never calls them.
 //
 // What does a kernel that does nothing but FP4 scaled MFMAs reach on this
 // GPU?  The published dense FP4 peak assumes the 2.4 GHz peak engine clock;
@@ -60,7 +60,37 @@ __global__ __launch_bounds__(256) void mfma_fp4_rate_kernel(float *out, long lon
   }
 }
 
+// What does a kernel that only reads reach on this GPU for a given size?
+// Each thread reads four 16-byte pieces (a wavefront four contiguous 1 KiB
+// runs), all loads issued before any is used; one word per workgroup is
+// written so that the loads are kept.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *src, unsigned *out) {
+  const size_t base = (size_t)blockIdx.x * 1024 + (threadIdx.x >> 6) * 256 + (threadIdx.x & 63);
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = src[base + 64 * i];
+  unsigned x = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  __shared__ unsigned part[4];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x ^= (unsigned)__shfl_xor((int)x, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 }  // namespace
+
+// Reads `bytes` bytes of src (a multiple of 16 KiB, 16-byte aligned) once;
+// out holds bytes / 16384 words.  Returns the launch's hipError_t.
+extern "C" int sharq_yardstick_stream_read(const void *src, size_t bytes, unsigned *out, void *stream) {
+  if (src == nullptr || out == nullptr || bytes == 0 || bytes % 16384 != 0 || (uintptr_t)src % 16 != 0)
+    return (int)hipErrorInvalidValue;
+  stream_read_kernel<<<dim3((unsigned)(bytes / 16384)), dim3(256), 0, (hipStream_t)stream>>>(
+      static_cast<const uint4 *>(src), out);
+  return (int)hipGetLastError();
+}
 
 // workgroups of 256 threads; out holds workgroups * 256 floats, ticks
 // 2 * workgroups int64 (per workgroup: 100 MHz ticks, engine clock ticks).

@@ -35,6 +35,11 @@ def test_yardstick_library_loads():
     # invalid arguments are refused before any launch
     L.sharq_yardstick_mfma_fp4.restype = ctypes.c_int
     assert L.sharq_yardstick_mfma_fp4(0, 1, 1, None, None, None) != 0
+    assert hasattr(L, "sharq_yardstick_stream_read")
+    L.sharq_yardstick_stream_read.restype = ctypes.c_int
+    L.sharq_yardstick_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.sharq_yardstick_stream_read(None, 16384, None, None) != 0
+    assert L.sharq_yardstick_stream_read(1 << 20, 1000, 1 << 20, None) != 0
 
 
 def test_status_strings_and_sizes():
