@@ -767,6 +767,21 @@ def test_dual_gemm_mx_large_tile_configs(m, n, k):
             check_gemm(y[rows, cols], ref, yabs, k, f"test_dual_gemm_mx_large_tile_configs {layout} {v}")
 
 
+@pytest.mark.parametrize("m,n,k", [(16, 16384 + 64 + 5, 256), (17, 16384 + 64 + 5, 384), (32, 20000, 128),
+                                   (1, 16448, 256), (9, 32768 + 128 + 3, 256), (32, 32768 + 128, 128)])
+def test_dual_gemm_decode_kernel(m, n, k):
+    """The decode kernel (m <= 32, dense view, at least 128 column tiles of
+    128): one A chunk (m <= 16) or two, ragged last tiles, both layouts.
+    Every output."""
+    x, w, g, p, q = _gemm_case(m, n, k, seed=m + n + k)
+    ref, yabs = oracle.dual_gemm_bound(sq.MXFP4, p, q)
+    for layout in (sq.LAYOUT_KSTEP_MAJOR, sq.LAYOUT_ROW_MAJOR):
+        sp, rs = to_dev_prep(sq.MXFP4, p, layout)
+        wq = to_dev_weight(sq.MXFP4, q, layout)
+        y = host(sq.dual_gemm(sp, rs, wq, variant=sq.GEMM_DENSE_EXPANDED))
+        check_gemm(y, ref, yabs, k, f"test_dual_gemm_decode_kernel {layout}")
+
+
 def test_dual_gemm_variants_bitwise_equal():
     x, w, g, p, q = _gemm_case(200, 300, 512, seed=3)
     sp, rs = to_dev_prep(sq.MXFP4, p, sq.LAYOUT_ROW_MAJOR)
