@@ -108,14 +108,6 @@ __device__ __forceinline__ void xcd_tile(uint32_t id, uint32_t gm, uint32_t gn, 
   tn = within / rows;
 }
 
-// The epilogue of a TBM x TBN tile (wavefront (wm, wn): 64 rows x TBN / 2
-// columns, 2 x TBN / 64 accumulators of 32 x 32; lane l holds column l % 32,
-// rows 8 (r / 4) + 4 h + r % 4), each value times `scale`, non-temporal.
-// A tile inside Y (the common case) stores through one wavefront-uniform
-// base per value row and a 32-bit lane offset, with no bounds checks; edge
-// tiles check every row and column.  (Per-value 64-bit addresses and checks
-// were about 12 VALU instructions a value, 96 values a lane: as long as the
-// main loop, and with every tile in one round they ran after the MFMAs.)
 // fp32 -> bf16, round to nearest even, two values at a time (lo in bits 0-15)
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   const f32x2 f = {lo, hi};
@@ -136,7 +128,51 @@ __device__ __forceinline__ void put_y(float *y, uint16_t *y16, int64_t off, floa
   }
 }
 
-// The bf16 form of store_tile below: each value rounded to bf16 (nearest
+// The fp32 epilogue of a TBM x TBN tile (wavefront (wm, wn): 64 rows x TBN / 2
+// columns, 2 x TBN / 64 accumulators of 32 x 32; lane l holds column l % 32,
+// rows 8 (r / 4) + 4 h + r % 4), each value times `scale`, non-temporal.
+// A tile inside Y (the common case) stores through one wavefront-uniform
+// base per value row and a 32-bit lane offset, with no bounds checks; edge
+// tiles check every row and column.  (Per-value 64-bit addresses and checks
+// were about 12 VALU instructions a value, 96 values a lane: as long as the
+// main loop, and with every tile in one round they ran after the MFMAs.)
+template <int TBM, int TBN>
+__device__ __forceinline__ void store_tile(float *y, int64_t ld, int64_t m0, int64_t n0, int64_t m_end,
+                                           int64_t n, int wm, int wn, int h, int li,
+                                           const v16f (&acc)[2][TBN / 64], float scale) {
+  constexpr int TN = TBN / 64;
+  const bool inside = m0 + TBM <= m_end && n0 + TBN <= n && ld < ((int64_t)1 << 22);
+  if (inside) {
+    float *tile = y + m0 * ld + n0;
+    const uint32_t lane_off = ((uint32_t)(wm * 64 + 4 * h) * (uint32_t)ld + (uint32_t)(wn * (TBN / 2) + li)) * 4u;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // rows it 32 + 8 (r / 4) + r % 4 of the wavefront's first row: uniform
+        char *row = reinterpret_cast<char *>(tile + (int64_t)(it * 32 + 8 * (r >> 2) + (r & 3)) * ld);
+#pragma unroll
+        for (int jt = 0; jt < TN; ++jt)
+          __builtin_nontemporal_store(acc[it][jt][r] * scale,
+                                      reinterpret_cast<float *>(row + lane_off + 128u * jt));
+      }
+    return;
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < TN; ++jt) {
+      const int64_t col = n0 + wn * (TBN / 2) + jt * 32 + li;
+      if (col >= n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < m_end) __builtin_nontemporal_store(acc[it][jt][r] * scale, &y[row * ld + col]);
+      }
+    }
+}
+
+// The bf16 form of store_tile above: each value rounded to bf16 (nearest
 // even) from the fp32 value store_tile would write.  Values of rows r and
 // r + 1 (r even) convert in one instruction; each row of a wavefront's store
 // is 32 lanes x 2 bytes, one aligned 64-byte piece when Y's rows are.
@@ -176,42 +212,6 @@ __device__ __forceinline__ void store_tile_bf16(uint16_t *y, int64_t ld, int64_t
         const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < m_end)
           __builtin_nontemporal_store((uint16_t)bf16_pair(acc[it][jt][r] * scale, 0.0f), &y[row * ld + col]);
-      }
-    }
-}
-
-template <int TBM, int TBN>
-__device__ __forceinline__ void store_tile(float *y, int64_t ld, int64_t m0, int64_t n0, int64_t m_end,
-                                           int64_t n, int wm, int wn, int h, int li,
-                                           const v16f (&acc)[2][TBN / 64], float scale) {
-  constexpr int TN = TBN / 64;
-  const bool inside = m0 + TBM <= m_end && n0 + TBN <= n && ld < ((int64_t)1 << 22);
-  if (inside) {
-    float *tile = y + m0 * ld + n0;
-    const uint32_t lane_off = ((uint32_t)(wm * 64 + 4 * h) * (uint32_t)ld + (uint32_t)(wn * (TBN / 2) + li)) * 4u;
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // rows it 32 + 8 (r / 4) + r % 4 of the wavefront's first row: uniform
-        char *row = reinterpret_cast<char *>(tile + (int64_t)(it * 32 + 8 * (r >> 2) + (r & 3)) * ld);
-#pragma unroll
-        for (int jt = 0; jt < TN; ++jt)
-          __builtin_nontemporal_store(acc[it][jt][r] * scale,
-                                      reinterpret_cast<float *>(row + lane_off + 128u * jt));
-      }
-    return;
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int jt = 0; jt < TN; ++jt) {
-      const int64_t col = n0 + wn * (TBN / 2) + jt * 32 + li;
-      if (col >= n) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + it * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < m_end) __builtin_nontemporal_store(acc[it][jt][r] * scale, &y[row * ld + col]);
       }
     }
 }
