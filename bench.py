@@ -1014,7 +1014,11 @@ def main():
             roofline["peak_at_that_sclk"] = round(peak * sclk / 2400.0, 1)
             roofline["frac_at_that_sclk"] = round(roofline["achieved"] / (peak * sclk / 2400.0), 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x_np, W_np, g_np)
+        cb = cpu_baseline(w, x_np, W_np, g_np)
+        # the step's rate on the GPU over the oracle's on every host thread
+        if cb.get("value"):
+            cb["gpu_over_cpu"] = round(value / cb["value"], 1)
+        out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
 
